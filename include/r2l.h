@@ -1,0 +1,195 @@
+/*
+ * r2l.h -- C ABI of libr2l.so, an MI355X (gfx950) implementation of the
+ * R2LM ReverseMambaLayer forward.
+ *
+ * Source of the operation: "Bifocal Diffusion Language Models: Asymmetric
+ * Bidirectional Context for Parallel Generation" (arXiv 2606.27732),
+ * §3.4 "R2LM Architecture" (the four steps of the R2L stream: flip, Mamba-1
+ * selective-scan block, unflip + stream-local LayerNorm, tanh(s)-gated
+ * residual) and §4.1 "Experimental Setup" (d_state 16, d_conv 4, expand 2,
+ * one hook after every 4th decoder layer).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Sequences are packed back to back: token t of the packed array belongs
+ *    to sequence q when cu_seqlens[q] <= t < cu_seqlens[q+1].  A dense
+ *    [B, L] batch is cu_seqlens = {0, L, 2L, ..., BL}.  Zero-length
+ *    sequences are allowed.  The "flip" of the pages is never materialised:
+ *    every kernel works in the original token order with anti-causal
+ *    indexing (a token sees itself and the tokens to its right, up to its
+ *    sequence's end).
+ *  - All pointers except the r2l_dims / r2l_weights structs themselves and
+ *    the optional host copy in r2l_check_cu_seqlens are DEVICE pointers on
+ *    the current HIP device.  Matrices are row-major; weights use the
+ *    nn.Linear [out_features, in_features] layout.
+ *  - Activation tensors and the weights listed as "act" use the activation
+ *    dtype (R2L_F32 or R2L_BF16).  Scan state, dt, B, C and all
+ *    accumulations are fp32 in both cases.
+ *  - Ownership: the caller allocates and owns every buffer (weights,
+ *    activations, cu_seqlens, workspace).  The library allocates no device
+ *    memory and keeps no pointer after a call returns.
+ *  - Execution: work is enqueued on `stream` (a hipStream_t; NULL = the
+ *    null stream) without any host synchronisation.  A fault during
+ *    execution surfaces at the caller's next synchronisation.
+ *  - Errors: every entry point validates its arguments before launching
+ *    anything and returns one of the R2L_* status codes; nothing is
+ *    launched on error.  cu_seqlens lives on the device and is not read by
+ *    the host: the kernels clamp every offset into [0, n_tokens] and treat a
+ *    decreasing entry as an empty sequence, so a malformed cu_seqlens gives
+ *    wrong numbers but never an out-of-bounds access.  Callers that hold a
+ *    host copy can validate it with r2l_check_cu_seqlens first.
+ *  - Threading: calls are reentrant; concurrent calls must use distinct
+ *    workspaces and outputs.
+ *  - Supported shapes: d_state == 16, d_conv == 4, d_model and d_inner
+ *    multiples of 64 with d_model <= 8192, 1 <= dt_rank <= 1024,
+ *    nseq >= 1, n_tokens >= 0 (all int32-indexable).
+ */
+#ifndef R2L_H
+#define R2L_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define R2L_VERSION 100
+
+/* Status codes. */
+enum {
+  R2L_OK = 0,
+  R2L_ERR_INVALID_ARG = -1,  /* null pointer, bad size, malformed host cu_seqlens */
+  R2L_ERR_UNSUPPORTED = -2,  /* shape or dtype outside the supported set */
+  R2L_ERR_WORKSPACE = -3,    /* workspace missing or smaller than the query */
+  R2L_ERR_HIP = -4           /* a HIP launch or runtime call failed */
+};
+
+/* Flags for r2l_layer_fwd. */
+#define R2L_FLAG_NO_LN 0x1u  /* skip the stream LayerNorm: r = unflipped Mamba output */
+
+/* LayerNorm epsilon used by r2l_layer_fwd (biased variance over d_model). */
+#define R2L_LN_EPS 1e-5f
+
+typedef enum { R2L_F32 = 0, R2L_BF16 = 1 } r2l_dtype;
+
+/* Layer dimensions: D = d_model, E = d_inner (expand * D), N = d_state,
+ * R = dt_rank, K = d_conv. */
+typedef struct {
+  int32_t d_model, d_inner, d_state, dt_rank, d_conv;
+} r2l_dims;
+
+/* One hook's parameters (device pointers).  "act" = activation dtype. */
+typedef struct {
+  const void* in_proj_w;   /* act  [2E, D]: rows [0,E) give x, rows [E,2E) give z */
+  const void* conv_w;      /* act  [E, K]: depthwise taps in causal order of the flipped sequence */
+  const void* conv_b;      /* act  [E] */
+  const void* x_proj_w;    /* act  [R+2N, E]: rows [0,R) delta, [R,R+N) B, [R+N,R+2N) C */
+  const void* dt_proj_w;   /* act  [E, R] */
+  const void* out_proj_w;  /* act  [D, E] */
+  const float* dt_proj_b;  /* f32  [E]   (added before softplus) */
+  const float* A_log;      /* f32  [E, N] (A = -exp(A_log)) */
+  const float* Dskip;      /* f32  [E] */
+  const float* ln_w;       /* f32  [D]   LayerNorm gamma */
+  const float* ln_b;       /* f32  [D]   LayerNorm beta */
+  const float* s;          /* f32  [1]   scalar gate s (device) */
+} r2l_weights;
+
+/* ------------------------------------------------------------------------
+ * r2l_layer_fwd -- one ReverseMambaLayer hook (§3.4 steps 1-4):
+ *   h_out = h_in + tanh(s) * LN(flip(Mamba1(flip(h_in))))   per sequence.
+ * h_in, h_out: act [n_tokens, D]; h_out may equal h_in (in place).
+ * When tanh(s) == 0 the output is a bit-exact copy of h_in (§3.5: a zero
+ * gate leaves the causal baseline unchanged).
+ * branch_out: optional f32 [n_tokens, D] receiving the branch r (the LN
+ * output, or the raw Mamba output under R2L_FLAG_NO_LN); NULL to skip.
+ * max_seqlen: an upper bound on the longest sequence (used to plan the
+ * scan's time chunks; correctness does not depend on it).
+ * workspace: device buffer of at least r2l_layer_workspace_bytes(...)
+ * bytes, 256-byte aligned; its contents on entry are ignored.
+ * ---------------------------------------------------------------------- */
+size_t r2l_layer_workspace_bytes(const r2l_dims* dims, r2l_dtype act, int64_t n_tokens,
+                                 int32_t nseq, int32_t max_seqlen);
+
+int r2l_layer_fwd(const r2l_dims* dims, r2l_dtype act, uint32_t flags, const r2l_weights* w,
+                  const void* h_in, void* h_out, const int32_t* cu_seqlens, int32_t nseq,
+                  int64_t n_tokens, int32_t max_seqlen, void* workspace, size_t workspace_bytes,
+                  float* branch_out, void* stream);
+
+/* ------------------------------------------------------------------------
+ * r2l_conv_fwd -- the anti-causal depthwise conv1d + bias + SiLU of the
+ * flipped Mamba block (§3.4 steps 1-2), optionally followed by x_proj:
+ *   u[t,e]  = SiLU(conv_b[e] + sum_{j=0}^{K-1} conv_w[e,K-1-j] * x[t+j,e]),
+ *             x past the end of t's sequence taken as 0;
+ *   xdbl[t] = x_proj_w @ u[t]            (only when x_proj_w != NULL).
+ * x: act [n_tokens, E] with row stride ld_x elements (ld_x >= E; e.g. the
+ * x half of an in_proj output has ld_x = 2E).  u_out: act [n_tokens, E]
+ * (contiguous) or NULL when only xdbl is wanted; xdbl_out: f32
+ * [n_tokens, R+2N] (contiguous), required iff x_proj_w != NULL.  At least
+ * one output must be requested.  Needs no workspace.
+ * ---------------------------------------------------------------------- */
+int r2l_conv_fwd(const r2l_dims* dims, r2l_dtype act, const void* x, int64_t ld_x,
+                 const void* conv_w, const void* conv_b, const void* x_proj_w, void* u_out,
+                 float* xdbl_out, const int32_t* cu_seqlens, int32_t nseq, int64_t n_tokens,
+                 int32_t max_seqlen, void* stream);
+
+/* ------------------------------------------------------------------------
+ * r2l_scan_fwd -- the selective scan run right to left per sequence (the
+ * scan of §3.4 step 2 seen from the original token order), with the skip
+ * term and the SiLU(z) gate:
+ *   h_t = exp(dt_t * A) (.) h_{t+1} + (dt_t * u_t) (x) B_t,  h = 0 past the
+ *   sequence end, A = -exp(A_log);
+ *   y_t = (h_t . C_t + Dskip (.) u_t) * SiLU(z_t).
+ * u: act [n_tokens, E] (row stride ld_u); dt: f32 [n_tokens, E] (row
+ * stride ld_dt), already softplus-ed; B, C: f32 [n_tokens, N] (row stride
+ * ld_bc each); Dskip: f32 [E] or NULL (no skip term); z: act (row stride
+ * ld_z) or NULL (no gate); y_out: act [n_tokens, E] contiguous.
+ * workspace: r2l_scan_workspace_bytes(...) bytes (may be 0 bytes; then
+ * NULL is accepted).
+ * ---------------------------------------------------------------------- */
+size_t r2l_scan_workspace_bytes(const r2l_dims* dims, int64_t n_tokens, int32_t nseq,
+                                int32_t max_seqlen);
+
+int r2l_scan_fwd(const r2l_dims* dims, r2l_dtype act, const void* u, int64_t ld_u,
+                 const float* dt, int64_t ld_dt, const float* A_log, const float* B,
+                 const float* C, int64_t ld_bc, const float* Dskip, const void* z, int64_t ld_z,
+                 void* y_out, const int32_t* cu_seqlens, int32_t nseq, int64_t n_tokens,
+                 int32_t max_seqlen, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * r2l_gemm_nt -- the dense projection used by the layer (in_proj, out_proj):
+ *   C[m, n] = sum_k A[m, k] * B[n, k]      (C = A @ B^T, fp32 accumulate).
+ * A: act [M, K] (row stride lda); B: act [N, K] (row stride ldb);
+ * C: [M, N] (row stride ldc) in the activation dtype (out_f32 == 0) or in
+ * f32 (out_f32 != 0).  bf16 runs on the MFMA matrix cores.  K must be a
+ * multiple of 8 and lda/ldb multiples of 8 for bf16.
+ * ---------------------------------------------------------------------- */
+int r2l_gemm_nt(r2l_dtype act, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
+                const void* B, int64_t ldb, void* C, int64_t ldc, int out_f32, void* stream);
+
+/* Host-side validation of a host copy of cu_seqlens: cu[0] == 0,
+ * non-decreasing, cu[nseq] == n_tokens, every length <= max_seqlen.
+ * Returns R2L_OK or R2L_ERR_INVALID_ARG.  Touches no device. */
+int r2l_check_cu_seqlens(const int32_t* cu_seqlens_host, int32_t nseq, int64_t n_tokens,
+                         int32_t max_seqlen);
+
+/* ------------------------------------------------------------------------
+ * Per-kernel timing (process-wide, for benchmarking).  While enabled, each
+ * kernel launched by the library is bracketed by a pair of HIP events on
+ * its own stream.  r2l_timing_read synchronises on those events, adds each
+ * kernel's elapsed time to a per-kernel-name total and clears the event
+ * list; it returns the number of distinct kernel names (at most max_names
+ * are written).  names[i] point to static strings.
+ * ---------------------------------------------------------------------- */
+int r2l_timing_enable(int enable);
+int r2l_timing_read(const char** names, double* total_ms, int64_t* counts, int max_names);
+int r2l_timing_reset(void);
+
+const char* r2l_status_string(int status);
+int r2l_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* R2L_H */

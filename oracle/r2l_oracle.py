@@ -132,7 +132,7 @@ def mamba_block(F, W, return_parts=False):
     output is [delta (R) | B (N) | C (N)].
     """
     f = lambda k: np.asarray(W[k], np.float64)  # noqa: E731
-    F = np.asarray(F, np.float64)
+    F = np.ascontiguousarray(F, np.float64)     # (a flipped view would bypass BLAS)
     E = f("conv_w").shape[0]
     N = f("A_log").shape[1]
     R = f("dt_proj_w").shape[1]

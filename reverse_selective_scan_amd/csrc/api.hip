@@ -1,0 +1,447 @@
+// C ABI of libr2l.so: argument validation, workspace layout, the launch
+// sequence of one ReverseMambaLayer hook, and optional per-kernel timing.
+// The operations are those of "Bifocal Diffusion Language Models", §3.4
+// (R2L stream steps 1-4); shapes per §4.1.
+#include <cstdint>
+#include <cstring>
+#include <mutex>
+#include <vector>
+
+#include "../../include/r2l.h"
+#include "kernels.h"
+
+using namespace r2l;
+
+namespace {
+
+// ---------------------------------------------------------------------------
+// per-kernel timing
+// ---------------------------------------------------------------------------
+struct TimingRec {
+  const char* name;
+  hipEvent_t a, b;
+};
+struct TimingState {
+  std::mutex mu;
+  bool enabled = false;
+  std::vector<TimingRec> recs;
+  std::vector<hipEvent_t> pool;
+  std::vector<const char*> names;
+  std::vector<double> totals;
+  std::vector<int64_t> counts;
+};
+TimingState& timing() {
+  static TimingState* t = new TimingState();  // never destroyed: safe at process exit
+  return *t;
+}
+hipEvent_t take_event(TimingState& t) {
+  if (!t.pool.empty()) {
+    hipEvent_t e = t.pool.back();
+    t.pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+template <typename F>
+int run_kernel(const char* name, hipStream_t st, F&& launch) {
+  TimingState& t = timing();
+  hipEvent_t ea = nullptr, eb = nullptr;
+  bool en;
+  {
+    std::lock_guard<std::mutex> g(t.mu);
+    en = t.enabled;
+    if (en) {
+      ea = take_event(t);
+      eb = take_event(t);
+      if (!ea || !eb) en = false;
+    }
+  }
+  if (en && hipEventRecord(ea, st) != hipSuccess) en = false;
+  hipError_t err = launch();
+  if (en) {
+    const bool ok = hipEventRecord(eb, st) == hipSuccess;
+    std::lock_guard<std::mutex> g(t.mu);
+    if (ok) {
+      t.recs.push_back({name, ea, eb});
+    } else {
+      t.pool.push_back(ea);
+      t.pool.push_back(eb);
+    }
+  } else if (ea || eb) {
+    std::lock_guard<std::mutex> g(t.mu);
+    if (ea) t.pool.push_back(ea);
+    if (eb) t.pool.push_back(eb);
+  }
+  return err == hipSuccess ? R2L_OK : R2L_ERR_HIP;
+}
+
+#define R2L_RUN(name, st, expr)                                 \
+  do {                                                          \
+    int _rc = run_kernel(name, st, [&]() { return (expr); });   \
+    if (_rc != R2L_OK) return _rc;                              \
+  } while (0)
+
+// ---------------------------------------------------------------------------
+// validation helpers
+// ---------------------------------------------------------------------------
+constexpr int kTB = 32;
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) & ~(kAlign - 1); }
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+int check_dims(const r2l_dims* d) {
+  if (!d) return R2L_ERR_INVALID_ARG;
+  if (d->d_model <= 0 || d->d_inner <= 0 || d->d_state <= 0 || d->dt_rank <= 0 || d->d_conv <= 0)
+    return R2L_ERR_INVALID_ARG;
+  if (d->d_state != 16 || d->d_conv != 4) return R2L_ERR_UNSUPPORTED;
+  if (d->d_model % 64 || d->d_inner % 64 || d->d_model > 8192 || d->d_inner > (1 << 20))
+    return R2L_ERR_UNSUPPORTED;
+  if (d->dt_rank > 1024) return R2L_ERR_UNSUPPORTED;
+  return R2L_OK;
+}
+
+int check_tokens(r2l_dtype act, int64_t n_tokens, int32_t nseq, int32_t max_seqlen) {
+  if (act != R2L_F32 && act != R2L_BF16) return R2L_ERR_UNSUPPORTED;
+  if (n_tokens < 0 || nseq < 1 || max_seqlen < 0) return R2L_ERR_INVALID_ARG;
+  if (n_tokens > INT32_MAX / 2 || nseq > (1 << 24)) return R2L_ERR_UNSUPPORTED;
+  return R2L_OK;
+}
+
+// ---------------------------------------------------------------------------
+// scan planning: time-chunk length so that enough blocks exist
+// ---------------------------------------------------------------------------
+struct ScanPlan {
+  int Lc, max_chunks;
+  bool summary;
+  size_t off_cu, off_chunks, off_n, off_sumS, off_sumP, total;
+};
+
+ScanPlan plan_scan(int E, int64_t T, int32_t nseq, int32_t max_seqlen, size_t base) {
+  ScanPlan p{};
+  const int64_t NB = E / 64;
+  const int64_t target = 1024;  // blocks wanted in flight (256 CUs)
+  int64_t ms = max_seqlen < 1 ? 1 : max_seqlen;
+  if (T > 0 && ms > T) ms = T;
+  int64_t Lc = ms;
+  if ((int64_t)nseq * NB < target && T > 0) {
+    int64_t want = (T * NB + target - 1) / target;
+    want = ((want + kTB - 1) / kTB) * kTB;
+    if (want < 4 * kTB) want = 4 * kTB;
+    if (want < Lc) Lc = want;
+  }
+  p.Lc = (int)Lc;
+  p.max_chunks = (int)(nseq + (T + Lc - 1) / Lc);
+  if (p.max_chunks < 1) p.max_chunks = 1;
+  p.summary = Lc < T;  // some sequence may span several chunks
+  size_t off = base;
+  p.off_cu = off;      off = align_up(off + sizeof(int32_t) * ((size_t)nseq + 1));
+  p.off_chunks = off;  off = align_up(off + sizeof(ChunkDesc) * (size_t)p.max_chunks);
+  p.off_n = off;       off = align_up(off + sizeof(int32_t));
+  const size_t sums = p.summary ? sizeof(float) * 16 * (size_t)E * (size_t)p.max_chunks : 0;
+  p.off_sumS = off;    off = align_up(off + sums);
+  p.off_sumP = off;    off = align_up(off + sums);
+  p.total = off;
+  return p;
+}
+
+struct LayerPlan {
+  size_t off_xz, off_xdbl, off_u, off_y;
+  bool need_u;
+  ScanPlan scan;
+  size_t total;
+};
+
+LayerPlan plan_layer(const r2l_dims* d, r2l_dtype act, int64_t T, int32_t nseq, int32_t max_seqlen) {
+  LayerPlan p{};
+  const size_t sa = act == R2L_BF16 ? 2 : 4;
+  const size_t D = d->d_model, E = d->d_inner, P = d->dt_rank + 2 * d->d_state;
+  const size_t Tz = (size_t)T;
+  size_t off = 0;
+  size_t xz = Tz * 2 * E * sa, o = Tz * D * 4;  // out_proj's fp32 output reuses xz
+  p.off_xz = off;   off = align_up(off + (xz > o ? xz : o));
+  p.off_xdbl = off; off = align_up(off + Tz * P * 4);
+  p.need_u = act == R2L_F32 || P > 256;
+  p.off_u = off;    off = align_up(off + (p.need_u ? Tz * E * sa : 0));
+  p.off_y = off;    off = align_up(off + Tz * E * sa);
+  p.scan = plan_scan((int)E, T, nseq, max_seqlen, off);
+  p.total = p.scan.total;
+  return p;
+}
+
+template <typename Tp>
+Tp* at(void* ws, size_t off) {
+  return (Tp*)((char*)ws + off);
+}
+
+template <typename T>
+int run_scan(const ScanArgs& a, const ScanPlan& sp, bool fused, const int32_t* cu, int nseq,
+             int64_t Tn, int32_t* cu_clean, ChunkDesc* chunks, int32_t* nch, hipStream_t st) {
+  R2L_RUN("plan_chunks", st, plan_chunks(cu, nseq, (int)Tn, sp.Lc, sp.max_chunks, cu_clean, chunks, nch, st));
+  if (sp.summary) R2L_RUN("scan_summary", st, scan_summary<T>(a, fused, st));
+  R2L_RUN("scan_main", st, scan_main<T>(a, fused, st));
+  return R2L_OK;
+}
+
+}  // namespace
+
+// ===========================================================================
+extern "C" {
+
+const char* r2l_status_string(int status) {
+  switch (status) {
+    case R2L_OK: return "ok";
+    case R2L_ERR_INVALID_ARG: return "invalid argument";
+    case R2L_ERR_UNSUPPORTED: return "unsupported shape or dtype";
+    case R2L_ERR_WORKSPACE: return "workspace missing or too small";
+    case R2L_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+int r2l_version(void) { return R2L_VERSION; }
+
+int r2l_check_cu_seqlens(const int32_t* cu, int32_t nseq, int64_t n_tokens, int32_t max_seqlen) {
+  if (!cu || nseq < 1 || n_tokens < 0) return R2L_ERR_INVALID_ARG;
+  if (cu[0] != 0 || (int64_t)cu[nseq] != n_tokens) return R2L_ERR_INVALID_ARG;
+  for (int32_t q = 0; q < nseq; ++q) {
+    const int64_t len = (int64_t)cu[q + 1] - cu[q];
+    if (len < 0 || len > max_seqlen) return R2L_ERR_INVALID_ARG;
+  }
+  return R2L_OK;
+}
+
+size_t r2l_layer_workspace_bytes(const r2l_dims* dims, r2l_dtype act, int64_t n_tokens,
+                                 int32_t nseq, int32_t max_seqlen) {
+  if (check_dims(dims) != R2L_OK || check_tokens(act, n_tokens, nseq, max_seqlen) != R2L_OK)
+    return 0;
+  return plan_layer(dims, act, n_tokens, nseq, max_seqlen).total;
+}
+
+size_t r2l_scan_workspace_bytes(const r2l_dims* dims, int64_t n_tokens, int32_t nseq,
+                                int32_t max_seqlen) {
+  if (check_dims(dims) != R2L_OK || check_tokens(R2L_F32, n_tokens, nseq, max_seqlen) != R2L_OK)
+    return 0;
+  return plan_scan(dims->d_inner, n_tokens, nseq, max_seqlen, 0).total;
+}
+
+int r2l_layer_fwd(const r2l_dims* d, r2l_dtype act, uint32_t flags, const r2l_weights* w,
+                  const void* h_in, void* h_out, const int32_t* cu_seqlens, int32_t nseq,
+                  int64_t n_tokens, int32_t max_seqlen, void* workspace, size_t workspace_bytes,
+                  float* branch_out, void* stream) {
+  int rc = check_dims(d);
+  if (rc != R2L_OK) return rc;
+  if ((rc = check_tokens(act, n_tokens, nseq, max_seqlen)) != R2L_OK) return rc;
+  if (flags & ~R2L_FLAG_NO_LN) return R2L_ERR_INVALID_ARG;
+  if (!w || !h_in || !h_out || !cu_seqlens) return R2L_ERR_INVALID_ARG;
+  if (!w->in_proj_w || !w->conv_w || !w->conv_b || !w->x_proj_w || !w->dt_proj_w ||
+      !w->out_proj_w || !w->dt_proj_b || !w->A_log || !w->Dskip || !w->s)
+    return R2L_ERR_INVALID_ARG;
+  const bool no_ln = flags & R2L_FLAG_NO_LN;
+  if (!no_ln && (!w->ln_w || !w->ln_b)) return R2L_ERR_INVALID_ARG;
+  if (act == R2L_BF16) {
+    const void* ptrs[] = {h_in, w->in_proj_w, w->conv_w, w->conv_b, w->x_proj_w, w->dt_proj_w, w->out_proj_w};
+    for (const void* p : ptrs)
+      if (!aligned16(p)) return R2L_ERR_INVALID_ARG;
+  }
+  const LayerPlan lp = plan_layer(d, act, n_tokens, nseq, max_seqlen);
+  if (!workspace || workspace_bytes < lp.total) return R2L_ERR_WORKSPACE;
+  if (((uintptr_t)workspace & (kAlign - 1)) != 0) return R2L_ERR_INVALID_ARG;
+  if (n_tokens == 0) return R2L_OK;
+
+  hipStream_t st = (hipStream_t)stream;
+  const int T = (int)n_tokens, D = d->d_model, E = d->d_inner, R = d->dt_rank;
+  const int P = R + 2 * d->d_state;
+  const ScanPlan& sp = lp.scan;
+  int32_t* cu_clean = at<int32_t>(workspace, sp.off_cu);
+  ChunkDesc* chunks = at<ChunkDesc>(workspace, sp.off_chunks);
+  int32_t* nch = at<int32_t>(workspace, sp.off_n);
+  float* xdbl = at<float>(workspace, lp.off_xdbl);
+  float* o = at<float>(workspace, lp.off_xz);  // aliases xz, which is dead by then
+
+  ScanArgs a{};
+  a.T = T; a.E = E; a.R = R; a.ldp = P;
+  a.ld_x = 2L * E; a.ld_z = 2L * E;
+  a.xdbl = xdbl;
+  a.conv_w = w->conv_w; a.conv_b = w->conv_b;
+  a.dt_w = w->dt_proj_w; a.dt_b = w->dt_proj_b;
+  a.A_log = w->A_log; a.Dskip = w->Dskip;
+  a.chunks = chunks; a.n_chunks = nch; a.max_chunks = sp.max_chunks;
+  a.sumS = at<float>(workspace, sp.off_sumS);
+  a.sumP = at<float>(workspace, sp.off_sumP);
+
+  // chunk table first: the conv kernel also reads the sanitised offsets
+  R2L_RUN("plan_chunks", st, plan_chunks(cu_seqlens, nseq, T, sp.Lc, sp.max_chunks, cu_clean, chunks, nch, st));
+
+  if (act == R2L_BF16) {
+    bf16* xz = at<bf16>(workspace, lp.off_xz);
+    bf16* y = at<bf16>(workspace, lp.off_y);
+    R2L_RUN("in_proj_gemm", st, gemm_bf16_nt(T, 2 * E, D, (const bf16*)h_in, D, (const bf16*)w->in_proj_w, D, xz, 2L * E, false, st));
+    if (!lp.need_u) {
+      R2L_RUN("conv_xproj", st, conv_xproj_bf16(T, E, P, xz, 2L * E, (const bf16*)w->conv_w, (const bf16*)w->conv_b, (const bf16*)w->x_proj_w, nullptr, xdbl, cu_clean, nseq, st));
+    } else {
+      bf16* u = at<bf16>(workspace, lp.off_u);
+      R2L_RUN("conv_silu", st, conv_silu<bf16>(T, E, xz, 2L * E, (const bf16*)w->conv_w, (const bf16*)w->conv_b, u, cu_clean, nseq, st));
+      // x_proj with a bf16 output would lose precision; run it through the fp32-out MFMA GEMM
+      R2L_RUN("x_proj_gemm", st, gemm_bf16_nt(T, P, E, u, E, (const bf16*)w->x_proj_w, E, xdbl, P, true, st));
+    }
+    a.x = xz; a.z = xz + E; a.y = y;
+    if (sp.summary) R2L_RUN("scan_summary", st, scan_summary<bf16>(a, true, st));
+    R2L_RUN("scan_main", st, scan_main<bf16>(a, true, st));
+    R2L_RUN("out_proj_gemm", st, gemm_bf16_nt(T, D, E, y, E, (const bf16*)w->out_proj_w, E, o, D, true, st));
+    R2L_RUN("ln_gate", st, ln_gate<bf16>(T, D, o, (const bf16*)h_in, (bf16*)h_out, w->ln_w, w->ln_b, w->s, branch_out, no_ln, R2L_LN_EPS, st));
+  } else {
+    float* xz = at<float>(workspace, lp.off_xz);
+    float* u = at<float>(workspace, lp.off_u);
+    float* y = at<float>(workspace, lp.off_y);
+    R2L_RUN("in_proj_gemm", st, gemm_f32_nt(T, 2 * E, D, (const float*)h_in, D, (const float*)w->in_proj_w, D, xz, 2L * E, st));
+    R2L_RUN("conv_silu", st, conv_silu<float>(T, E, xz, 2L * E, (const float*)w->conv_w, (const float*)w->conv_b, u, cu_clean, nseq, st));
+    R2L_RUN("x_proj_gemm", st, gemm_f32_nt(T, P, E, u, E, (const float*)w->x_proj_w, E, xdbl, P, st));
+    a.x = xz; a.z = xz + E; a.y = y;
+    if (sp.summary) R2L_RUN("scan_summary", st, scan_summary<float>(a, true, st));
+    R2L_RUN("scan_main", st, scan_main<float>(a, true, st));
+    R2L_RUN("out_proj_gemm", st, gemm_f32_nt(T, D, E, y, E, (const float*)w->out_proj_w, E, o, D, st));
+    R2L_RUN("ln_gate", st, ln_gate<float>(T, D, o, (const float*)h_in, (float*)h_out, w->ln_w, w->ln_b, w->s, branch_out, no_ln, R2L_LN_EPS, st));
+  }
+  return R2L_OK;
+}
+
+int r2l_conv_fwd(const r2l_dims* d, r2l_dtype act, const void* x, int64_t ld_x, const void* conv_w,
+                 const void* conv_b, const void* x_proj_w, void* u_out, float* xdbl_out,
+                 const int32_t* cu_seqlens, int32_t nseq, int64_t n_tokens, int32_t max_seqlen,
+                 void* stream) {
+  int rc = check_dims(d);
+  if (rc != R2L_OK) return rc;
+  if ((rc = check_tokens(act, n_tokens, nseq, max_seqlen)) != R2L_OK) return rc;
+  const int E = d->d_inner, P = d->dt_rank + 2 * d->d_state;
+  if (!x || !conv_w || !conv_b || !cu_seqlens || ld_x < E) return R2L_ERR_INVALID_ARG;
+  if (!u_out && !x_proj_w) return R2L_ERR_INVALID_ARG;
+  if ((x_proj_w != nullptr) != (xdbl_out != nullptr)) return R2L_ERR_INVALID_ARG;
+  if (act == R2L_BF16 && (!aligned16(x) || ld_x % 8 || !aligned16(conv_w) || !aligned16(conv_b) ||
+                          (x_proj_w && !aligned16(x_proj_w)) || (u_out && !aligned16(u_out))))
+    return R2L_ERR_INVALID_ARG;
+  const bool fused = act == R2L_BF16 && x_proj_w && P <= 256;
+  if (x_proj_w && !fused && !u_out) return R2L_ERR_UNSUPPORTED;  // the unfused path stages u in u_out
+  if (n_tokens == 0) return R2L_OK;
+  hipStream_t st = (hipStream_t)stream;
+  const int T = (int)n_tokens;
+  if (act == R2L_BF16) {
+    if (fused) {
+      R2L_RUN("conv_xproj", st, conv_xproj_bf16(T, E, P, (const bf16*)x, ld_x, (const bf16*)conv_w, (const bf16*)conv_b, (const bf16*)x_proj_w, (bf16*)u_out, xdbl_out, cu_seqlens, nseq, st));
+    } else {
+      R2L_RUN("conv_silu", st, conv_silu<bf16>(T, E, (const bf16*)x, ld_x, (const bf16*)conv_w, (const bf16*)conv_b, (bf16*)u_out, cu_seqlens, nseq, st));
+      if (x_proj_w) R2L_RUN("x_proj_gemm", st, gemm_bf16_nt(T, P, E, (const bf16*)u_out, E, (const bf16*)x_proj_w, E, xdbl_out, P, true, st));
+    }
+  } else {
+    R2L_RUN("conv_silu", st, conv_silu<float>(T, E, (const float*)x, ld_x, (const float*)conv_w, (const float*)conv_b, (float*)u_out, cu_seqlens, nseq, st));
+    if (x_proj_w) R2L_RUN("x_proj_gemm", st, gemm_f32_nt(T, P, E, (const float*)u_out, E, (const float*)x_proj_w, E, xdbl_out, P, st));
+  }
+  return R2L_OK;
+}
+
+int r2l_scan_fwd(const r2l_dims* d, r2l_dtype act, const void* u, int64_t ld_u, const float* dt,
+                 int64_t ld_dt, const float* A_log, const float* B, const float* C, int64_t ld_bc,
+                 const float* Dskip, const void* z, int64_t ld_z, void* y_out,
+                 const int32_t* cu_seqlens, int32_t nseq, int64_t n_tokens, int32_t max_seqlen,
+                 void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = check_dims(d);
+  if (rc != R2L_OK) return rc;
+  if ((rc = check_tokens(act, n_tokens, nseq, max_seqlen)) != R2L_OK) return rc;
+  const int E = d->d_inner;
+  if (!u || !dt || !A_log || !B || !C || !y_out || !cu_seqlens) return R2L_ERR_INVALID_ARG;
+  if (ld_u < E || ld_dt < E || ld_bc < d->d_state || (z && ld_z < E)) return R2L_ERR_INVALID_ARG;
+  const ScanPlan sp = plan_scan(E, n_tokens, nseq, max_seqlen, 0);
+  if (!workspace || workspace_bytes < sp.total) return R2L_ERR_WORKSPACE;
+  if (((uintptr_t)workspace & (kAlign - 1)) != 0) return R2L_ERR_INVALID_ARG;
+  if (n_tokens == 0) return R2L_OK;
+  hipStream_t st = (hipStream_t)stream;
+  ScanArgs a{};
+  a.T = (int)n_tokens; a.E = E; a.R = d->dt_rank; a.ldp = 0;
+  a.u = u; a.ld_u = ld_u; a.dt = dt; a.ld_dt = ld_dt;
+  a.Bm = B; a.Cm = C; a.ld_bc = ld_bc;
+  a.z = z; a.ld_z = ld_z;
+  a.A_log = A_log; a.Dskip = Dskip; a.y = y_out;
+  a.chunks = at<ChunkDesc>(workspace, sp.off_chunks);
+  a.n_chunks = at<int32_t>(workspace, sp.off_n);
+  a.max_chunks = sp.max_chunks;
+  a.sumS = at<float>(workspace, sp.off_sumS);
+  a.sumP = at<float>(workspace, sp.off_sumP);
+  int32_t* cu_clean = at<int32_t>(workspace, sp.off_cu);
+  if (act == R2L_BF16)
+    return run_scan<bf16>(a, sp, false, cu_seqlens, nseq, n_tokens, cu_clean, (ChunkDesc*)a.chunks, (int32_t*)a.n_chunks, st);
+  return run_scan<float>(a, sp, false, cu_seqlens, nseq, n_tokens, cu_clean, (ChunkDesc*)a.chunks, (int32_t*)a.n_chunks, st);
+}
+
+int r2l_gemm_nt(r2l_dtype act, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
+                const void* B, int64_t ldb, void* C, int64_t ldc, int out_f32, void* stream) {
+  if (act != R2L_F32 && act != R2L_BF16) return R2L_ERR_UNSUPPORTED;
+  if (M < 0 || N < 0 || K < 0 || M > INT32_MAX || N > INT32_MAX || K > INT32_MAX)
+    return R2L_ERR_INVALID_ARG;
+  if (!A || !B || !C || lda < K || ldb < K || ldc < N) return R2L_ERR_INVALID_ARG;
+  hipStream_t st = (hipStream_t)stream;
+  if (act == R2L_BF16) {
+    if (K % 8 || lda % 8 || ldb % 8 || !aligned16(A) || !aligned16(B)) return R2L_ERR_UNSUPPORTED;
+    R2L_RUN("gemm_bf16", st, gemm_bf16_nt((int)M, (int)N, (int)K, (const bf16*)A, lda, (const bf16*)B, ldb, C, ldc, out_f32 != 0, st));
+  } else {
+    R2L_RUN("gemm_f32", st, gemm_f32_nt((int)M, (int)N, (int)K, (const float*)A, lda, (const float*)B, ldb, (float*)C, ldc, st));
+  }
+  return R2L_OK;
+}
+
+int r2l_timing_enable(int enable) {
+  TimingState& t = timing();
+  std::lock_guard<std::mutex> g(t.mu);
+  t.enabled = enable != 0;
+  return R2L_OK;
+}
+
+int r2l_timing_reset(void) {
+  TimingState& t = timing();
+  std::lock_guard<std::mutex> g(t.mu);
+  for (auto& r : t.recs) {
+    (void)hipEventSynchronize(r.b);
+    t.pool.push_back(r.a);
+    t.pool.push_back(r.b);
+  }
+  t.recs.clear();
+  t.names.clear();
+  t.totals.clear();
+  t.counts.clear();
+  return R2L_OK;
+}
+
+int r2l_timing_read(const char** names, double* total_ms, int64_t* counts, int max_names) {
+  TimingState& t = timing();
+  std::lock_guard<std::mutex> g(t.mu);
+  int status = R2L_OK;
+  for (auto& r : t.recs) {
+    float ms = 0.0f;
+    if (hipEventSynchronize(r.b) != hipSuccess || hipEventElapsedTime(&ms, r.a, r.b) != hipSuccess)
+      status = R2L_ERR_HIP;
+    size_t k = 0;
+    while (k < t.names.size() && std::strcmp(t.names[k], r.name) != 0) ++k;
+    if (k == t.names.size()) {
+      t.names.push_back(r.name);
+      t.totals.push_back(0.0);
+      t.counts.push_back(0);
+    }
+    t.totals[k] += ms;
+    t.counts[k] += 1;
+    t.pool.push_back(r.a);
+    t.pool.push_back(r.b);
+  }
+  t.recs.clear();
+  if (status != R2L_OK) return status;
+  const int n = (int)t.names.size();
+  for (int i = 0; i < n && i < max_names; ++i) {
+    if (names) names[i] = t.names[i];
+    if (total_ms) total_ms[i] = t.totals[i];
+    if (counts) counts[i] = t.counts[i];
+  }
+  return n;
+}
+
+}  // extern "C"

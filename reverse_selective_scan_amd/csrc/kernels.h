@@ -1,0 +1,65 @@
+// Launchers of the device kernels (internal to libr2l.so).  Each launcher
+// enqueues its kernel(s) on `st` and returns hipGetLastError().
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "common.h"
+
+namespace r2l {
+
+// C[M,N] = A[M,K] . B[N,K]^T.  bf16 inputs on MFMA; output bf16 or f32.
+hipError_t gemm_bf16_nt(int M, int N, int K, const bf16* A, long lda, const bf16* B, long ldb,
+                        void* C, long ldc, bool out_f32, hipStream_t st);
+// fp32 inputs on the VALU; output f32.
+hipError_t gemm_f32_nt(int M, int N, int K, const float* A, long lda, const float* B, long ldb,
+                       float* C, long ldc, hipStream_t st);
+
+// Anti-causal depthwise conv + bias + SiLU -> u (act, contiguous [T,E]).
+template <typename T>
+hipError_t conv_silu(int T_, int E, const T* x, long ld_x, const T* conv_w, const T* conv_b,
+                     T* u, const int32_t* cu, int nseq, hipStream_t st);
+// Fused conv + SiLU + x_proj (bf16, MFMA): xdbl f32 [T, P] with P = R+2N;
+// u_out optional.  Requires E % 64 == 0 and P <= 256.
+hipError_t conv_xproj_bf16(int T_, int E, int P, const bf16* x, long ld_x, const bf16* conv_w,
+                           const bf16* conv_b, const bf16* x_proj_w, bf16* u_out, float* xdbl,
+                           const int32_t* cu, int nseq, hipStream_t st);
+
+// Chunk planning for the scan: sanitised cu_seqlens and the chunk table.
+hipError_t plan_chunks(const int32_t* cu, int nseq, int T_, int Lc, int max_chunks,
+                       int32_t* cu_clean, ChunkDesc* chunks, int32_t* n_chunks, hipStream_t st);
+
+struct ScanArgs {
+  int T, E, R, ldp;            // ldp: row stride of xdbl (fused) in floats
+  // fused mode: x (in xz), z, xdbl (delta|B|C), conv and dt_proj weights
+  const void* x; long ld_x;
+  const void* z; long ld_z;
+  const float* xdbl;
+  const void* conv_w; const void* conv_b;
+  const void* dt_w; const float* dt_b;
+  // standalone mode: u, dt, B, C
+  const void* u; long ld_u;
+  const float* dt; long ld_dt;
+  const float* Bm; const float* Cm; long ld_bc;
+  // both
+  const float* A_log; const float* Dskip;
+  void* y;
+  const ChunkDesc* chunks; const int32_t* n_chunks; int max_chunks;
+  float* sumS; float* sumP;    // [max_chunks][16][E] each
+};
+
+// Pass 1 (only when some sequence spans several chunks): per-chunk decay
+// product and local state.  Pass 2: outputs, with the carry-in of each chunk
+// combined from the summaries of the chunks to its right.
+template <typename T>
+hipError_t scan_summary(const ScanArgs& a, bool fused, hipStream_t st);
+template <typename T>
+hipError_t scan_main(const ScanArgs& a, bool fused, hipStream_t st);
+
+template <typename T>
+hipError_t ln_gate(int T_, int D, const float* o, const T* h_in, T* h_out, const float* gamma,
+                   const float* beta, const float* s, float* branch, bool no_ln, float eps,
+                   hipStream_t st);
+
+}  // namespace r2l

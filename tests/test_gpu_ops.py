@@ -1,0 +1,150 @@
+"""GPU parity of the library's operators against the fp64 oracle / numpy
+fp64 products on the same (exactly representable) inputs."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import r2l_oracle as O
+from parity import TOL_BF16, err_f32, err_rms, report, to_np
+from reverse_selective_scan_amd import binding as B
+from reverse_selective_scan_amd import synth
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _dev(a, act):
+    t = torch.from_numpy(np.ascontiguousarray(a, np.float32))
+    return (t.to(torch.bfloat16) if act == "bf16" else t).to(DEV)
+
+
+def _q(a, act):
+    return synth.bf16_round(a) if act == "bf16" else np.asarray(a, np.float32)
+
+
+def _case(name):
+    print(f"\n[case] {name}", flush=True)
+
+
+# ---------------------------------------------------------------------------
+# dense projection (P14: numpy fp64 product of the same operands)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("M,N,K", [(1, 1, 8), (33, 17, 64), (128, 128, 64), (300, 520, 136),
+                                   (1031, 257, 2048), (640, 8192, 2048)])
+def test_gemm_bf16_matches_fp64_product(M, N, K):
+    _case(f"gemm bf16 {M}x{N}x{K}")
+    A = synth.make_aux(M * 7 + 1, (M, K))
+    Bm = synth.make_aux(N * 7 + 2, (N, K))
+    A, Bm = synth.bf16_round(A), synth.bf16_round(Bm)
+    ref = A.astype(np.float64) @ Bm.astype(np.float64).T
+    g32 = to_np(B.r2l_gemm_nt(_dev(A, "bf16"), _dev(Bm, "bf16"), out_f32=True))
+    g16 = to_np(B.r2l_gemm_nt(_dev(A, "bf16"), _dev(Bm, "bf16"), out_f32=False))
+    torch.cuda.synchronize()
+    assert report("gemm f32-out", err_f32(g32, ref), 1e-4) <= 1e-4
+    assert report("gemm bf16-out", err_f32(g16, ref), 5e-3) <= 5e-3   # one bf16 rounding (2^-8)
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 1, 1), (65, 130, 33), (256, 96, 128)])
+def test_gemm_f32_matches_fp64_product(M, N, K):
+    _case(f"gemm f32 {M}x{N}x{K}")
+    A = synth.make_aux(M + 11, (M, K))
+    Bm = synth.make_aux(N + 13, (N, K))
+    ref = A.astype(np.float64) @ Bm.astype(np.float64).T
+    g = to_np(B.r2l_gemm_nt(_dev(A, "f32"), _dev(Bm, "f32")))
+    assert report("gemm f32", err_f32(g, ref), 1e-5) <= 1e-5
+
+
+# ---------------------------------------------------------------------------
+# conv + SiLU (+ x_proj)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("act", ["f32", "bf16"])
+@pytest.mark.parametrize("lens,E,R", [([1], 64, 8), ([2, 3, 1, 0, 40], 128, 16), ([257, 64, 3], 256, 16),
+                                      ([300, 41], 4096, 128)])
+def test_conv_fwd_matches_oracle(act, lens, E, R):
+    _case(f"conv {act} lens={lens} E={E} R={R}")
+    N = 16
+    T = sum(lens)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    xz = _q(synth.make_aux(1, (T, 2 * E)), act)
+    cw = _q(synth.make_aux(2, (E, 4), scale=0.5), act)
+    cb = _q(synth.make_aux(3, (E,), scale=0.5), act)
+    xw = _q(synth.make_aux(4, (R + 2 * N, E), scale=E ** -0.5), act)
+    ref_u, ref_x = O.reverse_conv_silu(xz[:, :E], cu, cw, cb, xw)
+    xz_d = _dev(xz, act)
+    u, xd = B.r2l_conv_fwd(xz_d[:, :E], _dev(cw, act), _dev(cb, act), cu, x_proj_w=_dev(xw, act), dt_rank=R)
+    u, xd = to_np(u), to_np(xd)
+    if act == "f32":
+        assert report("conv u", err_f32(u, ref_u), 1e-5) <= 1e-5
+        assert report("conv xdbl", err_f32(xd, ref_x), 1e-4) <= 1e-4
+    else:
+        assert report("conv u", err_f32(u, ref_u), 5e-3) <= 5e-3
+        assert report("conv xdbl", err_rms(xd, ref_x), 1e-2) <= 1e-2
+        # xdbl does not depend on whether u is also written
+        _, xd2 = B.r2l_conv_fwd(xz_d[:, :E], _dev(cw, act), _dev(cb, act), cu, x_proj_w=_dev(xw, act),
+                                dt_rank=R, want_u=False)
+        assert np.array_equal(to_np(xd2), xd)
+
+
+def test_conv_fwd_bf16_wide_xproj_uses_staged_u():
+    _case("conv bf16 wide x_proj (R+2N > 256)")
+    E, R, N, T = 128, 240, 16, 70
+    cu = np.array([0, 30, 70], np.int32)
+    xz = _q(synth.make_aux(5, (T, E)), "bf16")
+    cw = _q(synth.make_aux(6, (E, 4), scale=0.5), "bf16")
+    cb = _q(synth.make_aux(7, (E,), scale=0.5), "bf16")
+    xw = _q(synth.make_aux(8, (R + 2 * N, E), scale=E ** -0.5), "bf16")
+    ref_u, ref_x = O.reverse_conv_silu(xz, cu, cw, cb, xw)
+    u, xd = B.r2l_conv_fwd(_dev(xz, "bf16"), _dev(cw, "bf16"), _dev(cb, "bf16"), cu, x_proj_w=_dev(xw, "bf16"),
+                           dt_rank=R)
+    assert report("conv u", err_f32(to_np(u), ref_u), 5e-3) <= 5e-3
+    assert report("conv xdbl", err_rms(to_np(xd), ref_x), 1e-2) <= 1e-2
+
+
+# ---------------------------------------------------------------------------
+# reverse selective scan (standalone: dt given)
+# ---------------------------------------------------------------------------
+def _scan_inputs(T, E, act, seed):
+    N = 16
+    u = _q(synth.make_aux(seed, (T, E)), act)
+    dt = synth.make_aux(seed + 1, (T, E), kind="uniform", lo=1e-3, hi=0.2)
+    A_log = synth.make_aux(seed + 2, (E, N), kind="uniform", lo=-1.0, hi=2.5)
+    bcx = synth.make_aux(seed + 3, (T, 40))          # B at columns 8..23, C at 24..39
+    Dskip = synth.make_aux(seed + 4, (E,), kind="uniform", lo=0.5, hi=1.5)
+    z = _q(synth.make_aux(seed + 5, (T, E)), act)
+    return u, dt, A_log, bcx, Dskip, z
+
+
+@pytest.mark.parametrize("act", ["f32", "bf16"])
+@pytest.mark.parametrize("lens,E", [([1], 64), ([37], 128), ([5, 0, 130, 1, 300], 128), ([700, 2, 129], 192),
+                                    ([2048], 1024)])
+@pytest.mark.parametrize("with_z", [True, False])
+def test_scan_fwd_matches_oracle(act, lens, E, with_z):
+    _case(f"scan {act} lens={lens} E={E} z={with_z}")
+    T = sum(lens)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    u, dt, A_log, bcx, Dskip, z = _scan_inputs(T, E, act, 20 + len(lens))
+    zz = z if with_z else None
+    Dk = Dskip if with_z else None
+    ref = O.reverse_selective_scan(u, dt, A_log, bcx[:, 8:24], bcx[:, 24:40], cu, Dskip=Dk, z=zz)
+    bc_d = _dev(bcx, "f32")
+    y = B.r2l_scan_fwd(_dev(u, act), _dev(dt, "f32"), _dev(A_log, "f32"), bc_d[:, 8:24], bc_d[:, 24:40], cu,
+                       Dskip=_dev(Dk, "f32") if Dk is not None else None,
+                       z=_dev(zz, act) if zz is not None else None)
+    g = to_np(y)
+    tol = 1e-4 if act == "f32" else 5e-3
+    assert report("scan", err_f32(g, ref), tol) <= tol
+
+
+def test_scan_strong_decay_is_pointwise_on_gpu():
+    """A -> -inf: only the token's own term survives (closed form, any length)."""
+    _case("scan strong decay")
+    T, E = 500, 128
+    cu = np.array([0, 200, 500], np.int32)
+    u, dt, _, bcx, Dskip, _ = _scan_inputs(T, E, "f32", 60)
+    A_log = np.full((E, 16), 80.0, np.float32)
+    Bm, Cm = bcx[:, 8:24].astype(np.float64), bcx[:, 24:40].astype(np.float64)
+    ref = dt * u * (Bm * Cm).sum(axis=1)[:, None] + Dskip * u
+    bc_d = _dev(bcx, "f32")
+    g = to_np(B.r2l_scan_fwd(_dev(u, "f32"), _dev(dt, "f32"), _dev(A_log, "f32"), bc_d[:, 8:24], bc_d[:, 24:40],
+                             cu, Dskip=_dev(Dskip, "f32")))
+    assert report("scan strong decay", err_f32(g, ref), 1e-5) <= 1e-5
