@@ -144,8 +144,10 @@ int r2l_conv_fwd(const r2l_dims* dims, r2l_dtype act, const void* x, int64_t ld_
  * stride ld_dt), already softplus-ed; B, C: f32 [n_tokens, N] (row stride
  * ld_bc each); Dskip: f32 [E] or NULL (no skip term); z: act (row stride
  * ld_z) or NULL (no gate); y_out: act [n_tokens, E] contiguous.
- * workspace: r2l_scan_workspace_bytes(...) bytes (may be 0 bytes; then
- * NULL is accepted).
+ * u, dt, z and y_out must be 16-byte aligned, with ld_u and ld_z multiples
+ * of 8 (bf16) or 4 (f32) elements and ld_dt a multiple of 4; B and C have
+ * no alignment requirement.
+ * workspace: r2l_scan_workspace_bytes(...) bytes, 256-byte aligned.
  * ---------------------------------------------------------------------- */
 size_t r2l_scan_workspace_bytes(const r2l_dims* dims, int64_t n_tokens, int32_t nseq,
                                 int32_t max_seqlen);

@@ -123,7 +123,7 @@ struct ScanPlan {
 ScanPlan plan_scan(int E, int64_t T, int32_t nseq, int32_t max_seqlen, size_t base) {
   ScanPlan p{};
   const int64_t NB = E / 64;
-  const int64_t target = 1024;  // blocks wanted in flight (256 CUs)
+  const int64_t target = 512;  // scan blocks resident at once: 2 per CU (LDS-bound)
   int64_t ms = max_seqlen < 1 ? 1 : max_seqlen;
   if (T > 0 && ms > T) ms = T;
   int64_t Lc = ms;
@@ -353,6 +353,11 @@ int r2l_scan_fwd(const r2l_dims* d, r2l_dtype act, const void* u, int64_t ld_u, 
   const int E = d->d_inner;
   if (!u || !dt || !A_log || !B || !C || !y_out || !cu_seqlens) return R2L_ERR_INVALID_ARG;
   if (ld_u < E || ld_dt < E || ld_bc < d->d_state || (z && ld_z < E)) return R2L_ERR_INVALID_ARG;
+  // u, z, dt rows and y are accessed with 16-byte vectors
+  const int64_t vec = act == R2L_BF16 ? 8 : 4;
+  if (!aligned16(u) || !aligned16(dt) || !aligned16(y_out) || (z && !aligned16(z)) || ld_u % vec ||
+      ld_dt % 4 || (z && ld_z % vec))
+    return R2L_ERR_INVALID_ARG;
   const ScanPlan sp = plan_scan(E, n_tokens, nseq, max_seqlen, 0);
   if (!workspace || workspace_bytes < sp.total) return R2L_ERR_WORKSPACE;
   if (((uintptr_t)workspace & (kAlign - 1)) != 0) return R2L_ERR_INVALID_ARG;

@@ -6,6 +6,7 @@
 
 typedef __bf16 bf16;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
@@ -28,10 +29,19 @@ R2L_DEV float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 // sigmoid(v) = 1 / (1 + e^-v); e^-v via 2^(-v log2 e).
 R2L_DEV float sigmoid_fast(float v) { return __builtin_amdgcn_rcpf(1.0f + exp2_fast(-v * kLog2e)); }
 R2L_DEV float silu_fast(float v) { return v * sigmoid_fast(v); }
-// softplus(v) = log(1 + e^v) = max(v, 0) + log1p(e^-|v|), with the device log1pf.
+// softplus(v) = log(1 + e^v) = max(v, 0) + log1p(w), w = e^-|v| in (0, 1].
+// log1p(w): below w = 2^-5 the alternating series to the w^6 term (truncation
+// under w^7/7, i.e. ~1e-10 relative); above, log2(1 + w) ln 2 on the
+// transcendental unit (rounding 1 + w costs at most 2^-19 of w there).
 R2L_DEV float softplus_f(float v) {
-  float a = fabsf(v);
-  return fmaxf(v, 0.0f) + log1pf(exp2_fast(-a * kLog2e));
+  const float w = exp2_fast(-fabsf(v) * kLog2e);
+  float ser = fmaf(w, -1.0f / 6.0f, 0.2f);
+  ser = fmaf(w, ser, -0.25f);
+  ser = fmaf(w, ser, 1.0f / 3.0f);
+  ser = fmaf(w, ser, -0.5f);
+  ser = fmaf(w, ser, 1.0f) * w;
+  const float lg = __builtin_amdgcn_logf(1.0f + w) * kLn2;
+  return fmaxf(v, 0.0f) + (w < 0.03125f ? ser : lg);
 }
 
 // ---- wave / lane helpers ------------------------------------------------------

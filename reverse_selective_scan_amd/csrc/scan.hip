@@ -118,17 +118,74 @@ hipError_t plan_chunks(const int32_t* cu, int nseq, int Tn, int Lc, int max_chun
 }
 
 // ---------------------------------------------------------------------------
+// 8-channel vector helpers (16-byte loads/stores for bf16, 2 x 16 for fp32)
+// ---------------------------------------------------------------------------
+R2L_DEV void load8(const bf16* p, float v[8]) {
+  const bf16x8 q = *(const bf16x8*)p;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] = (float)q[i];
+}
+R2L_DEV void load8(const float* p, float v[8]) {
+  const f32x4 a = *(const f32x4*)p, b = *(const f32x4*)(p + 4);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) { v[i] = a[i]; v[4 + i] = b[i]; }
+}
+R2L_DEV void store8(bf16* p, const float v[8]) {
+  bf16x8 q;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) q[i] = (bf16)v[i];
+  *(bf16x8*)p = q;
+}
+R2L_DEV void store8(float* p, const float v[8]) {
+  f32x4 a, b;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) { a[i] = v[i]; b[i] = v[4 + i]; }
+  *(f32x4*)p = a;
+  *(f32x4*)(p + 4) = b;
+}
+template <typename T> struct Raw8;
+template <> struct Raw8<bf16> { bf16x8 v; };
+template <> struct Raw8<float> { f32x4 a, b; };
+R2L_DEV void raw_load(Raw8<bf16>& r, const bf16* p) { r.v = *(const bf16x8*)p; }
+R2L_DEV void raw_load(Raw8<float>& r, const float* p) { r.a = *(const f32x4*)p; r.b = *(const f32x4*)(p + 4); }
+R2L_DEV void raw_zero(Raw8<bf16>& r) { r.v = bf16x8{}; }
+R2L_DEV void raw_zero(Raw8<float>& r) { r.a = f32x4{0, 0, 0, 0}; r.b = r.a; }
+R2L_DEV void raw_get(const Raw8<bf16>& r, float v[8]) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] = (float)r.v[i];
+}
+R2L_DEV void raw_get(const Raw8<float>& r, float v[8]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) { v[i] = r.a[i]; v[4 + i] = r.b[i]; }
+}
+
+// ---------------------------------------------------------------------------
 // the scan kernel: SUMMARY = pass 1, otherwise the main pass.
-// KS = number of 32-wide k-steps of dt_proj on MFMA (fused bf16 only).
+// KS = number of 32-wide k-steps of dt_proj on MFMA (fused bf16 only; 0 = VALU).
+//
+// Thread layouts inside a block of TB = 32 tokens x 64 channels:
+//   A, C  thread (r = tid / 8, c8 = tid % 8): token row r, channels 8 c8 .. +7,
+//         so every global access is one 16-byte vector per thread;
+//   M     wave w: channels 16 w .. +15 of all 32 rows (two 16x16 MFMA tiles);
+//   B     wave w, lane c: channel c, states 4 w .. 4 w + 3, tokens in order.
+// The next block's global loads are issued before the current block's
+// compute, so memory latency overlaps the recurrence.
 // ---------------------------------------------------------------------------
 template <typename T, bool FUSED, bool SUMMARY, int KS>
-__global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
-  __shared__ float u_s[TB][64];
-  __shared__ float dt_s[TB][64];
-  __shared__ float g_s[SUMMARY ? 1 : TB][64];
-  __shared__ float du_s[SUMMARY ? 1 : TB][64];
-  __shared__ f32x4 bc_s[TB][8];
-  __shared__ float yp_s[SUMMARY ? 1 : 4][TB][64];
+__global__ __launch_bounds__(256, 2) void scan_kernel(ScanArgs a) {
+  constexpr bool MFMA_DT = FUSED && KS > 0;
+  constexpr int RP = MFMA_DT ? KS * 32 : 32;   // padded dt_rank for the MFMA k loop
+  constexpr int DLS = RP + 8;                   // delta row stride in LDS (bf16)
+  constexpr int DPT = RP / 8;                   // delta floats per thread per row
+  static_assert(TB * DLS * 2 + TB * 64 * 4 <= 4 * TB * 64 * 4, "aliases must fit in yp_s");
+  // yp_s (partial C.h sums, phase B/C) also hosts u (phases A/M) and delta (A/M)
+  __shared__ __attribute__((aligned(16))) float yp_s[4][TB][64];
+  __shared__ __attribute__((aligned(16))) float g_s[SUMMARY ? 1 : TB][64];
+  __shared__ __attribute__((aligned(16))) float du_s[SUMMARY ? 1 : TB][64];
+  __shared__ __attribute__((aligned(16))) float2 pre_s[TB][64];   // (dt, dt*u)
+  __shared__ __attribute__((aligned(16))) f32x4 bc_s[TB][8];      // B[0..16) C[0..16)
+  float (*u_s)[64] = yp_s[0];
+  bf16* dl_s = (bf16*)&yp_s[1][0][0];
 
   const int E = a.E;
   const int NB = E / 64;
@@ -140,40 +197,39 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
   const int tid = threadIdx.x;
   const int lane = lane_id(), w = wave_id();
   const int e0 = cblk * 64;
-  const int e = e0 + lane;
+  const int e = e0 + lane;                 // phase B channel
+  const int r8 = tid >> 3, c8 = tid & 7;   // phase A/C row and channel group
+  const int ea = e0 + 8 * c8;              // phase A/C first channel
 
   float A2[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) A2[i] = -expf(a.A_log[(long)e * NS + 4 * w + i]) * kLog2e;
-  const float Dsk = a.Dskip ? a.Dskip[e] : 0.0f;
 
-  const T* x = (const T*)a.x;
-  const T* z = (const T*)a.z;
-  const T* uin = (const T*)a.u;
-  float cw[4] = {0, 0, 0, 0}, cbias = 0.0f;
-  if (FUSED) {
+  // phase A constants for channels ea .. ea+7
+  float cwr[8][4], cb8[8], dsk8[8];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) cw[k] = to_f32(((const T*)a.conv_w)[(long)e * 4 + k]);
-    cbias = to_f32(((const T*)a.conv_b)[e]);
+  for (int i = 0; i < 8; ++i) {
+    dsk8[i] = a.Dskip ? a.Dskip[ea + i] : 0.0f;
+    cb8[i] = FUSED ? to_f32(((const T*)a.conv_b)[ea + i]) : 0.0f;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) cwr[i][k] = FUSED ? to_f32(((const T*)a.conv_w)[(long)(ea + i) * 4 + k]) : 0.0f;
   }
   // dt_proj fragments (B operand of the 16x16x32 MFMA): channel
-  // e0 + 16w + (lane & 15), k = 32 ks + 8 (lane >> 4) .. +7.
-  constexpr bool MFMA_DT = FUSED && KS > 0;
+  // e0 + 16 w + (lane & 15), k = 32 ks + 8 (lane >> 4) .. +7.
   bf16x8 wdt[MFMA_DT ? KS : 1];
   const int dcol = 16 * w + (lane & 15);
   float dtb_col = 0.0f;
-  if (MFMA_DT) {
+  if constexpr (MFMA_DT) {
     const bf16* W = (const bf16*)a.dt_w;
     const long rowoff = (long)(e0 + dcol) * a.R;
 #pragma unroll
-    for (int ks = 0; ks < (MFMA_DT ? KS : 1); ++ks) {
+    for (int ks = 0; ks < KS; ++ks) {
       const int k = ks * 32 + (lane >> 4) * 8;
 #pragma unroll
       for (int p = 0; p < 8; ++p) wdt[ks][p] = (k + p < a.R) ? W[rowoff + k + p] : (bf16)0.0f;
     }
     dtb_col = a.dt_b[e0 + dcol];
   }
-  const float dtb_lane = FUSED ? a.dt_b[e] : 0.0f;
 
   // carry into this chunk from the chunks to its right
   float h[4] = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -189,135 +245,192 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
   }
   float sdt = 0.0f;
 
-  for (int bhi = d.hi; bhi > d.lo; bhi -= TB) {
-    const int blo = max(d.lo, bhi - TB);
-    const int nt = bhi - blo;
-    // ---------------- A1: per-(token, channel) inputs ----------------
-    if (FUSED) {
-      float xw[8 + 3];
+  // ---------------- prefetch registers ----------------
+  const T* xin = FUSED ? (const T*)a.x : (const T*)a.u;
+  const long ldx = FUSED ? a.ld_x : a.ld_u;
+  const T* zin = (const T*)a.z;
+  Raw8<T> px[FUSED ? 4 : 1];   // x rows r8 .. r8+3 (fused) or u row r8
+  Raw8<T> pz;                  // z row r8
+  f32x4 pd[FUSED ? DPT / 4 : 2];  // delta (fused) or dt (standalone) of row r8
+  f32x4 pbc;                   // 4 of the row's 32 B/C floats
+  const bool vec_bc = FUSED ? ((a.R & 3) == 0 && (a.ldp & 3) == 0) : false;
+
+  auto issue = [&](int blo, int bhi) {
+    const int t = blo + r8;
+    const bool tv = t < bhi;
+    if constexpr (FUSED) {
 #pragma unroll
-      for (int q = 0; q < 11; ++q) {
-        const int t = blo + 8 * w + q;
-        xw[q] = (t < d.seq_end) ? to_f32(x[(long)t * a.ld_x + e]) : 0.0f;
+      for (int j = 0; j < 4; ++j) {
+        if (t + j < d.seq_end) raw_load(px[j], xin + (long)(t + j) * ldx + ea);
+        else raw_zero(px[j]);
       }
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int r = 8 * w + i;
-        const int t = blo + r;
-        float c = cbias;
+      for (int q = 0; q < (MFMA_DT ? DPT / 4 : 0); ++q) {
+        const int k = c8 * DPT + 4 * q;
+        if (tv && vec_bc && k + 3 < a.R) {
+          pd[q] = *(const f32x4*)(a.xdbl + (long)t * a.ldp + k);
+        } else {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) c = fmaf(cw[3 - j], xw[i + j], c);
-        const float uu = silu_fast(c);
-        u_s[r][lane] = uu;
-        if (!SUMMARY) {
-          const float zz = (z != nullptr && t < bhi) ? to_f32(z[(long)t * a.ld_z + e]) : 0.0f;
-          g_s[r][lane] = z != nullptr ? silu_fast(zz) : 1.0f;
-          du_s[r][lane] = Dsk * uu;
+          for (int p = 0; p < 4; ++p) pd[q][p] = (tv && k + p < a.R) ? a.xdbl[(long)t * a.ldp + k + p] : 0.0f;
         }
+      }
+      if (tv && vec_bc) {
+        pbc = *(const f32x4*)(a.xdbl + (long)t * a.ldp + a.R + 4 * c8);
+      } else {
+#pragma unroll
+        for (int p = 0; p < 4; ++p) pbc[p] = tv ? a.xdbl[(long)t * a.ldp + a.R + 4 * c8 + p] : 0.0f;
       }
     } else {
+      if (tv) raw_load(px[0], xin + (long)t * ldx + ea);
+      else raw_zero(px[0]);
+      if (tv) {
+        pd[0] = *(const f32x4*)(a.dt + (long)t * a.ld_dt + ea);
+        pd[1] = *(const f32x4*)(a.dt + (long)t * a.ld_dt + ea + 4);
+      } else {
+        pd[0] = f32x4{0, 0, 0, 0};
+        pd[1] = pd[0];
+      }
+      const float* src = (c8 < 4 ? a.Bm + 4 * c8 : a.Cm + 4 * (c8 - 4)) + (long)t * a.ld_bc;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int r = 8 * w + i;
-        const int t = blo + r;
-        const bool v = t < bhi;
-        const float uu = v ? to_f32(uin[(long)t * a.ld_u + e]) : 0.0f;
-        u_s[r][lane] = uu;
-        dt_s[r][lane] = v ? a.dt[(long)t * a.ld_dt + e] : 0.0f;
-        if (!SUMMARY) {
-          const float zz = (z != nullptr && v) ? to_f32(z[(long)t * a.ld_z + e]) : 0.0f;
-          g_s[r][lane] = z != nullptr ? silu_fast(zz) : 1.0f;
-          du_s[r][lane] = Dsk * uu;
+      for (int p = 0; p < 4; ++p) pbc[p] = tv ? src[p] : 0.0f;
+    }
+    if (!SUMMARY) {
+      if (zin != nullptr && tv) raw_load(pz, zin + (long)t * a.ld_z + ea);
+      else raw_zero(pz);
+    }
+  };
+
+  int bhi = d.hi;
+  if (bhi > d.lo) issue(max(d.lo, bhi - TB), bhi);
+  for (; bhi > d.lo; bhi -= TB) {
+    const int blo = max(d.lo, bhi - TB);
+    const int nt = bhi - blo;
+    // ---------------- A: per-(token, channel) inputs ----------------
+    {
+      float uu[8];
+      if constexpr (FUSED) {
+        float xr[4][8];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) raw_get(px[j], xr[j]);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          float c = cb8[i];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) c = fmaf(cwr[i][3 - j], xr[j][i], c);
+          uu[i] = silu_fast(c);
+        }
+        if constexpr (MFMA_DT) {
+          // delta -> bf16 -> LDS (A operand of the dt MFMA)
+#pragma unroll
+          for (int q = 0; q < DPT / 4; ++q) {   // DPT is 4, 8, 16 or 32
+            bf16x4 pk;
+#pragma unroll
+            for (int p = 0; p < 4; ++p) pk[p] = (bf16)pd[q][p];
+            *(bf16x4*)(dl_s + r8 * DLS + c8 * DPT + 4 * q) = pk;
+          }
+        }
+      } else {
+        raw_get(px[0], uu);
+        float dtv[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) { dtv[i] = pd[0][i]; dtv[4 + i] = pd[1][i]; }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) pre_s[r8][8 * c8 + i] = make_float2(dtv[i], dtv[i] * uu[i]);
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) u_s[r8][8 * c8 + i] = uu[i];
+      if constexpr (!SUMMARY) {
+        float zz[8];
+        raw_get(pz, zz);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          g_s[r8][8 * c8 + i] = zin != nullptr ? silu_fast(zz[i]) : 1.0f;
+          du_s[r8][8 * c8 + i] = dsk8[i] * uu[i];
         }
       }
+      bc_s[r8][c8] = pbc;
     }
-    {
-      const int r = tid >> 3, q = tid & 7;
-      const int t = blo + r;
-      f32x4 v = {0.0f, 0.0f, 0.0f, 0.0f};
-      if (t < bhi) {
-        const float* src;
-        if (FUSED) src = a.xdbl + (long)t * a.ldp + a.R + 4 * q;  // B then C, contiguous
-        else src = (q < 4 ? a.Bm + 4 * q : a.Cm + 4 * (q - 4)) + (long)t * a.ld_bc;
-#pragma unroll
-        for (int p = 0; p < 4; ++p) v[p] = src[p];
-      }
-      bc_s[r][q] = v;
-    }
+    // the next block's loads go out now and land during this block's compute
+    if (bhi - TB > d.lo) issue(max(d.lo, bhi - 2 * TB), bhi - TB);
     __syncthreads();
-    // ---------------- A2: dt = softplus(delta . W_dt^T + b) ----------------
-    if (FUSED) {
-      if (MFMA_DT) {
+    // ---------------- M: dt = softplus(delta . W_dt^T + b) ----------------
+    if constexpr (FUSED) {
+      if constexpr (MFMA_DT) {
 #pragma unroll
         for (int rt = 0; rt < TB / 16; ++rt) {
           f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
           const int row = rt * 16 + (lane & 15);
-          const int t = blo + row;
 #pragma unroll
-          for (int ks = 0; ks < (MFMA_DT ? KS : 1); ++ks) {
-            const int k = ks * 32 + (lane >> 4) * 8;
-            bf16x8 af;
-#pragma unroll
-            for (int p = 0; p < 8; ++p)
-              af[p] = (t < bhi && k + p < a.R) ? (bf16)a.xdbl[(long)t * a.ldp + k + p] : (bf16)0.0f;
+          for (int ks = 0; ks < KS; ++ks) {
+            const bf16x8 af = *(const bf16x8*)(dl_s + row * DLS + ks * 32 + (lane >> 4) * 8);
             acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, wdt[ks], acc, 0, 0, 0);
           }
-          // D layout: lane holds rows 4*(lane>>4) + i, column (lane & 15)
+          // D layout: lane holds rows 4 (lane >> 4) + i, column (lane & 15)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) dt_s[rt * 16 + 4 * (lane >> 4) + i][dcol] = softplus_f(acc[i] + dtb_col);
+          for (int i = 0; i < 4; ++i) {
+            const int rr = rt * 16 + 4 * (lane >> 4) + i;
+            const float dtv = softplus_f(acc[i] + dtb_col);
+            pre_s[rr][dcol] = make_float2(dtv, dtv * u_s[rr][dcol]);
+          }
         }
       } else {
         const T* W = (const T*)a.dt_w;
-        for (int i = 0; i < 8; ++i) {
-          const int r = 8 * w + i;
-          const int t = blo + r;
+        const float dtb = a.dt_b[e];
+        for (int i = 0; i < TB / 4; ++i) {
+          const int rr = (TB / 4) * w + i;
+          const int t = blo + rr;
           float acc = 0.0f;
           if (t < bhi)
             for (int k = 0; k < a.R; ++k)
               acc = fmaf(a.xdbl[(long)t * a.ldp + k], to_f32(W[(long)e * a.R + k]), acc);
-          dt_s[r][lane] = softplus_f(acc + dtb_lane);
+          const float dtv = softplus_f(acc + dtb);
+          pre_s[rr][lane] = make_float2(dtv, dtv * u_s[rr][lane]);
         }
       }
       __syncthreads();
     }
     // ---------------- B: the recurrence, right to left ----------------
-    for (int r = nt - 1; r >= 0; --r) {
-      const float dtv = dt_s[r][lane];
-      const float dtu = dtv * u_s[r][lane];
+    auto step = [&](int r) {
+      const float2 p = pre_s[r][lane];
       const f32x4 Bv = bc_s[r][w];
-      if (SUMMARY) sdt += dtv;
-      if constexpr (!SUMMARY) {
+      if constexpr (SUMMARY) {
+        sdt += p.x;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) h[i] = fmaf(exp2_fast(p.x * A2[i]), h[i], p.y * Bv[i]);
+      } else {
         const f32x4 Cv = bc_s[r][4 + w];
         float y = 0.0f;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          h[i] = fmaf(exp2_fast(dtv * A2[i]), h[i], dtu * Bv[i]);
+          h[i] = fmaf(exp2_fast(p.x * A2[i]), h[i], p.y * Bv[i]);
           y = fmaf(Cv[i], h[i], y);
         }
         yp_s[w][r][lane] = y;
-      } else {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) h[i] = fmaf(exp2_fast(dtv * A2[i]), h[i], dtu * Bv[i]);
       }
+    };
+    if (nt == TB) {
+#pragma unroll
+      for (int r = TB - 1; r >= 0; --r) step(r);
+    } else {
+      for (int r = nt - 1; r >= 0; --r) step(r);
     }
     __syncthreads();
     // ---------------- C: combine and store ----------------
     if constexpr (!SUMMARY) {
-      T* y = (T*)a.y;
+      if (r8 < nt) {
+        float v[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int r = 8 * w + i;
-        if (r < nt) {
-          float v = yp_s[0][r][lane] + yp_s[1][r][lane] + yp_s[2][r][lane] + yp_s[3][r][lane] +
-                    du_s[r][lane];
-          v *= g_s[r][lane];
-          y[(long)(blo + r) * E + e] = from_f32<T>(v);
+        for (int i = 0; i < 8; ++i) {
+          const int cc = 8 * c8 + i;
+          v[i] = (yp_s[0][r8][cc] + yp_s[1][r8][cc] + yp_s[2][r8][cc] + yp_s[3][r8][cc] + du_s[r8][cc]) *
+                 g_s[r8][cc];
         }
+        store8((T*)a.y + (long)(blo + r8) * E + ea, v);
       }
       __syncthreads();
     }
   }
-  if (SUMMARY) {
+  if constexpr (SUMMARY) {
     const long base = (long)ci * NS * E;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
