@@ -25,6 +25,8 @@
  *  - Activation tensors and the weights listed as "act" use the activation
  *    dtype (R2L_F32 or R2L_BF16).  Scan state, dt, B, C and all
  *    accumulations are fp32 in both cases.
+ *  - Alignment: r2l_layer_fwd needs every tensor pointer it takes to be
+ *    16-byte aligned (torch and hipMalloc allocations are).
  *  - Ownership: the caller allocates and owns every buffer (weights,
  *    activations, cu_seqlens, workspace).  The library allocates no device
  *    memory and keeps no pointer after a call returns.

@@ -242,10 +242,12 @@ int r2l_layer_fwd(const r2l_dims* d, r2l_dtype act, uint32_t flags, const r2l_we
     return R2L_ERR_INVALID_ARG;
   const bool no_ln = flags & R2L_FLAG_NO_LN;
   if (!no_ln && (!w->ln_w || !w->ln_b)) return R2L_ERR_INVALID_ARG;
-  if (act == R2L_BF16) {
-    const void* ptrs[] = {h_in, w->in_proj_w, w->conv_w, w->conv_b, w->x_proj_w, w->dt_proj_w, w->out_proj_w};
+  {
+    // every tensor is accessed with 16-byte vectors somewhere on the path
+    const void* ptrs[] = {h_in, h_out, branch_out, w->in_proj_w, w->conv_w, w->conv_b, w->x_proj_w,
+                          w->dt_proj_w, w->out_proj_w, w->ln_w, w->ln_b};
     for (const void* p : ptrs)
-      if (!aligned16(p)) return R2L_ERR_INVALID_ARG;
+      if (p && !aligned16(p)) return R2L_ERR_INVALID_ARG;
   }
   const LayerPlan lp = plan_layer(d, act, n_tokens, nseq, max_seqlen);
   if (!workspace || workspace_bytes < lp.total) return R2L_ERR_WORKSPACE;

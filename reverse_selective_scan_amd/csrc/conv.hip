@@ -93,24 +93,38 @@ __global__ __launch_bounds__(256) void conv_xproj_kernel(int Tn, int E, int P,
     for (int r = 0; r < 16; ++r) acc[c][r] = 0.0f;
 
   const bf16x8 zero8 = {};
-  for (int k0 = cbeg; k0 < cbeg + Ew; k0 += 16) {
+  // Operands of one 16-channel k-step; the next step's are loaded while the
+  // current one is computed (the loads would otherwise stall every step).
+  struct Step {
+    bf16x8 wv[4], bv, xv[KC], wx[NCS];
+  };
+  auto load_step = [&](Step& s, int k0) {
     const int c0 = k0 + kh * 8;
-    bf16x8 wv[4];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) wv[q] = *(const bf16x8*)(cw + (long)c0 * KC + 8 * q);
-    const bf16x8 bv = *(const bf16x8*)(cb + c0);
+    for (int q = 0; q < 4; ++q) s.wv[q] = *(const bf16x8*)(cw + (long)c0 * KC + 8 * q);
+    s.bv = *(const bf16x8*)(cb + c0);
+#pragma unroll
+    for (int j = 0; j < KC; ++j) s.xv[j] = (t + j < se) ? *(const bf16x8*)(x + (long)(t + j) * ld_x + c0) : zero8;
+#pragma unroll
+    for (int c = 0; c < NCS; ++c) {
+      const int row = c * 32 + tr;
+      s.wx[c] = row < P ? *(const bf16x8*)(Wx + (long)row * E + c0) : zero8;
+    }
+  };
+  Step cur, nxt;
+  load_step(cur, cbeg);
+  for (int k0 = cbeg; k0 < cbeg + Ew; k0 += 16) {
+    if (k0 + 16 < cbeg + Ew) load_step(nxt, k0 + 16);
+    const int c0 = k0 + kh * 8;
     float ca[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) ca[i] = (float)bv[i];
+    for (int i = 0; i < 8; ++i) ca[i] = (float)cur.bv[i];
 #pragma unroll
     for (int j = 0; j < KC; ++j) {
-      if (t + j < se) {
-        const bf16x8 xv = *(const bf16x8*)(x + (long)(t + j) * ld_x + c0);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const int el = i * KC + (KC - 1 - j);  // channel i, tap K-1-j
-          ca[i] = fmaf((float)wv[el >> 3][el & 7], (float)xv[i], ca[i]);
-        }
+      for (int i = 0; i < 8; ++i) {
+        const int el = i * KC + (KC - 1 - j);  // channel i, tap K-1-j
+        ca[i] = fmaf((float)cur.wv[el >> 3][el & 7], (float)cur.xv[j][i], ca[i]);
       }
     }
     bf16x8 af;
@@ -119,11 +133,9 @@ __global__ __launch_bounds__(256) void conv_xproj_kernel(int Tn, int E, int P,
     if (!tv) af = zero8;
     if (u_out != nullptr && tv) *(bf16x8*)(u_out + (long)t * E + c0) = af;
 #pragma unroll
-    for (int c = 0; c < NCS; ++c) {
-      const int row = c * 32 + tr;
-      const bf16x8 bfr = row < P ? *(const bf16x8*)(Wx + (long)row * E + c0) : zero8;
-      acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bfr, acc[c], 0, 0, 0);
-    }
+    for (int c = 0; c < NCS; ++c)
+      acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, cur.wx[c], acc[c], 0, 0, 0);
+    cur = nxt;
   }
   // D layout: lane holds output column (lane & 31) of each 32-wide slice and
   // token rows 8*(r/4) + 4*(lane/32) + r%4.

@@ -13,7 +13,34 @@
 
 namespace r2l {
 
-template <typename T, int VPL>
+// Lane layout: chunk i of the row (i = 0 .. D/512 - 1) gives lane l the 8
+// consecutive elements [512 i + 8 l, +8): 16-byte loads of h and stores of h+
+// (bf16), 2 x 16-byte loads of the fp32 branch input.
+R2L_DEV void ld8(const float* p, float v[8]) {
+  const f32x4 a = *(const f32x4*)p, b = *(const f32x4*)(p + 4);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) { v[i] = a[i]; v[4 + i] = b[i]; }
+}
+R2L_DEV void ld8(const bf16* p, float v[8]) {
+  const bf16x8 q = *(const bf16x8*)p;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] = (float)q[i];
+}
+R2L_DEV void st8(float* p, const float v[8]) {
+  *(f32x4*)p = f32x4{v[0], v[1], v[2], v[3]};
+  *(f32x4*)(p + 4) = f32x4{v[4], v[5], v[6], v[7]};
+}
+R2L_DEV void st8(bf16* p, const float v[8]) {
+  bf16x8 q;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) q[i] = (bf16)v[i];
+  *(bf16x8*)p = q;
+}
+template <typename T> struct Raw8h;
+template <> struct Raw8h<bf16> { bf16x8 v; };
+template <> struct Raw8h<float> { f32x4 a, b; };
+
+template <typename T, int NCH>
 __global__ __launch_bounds__(256) void ln_gate_kernel(int Tn, int D, const float* __restrict__ o,
                                                       const T* h_in, T* h_out,  // may alias
                                                       const float* __restrict__ gamma,
@@ -21,6 +48,78 @@ __global__ __launch_bounds__(256) void ln_gate_kernel(int Tn, int D, const float
                                                       const float* __restrict__ s,
                                                       float* __restrict__ branch, int no_ln,
                                                       float eps) {
+  const int lane = lane_id();
+  const int row = blockIdx.x * 4 + wave_id();
+  if (row >= Tn) return;
+  const int nch = D / 512;  // D % 512 == 0 here (other widths use the generic kernel)
+  const float* orow = o + (long)row * D;
+  float v[NCH][8];
+  float sum = 0.0f;
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    if (c < nch) {
+      ld8(orow + 512 * c + 8 * lane, v[c]);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) sum += v[c][i];
+    }
+  }
+  const float invD = 1.0f / (float)D;
+  if (!no_ln) {
+    const float mu = wave_sum(sum) * invD;
+    float sq = 0.0f;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c)
+      if (c < nch)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          v[c][i] -= mu;
+          sq = fmaf(v[c][i], v[c][i], sq);
+        }
+    const float rstd = 1.0f / sqrtf(wave_sum(sq) * invD + eps);
+#pragma unroll
+    for (int c = 0; c < NCH; ++c)
+      if (c < nch) {
+        float gm[8], bt[8];
+        ld8(gamma + 512 * c + 8 * lane, gm);
+        ld8(beta + 512 * c + 8 * lane, bt);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[c][i] = fmaf(gm[i], v[c][i] * rstd, bt[i]);
+      }
+  }
+  const float g = tanhf(s[0]);
+  const long rb = (long)row * D;
+#pragma unroll
+  for (int c = 0; c < NCH; ++c)
+    if (c < nch) {
+      const long off = rb + 512 * c + 8 * lane;
+      if (branch != nullptr) st8(branch + off, v[c]);
+      if (g == 0.0f) {
+        // a zero gate copies h bit for bit (no arithmetic on it at all)
+        if constexpr (sizeof(T) == 2) {
+          *(bf16x8*)(h_out + off) = *(const bf16x8*)(h_in + off);
+        } else {
+          *(f32x4*)(h_out + off) = *(const f32x4*)(h_in + off);
+          *(f32x4*)(h_out + off + 4) = *(const f32x4*)(h_in + off + 4);
+        }
+      } else {
+        float hv[8];
+        ld8(h_in + off, hv);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) hv[i] = fmaf(g, v[c][i], hv[i]);
+        st8(h_out + off, hv);
+      }
+    }
+}
+
+// Generic widths (D a multiple of 64): lane l holds elements 64 i + l.
+template <typename T, int VPL>
+__global__ __launch_bounds__(256) void ln_gate_generic_kernel(int Tn, int D, const float* __restrict__ o,
+                                                              const T* h_in, T* h_out,  // may alias
+                                                              const float* __restrict__ gamma,
+                                                              const float* __restrict__ beta,
+                                                              const float* __restrict__ s,
+                                                              float* __restrict__ branch, int no_ln,
+                                                              float eps) {
   const int lane = lane_id();
   const int row = blockIdx.x * 4 + wave_id();
   if (row >= Tn) return;
@@ -70,10 +169,21 @@ hipError_t ln_gate(int Tn, int D, const float* o, const T* h_in, T* h_out, const
                    hipStream_t st) {
   if (Tn <= 0) return hipSuccess;
   dim3 grid((Tn + 3) / 4), block(256);
+  const int nl = no_ln ? 1 : 0;
+  if (D % 512 == 0 && D <= 8192) {
+#define R2L_LNV(C) \
+  hipLaunchKernelGGL((ln_gate_kernel<T, C>), grid, block, 0, st, Tn, D, o, h_in, h_out, gamma, beta, s, branch, nl, eps)
+    if (D <= 1024) R2L_LNV(2);
+    else if (D <= 2048) R2L_LNV(4);
+    else if (D <= 4096) R2L_LNV(8);
+    else R2L_LNV(16);
+#undef R2L_LNV
+    return hipGetLastError();
+  }
   const int cnt = D / 64;
-#define R2L_LN(V)                                                                              \
-  hipLaunchKernelGGL((ln_gate_kernel<T, V>), grid, block, 0, st, Tn, D, o, h_in, h_out, gamma, \
-                     beta, s, branch, no_ln ? 1 : 0, eps)
+#define R2L_LN(V)                                                                                      \
+  hipLaunchKernelGGL((ln_gate_generic_kernel<T, V>), grid, block, 0, st, Tn, D, o, h_in, h_out, gamma, \
+                     beta, s, branch, nl, eps)
   if (cnt <= 4) R2L_LN(4);
   else if (cnt <= 16) R2L_LN(16);
   else if (cnt <= 32) R2L_LN(32);
