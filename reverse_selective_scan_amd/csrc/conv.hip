@@ -98,17 +98,25 @@ __global__ __launch_bounds__(256) void conv_xproj_kernel(int Tn, int E, int P,
   struct Step {
     bf16x8 wv[4], bv, xv[KC], wx[NCS];
   };
+  // Loads are unconditional, from clamped (valid) rows; masks are applied
+  // when the values are used.  (A per-lane branch around a load makes both
+  // paths write the same registers and forces an immediate wait.)
+  const int tt = min(t, Tn - 1);
+  const int xlast = (tv ? se : tt + 1) - 1;   // last row this lane may read
+  bool xok[KC];
+#pragma unroll
+  for (int j = 0; j < KC; ++j) xok[j] = tv && t + j < se;
   auto load_step = [&](Step& s, int k0) {
     const int c0 = k0 + kh * 8;
 #pragma unroll
     for (int q = 0; q < 4; ++q) s.wv[q] = *(const bf16x8*)(cw + (long)c0 * KC + 8 * q);
     s.bv = *(const bf16x8*)(cb + c0);
 #pragma unroll
-    for (int j = 0; j < KC; ++j) s.xv[j] = (t + j < se) ? *(const bf16x8*)(x + (long)(t + j) * ld_x + c0) : zero8;
+    for (int j = 0; j < KC; ++j) s.xv[j] = *(const bf16x8*)(x + (long)min(tt + j, xlast) * ld_x + c0);
 #pragma unroll
     for (int c = 0; c < NCS; ++c) {
-      const int row = c * 32 + tr;
-      s.wx[c] = row < P ? *(const bf16x8*)(Wx + (long)row * E + c0) : zero8;
+      const int row = min(c * 32 + tr, P - 1);
+      s.wx[c] = *(const bf16x8*)(Wx + (long)row * E + c0);
     }
   };
   Step cur, nxt;
@@ -121,10 +129,11 @@ __global__ __launch_bounds__(256) void conv_xproj_kernel(int Tn, int E, int P,
     for (int i = 0; i < 8; ++i) ca[i] = (float)cur.bv[i];
 #pragma unroll
     for (int j = 0; j < KC; ++j) {
+      const bf16x8 xj = xok[j] ? cur.xv[j] : zero8;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const int el = i * KC + (KC - 1 - j);  // channel i, tap K-1-j
-        ca[i] = fmaf((float)cur.wv[el >> 3][el & 7], (float)cur.xv[j][i], ca[i]);
+        ca[i] = fmaf((float)cur.wv[el >> 3][el & 7], (float)xj[i], ca[i]);
       }
     }
     bf16x8 af;
@@ -133,8 +142,10 @@ __global__ __launch_bounds__(256) void conv_xproj_kernel(int Tn, int E, int P,
     if (!tv) af = zero8;
     if (u_out != nullptr && tv) *(bf16x8*)(u_out + (long)t * E + c0) = af;
 #pragma unroll
-    for (int c = 0; c < NCS; ++c)
-      acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, cur.wx[c], acc[c], 0, 0, 0);
+    for (int c = 0; c < NCS; ++c) {
+      const bf16x8 bfr = (c * 32 + tr < P) ? cur.wx[c] : zero8;
+      acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bfr, acc[c], 0, 0, 0);
+    }
     cur = nxt;
   }
   // D layout: lane holds output column (lane & 31) of each 32-wide slice and
