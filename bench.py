@@ -48,9 +48,20 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="serve_b8")
-    ap.add_argument("--cpu-sample-seqs", type=int, default=2)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="approximate CPU time spent on the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calib-mib", type=int, default=0,
+                    help="run one plain device copy of this many MiB first (counter calibration)")
+    ap.add_argument("--calib-mib", type=float, default=0.0,
+                    help="with --summarize: size of the calibration copy that was profiled")
+    ap.add_argument("--summarize", nargs="+", metavar=("OUT_MD", "DIR"),
+                    help="write a profile summary from rocprofv3 outputs instead of benchmarking: "
+                         "OUT_MD TRACE_DIR [FETCH_DIR WRITE_DIR]")
     args = ap.parse_args()
+    if args.summarize:
+        summarize_profiles(args.summarize, args.calib_mib * 1024.0)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU: this build runs the layer on a single MI355X "
@@ -80,6 +91,15 @@ def main():
 
     def step():
         B.r2l_layer_fwd(h, w, cu, out=out, workspace=ws, nseq=nseq, max_seqlen=max_seqlen)
+
+    if args.copy_calib_mib > 0:
+        # a plain copy kernel of known size, for scaling the HBM byte counters
+        n = args.copy_calib_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     print(f"[bench] workload {wl.name}: T={T} D={D} E={E} N={N} R={R}, warmup {args.warmup}", flush=True)
     for _ in range(args.warmup):
@@ -132,17 +152,27 @@ def main():
     roofline = None
     if dom is not None:
         k = kernels[dom]
+        tr = measured_traffic(dom)
+        traffic = None if tr is None else tr["read_bytes"] + tr["write_bytes"]
         if dom in flops:
             roofline = {"kernel": dom, "bound": "mfma", "achieved": k["achieved_tflops"],
-                        "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": k["frac"], "traffic": None}
+                        "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": k["frac"], "traffic": traffic,
+                        "traffic_detail": tr}
         elif dom in bytes_:
             roofline = {"kernel": dom, "bound": "hbm", "achieved": k["achieved_gbs"], "peak": HBM_PEAK_GBS,
-                        "unit": "GB/s", "frac": k["frac"], "traffic": None}
+                        "unit": "GB/s", "frac": k["frac"], "traffic": traffic,
+                        "traffic_detail": tr}
+        if dom == "scan_main":
+            # the recurrence is bound by the vector ALU, not by HBM: report that roofline
+            roofline = {"kernel": dom, "bound": "alu", "achieved": k["valu_gops"], "peak": round(VALU_PEAK_GOPS, 1),
+                        "unit": "Gop/s (state-update lane-ops, 5 per state per token)", "frac": k["valu_frac"],
+                        "hbm_gbs": k["achieved_gbs"], "hbm_frac": k["frac"], "traffic": traffic,
+                        "traffic_detail": tr}
     scan = kernels.get("scan_main", {})
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(wl, W, h_np, args.cpu_sample_seqs)
+        cpu = cpu_baseline(wl, W, h_np, args.cpu_seconds)
 
     rec = {
         "metric": "R2L layer tokens/sec at B=8,L=4096,D=2048; scan HBM GB/s (% peak)",
@@ -169,24 +199,129 @@ def main():
     print(json.dumps(rec), flush=True)
 
 
-def cpu_baseline(wl, W, h_np, nseqs):
-    """Time the fp64 oracle on whole sequences of the same workload."""
+KERNEL_SOURCES = {  # the source file that defines each timed kernel
+    "in_proj_gemm": "gemm.hip", "out_proj_gemm": "gemm.hip", "conv_xproj": "conv.hip",
+    "scan_main": "scan.hip", "scan_summary": "scan.hip", "ln_gate": "ln.hip", "plan_chunks": "scan.hip",
+}
+ROCPROF_NAMES = {  # substring of the demangled kernel name in rocprofv3 output
+    "in_proj_gemm": "gemm_bf16_nt_kernel<128, 128, false>", "out_proj_gemm": "gemm_bf16_nt_kernel<128, 128, true>",
+    "conv_xproj": "conv_xproj_kernel", "scan_main": "false, 4>(r2l::ScanArgs)",
+    "scan_summary": "true, 4>(r2l::ScanArgs)", "ln_gate": "ln_gate_kernel",
+}
+PROFILE_JSON = os.path.join(ROOT, "profiles", "traffic_serve_b8.json")
+
+
+def _source_hash(kernel):
+    import hashlib
+    f = os.path.join(ROOT, "reverse_selective_scan_amd", "csrc", KERNEL_SOURCES[kernel])
+    return hashlib.sha256(open(f, "rb").read()).hexdigest()[:16]
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch of `kernel` from the committed counter summary,
+    or None if there is none or the kernel source changed since."""
+    try:
+        rec = json.load(open(PROFILE_JSON))["kernels"][kernel]
+    except (OSError, KeyError, ValueError):
+        return None
+    if rec.get("source_sha256") != _source_hash(kernel):
+        return None
+    return {"read_bytes": rec["read_bytes"], "write_bytes": rec["write_bytes"],
+            "copy_scale": rec["copy_scale"], "source": os.path.relpath(PROFILE_JSON, ROOT)}
+
+
+def _rocprof_rows(d, name):
+    import csv
+    import glob
+    files = glob.glob(os.path.join(d, "**", name), recursive=True)
+    rows = []
+    for f in files:
+        rows += list(csv.DictReader(open(f)))
+    return rows
+
+
+def summarize_profiles(argv, size_kib=0.0):
+    """OUT_MD TRACE_DIR [FETCH_DIR WRITE_DIR]: kernel-trace stats and, when
+    counter runs are given, HBM bytes per dispatch scaled by the copy kernel."""
+    out_md, trace_dir = argv[0], argv[1]
+    lines = ["# Kernel profile: " + os.path.basename(out_md), "",
+             "Commands (from the repository root, TMPDIR=/tmp):", "",
+             "    rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/prof_trace -o run -- "
+             "python -u bench.py --steps 10 --warmup 3 --no-cpu-baseline",
+             "    rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/prof_fetch -o run -- "
+             "python -u bench.py --steps 2 --warmup 1 --no-cpu-baseline --copy-calib-mib 1024",
+             "    rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/prof_write -o run -- "
+             "python -u bench.py --steps 2 --warmup 1 --no-cpu-baseline --copy-calib-mib 1024",
+             "    python bench.py --summarize " + out_md + " gpurun_out/prof_trace gpurun_out/prof_fetch "
+             "gpurun_out/prof_write --calib-mib 1024", ""]
+    stats = _rocprof_rows(trace_dir, "*kernel_stats.csv")
+    if stats:
+        lines += ["## rocprofv3 --kernel-trace --stats", "", "| kernel | calls | avg us | total ms | % |",
+                  "|---|---|---|---|---|"]
+        for r in sorted(stats, key=lambda r: -float(r["TotalDurationNs"])):
+            lines.append(f"| `{r['Name'][:90]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                         f"{float(r['TotalDurationNs']) / 1e6:.3f} | {float(r['Percentage']):.1f} |")
+        lines.append("")
+    if len(argv) >= 4:
+        def per_kernel(d, counter):
+            acc = {}
+            for r in _rocprof_rows(d, "*counter_collection.csv"):
+                if r["Counter_Name"] != counter:
+                    continue
+                acc.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+            return acc
+        fetch, write = per_kernel(argv[2], "FETCH_SIZE"), per_kernel(argv[3], "WRITE_SIZE")
+        copy_k = [k for k in fetch if "copy" in k.lower() or "elementwise" in k.lower()]
+        calib = {}
+        for k in copy_k:   # the largest copy dispatch is the calibration copy
+            f, wr = max(fetch[k]), max(write.get(k, [0]))
+            calib = {"kernel": k, "fetch_kib": f, "write_kib": wr}
+        rec = {"copy": calib, "kernels": {}}
+        lines += ["## HBM traffic (rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE, KiB per dispatch)", ""]
+        if calib and size_kib:
+            rs, ws = size_kib / calib["fetch_kib"], size_kib / calib["write_kib"]
+            lines.append(f"Calibration: plain copy of {size_kib:.0f} KiB read as FETCH {calib['fetch_kib']:.0f} KiB, "
+                         f"WRITE {calib['write_kib']:.0f} KiB -> scale read x{rs:.4f}, write x{ws:.4f}.")
+            lines += ["", "| kernel | FETCH KiB | WRITE KiB | read MB (scaled) | write MB (scaled) |", "|---|---|---|---|---|"]
+            for ours, sub in ROCPROF_NAMES.items():
+                ks = [k for k in fetch if sub in k]
+                if not ks:
+                    continue
+                f = sum(sum(fetch[k]) / len(fetch[k]) for k in ks) / len(ks)
+                wv = [sum(write[k]) / len(write[k]) for k in ks if k in write]
+                wr = sum(wv) / len(wv) if wv else 0.0
+                rb, wb = f * 1024 * rs, wr * 1024 * ws
+                rec["kernels"][ours] = {"fetch_kib": f, "write_kib": wr, "read_bytes": round(rb),
+                                        "write_bytes": round(wb), "copy_scale": [round(rs, 5), round(ws, 5)],
+                                        "source_sha256": _source_hash(ours)}
+                lines.append(f"| {ours} | {f:.0f} | {wr:.0f} | {rb / 1e6:.1f} | {wb / 1e6:.1f} |")
+            json.dump(rec, open(PROFILE_JSON, "w"), indent=1)
+        lines.append("")
+    open(out_md, "w").write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def cpu_baseline(wl, W, h_np, seconds):
+    """Time the fp64 oracle on whole sequences of the same workload, taking
+    sequences in order until about `seconds` of CPU work have been done."""
     from threadpoolctl import threadpool_info
 
     from oracle import r2l_oracle as O
 
     cu = wl.cu_seqlens()
-    nseqs = max(1, min(nseqs, wl.nseq))
-    t0, t1 = int(cu[0]), int(cu[nseqs])
-    sample_cu = cu[: nseqs + 1] - cu[0]
-    print(f"[bench] cpu baseline: oracle on {nseqs} sequence(s), {t1 - t0} tokens", flush=True)
-    t = time.perf_counter()
-    O.reverse_mamba_layer(h_np[t0:t1], sample_cu, W, float(W["s"]))
-    dt = time.perf_counter() - t
+    done_tok, done_seq, dt = 0, 0, 0.0
+    while done_seq < wl.nseq and (dt < seconds or done_seq == 0):
+        t0, t1 = int(cu[done_seq]), int(cu[done_seq + 1])
+        print(f"[bench] cpu baseline: oracle on sequence {done_seq} ({t1 - t0} tokens)", flush=True)
+        t = time.perf_counter()
+        O.reverse_mamba_layer(h_np[t0:t1], np.array([0, t1 - t0]), W, float(W["s"]))
+        dt += time.perf_counter() - t
+        done_tok += t1 - t0
+        done_seq += 1
     threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
-    return {"value": round((t1 - t0) / dt, 1), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{nseqs} whole sequence(s) of {wl.name} ({t1 - t0} tokens), fp64 numpy oracle, "
-                      f"{dt:.1f} s on {os.cpu_count()} visible host cores"}
+    return {"value": round(done_tok / dt, 1), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"first {done_seq} whole sequence(s) of {wl.name} ({done_tok} tokens), fp64 numpy oracle, "
+                      f"{dt:.1f} s with a BLAS pool of {threads} thread(s)"}
 
 
 if __name__ == "__main__":
