@@ -1,15 +1,27 @@
 // Dense projections C = A . B^T (in_proj and out_proj of the Mamba-1 block,
 // "Bifocal Diffusion Language Models", §3.4 step 2).
 //
-// bf16: MFMA v_mfma_f32_32x32x16_bf16 on gfx950.  A block of 256 threads
-// (4 waves, 2 x 2) computes a BM x BN tile; each wave owns a (BM/2) x (BN/2)
-// sub-tile made of 32 x 32 MFMA tiles.  Both operands are K-contiguous, so a
-// lane's MFMA fragment (8 consecutive k of one row) is one 16-byte LDS read.
-// K is walked in BK = 64 steps through a double-buffered LDS tile; the next
-// step's global loads are issued into registers before the current step's
-// MFMAs.  Rows of the LDS tiles are padded by 16 bytes so that the 32 rows a
-// fragment read touches spread over the banks.  Block indices are remapped so
-// that each XCD works on a contiguous, group-M-ordered range of tiles.
+// Two bf16 kernels on the MFMA matrix cores (v_mfma_f32_32x32x16_bf16):
+//
+//  * gemm_bf16_big_kernel -- the large-problem kernel.  One block of 256
+//    threads (one wave per SIMD) owns a 256 x 256 tile; each wave owns a
+//    128 x 128 quarter (16 accumulator tiles, 256 AGPRs), so every 16-byte
+//    LDS fragment read feeds four MFMAs.  K is walked in 32-wide steps
+//    through four LDS stages filled directly from global memory by
+//    buffer_load ... lds (no VGPR round trip; rows past M or N read as zero
+//    through the buffer descriptor's range).  The block barrier of step kt
+//    waits for step kt+1's data, so each wave can read the first fragments
+//    of the next step before finishing the current one, and loads run two
+//    steps ahead.  Stage rows are 64 bytes with a 16-byte-chunk XOR swizzle
+//    so that fragment reads are bank-conflict free.  The MFMA operands are
+//    swapped (B-tile rows as the "A" operand) so that each lane ends up with
+//    4 consecutive output columns of one row: 8- or 16-byte stores.
+//  * gemm_bf16_nt_kernel -- the general kernel (any shape with K a multiple
+//    of 8): 128 x 128 tiles, 2 x 2 waves of 64 x 64, register-staged
+//    double-buffered LDS tiles.
+//
+// Block indices are remapped so that each XCD works on a contiguous,
+// group-M-ordered range of tiles (tiles that share operands share an L2).
 #include "kernels.h"
 
 namespace r2l {
@@ -124,6 +136,196 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_nt_kernel(int M, int N, int 
     }
 }
 
+
+// ---------------------------------------------------------------------------
+// Large-problem kernel (see the file header).
+// ---------------------------------------------------------------------------
+namespace {
+
+constexpr int kBigBM = 256, kBigBN = 256, kBigBK = 32, kBigST = 4;
+constexpr int kBigCPR = kBigBK / 8;            // 16-byte chunks per stage row
+constexpr int kBigLPT = 2 * kBigCPR;           // global->LDS loads per thread per stage
+constexpr int kBigSROW = kBigBK * 2;           // stage row bytes
+constexpr int kBigSBYTES = (kBigBM + kBigBN) * kBigSROW;
+constexpr int kBigSH = 2;                      // swizzle: chunk ^= (row >> 2) & 3
+
+// s_waitcnt immediate that waits for vmcnt <= n and leaves the other counters alone
+constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
+// 16-byte per lane global -> LDS copy; lane l writes lds + 16 l.
+R2L_DEV void lds_dma16(__amdgpu_buffer_rsrc_t r, void* lds, unsigned voff, unsigned soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voff, soff, 0, 0);
+}
+
+R2L_DEV int big_swz(int row, int chunk) { return chunk ^ ((row >> kBigSH) & (kBigCPR - 1)); }
+
+}  // namespace
+
+template <bool OUT_F32>
+__global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(int M, int N, int K,
+                                                               const bf16* __restrict__ A, long lda,
+                                                               const bf16* __restrict__ B, long ldb,
+                                                               void* __restrict__ Cv, long ldc) {
+  constexpr int BM = kBigBM, BN = kBigBN, BK = kBigBK, ST = kBigST, LPT = kBigLPT, SROW = kBigSROW;
+  // one LDS object per stage: the compiler then knows that reading one stage
+  // does not have to wait for the loads still in flight into another
+  __shared__ __attribute__((aligned(1024))) char s0[kBigSBYTES];
+  __shared__ __attribute__((aligned(1024))) char s1[kBigSBYTES];
+  __shared__ __attribute__((aligned(1024))) char s2[kBigSBYTES];
+  __shared__ __attribute__((aligned(1024))) char s3[kBigSBYTES];
+  auto stage = [&](int s) -> char* { return s == 0 ? s0 : s == 1 ? s1 : s == 2 ? s2 : s3; };
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
+  const int wm = (wave >> 1) * 128, wn = (wave & 1) * 128;
+  const int nTm = (M + BM - 1) / BM, nTn = (N + BN - 1) / BN;
+  const int lid = xcd_remap(blockIdx.x, nTm * nTn);
+  constexpr int G = 4;
+  const int per_group = G * nTn;
+  const int first_m = (lid / per_group) * G;
+  const int gsz = min(nTm - first_m, G);
+  const int tm = first_m + (lid % per_group) % gsz;
+  const int tn = (lid % per_group) / gsz;
+  const int m0 = tm * BM, n0 = tn * BN;
+
+  // Buffer descriptors over this tile's rows: reads past row M (N) return 0.
+  const __amdgpu_buffer_rsrc_t rA = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(A + (long)m0 * lda), 0, (int)((long)min(BM, M - m0) * lda * 2), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rB = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(B + (long)n0 * ldb), 0, (int)((long)min(BN, N - n0) * ldb * 2), 0x00020000);
+  // Stage layout: rows [0, BM) hold A rows, rows [BM, BM+BN) hold B rows; load
+  // i of this thread fills 16-byte slot i*256 + tid, i.e. row (i*256+tid)/4,
+  // physical chunk tid%4, which holds logical k-chunk big_swz(row, tid%4).
+  unsigned voff[LPT];
+#pragma unroll
+  for (int i = 0; i < LPT; ++i) {
+    const int p = i * 256 + tid, row = p / kBigCPR;
+    const int kc = big_swz(row, p % kBigCPR);
+    voff[i] = i < LPT / 2 ? (unsigned)(((long)row * lda + kc * 8) * 2)
+                          : (unsigned)(((long)(row - BM) * ldb + kc * 8) * 2);
+  }
+  const int nk = K / BK;
+  auto issue = [&](int s, int kt) {  // k-step kt -> stage s (past the end: reload the last step)
+    char* base = stage(s);
+    const unsigned kb = (unsigned)(min(kt, nk - 1) * BK * 2);
+#pragma unroll
+    for (int i = 0; i < LPT; ++i)
+      lds_dma16(i < LPT / 2 ? rA : rB, base + (i * 256 + wave * 64) * 16, voff[i], kb);
+  };
+
+  // fragment byte offsets inside a stage: k-chunk fh (first 16 of the step) and 2 + fh
+  const int fr = lane & 31, fh = lane >> 5;
+  int offA0[4], offB0[4], offA1[4], offB1[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int ra = wm + 32 * i + fr, rb = BM + wn + 32 * i + fr;
+    offA0[i] = ra * SROW + big_swz(ra, fh) * 16;
+    offB0[i] = rb * SROW + big_swz(rb, fh) * 16;
+    offA1[i] = ra * SROW + big_swz(ra, 2 + fh) * 16;
+    offB1[i] = rb * SROW + big_swz(rb, 2 + fh) * 16;
+  }
+  bf16x8 fa0[4], fb0[4], fa1[4], fb1[4];
+  auto rd0 = [&](const char* base) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      fa0[i] = *(const bf16x8*)(base + offA0[i]);
+      fb0[i] = *(const bf16x8*)(base + offB0[i]);
+    }
+  };
+  auto rd1 = [&](const char* base) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      fa1[i] = *(const bf16x8*)(base + offA1[i]);
+      fb1[i] = *(const bf16x8*)(base + offB1[i]);
+    }
+  };
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+  // acc[i][j] = (B rows wn+32j..) x (A rows wm+32i..)^T = C^T sub-tile
+  auto mm0 = [&]() {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb0[j], fa0[i], acc[i][j], 0, 0, 0);
+  };
+  auto mm1 = [&]() {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb1[j], fa1[i], acc[i][j], 0, 0, 0);
+  };
+
+  // Prologue: steps 0..2 in flight, step 0 visible to all waves, its first
+  // fragments in registers.  A bare s_barrier (no fence) is used so that the
+  // loads still in flight into other stages are not drained; the explicit
+  // vmcnt wait before it makes this wave's own loads of the awaited step
+  // complete, and the barrier then makes every wave's loads complete.
+  issue(0, 0);
+  issue(1, 1);
+  issue(2, 2);
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * LPT));
+  asm volatile("s_barrier" ::: "memory");
+  rd0(s0);
+  for (int kt0 = 0; kt0 < nk; kt0 += ST) {
+#pragma unroll
+    for (int s = 0; s < ST; ++s) {
+      const int kt = kt0 + s;
+      // this wave's loads of step kt+1 are done (step kt+2 may still fly);
+      // after the barrier every wave's are, and every wave has finished
+      // reading the stage of step kt-1, which is refilled with step kt+3
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(LPT));
+      asm volatile("s_barrier" ::: "memory");
+      issue((s + ST - 1) % ST, kt + ST - 1);
+      rd1(stage(s));
+      mm0();
+#pragma unroll
+      for (int q = 0; q < LPT; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // one global->LDS load
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+      }
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      }
+      rd0(stage((s + 1) % ST));  // step kt+1: visible since this step's barrier
+      mm1();
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      }
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+
+  // acc[i][j] register 4q+e holds C[m][n] with m = m0+wm+32i+(lane&31) and
+  // n = n0+wn+32j+8q+4*(lane>>5)+e: four consecutive columns per store.
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int m = m0 + wm + 32 * i + fr;
+    if (m >= M) continue;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int n = n0 + wn + 32 * j + 8 * q + 4 * fh;
+        if (n >= N) continue;
+        const f32x4 v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+        if (OUT_F32) {
+          *(f32x4*)((float*)Cv + (long)m * ldc + n) = v;
+        } else {
+          const bf16x4 b = {(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]};
+          *(bf16x4*)((bf16*)Cv + (long)m * ldc + n) = b;
+        }
+      }
+  }
+}
+
 template <int BM, int BN>
 static void launch_gemm(int M, int N, int K, const bf16* A, long lda, const bf16* B, long ldb,
                         void* C, long ldc, bool out_f32, hipStream_t st) {
@@ -139,9 +341,26 @@ static void launch_gemm(int M, int N, int K, const bf16* A, long lda, const bf16
 hipError_t gemm_bf16_nt(int M, int N, int K, const bf16* A, long lda, const bf16* B, long ldb,
                         void* C, long ldc, bool out_f32, hipStream_t st) {
   if (M <= 0 || N <= 0) return hipSuccess;
-  // 128 x 128 tiles (4 waves of 64 x 64, two blocks per CU) measured fastest
-  // on the layer's projection shapes; 256 x 256 (one block per CU) exposes
-  // more latency than it saves in LDS traffic.
+  const long big_tiles = (long)((M + kBigBM - 1) / kBigBM) * ((N + kBigBN - 1) / kBigBN);
+  const unsigned long align = out_f32 ? 16 : 8;
+  // The large-problem kernel needs whole 128-wide K chunks (four stages of
+  // 32), 4-column output groups, 16-byte operand rows, per-tile byte ranges
+  // that fit the 32-bit buffer descriptor, and enough tiles to fill the GPU.
+  const bool big = K % (kBigBK * kBigST) == 0 && N % 4 == 0 && ldc % 4 == 0 &&
+                   lda % 8 == 0 && ldb % 8 == 0 && ((uintptr_t)A & 15) == 0 &&
+                   ((uintptr_t)B & 15) == 0 && ((uintptr_t)C & (align - 1)) == 0 &&
+                   (long)kBigBM * lda * 2 < (1L << 31) && (long)kBigBN * ldb * 2 < (1L << 31) &&
+                   big_tiles >= 128;
+  if (big) {
+    if (out_f32)
+      hipLaunchKernelGGL((gemm_bf16_big_kernel<true>), dim3(big_tiles), dim3(256), 0, st, M, N, K, A, lda,
+                         B, ldb, C, ldc);
+    else
+      hipLaunchKernelGGL((gemm_bf16_big_kernel<false>), dim3(big_tiles), dim3(256), 0, st, M, N, K, A, lda,
+                         B, ldb, C, ldc);
+    return hipGetLastError();
+  }
+  // 128 x 128 tiles (4 waves of 64 x 64, two blocks per CU).
   launch_gemm<128, 128>(M, N, K, A, lda, B, ldb, C, ldc, out_f32, st);
   return hipGetLastError();
 }

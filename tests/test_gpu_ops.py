@@ -30,7 +30,9 @@ def _case(name):
 # dense projection (P14: numpy fp64 product of the same operands)
 # ---------------------------------------------------------------------------
 @pytest.mark.parametrize("M,N,K", [(1, 1, 8), (33, 17, 64), (128, 128, 64), (300, 520, 136),
-                                   (1031, 257, 2048), (640, 8192, 2048)])
+                                   (1031, 257, 2048), (640, 8192, 2048),
+                                   # large-tile kernel: ragged M and N, and an N%4 != 0 fallback
+                                   (8200, 2052, 512), (4099, 4096, 256), (8200, 2050, 512)])
 def test_gemm_bf16_matches_fp64_product(M, N, K):
     _case(f"gemm bf16 {M}x{N}x{K}")
     A = synth.make_aux(M * 7 + 1, (M, K))
