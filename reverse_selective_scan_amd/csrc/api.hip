@@ -134,6 +134,8 @@ ScanPlan plan_scan(int E, int64_t T, int32_t nseq, int32_t max_seqlen, size_t ba
     if (want < Lc) Lc = want;
   }
   p.Lc = (int)Lc;
+  // every chunk but a sequence's leftmost is full, so there are at most
+  // nseq + T / Lc chunks whatever the true sequence lengths are
   p.max_chunks = (int)(nseq + (T + Lc - 1) / Lc);
   if (p.max_chunks < 1) p.max_chunks = 1;
   p.summary = Lc < T;  // some sequence may span several chunks

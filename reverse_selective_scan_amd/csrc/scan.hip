@@ -181,8 +181,12 @@ __global__ __launch_bounds__(256, 2) void scan_kernel(ScanArgs a) {
 
   const int E = a.E;
   const int NB = E / 64;
-  const int lid = xcd_remap(blockIdx.x, a.max_chunks * NB);
-  const int ci = lid / NB, cblk = lid % NB;
+  // Blocks of one chunk are consecutive, so the hardware's round-robin
+  // spreads every chunk over all XCDs; the grid is sized by an upper bound on
+  // the chunk count, and the surplus blocks (the highest indices) exit here
+  // evenly across the XCDs.  (Blocks share no operands worth keeping in one
+  // XCD's L2.)
+  const int ci = blockIdx.x / NB, cblk = blockIdx.x % NB;
   if (ci >= *a.n_chunks) return;
   const ChunkDesc d = a.chunks[ci];
   if (SUMMARY && d.j == d.n_in_seq - 1) return;  // leftmost chunk: its summary is never used
