@@ -120,6 +120,20 @@ struct ScanPlan {
   size_t off_cu, off_chunks, off_n, off_sumS, off_sumP, total;
 };
 
+// Compute units of the current device (cached per device; a race between
+// threads only stores the same value twice).
+int num_cus() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
+
 ScanPlan plan_scan(int E, int64_t T, int32_t nseq, int32_t max_seqlen, size_t base) {
   ScanPlan p{};
   const int64_t NB = E / 64;
@@ -151,7 +165,7 @@ ScanPlan plan_scan(int E, int64_t T, int32_t nseq, int32_t max_seqlen, size_t ba
 }
 
 struct LayerPlan {
-  size_t off_xz, off_xdbl, off_u, off_y;
+  size_t off_xz, off_xdbl, off_xdbl2, off_u, off_y;
   bool need_u;
   ScanPlan scan;
   size_t total;
@@ -166,6 +180,8 @@ LayerPlan plan_layer(const r2l_dims* d, r2l_dtype act, int64_t T, int32_t nseq, 
   size_t xz = Tz * 2 * E * sa, o = Tz * D * 4;  // out_proj's fp32 output reuses xz
   p.off_xz = off;   off = align_up(off + (xz > o ? xz : o));
   p.off_xdbl = off; off = align_up(off + Tz * P * 4);
+  // second partial x_proj sum of the split-K conv kernel (bf16, large T)
+  p.off_xdbl2 = off; off = align_up(off + (act == R2L_BF16 ? Tz * P * 4 : 0));
   p.need_u = act == R2L_F32 || P > 256;
   p.off_u = off;    off = align_up(off + (p.need_u ? Tz * E * sa : 0));
   p.off_y = off;    off = align_up(off + Tz * E * sa);
@@ -285,7 +301,15 @@ int r2l_layer_fwd(const r2l_dims* d, r2l_dtype act, uint32_t flags, const r2l_we
     bf16* y = at<bf16>(workspace, lp.off_y);
     R2L_RUN("in_proj_gemm", st, gemm_bf16_nt(T, 2 * E, D, (const bf16*)h_in, D, (const bf16*)w->in_proj_w, D, xz, 2L * E, false, st));
     if (!lp.need_u) {
-      R2L_RUN("conv_xproj", st, conv_xproj_bf16(T, E, P, xz, 2L * E, (const bf16*)w->conv_w, (const bf16*)w->conv_b, (const bf16*)w->x_proj_w, nullptr, xdbl, cu_clean, nseq, st));
+      const int ncu = num_cus();
+      if ((T + 127) / 128 >= ncu) {
+        // large input: split-K over one block per CU, then part0 += part1
+        float* xdbl2 = at<float>(workspace, lp.off_xdbl2);
+        R2L_RUN("conv_xproj", st, conv_xproj_bf16_sk(T, E, P, xz, 2L * E, (const bf16*)w->conv_w, (const bf16*)w->conv_b, (const bf16*)w->x_proj_w, xdbl, xdbl2, cu_clean, nseq, ncu, st));
+        R2L_RUN("add_parts", st, add_parts((long)T * P, xdbl, xdbl2, st));
+      } else {
+        R2L_RUN("conv_xproj", st, conv_xproj_bf16(T, E, P, xz, 2L * E, (const bf16*)w->conv_w, (const bf16*)w->conv_b, (const bf16*)w->x_proj_w, nullptr, xdbl, cu_clean, nseq, st));
+      }
     } else {
       bf16* u = at<bf16>(workspace, lp.off_u);
       R2L_RUN("conv_silu", st, conv_silu<bf16>(T, E, xz, 2L * E, (const bf16*)w->conv_w, (const bf16*)w->conv_b, u, cu_clean, nseq, st));

@@ -194,4 +194,275 @@ hipError_t conv_xproj_bf16(int Tn, int E, int P, const bf16* x, long ld_x, const
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Fused conv + SiLU + x_proj for large inputs, split along K ("stream-K").
+//
+// Work is the grid of (128-token tile, 32-channel step) pairs, walked tile
+// by tile; block b of G takes the contiguous range [b W / G, (b+1) W / G) of
+// the W = tiles * E/32 steps, so every block does the same amount of work
+// whatever the token count (a plain split into 128-token tiles would leave
+// e.g. 258 tiles for 256 CUs, i.e. two rounds).  With tiles >= G every tile is
+// covered by at most two blocks: the one holding its step 0 writes its
+// partial sum to part0, the other to part1 (whole tiles zero part1); the
+// consumer adds part0 + part1, in that order, so results are deterministic.
+//
+// The 4 waves of a block own 32 tokens each and walk the same steps, so one
+// copy of each W_x slice (and the conv taps) per block serves 128 tokens.
+// Every operand of a step is copied global -> LDS by buffer_load ... lds
+// into a 5-stage ring (rows past the token count read as zero through the
+// buffer descriptor's range); the barrier of step q waits for step q+1, and
+// loads run three steps ahead.  x and W_x stage rows are 64 bytes with the
+// 16-byte chunk index XOR-ed by (row >> 2) & 3 against bank conflicts.
+// Lanes compute their own MFMA A-fragments (token lane & 31, 8 channels) as
+// in conv_xproj_kernel.
+// ---------------------------------------------------------------------------
+namespace {
+
+constexpr int kSkTok = 128, kSkK = 32;
+
+template <int NCS>
+struct SkGeo {
+  // copy instructions per step, each group padded to a multiple of the 4
+  // waves so that the m-th copy of every wave is of the same kind
+  static constexpr int NW = ((NCS * 32 * 4 + 63) / 64 + 3) / 4 * 4;       // W_x rows x 4 chunks
+  static constexpr int NX = (((kSkTok + 3) * 4 + 63) / 64 + 3) / 4 * 4;   // x rows t0 .. t0+130
+  static constexpr int NI = NW + NX + 4;                                  // + conv taps, bias, 2 spare
+  static constexpr int PER_WAVE = NI / 4;
+  static constexpr int SBYTES = NI * 1024;
+  static constexpr int OFF_X = NW * 1024, OFF_CW = (NW + NX) * 1024, OFF_CB = OFF_CW + 1024;
+  static constexpr int RS = 5 * SBYTES <= 160 * 1024 ? 5 : 4;             // ring stages
+};
+
+constexpr int sk_vmcnt(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
+R2L_DEV void sk_dma16(__amdgpu_buffer_rsrc_t r, void* lds, unsigned voff, unsigned soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voff, soff, 0, 0);
+}
+R2L_DEV int sk_swz(int row, int chunk) { return chunk ^ ((row >> 2) & 3); }
+
+}  // namespace
+
+template <int NCS>
+__global__ __launch_bounds__(256, 1) void conv_xproj_sk_kernel(int Tn, int E, int P,
+                                                               const bf16* __restrict__ x, long ld_x,
+                                                               const bf16* __restrict__ cw,
+                                                               const bf16* __restrict__ cb,
+                                                               const bf16* __restrict__ Wx,
+                                                               float* __restrict__ part0,
+                                                               float* __restrict__ part1,
+                                                               const int32_t* __restrict__ cu, int nseq) {
+  using Geo = SkGeo<NCS>;
+  constexpr int RS = Geo::RS, PW = Geo::PER_WAVE;
+  __shared__ __attribute__((aligned(1024))) char s0[Geo::SBYTES];
+  __shared__ __attribute__((aligned(1024))) char s1[Geo::SBYTES];
+  __shared__ __attribute__((aligned(1024))) char s2[Geo::SBYTES];
+  __shared__ __attribute__((aligned(1024))) char s3[Geo::SBYTES];
+  __shared__ __attribute__((aligned(1024))) char s4[Geo::RS > 4 ? Geo::SBYTES : 16];
+  auto stage = [&](int s) -> char* { return s == 0 ? s0 : s == 1 ? s1 : s == 2 ? s2 : s == 3 ? s3 : s4; };
+
+  const int lane = lane_id(), w = wave_id();
+  const int tr = lane & 31, kh = lane >> 5;
+  const int S = E / kSkK;                       // steps per tile
+  const long ntiles = (Tn + kSkTok - 1) / kSkTok;
+  const long W = ntiles * S;
+  const long lo = W * blockIdx.x / gridDim.x, hi = W * (blockIdx.x + 1) / gridDim.x;
+  if (lo >= hi) return;
+
+  // constant descriptors (W_x, conv taps, conv bias) and this lane's offsets
+  const __amdgpu_buffer_rsrc_t rW = __builtin_amdgcn_make_buffer_rsrc((void*)Wx, 0, (int)((long)P * E * 2), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rCW = __builtin_amdgcn_make_buffer_rsrc((void*)cw, 0, (int)((long)E * 8), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rCB = __builtin_amdgcn_make_buffer_rsrc((void*)cb, 0, (int)((long)E * 2), 0x00020000);
+  // copy m of this wave is copy i = 4 m + w of the step; its kind depends on m only
+  constexpr int MW = Geo::NW / 4, MX = Geo::NX / 4;
+  unsigned voff[PW];
+#pragma unroll
+  for (int m = 0; m < PW; ++m) {
+    const int i = 4 * m + w;
+    if (m < MW) {
+      const int p = i * 64 + lane, row = p >> 2;
+      voff[m] = (unsigned)(((long)min(row, P - 1) * E + sk_swz(row, p & 3) * 8) * 2);
+    } else if (m < MW + MX) {
+      const int p = (i - Geo::NW) * 64 + lane, row = p >> 2;
+      voff[m] = (unsigned)(((long)row * ld_x + sk_swz(row, p & 3) * 8) * 2);
+    } else {
+      // copy NW+NX (wave 0): taps of channels c0 + 2 lane, +1; copies
+      // NW+NX+1.. (waves 1-3): bias of channels c0 + 8 lane .. +7
+      voff[m] = w == 0 ? (lane < 16 ? lane * 16 : 0) : (lane < 4 ? lane * 16 : 0);
+    }
+  }
+  const bool taps_copy = w == 0;
+  // step q -> stage slot: copies of every operand of step q (q clamped to hi - 1)
+  auto issue = [&](int s, long q) {
+    q = q < hi ? q : hi - 1;
+    const long tile = q / S;
+    const int c0 = (int)(q % S) * kSkK;
+    const long t0 = tile * kSkTok;
+    const long xbytes = (long)(Tn - t0) * ld_x * 2;
+    const __amdgpu_buffer_rsrc_t rX = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(x + t0 * ld_x), 0, (int)(xbytes < (1L << 30) ? xbytes : (1L << 30)), 0x00020000);
+    // taps (wave 0) and bias (waves 1-3) share the last copy slot through a
+    // uniform choice of descriptor and offset
+    const __amdgpu_buffer_rsrc_t rT = taps_copy ? rCW : rCB;
+    const unsigned soffT = taps_copy ? (unsigned)(c0 * 8) : (unsigned)(c0 * 2);
+    char* base = stage(s);
+#pragma unroll
+    for (int m = 0; m < PW; ++m) {
+      char* dst = base + (4 * m + w) * 1024;   // lane l lands at dst + 16 l
+      if (m < MW) sk_dma16(rW, dst, voff[m], (unsigned)(c0 * 2));
+      else if (m < MW + MX) sk_dma16(rX, dst, voff[m], (unsigned)(c0 * 2));
+      else sk_dma16(rT, dst, voff[m], soffT);
+    }
+  };
+
+  f32x16 acc[NCS];
+  const bf16x8 zero8 = {};
+  long t = 0;
+  bool tv = false, xok[KC] = {false, false, false, false};
+  long piece_lo = lo;   // first step of the current piece
+  // Look up this lane's sequence end in the block's first and last tile now,
+  // before any copy is in flight (a lookup inside the loop waits for all of
+  // them); tiles in between, when the range spans more than two, are looked
+  // up when they start.
+  const long tileA = lo / S, tileB = (hi - 1) / S;
+  const long tA = tileA * kSkTok + w * 32 + tr, tB = tileB * kSkTok + w * 32 + tr;
+  const int seA = tA < Tn ? seq_end_of(cu, nseq, (int)tA, Tn) : 0;
+  const int seB = tB < Tn ? seq_end_of(cu, nseq, (int)tB, Tn) : 0;
+  auto start_piece = [&](long q) {
+#pragma unroll
+    for (int c = 0; c < NCS; ++c)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[c][r] = 0.0f;
+    const long tile = q / S;
+    t = tile * kSkTok + w * 32 + tr;
+    tv = t < Tn;
+    const int se = tile == tileA ? seA : tile == tileB ? seB : (tv ? seq_end_of(cu, nseq, (int)t, Tn) : 0);
+#pragma unroll
+    for (int j = 0; j < KC; ++j) xok[j] = tv && t + j < se;
+    piece_lo = q;
+  };
+  auto end_piece = [&](long q) {   // q = last step of the piece
+    const long tile = q / S;
+    const bool head = piece_lo % S == 0, full = head && q % S == S - 1;
+    float* dst = head ? part0 : part1;
+    const long tb = tile * kSkTok + w * 32;
+#pragma unroll
+    for (int c = 0; c < NCS; ++c) {
+      const int col = c * 32 + tr;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const long tt = tb + 8 * (r >> 2) + 4 * kh + (r & 3);
+        if (col < P && tt < Tn) {
+          dst[tt * P + col] = acc[c][r];
+          if (full && part1 != nullptr) part1[tt * P + col] = 0.0f;
+        }
+      }
+    }
+  };
+  auto compute = [&](const char* base, long q) {
+    if (q == lo || q % S == 0) start_piece(q);
+    const char* wx_s = base;
+    const char* x_s = base + Geo::OFF_X;
+    const char* cw_s = base + Geo::OFF_CW;
+    const char* cb_s = base + Geo::OFF_CB;
+#pragma unroll
+    for (int ss = 0; ss < 2; ++ss) {
+      const int kc = ss * 2 + kh;            // 16-byte chunk of the 64-byte row
+      const int cc = ss * 16 + kh * 8;       // first of this lane's 8 channels in the step
+      bf16x8 xv[KC], wv[4];
+#pragma unroll
+      for (int j = 0; j < KC; ++j) {
+        const int row = w * 32 + tr + j;
+        xv[j] = *(const bf16x8*)(x_s + row * 64 + sk_swz(row, kc) * 16);
+      }
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) wv[q4] = *(const bf16x8*)(cw_s + cc * 8 + 16 * q4);
+      const bf16x8 bv = *(const bf16x8*)(cb_s + cc * 2);
+      bf16x8 wf[NCS];
+#pragma unroll
+      for (int c = 0; c < NCS; ++c) {
+        const int row = c * 32 + tr;
+        wf[c] = *(const bf16x8*)(wx_s + row * 64 + sk_swz(row, kc) * 16);
+      }
+      float ca[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) ca[i] = (float)bv[i];
+#pragma unroll
+      for (int j = 0; j < KC; ++j) {
+        const bf16x8 xj = xok[j] ? xv[j] : zero8;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int el = i * KC + (KC - 1 - j);   // channel i, tap K-1-j
+          ca[i] = fmaf((float)wv[el >> 3][el & 7], (float)xj[i], ca[i]);
+        }
+      }
+      bf16x8 af;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) af[i] = (bf16)silu_fast(ca[i]);
+      if (!tv) af = zero8;
+#pragma unroll
+      for (int c = 0; c < NCS; ++c) {
+        const bf16x8 bfr = (c * 32 + tr < P) ? wf[c] : zero8;
+        acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bfr, acc[c], 0, 0, 0);
+      }
+    }
+    if (q == hi - 1 || q % S == S - 1) end_piece(q);
+  };
+
+  const long n = hi - lo;
+#pragma unroll
+  for (int s = 0; s + 1 < RS; ++s) issue(s, lo + s);
+  __builtin_amdgcn_s_waitcnt(sk_vmcnt((RS - 2) * PW));
+  asm volatile("s_barrier" ::: "memory");
+  for (long i0 = 0; i0 < n; i0 += RS) {
+#pragma unroll
+    for (int s = 0; s < RS; ++s) {
+      const long q = lo + i0 + s;
+      // own copies of step q+1 done (later steps may fly); after the barrier
+      // everyone's are, and every wave is done with the stage of step q-1
+      __builtin_amdgcn_s_waitcnt(sk_vmcnt((RS - 3) * PW));
+      asm volatile("s_barrier" ::: "memory");
+      issue((s + RS - 1) % RS, q + RS - 1);
+      if (q < hi) compute(stage(s), q);
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(sk_vmcnt(0));
+}
+
+// part0 += part1 over n floats (both 16-byte aligned); the last n % 4 by the first thread.
+__global__ __launch_bounds__(256) void add_parts_kernel(long n, float* __restrict__ a,
+                                                        const float* __restrict__ b) {
+  const long n4 = n / 4;
+  for (long i = blockIdx.x * 256L + threadIdx.x; i < n4; i += (long)gridDim.x * 256)
+    ((f32x4*)a)[i] = ((f32x4*)a)[i] + ((const f32x4*)b)[i];
+  if (blockIdx.x == 0 && threadIdx.x == 0)
+    for (long i = n4 * 4; i < n; ++i) a[i] += b[i];
+}
+
+hipError_t add_parts(long n, float* part0, const float* part1, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  const long want = (n / 4 + 255) / 256;
+  const long blocks = want < 1 ? 1 : (want < 4096 ? want : 4096);
+  hipLaunchKernelGGL(add_parts_kernel, dim3(blocks), dim3(256), 0, st, n, part0, part1);
+  return hipGetLastError();
+}
+
+hipError_t conv_xproj_bf16_sk(int Tn, int E, int P, const bf16* x, long ld_x, const bf16* conv_w,
+                              const bf16* conv_b, const bf16* x_proj_w, float* part0, float* part1,
+                              const int32_t* cu, int nseq, int nblocks, hipStream_t st) {
+  if (Tn <= 0) return hipSuccess;
+  const int ncs = (P + 31) / 32;
+  dim3 grid(nblocks), block(256);
+#define R2L_SK(n)                                                                                \
+  case n:                                                                                        \
+    hipLaunchKernelGGL((conv_xproj_sk_kernel<n>), grid, block, 0, st, Tn, E, P, x, ld_x, conv_w, \
+                       conv_b, x_proj_w, part0, part1, cu, nseq);                                \
+    break;
+  switch (ncs) {
+    R2L_SK(1) R2L_SK(2) R2L_SK(3) R2L_SK(4) R2L_SK(5) R2L_SK(6) R2L_SK(7) R2L_SK(8)
+    default: return hipErrorInvalidValue;
+  }
+#undef R2L_SK
+  return hipGetLastError();
+}
+
 }  // namespace r2l

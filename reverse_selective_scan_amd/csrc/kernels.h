@@ -26,6 +26,15 @@ hipError_t conv_xproj_bf16(int T_, int E, int P, const bf16* x, long ld_x, const
                            const bf16* conv_b, const bf16* x_proj_w, bf16* u_out, float* xdbl,
                            const int32_t* cu, int nseq, hipStream_t st);
 
+// The same for large inputs, split along K over `nblocks` blocks (one per
+// CU): xdbl = part0 + part1 (add_parts), part1 16-byte aligned.  Requires
+// E % 64 == 0, P <= 256 and ceil(T / 128) >= nblocks.
+hipError_t conv_xproj_bf16_sk(int T_, int E, int P, const bf16* x, long ld_x, const bf16* conv_w,
+                              const bf16* conv_b, const bf16* x_proj_w, float* part0, float* part1,
+                              const int32_t* cu, int nseq, int nblocks, hipStream_t st);
+// part0[i] += part1[i] for i < n (both 16-byte aligned).
+hipError_t add_parts(long n, float* part0, const float* part1, hipStream_t st);
+
 // Chunk planning for the scan: sanitised cu_seqlens and the chunk table.
 hipError_t plan_chunks(const int32_t* cu, int nseq, int T_, int Lc, int max_chunks,
                        int32_t* cu_clean, ChunkDesc* chunks, int32_t* n_chunks, hipStream_t st);
