@@ -302,7 +302,8 @@ int r2l_layer_fwd(const r2l_dims* d, r2l_dtype act, uint32_t flags, const r2l_we
     R2L_RUN("in_proj_gemm", st, gemm_bf16_nt(T, 2 * E, D, (const bf16*)h_in, D, (const bf16*)w->in_proj_w, D, xz, 2L * E, false, st));
     if (!lp.need_u) {
       const int ncu = num_cus();
-      if ((T + 127) / 128 >= ncu) {
+      // (the split kernel counts (tile, step) pairs in 32 bits)
+      if ((T + 127) / 128 >= ncu && (long)((T + 127) / 128) * (E / 32) < (1L << 31)) {
         // large input: split-K over one block per CU, then part0 += part1
         float* xdbl2 = at<float>(workspace, lp.off_xdbl2);
         R2L_RUN("conv_xproj", st, conv_xproj_bf16_sk(T, E, P, xz, 2L * E, (const bf16*)w->conv_w, (const bf16*)w->conv_b, (const bf16*)w->x_proj_w, xdbl, xdbl2, cu_clean, nseq, ncu, st));

@@ -262,11 +262,12 @@ __global__ __launch_bounds__(256, 1) void conv_xproj_sk_kernel(int Tn, int E, in
 
   const int lane = lane_id(), w = wave_id();
   const int tr = lane & 31, kh = lane >> 5;
-  const int S = E / kSkK;                       // steps per tile
-  const long ntiles = (Tn + kSkTok - 1) / kSkTok;
-  const long W = ntiles * S;
-  const long lo = W * blockIdx.x / gridDim.x, hi = W * (blockIdx.x + 1) / gridDim.x;
+  const int S = E / kSkK;                        // steps per tile
+  const int ntiles = (Tn + kSkTok - 1) / kSkTok;
+  const long W = (long)ntiles * S;
+  const int lo = (int)(W * blockIdx.x / gridDim.x), hi = (int)(W * (blockIdx.x + 1) / gridDim.x);
   if (lo >= hi) return;
+  const int n = hi - lo;
 
   // constant descriptors (W_x, conv taps, conv bias) and this lane's offsets
   const __amdgpu_buffer_rsrc_t rW = __builtin_amdgcn_make_buffer_rsrc((void*)Wx, 0, (int)((long)P * E * 2), 0x00020000);
@@ -291,75 +292,84 @@ __global__ __launch_bounds__(256, 1) void conv_xproj_sk_kernel(int Tn, int E, in
     }
   }
   const bool taps_copy = w == 0;
-  // step q -> stage slot: copies of every operand of step q (q clamped to hi - 1)
-  auto issue = [&](int s, long q) {
-    q = q < hi ? q : hi - 1;
-    const long tile = q / S;
-    const int c0 = (int)(q % S) * kSkK;
-    const long t0 = tile * kSkTok;
+  // Copy position: the step RS-1 ahead of the one being computed, as
+  // (tile, channel offset); it stops advancing at the block's last step
+  // (later copies reload that step into stages that are never read).
+  int it_tile = lo / S, it_c0 = (lo % S) * kSkK, it_left = n;
+  auto issue = [&](int s) {
+    const long t0 = (long)it_tile * kSkTok;
     const long xbytes = (long)(Tn - t0) * ld_x * 2;
     const __amdgpu_buffer_rsrc_t rX = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(x + t0 * ld_x), 0, (int)(xbytes < (1L << 30) ? xbytes : (1L << 30)), 0x00020000);
     // taps (wave 0) and bias (waves 1-3) share the last copy slot through a
     // uniform choice of descriptor and offset
     const __amdgpu_buffer_rsrc_t rT = taps_copy ? rCW : rCB;
-    const unsigned soffT = taps_copy ? (unsigned)(c0 * 8) : (unsigned)(c0 * 2);
+    const unsigned soffT = taps_copy ? (unsigned)(it_c0 * 8) : (unsigned)(it_c0 * 2);
     char* base = stage(s);
 #pragma unroll
     for (int m = 0; m < PW; ++m) {
       char* dst = base + (4 * m + w) * 1024;   // lane l lands at dst + 16 l
-      if (m < MW) sk_dma16(rW, dst, voff[m], (unsigned)(c0 * 2));
-      else if (m < MW + MX) sk_dma16(rX, dst, voff[m], (unsigned)(c0 * 2));
+      if (m < MW) sk_dma16(rW, dst, voff[m], (unsigned)(it_c0 * 2));
+      else if (m < MW + MX) sk_dma16(rX, dst, voff[m], (unsigned)(it_c0 * 2));
       else sk_dma16(rT, dst, voff[m], soffT);
+    }
+    if (--it_left > 0) {
+      it_c0 += kSkK;
+      if (it_c0 == E) { it_c0 = 0; ++it_tile; }
     }
   };
 
-  f32x16 acc[NCS];
-  const bf16x8 zero8 = {};
-  long t = 0;
-  bool tv = false, xok[KC] = {false, false, false, false};
-  long piece_lo = lo;   // first step of the current piece
   // Look up this lane's sequence end in the block's first and last tile now,
   // before any copy is in flight (a lookup inside the loop waits for all of
   // them); tiles in between, when the range spans more than two, are looked
   // up when they start.
-  const long tileA = lo / S, tileB = (hi - 1) / S;
-  const long tA = tileA * kSkTok + w * 32 + tr, tB = tileB * kSkTok + w * 32 + tr;
-  const int seA = tA < Tn ? seq_end_of(cu, nseq, (int)tA, Tn) : 0;
-  const int seB = tB < Tn ? seq_end_of(cu, nseq, (int)tB, Tn) : 0;
-  auto start_piece = [&](long q) {
+  const int tileA = lo / S, tileB = (hi - 1) / S;
+  const int tA = tileA * kSkTok + w * 32 + tr, tB = tileB * kSkTok + w * 32 + tr;
+  const int seA = tA < Tn ? seq_end_of(cu, nseq, tA, Tn) : 0;
+  const int seB = tB < Tn ? seq_end_of(cu, nseq, tB, Tn) : 0;
+
+  f32x16 acc[NCS];
+  int c_tile = lo / S, c_ks = lo % S;   // step being computed
+  bool head = c_ks == 0;                // this piece holds the tile's step 0
+  bool tv = false, ok1 = false, ok2 = false, ok3 = false, masked = false;
+  auto start_piece = [&]() {
 #pragma unroll
     for (int c = 0; c < NCS; ++c)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[c][r] = 0.0f;
-    const long tile = q / S;
-    t = tile * kSkTok + w * 32 + tr;
+    const int t = c_tile * kSkTok + w * 32 + tr;
     tv = t < Tn;
-    const int se = tile == tileA ? seA : tile == tileB ? seB : (tv ? seq_end_of(cu, nseq, (int)t, Tn) : 0);
-#pragma unroll
-    for (int j = 0; j < KC; ++j) xok[j] = tv && t + j < se;
-    piece_lo = q;
+    const int se = c_tile == tileA ? seA : c_tile == tileB ? seB : (tv ? seq_end_of(cu, nseq, t, Tn) : 0);
+    ok1 = t + 1 < se;
+    ok2 = t + 2 < se;
+    ok3 = t + 3 < se;
+    // taps past a sequence end are zeroed only in waves that have such a lane
+    masked = __any(tv && !(ok1 && ok2 && ok3));
   };
-  auto end_piece = [&](long q) {   // q = last step of the piece
-    const long tile = q / S;
-    const bool head = piece_lo % S == 0, full = head && q % S == S - 1;
-    float* dst = head ? part0 : part1;
-    const long tb = tile * kSkTok + w * 32;
+  auto end_piece = [&]() {
+    const bool full = head && c_ks == S - 1;
+    float* dst = (head ? part0 : part1) + ((long)c_tile * kSkTok + w * 32) * P;
+    const int rows = min(32, Tn - (c_tile * kSkTok + w * 32));
 #pragma unroll
     for (int c = 0; c < NCS; ++c) {
       const int col = c * 32 + tr;
+      if (col >= P) continue;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const long tt = tb + 8 * (r >> 2) + 4 * kh + (r & 3);
-        if (col < P && tt < Tn) {
-          dst[tt * P + col] = acc[c][r];
-          if (full && part1 != nullptr) part1[tt * P + col] = 0.0f;
+        const int row = 8 * (r >> 2) + 4 * kh + (r & 3);
+        if (row < rows) {
+          dst[row * P + col] = acc[c][r];
+          if (full && part1 != nullptr) part1[((long)c_tile * kSkTok + w * 32 + row) * P + col] = 0.0f;
         }
       }
     }
   };
-  auto compute = [&](const char* base, long q) {
-    if (q == lo || q % S == 0) start_piece(q);
+  const bf16x8 zero8 = {};
+  auto compute = [&](const char* base) {
+    if (c_tile * S + c_ks == lo || c_ks == 0) {
+      head = c_ks == 0;
+      start_piece();
+    }
     const char* wx_s = base;
     const char* x_s = base + Geo::OFF_X;
     const char* cw_s = base + Geo::OFF_CW;
@@ -368,31 +378,48 @@ __global__ __launch_bounds__(256, 1) void conv_xproj_sk_kernel(int Tn, int E, in
     for (int ss = 0; ss < 2; ++ss) {
       const int kc = ss * 2 + kh;            // 16-byte chunk of the 64-byte row
       const int cc = ss * 16 + kh * 8;       // first of this lane's 8 channels in the step
-      bf16x8 xv[KC], wv[4];
+      i32x4 xr[KC], wt[4];
 #pragma unroll
       for (int j = 0; j < KC; ++j) {
         const int row = w * 32 + tr + j;
-        xv[j] = *(const bf16x8*)(x_s + row * 64 + sk_swz(row, kc) * 16);
+        xr[j] = *(const i32x4*)(x_s + row * 64 + sk_swz(row, kc) * 16);
       }
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) wv[q4] = *(const bf16x8*)(cw_s + cc * 8 + 16 * q4);
-      const bf16x8 bv = *(const bf16x8*)(cb_s + cc * 2);
+      for (int q4 = 0; q4 < 4; ++q4) wt[q4] = *(const i32x4*)(cw_s + cc * 8 + 16 * q4);
+      const i32x4 bv = *(const i32x4*)(cb_s + cc * 2);
       bf16x8 wf[NCS];
 #pragma unroll
       for (int c = 0; c < NCS; ++c) {
         const int row = c * 32 + tr;
         wf[c] = *(const bf16x8*)(wx_s + row * 64 + sk_swz(row, kc) * 16);
       }
+      if (masked) {
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          xr[1][d] = ok1 ? xr[1][d] : 0;
+          xr[2][d] = ok2 ? xr[2][d] : 0;
+          xr[3][d] = ok3 ? xr[3][d] : 0;
+        }
+      }
+      // channel 2d (+1) of the lane's 8: dword d of each x row holds the
+      // pair; taps (w0, w1) and (w2, w3) of channel i are dwords 2i, 2i+1.
+      // c_i = b_i + w3 x(t) + w2 x(t+1) + w1 x(t+2) + w0 x(t+3)
       float ca[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) ca[i] = (float)bv[i];
+      for (int d = 0; d < 4; ++d) {
+        const unsigned b = (unsigned)bv[d];
+        const unsigned x0 = xr[0][d], x1 = xr[1][d], x2 = xr[2][d], x3 = xr[3][d];
 #pragma unroll
-      for (int j = 0; j < KC; ++j) {
-        const bf16x8 xj = xok[j] ? xv[j] : zero8;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const int el = i * KC + (KC - 1 - j);   // channel i, tap K-1-j
-          ca[i] = fmaf((float)wv[el >> 3][el & 7], (float)xj[i], ca[i]);
+        for (int hh = 0; hh < 2; ++hh) {
+          const int i = 2 * d + hh;
+          const unsigned sel = hh ? 0x07060302u : 0x05040100u;   // high / low bf16 of each row
+          const unsigned x10 = __builtin_amdgcn_perm(x0, x1, sel);   // (x(t+1), x(t))
+          const unsigned x32 = __builtin_amdgcn_perm(x2, x3, sel);   // (x(t+3), x(t+2))
+          const unsigned w01 = (unsigned)wt[i >> 1][2 * (i & 1)], w23 = (unsigned)wt[i >> 1][2 * (i & 1) + 1];
+          float c = __builtin_bit_cast(float, hh ? (b & 0xffff0000u) : (b << 16));
+          c = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w23), __builtin_bit_cast(bf16x2, x10), c, false);
+          c = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w01), __builtin_bit_cast(bf16x2, x32), c, false);
+          ca[i] = c;
         }
       }
       bf16x8 af;
@@ -405,24 +432,25 @@ __global__ __launch_bounds__(256, 1) void conv_xproj_sk_kernel(int Tn, int E, in
         acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bfr, acc[c], 0, 0, 0);
       }
     }
-    if (q == hi - 1 || q % S == S - 1) end_piece(q);
+    const bool last = c_tile * S + c_ks == hi - 1;
+    if (last || c_ks == S - 1) end_piece();
+    if (++c_ks == S) { c_ks = 0; ++c_tile; }
   };
 
-  const long n = hi - lo;
 #pragma unroll
-  for (int s = 0; s + 1 < RS; ++s) issue(s, lo + s);
+  for (int s = 0; s + 1 < RS; ++s) issue(s);
   __builtin_amdgcn_s_waitcnt(sk_vmcnt((RS - 2) * PW));
   asm volatile("s_barrier" ::: "memory");
-  for (long i0 = 0; i0 < n; i0 += RS) {
+  for (int i0 = 0; i0 < n; i0 += RS) {
 #pragma unroll
     for (int s = 0; s < RS; ++s) {
-      const long q = lo + i0 + s;
       // own copies of step q+1 done (later steps may fly); after the barrier
-      // everyone's are, and every wave is done with the stage of step q-1
+      // everyone's are, and every wave is done with the stage of step q-1,
+      // which receives the copies of step q+RS-1
       __builtin_amdgcn_s_waitcnt(sk_vmcnt((RS - 3) * PW));
       asm volatile("s_barrier" ::: "memory");
-      issue((s + RS - 1) % RS, q + RS - 1);
-      if (q < hi) compute(stage(s), q);
+      issue((s + RS - 1) % RS);
+      if (i0 + s < n) compute(stage(s));
     }
   }
   __builtin_amdgcn_s_waitcnt(sk_vmcnt(0));
