@@ -281,7 +281,8 @@ __global__ __launch_bounds__(256, 1) void conv_xproj_sk_kernel(int Tn, int E, in
     const int i = 4 * m + w;
     if (m < MW) {
       const int p = i * 64 + lane, row = p >> 2;
-      voff[m] = (unsigned)(((long)min(row, P - 1) * E + sk_swz(row, p & 3) * 8) * 2);
+      // rows past P lie past the descriptor's range and read as zero
+      voff[m] = (unsigned)(((long)row * E + sk_swz(row, p & 3) * 8) * 2);
     } else if (m < MW + MX) {
       const int p = (i - Geo::NW) * 64 + lane, row = p >> 2;
       voff[m] = (unsigned)(((long)row * ld_x + sk_swz(row, p & 3) * 8) * 2);
@@ -422,15 +423,12 @@ __global__ __launch_bounds__(256, 1) void conv_xproj_sk_kernel(int Tn, int E, in
           ca[i] = c;
         }
       }
+      // rows of tokens past the end get garbage here and are never stored
       bf16x8 af;
 #pragma unroll
       for (int i = 0; i < 8; ++i) af[i] = (bf16)silu_fast(ca[i]);
-      if (!tv) af = zero8;
 #pragma unroll
-      for (int c = 0; c < NCS; ++c) {
-        const bf16x8 bfr = (c * 32 + tr < P) ? wf[c] : zero8;
-        acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bfr, acc[c], 0, 0, 0);
-      }
+      for (int c = 0; c < NCS; ++c) acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, wf[c], acc[c], 0, 0, 0);
     }
     const bool last = c_tile * S + c_ks == hi - 1;
     if (last || c_ks == S - 1) end_piece();
