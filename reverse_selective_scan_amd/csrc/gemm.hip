@@ -179,7 +179,9 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(int M, int N, int
   const int wm = (wave >> 1) * 128, wn = (wave & 1) * 128;
   const int nTm = (M + BM - 1) / BM, nTn = (N + BN - 1) / BN;
   const int lid = xcd_remap(blockIdx.x, nTm * nTn);
-  constexpr int G = 4;
+  // group-M raster: G row tiles sweep all column tiles; narrow outputs (few
+  // column tiles) use taller groups (measured best: 8 for <= 8 column tiles)
+  const int G = nTn <= 8 ? 8 : 4;
   const int per_group = G * nTn;
   const int first_m = (lid / per_group) * G;
   const int gsz = min(nTm - first_m, G);
