@@ -167,9 +167,15 @@ int r2l_scan_fwd(const r2l_dims* dims, r2l_dtype act, const void* u, int64_t ld_
  * C: [M, N] (row stride ldc) in the activation dtype (out_f32 == 0) or in
  * f32 (out_f32 != 0).  bf16 runs on the MFMA matrix cores.  K must be a
  * multiple of 8 and lda/ldb multiples of 8 for bf16.
+ * workspace (optional; NULL with workspace_bytes 0 is valid): device
+ * scratch, 16-byte aligned.  With it, large bf16 problems split the output
+ * tiles left over after the last whole round over the GPU's compute units
+ * along K (fp32 partial sums, added in a fixed order, so results are
+ * deterministic); up to 256 KiB per compute unit is used.
  * ---------------------------------------------------------------------- */
 int r2l_gemm_nt(r2l_dtype act, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
-                const void* B, int64_t ldb, void* C, int64_t ldc, int out_f32, void* stream);
+                const void* B, int64_t ldb, void* C, int64_t ldc, int out_f32, void* workspace,
+                size_t workspace_bytes, void* stream);
 
 /* Host-side validation of a host copy of cu_seqlens: cu[0] == 0,
  * non-decreasing, cu[nseq] == n_tokens, every length <= max_seqlen.

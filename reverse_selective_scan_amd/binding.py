@@ -52,7 +52,7 @@ _SIGS = {
     "r2l_scan_workspace_bytes": (_SZ, [C.POINTER(Dims), _I64, _I32, _I32]),
     "r2l_scan_fwd": (C.c_int, [C.POINTER(Dims), C.c_int, _P, _I64, _P, _I64, _P, _P, _P, _I64, _P, _P,
                                _I64, _P, _P, _I32, _I64, _I32, _P, _SZ, _P]),
-    "r2l_gemm_nt": (C.c_int, [C.c_int, _I64, _I64, _I64, _P, _I64, _P, _I64, _P, _I64, C.c_int, _P]),
+    "r2l_gemm_nt": (C.c_int, [C.c_int, _I64, _I64, _I64, _P, _I64, _P, _I64, _P, _I64, C.c_int, _P, C.c_size_t, _P]),
     "r2l_timing_enable": (C.c_int, [C.c_int]),
     "r2l_timing_reset": (C.c_int, []),
     "r2l_timing_read": (C.c_int, [C.POINTER(C.c_char_p), C.POINTER(C.c_double), C.POINTER(C.c_int64),
@@ -222,16 +222,20 @@ def r2l_scan_fwd(u: torch.Tensor, dt: torch.Tensor, A_log: torch.Tensor, B: torc
     return y
 
 
-def r2l_gemm_nt(A: torch.Tensor, B: torch.Tensor, *, out_f32: bool = False) -> torch.Tensor:
-    """C = A @ B^T on the library's GEMM (MFMA for bf16)."""
+def r2l_gemm_nt(A: torch.Tensor, B: torch.Tensor, *, out_f32: bool = False,
+                workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """C = A @ B^T on the library's GEMM (MFMA for bf16).  workspace: optional
+    device scratch (uint8) that lets large problems split their last partial
+    round of output tiles along K."""
     _need(A, "A")
     _need(B, "B", A.dtype)
     act = _act(A)
     M, K = A.shape
     N = B.shape[0]
     out = torch.empty(M, N, dtype=torch.float32 if (out_f32 or act == R2L_F32) else A.dtype, device=A.device)
+    ws_ptr, ws_bytes = (None, 0) if workspace is None else (_ptr(workspace), workspace.numel() * workspace.element_size())
     _check("r2l_gemm_nt", lib().r2l_gemm_nt(act, M, N, K, _ptr(A), K, _ptr(B), K, _ptr(out), N,
-                                            1 if out.dtype == torch.float32 else 0, _stream()))
+                                            1 if out.dtype == torch.float32 else 0, ws_ptr, ws_bytes, _stream()))
     return out
 
 

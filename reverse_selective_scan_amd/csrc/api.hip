@@ -299,9 +299,11 @@ int r2l_layer_fwd(const r2l_dims* d, r2l_dtype act, uint32_t flags, const r2l_we
   if (act == R2L_BF16) {
     bf16* xz = at<bf16>(workspace, lp.off_xz);
     bf16* y = at<bf16>(workspace, lp.off_y);
-    R2L_RUN("in_proj_gemm", st, gemm_bf16_nt(T, 2 * E, D, (const bf16*)h_in, D, (const bf16*)w->in_proj_w, D, xz, 2L * E, false, st));
+    const int ncu = num_cus();
+    // in_proj's K-split scratch: the y region, written only later by the scan
+    R2L_RUN("in_proj_gemm", st, gemm_bf16_nt(T, 2 * E, D, (const bf16*)h_in, D, (const bf16*)w->in_proj_w, D, xz, 2L * E, false, st,
+                                             at<float>(workspace, lp.off_y), (size_t)T * E * 2, ncu));
     if (!lp.need_u) {
-      const int ncu = num_cus();
       // (the split kernel counts (tile, step) pairs in 32 bits)
       if ((T + 127) / 128 >= ncu && (long)((T + 127) / 128) * (E / 32) < (1L << 31)) {
         // large input: split-K over one block per CU, then part0 += part1
@@ -320,7 +322,11 @@ int r2l_layer_fwd(const r2l_dims* d, r2l_dtype act, uint32_t flags, const r2l_we
     a.x = xz; a.z = xz + E; a.y = y;
     if (sp.summary) R2L_RUN("scan_summary", st, scan_summary<bf16>(a, true, st));
     R2L_RUN("scan_main", st, scan_main<bf16>(a, true, st));
-    R2L_RUN("out_proj_gemm", st, gemm_bf16_nt(T, D, E, y, E, (const bf16*)w->out_proj_w, E, o, D, true, st));
+    // out_proj's K-split scratch: the part of the (dead) xz region past o
+    const size_t o_bytes = align_up((size_t)T * D * 4), xz_bytes = (size_t)T * 2 * E * 2;
+    R2L_RUN("out_proj_gemm", st, gemm_bf16_nt(T, D, E, y, E, (const bf16*)w->out_proj_w, E, o, D, true, st,
+                                              xz_bytes > o_bytes ? (float*)((char*)o + o_bytes) : nullptr,
+                                              xz_bytes > o_bytes ? xz_bytes - o_bytes : 0, ncu));
     R2L_RUN("ln_gate", st, ln_gate<bf16>(T, D, o, (const bf16*)h_in, (bf16*)h_out, w->ln_w, w->ln_b, w->s, branch_out, no_ln, R2L_LN_EPS, st));
   } else {
     float* xz = at<float>(workspace, lp.off_xz);
@@ -410,15 +416,19 @@ int r2l_scan_fwd(const r2l_dims* d, r2l_dtype act, const void* u, int64_t ld_u, 
 }
 
 int r2l_gemm_nt(r2l_dtype act, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
-                const void* B, int64_t ldb, void* C, int64_t ldc, int out_f32, void* stream) {
+                const void* B, int64_t ldb, void* C, int64_t ldc, int out_f32, void* workspace,
+                size_t workspace_bytes, void* stream) {
   if (act != R2L_F32 && act != R2L_BF16) return R2L_ERR_UNSUPPORTED;
   if (M < 0 || N < 0 || K < 0 || M > INT32_MAX || N > INT32_MAX || K > INT32_MAX)
     return R2L_ERR_INVALID_ARG;
   if (!A || !B || !C || lda < K || ldb < K || ldc < N) return R2L_ERR_INVALID_ARG;
+  if ((workspace == nullptr) != (workspace_bytes == 0) || (workspace && !aligned16(workspace)))
+    return R2L_ERR_INVALID_ARG;
   hipStream_t st = (hipStream_t)stream;
   if (act == R2L_BF16) {
     if (K % 8 || lda % 8 || ldb % 8 || !aligned16(A) || !aligned16(B)) return R2L_ERR_UNSUPPORTED;
-    R2L_RUN("gemm_bf16", st, gemm_bf16_nt((int)M, (int)N, (int)K, (const bf16*)A, lda, (const bf16*)B, ldb, C, ldc, out_f32 != 0, st));
+    R2L_RUN("gemm_bf16", st, gemm_bf16_nt((int)M, (int)N, (int)K, (const bf16*)A, lda, (const bf16*)B, ldb, C, ldc, out_f32 != 0, st,
+                                          (float*)workspace, workspace_bytes, num_cus()));
   } else {
     R2L_RUN("gemm_f32", st, gemm_f32_nt((int)M, (int)N, (int)K, (const float*)A, lda, (const float*)B, ldb, (float*)C, ldc, st));
   }

@@ -159,13 +159,32 @@ R2L_DEV void lds_dma16(__amdgpu_buffer_rsrc_t r, void* lds, unsigned voff, unsig
 
 R2L_DEV int big_swz(int row, int chunk) { return chunk ^ ((row >> kBigSH) & (kBigCPR - 1)); }
 
+// Linear tile index -> (row tile, column tile): group-M raster, G row tiles
+// sweep all column tiles; narrow outputs (few column tiles) use taller groups
+// (measured best: 8 for <= 8 column tiles).
+R2L_DEV void big_tile(int lid, int nTm, int nTn, int& tm, int& tn) {
+  const int G = nTn <= 8 ? 8 : 4;
+  const int per_group = G * nTn;
+  const int first_m = (lid / per_group) * G;
+  const int gsz = min(nTm - first_m, G);
+  tm = first_m + (lid % per_group) % gsz;
+  tn = (lid % per_group) / gsz;
+}
+
 }  // namespace
 
+// n_dp = number of whole tiles of the main launch.  splits == 0: block b
+// computes tile xcd_remap(b) of those, over all of K, into C.  splits > 0
+// (the tail launch): block u computes K-steps [s ksteps, (s+1) ksteps) with
+// s = u % splits of tile n_dp + u / splits, as an fp32 partial sum into
+// part[u][256][256].
 template <bool OUT_F32>
 __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(int M, int N, int K,
                                                                const bf16* __restrict__ A, long lda,
                                                                const bf16* __restrict__ B, long ldb,
-                                                               void* __restrict__ Cv, long ldc) {
+                                                               void* __restrict__ Cv, long ldc,
+                                                               int n_dp, int splits, int ksteps,
+                                                               float* __restrict__ part) {
   constexpr int BM = kBigBM, BN = kBigBN, BK = kBigBK, ST = kBigST, LPT = kBigLPT, SROW = kBigSROW;
   // one LDS object per stage: the compiler then knows that reading one stage
   // does not have to wait for the loads still in flight into another
@@ -178,15 +197,10 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(int M, int N, int
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int wm = (wave >> 1) * 128, wn = (wave & 1) * 128;
   const int nTm = (M + BM - 1) / BM, nTn = (N + BN - 1) / BN;
-  const int lid = xcd_remap(blockIdx.x, nTm * nTn);
-  // group-M raster: G row tiles sweep all column tiles; narrow outputs (few
-  // column tiles) use taller groups (measured best: 8 for <= 8 column tiles)
-  const int G = nTn <= 8 ? 8 : 4;
-  const int per_group = G * nTn;
-  const int first_m = (lid / per_group) * G;
-  const int gsz = min(nTm - first_m, G);
-  const int tm = first_m + (lid % per_group) % gsz;
-  const int tn = (lid % per_group) / gsz;
+  const int lid = splits ? n_dp + (int)blockIdx.x / splits : xcd_remap(blockIdx.x, n_dp);
+  const int kbeg = splits ? ((int)blockIdx.x % splits) * ksteps : 0;
+  int tm, tn;
+  big_tile(lid, nTm, nTn, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
 
   // Buffer descriptors over this tile's rows: reads past row M (N) return 0.
@@ -205,10 +219,10 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(int M, int N, int
     voff[i] = i < LPT / 2 ? (unsigned)(((long)row * lda + kc * 8) * 2)
                           : (unsigned)(((long)(row - BM) * ldb + kc * 8) * 2);
   }
-  const int nk = K / BK;
+  const int nk = splits ? ksteps : K / BK;
   auto issue = [&](int s, int kt) {  // k-step kt -> stage s (past the end: reload the last step)
     char* base = stage(s);
-    const unsigned kb = (unsigned)(min(kt, nk - 1) * BK * 2);
+    const unsigned kb = (unsigned)((kbeg + min(kt, nk - 1)) * BK * 2);
 #pragma unroll
     for (int i = 0; i < LPT; ++i)
       lds_dma16(i < LPT / 2 ? rA : rB, base + (i * 256 + wave * 64) * 16, voff[i], kb);
@@ -307,6 +321,19 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(int M, int N, int
 
   // acc[i][j] register 4q+e holds C[m][n] with m = m0+wm+32i+(lane&31) and
   // n = n0+wn+32j+8q+4*(lane>>5)+e: four consecutive columns per store.
+  if (splits) {
+    float* pt = part + (long)blockIdx.x * (BM * BN);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int r = wm + 32 * i + fr, c = wn + 32 * j + 8 * q + 4 * fh;
+          *(f32x4*)(pt + r * BN + c) = f32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+        }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int m = m0 + wm + 32 * i + fr;
@@ -328,6 +355,25 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(int M, int N, int
   }
 }
 
+// C tile n_dp + t = sum over s of part[t * splits + s], in order of s.
+// Block: 4 rows of 256 columns of one tail tile; thread: 4 consecutive columns.
+template <bool OUT_F32>
+__global__ __launch_bounds__(256) void gemm_tail_reduce_kernel(int M, int N, int n_dp, int splits,
+                                                               const float* __restrict__ part,
+                                                               void* __restrict__ Cv, long ldc) {
+  const int nTm = (M + kBigBM - 1) / kBigBM, nTn = (N + kBigBN - 1) / kBigBN;
+  const int t = blockIdx.x / (kBigBM / 4), r = (blockIdx.x % (kBigBM / 4)) * 4 + (threadIdx.x >> 6);
+  const int c = (threadIdx.x & 63) * 4;
+  int tm, tn;
+  big_tile(n_dp + t, nTm, nTn, tm, tn);
+  const int m = tm * kBigBM + r, n = tn * kBigBN + c;
+  if (m >= M || n >= N) return;
+  f32x4 v = {0.0f, 0.0f, 0.0f, 0.0f};
+  for (int s = 0; s < splits; ++s) v = v + *(const f32x4*)(part + ((long)t * splits + s) * (kBigBM * kBigBN) + r * kBigBN + c);
+  if (OUT_F32) *(f32x4*)((float*)Cv + (long)m * ldc + n) = v;
+  else *(bf16x4*)((bf16*)Cv + (long)m * ldc + n) = bf16x4{(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]};
+}
+
 template <int BM, int BN>
 static void launch_gemm(int M, int N, int K, const bf16* A, long lda, const bf16* B, long ldb,
                         void* C, long ldc, bool out_f32, hipStream_t st) {
@@ -341,7 +387,8 @@ static void launch_gemm(int M, int N, int K, const bf16* A, long lda, const bf16
 }
 
 hipError_t gemm_bf16_nt(int M, int N, int K, const bf16* A, long lda, const bf16* B, long ldb,
-                        void* C, long ldc, bool out_f32, hipStream_t st) {
+                        void* C, long ldc, bool out_f32, hipStream_t st, float* ws, size_t ws_bytes,
+                        int ncu) {
   if (M <= 0 || N <= 0) return hipSuccess;
   const long big_tiles = (long)((M + kBigBM - 1) / kBigBM) * ((N + kBigBN - 1) / kBigBN);
   const unsigned long align = out_f32 ? 16 : 8;
@@ -354,12 +401,41 @@ hipError_t gemm_bf16_nt(int M, int N, int K, const bf16* A, long lda, const bf16
                    (long)kBigBM * lda * 2 < (1L << 31) && (long)kBigBN * ldb * 2 < (1L << 31) &&
                    big_tiles >= 128;
   if (big) {
+    // Tiles beyond the last whole round (tiles mod #CUs) would take a round of
+    // their own; with a workspace they are split along K over up to all CUs
+    // instead, and their fp32 partial sums added in a fixed order.  The split
+    // costs two launches and the partials' traffic, so it is used only for a
+    // small leftover (measured: a gain at 1/32 of a round, a loss at 1/8).
+    const int nk = K / kBigBK;
+    const int rem = ncu > 0 ? (int)(big_tiles % ncu) : 0;
+    int splits = 0;
+    if (ws != nullptr && rem > 0 && rem * 16 <= ncu && big_tiles > ncu) {
+      for (int s = 64; s >= 2; s /= 2)
+        if ((long)rem * s <= ncu && nk % (s * kBigST) == 0 &&
+            (size_t)rem * s * kBigBM * kBigBN * sizeof(float) <= ws_bytes && ((uintptr_t)ws & 15) == 0) {
+          splits = s;
+          break;
+        }
+    }
+    const int n_dp = (int)big_tiles - (splits ? rem : 0);
     if (out_f32)
-      hipLaunchKernelGGL((gemm_bf16_big_kernel<true>), dim3(big_tiles), dim3(256), 0, st, M, N, K, A, lda,
-                         B, ldb, C, ldc);
+      hipLaunchKernelGGL((gemm_bf16_big_kernel<true>), dim3(n_dp), dim3(256), 0, st, M, N, K, A, lda,
+                         B, ldb, C, ldc, n_dp, 0, 0, (float*)nullptr);
     else
-      hipLaunchKernelGGL((gemm_bf16_big_kernel<false>), dim3(big_tiles), dim3(256), 0, st, M, N, K, A, lda,
-                         B, ldb, C, ldc);
+      hipLaunchKernelGGL((gemm_bf16_big_kernel<false>), dim3(n_dp), dim3(256), 0, st, M, N, K, A, lda,
+                         B, ldb, C, ldc, n_dp, 0, 0, (float*)nullptr);
+    if (splits) {
+      const int ksteps = nk / splits;
+      // (the kernel's OUT_F32 only shapes the direct epilogue; partials are fp32)
+      hipLaunchKernelGGL((gemm_bf16_big_kernel<true>), dim3(rem * splits), dim3(256), 0, st, M, N, K,
+                         A, lda, B, ldb, C, ldc, n_dp, splits, ksteps, ws);
+      if (out_f32)
+        hipLaunchKernelGGL((gemm_tail_reduce_kernel<true>), dim3(rem * (kBigBM / 4)), dim3(256), 0, st, M,
+                           N, n_dp, splits, (const float*)ws, C, ldc);
+      else
+        hipLaunchKernelGGL((gemm_tail_reduce_kernel<false>), dim3(rem * (kBigBM / 4)), dim3(256), 0, st, M,
+                           N, n_dp, splits, (const float*)ws, C, ldc);
+    }
     return hipGetLastError();
   }
   // 128 x 128 tiles (4 waves of 64 x 64, two blocks per CU).

@@ -10,8 +10,11 @@
 namespace r2l {
 
 // C[M,N] = A[M,K] . B[N,K]^T.  bf16 inputs on MFMA; output bf16 or f32.
+// ws (optional, 16-byte aligned, ws_bytes long; may be NULL): scratch for the
+// K-split partial sums of the tiles past the last whole round over ncu CUs.
 hipError_t gemm_bf16_nt(int M, int N, int K, const bf16* A, long lda, const bf16* B, long ldb,
-                        void* C, long ldc, bool out_f32, hipStream_t st);
+                        void* C, long ldc, bool out_f32, hipStream_t st, float* ws = nullptr,
+                        size_t ws_bytes = 0, int ncu = 0);
 // fp32 inputs on the VALU; output f32.
 hipError_t gemm_f32_nt(int M, int N, int K, const float* A, long lda, const float* B, long ldb,
                        float* C, long ldc, hipStream_t st);

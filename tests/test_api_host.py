@@ -144,10 +144,14 @@ def test_conv_scan_gemm_reject_bad_arguments():
     assert lib.r2l_scan_fwd(C.byref(d), B.R2L_F32, FAKE, 4096, FAKE, 4096, FAKE, FAKE, FAKE, 16, None, None, 0,
                             FAKE, FAKE, 1, 10, 10, None, 0, None) == B.R2L_ERR_WORKSPACE
     # gemm
-    assert lib.r2l_gemm_nt(B.R2L_BF16, 10, 10, 12, FAKE, 12, FAKE, 12, FAKE, 10, 0, None) == B.R2L_ERR_UNSUPPORTED
-    assert lib.r2l_gemm_nt(B.R2L_BF16, 10, 10, 16, FAKE, 8, FAKE, 16, FAKE, 10, 0, None) == B.R2L_ERR_INVALID_ARG
-    assert lib.r2l_gemm_nt(3, 10, 10, 16, FAKE, 16, FAKE, 16, FAKE, 10, 0, None) == B.R2L_ERR_UNSUPPORTED
-    assert lib.r2l_gemm_nt(B.R2L_F32, -1, 10, 16, FAKE, 16, FAKE, 16, FAKE, 10, 0, None) == B.R2L_ERR_INVALID_ARG
+    assert lib.r2l_gemm_nt(B.R2L_BF16, 10, 10, 12, FAKE, 12, FAKE, 12, FAKE, 10, 0, None, 0, None) == B.R2L_ERR_UNSUPPORTED
+    assert lib.r2l_gemm_nt(B.R2L_BF16, 10, 10, 16, FAKE, 8, FAKE, 16, FAKE, 10, 0, None, 0, None) == B.R2L_ERR_INVALID_ARG
+    assert lib.r2l_gemm_nt(3, 10, 10, 16, FAKE, 16, FAKE, 16, FAKE, 10, 0, None, 0, None) == B.R2L_ERR_UNSUPPORTED
+    assert lib.r2l_gemm_nt(B.R2L_F32, -1, 10, 16, FAKE, 16, FAKE, 16, FAKE, 10, 0, None, 0, None) == B.R2L_ERR_INVALID_ARG
+    # workspace pointer and size must agree, and the pointer be 16-byte aligned
+    assert lib.r2l_gemm_nt(B.R2L_BF16, 10, 10, 16, FAKE, 16, FAKE, 16, FAKE, 10, 0, None, 64, None) == B.R2L_ERR_INVALID_ARG
+    assert lib.r2l_gemm_nt(B.R2L_BF16, 10, 10, 16, FAKE, 16, FAKE, 16, FAKE, 10, 0, FAKE, 0, None) == B.R2L_ERR_INVALID_ARG
+    assert lib.r2l_gemm_nt(B.R2L_BF16, 10, 10, 16, FAKE, 16, FAKE, 16, FAKE, 10, 0, FAKE + 8, 64, None) == B.R2L_ERR_INVALID_ARG
 
 
 def test_timing_read_empty():

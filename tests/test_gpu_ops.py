@@ -32,7 +32,9 @@ def _case(name):
 @pytest.mark.parametrize("M,N,K", [(1, 1, 8), (33, 17, 64), (128, 128, 64), (300, 520, 136),
                                    (1031, 257, 2048), (640, 8192, 2048),
                                    # large-tile kernel: ragged M and N, and an N%4 != 0 fallback
-                                   (8200, 2052, 512), (4099, 4096, 256), (8200, 2050, 512)])
+                                   (8200, 2052, 512), (4099, 4096, 256), (8200, 2050, 512),
+                                   # 264 tiles of 256 x 256: 8 past a round of 256, split along K with a workspace
+                                   (8448, 2048, 1024)])
 def test_gemm_bf16_matches_fp64_product(M, N, K):
     _case(f"gemm bf16 {M}x{N}x{K}")
     A = synth.make_aux(M * 7 + 1, (M, K))
@@ -44,6 +46,13 @@ def test_gemm_bf16_matches_fp64_product(M, N, K):
     torch.cuda.synchronize()
     assert report("gemm f32-out", err_f32(g32, ref), 1e-4) <= 1e-4
     assert report("gemm bf16-out", err_f32(g16, ref), 5e-3) <= 5e-3   # one bf16 rounding (2^-8)
+    # with a workspace the tiles past the last whole round are split along K
+    ws = torch.empty(256 * 256 * 1024, dtype=torch.uint8, device=DEV)
+    w32 = to_np(B.r2l_gemm_nt(_dev(A, "bf16"), _dev(Bm, "bf16"), out_f32=True, workspace=ws))
+    w16 = to_np(B.r2l_gemm_nt(_dev(A, "bf16"), _dev(Bm, "bf16"), out_f32=False, workspace=ws))
+    torch.cuda.synchronize()
+    assert report("gemm f32-out (ws)", err_f32(w32, ref), 1e-4) <= 1e-4
+    assert report("gemm bf16-out (ws)", err_f32(w16, ref), 5e-3) <= 5e-3
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 1, 1), (65, 130, 33), (256, 96, 128)])
