@@ -334,24 +334,49 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(int M, int N, int
         }
     return;
   }
+  // Direct epilogue through LDS: the four stages (free now) hold the tile in
+  // row-major order, each 16-byte chunk of a row at chunk ^ (row & 31)
+  // against bank conflicts; then every store instruction writes whole rows
+  // (64 lanes x 16 bytes).  bf16: 64 rows of 512 bytes per stage, one pass;
+  // f32: 32 rows of 1 KB per stage, two passes.  (Scattered 8-byte stores
+  // straight from the MFMA layout took several times longer.)
+  constexpr int ES = OUT_F32 ? 4 : 2;
+  constexpr int RB = BN * ES;                  // row bytes
+  constexpr int RPS = kBigSBYTES / RB;         // rows per stage
+  constexpr int RPP = 4 * RPS;                 // rows per pass
+  constexpr int LPR = RB / 16;                 // lanes per row in the store phase
+  asm volatile("s_barrier" ::: "memory");      // every wave is done reading the stages
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int m = m0 + wm + 32 * i + fr;
-    if (m >= M) continue;
+  for (int pass = 0; pass < BM / RPP; ++pass) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int i = 0; i < 4; ++i) {
+      const int r = wm + 32 * i + fr;
+      if (r / RPP != pass) continue;           // uniform per (wave, i)
+      const int rl = r - pass * RPP, rr = rl % RPS;
+      char* sb = stage(rl / RPS) + rr * RB;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int n = n0 + wn + 32 * j + 8 * q + 4 * fh;
-        if (n >= N) continue;
-        const f32x4 v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
-        if (OUT_F32) {
-          *(f32x4*)((float*)Cv + (long)m * ldc + n) = v;
-        } else {
-          const bf16x4 b = {(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]};
-          *(bf16x4*)((bf16*)Cv + (long)m * ldc + n) = b;
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int cb = (wn + 32 * j + 8 * q + 4 * fh) * ES;
+          char* dst = sb + (((cb >> 4) ^ (rr & 31)) << 4) + (cb & 15);
+          const f32x4 v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+          if (OUT_F32) *(f32x4*)dst = v;
+          else *(bf16x4*)dst = bf16x4{(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]};
         }
+    }
+    __syncthreads();
+    for (int rl = wave * (64 / LPR) + lane / LPR; rl < RPP; rl += 4 * (64 / LPR)) {
+      const int rr = rl % RPS, ch = lane % LPR;
+      const int m = m0 + pass * RPP + rl, n = n0 + ch * (16 / ES);
+      const i32x4 v = *(const i32x4*)(stage(rl / RPS) + rr * RB + ((ch ^ (rr & 31)) << 4));
+      if (m < M) {
+        char* g = (char*)Cv + ((long)m * ldc + n) * ES;
+        if (n + 16 / ES <= N) *(i32x4*)g = v;
+        else if (!OUT_F32 && n + 4 <= N) *(int2*)g = int2{v[0], v[1]};   // N % 4 == 0 (bf16: 8-column chunks)
       }
+    }
+    if (pass + 1 < BM / RPP) __syncthreads();
   }
 }
 
