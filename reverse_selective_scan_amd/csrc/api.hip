@@ -147,12 +147,20 @@ ScanPlan plan_scan(int E, int64_t T, int32_t nseq, int32_t max_seqlen, size_t ba
     if (want < 4 * kTB) want = 4 * kTB;
     if (want < Lc) Lc = want;
   }
+  if (Lc >= ms) {
+    // No chunking wanted: every sequence is one chunk whatever its length
+    // (a max_seqlen below the true longest length then costs parallelism,
+    // never correctness), and no summary pass is needed.
+    Lc = T > 0 ? T : 1;
+    p.summary = false;
+  } else {
+    p.summary = true;  // some sequence may span several chunks
+  }
   p.Lc = (int)Lc;
   // every chunk but a sequence's leftmost is full, so there are at most
   // nseq + T / Lc chunks whatever the true sequence lengths are
   p.max_chunks = (int)(nseq + (T + Lc - 1) / Lc);
   if (p.max_chunks < 1) p.max_chunks = 1;
-  p.summary = Lc < T;  // some sequence may span several chunks
   size_t off = base;
   p.off_cu = off;      off = align_up(off + sizeof(int32_t) * ((size_t)nseq + 1));
   p.off_chunks = off;  off = align_up(off + sizeof(ChunkDesc) * (size_t)p.max_chunks);
@@ -164,8 +172,12 @@ ScanPlan plan_scan(int E, int64_t T, int32_t nseq, int32_t max_seqlen, size_t ba
   return p;
 }
 
+// Scratch for K-split partial sums (GEMM tiles, conv channel splits): up to
+// one 256 x 256 fp32 tile per compute unit of a 256-CU device.
+constexpr size_t kSplitScratch = 256ull * 256 * 256 * sizeof(float);
+
 struct LayerPlan {
-  size_t off_xz, off_xdbl, off_xdbl2, off_u, off_y;
+  size_t off_xz, off_xdbl, off_xdbl2, off_u, off_y, off_scratch;
   bool need_u;
   ScanPlan scan;
   size_t total;
@@ -185,6 +197,7 @@ LayerPlan plan_layer(const r2l_dims* d, r2l_dtype act, int64_t T, int32_t nseq, 
   p.need_u = act == R2L_F32 || P > 256;
   p.off_u = off;    off = align_up(off + (p.need_u ? Tz * E * sa : 0));
   p.off_y = off;    off = align_up(off + Tz * E * sa);
+  p.off_scratch = off; off = align_up(off + (act == R2L_BF16 ? kSplitScratch : 0));
   p.scan = plan_scan((int)E, T, nseq, max_seqlen, off);
   p.total = p.scan.total;
   return p;
@@ -300,9 +313,9 @@ int r2l_layer_fwd(const r2l_dims* d, r2l_dtype act, uint32_t flags, const r2l_we
     bf16* xz = at<bf16>(workspace, lp.off_xz);
     bf16* y = at<bf16>(workspace, lp.off_y);
     const int ncu = num_cus();
-    // in_proj's K-split scratch: the y region, written only later by the scan
+    float* scratch = at<float>(workspace, lp.off_scratch);
     R2L_RUN("in_proj_gemm", st, gemm_bf16_nt(T, 2 * E, D, (const bf16*)h_in, D, (const bf16*)w->in_proj_w, D, xz, 2L * E, false, st,
-                                             at<float>(workspace, lp.off_y), (size_t)T * E * 2, ncu));
+                                             scratch, kSplitScratch, ncu));
     if (!lp.need_u) {
       // (the split kernel counts (tile, step) pairs in 32 bits)
       if ((T + 127) / 128 >= ncu && (long)((T + 127) / 128) * (E / 32) < (1L << 31)) {
@@ -311,7 +324,8 @@ int r2l_layer_fwd(const r2l_dims* d, r2l_dtype act, uint32_t flags, const r2l_we
         R2L_RUN("conv_xproj", st, conv_xproj_bf16_sk(T, E, P, xz, 2L * E, (const bf16*)w->conv_w, (const bf16*)w->conv_b, (const bf16*)w->x_proj_w, xdbl, xdbl2, cu_clean, nseq, ncu, st));
         R2L_RUN("add_parts", st, add_parts((long)T * P, xdbl, xdbl2, st));
       } else {
-        R2L_RUN("conv_xproj", st, conv_xproj_bf16(T, E, P, xz, 2L * E, (const bf16*)w->conv_w, (const bf16*)w->conv_b, (const bf16*)w->x_proj_w, nullptr, xdbl, cu_clean, nseq, st));
+        R2L_RUN("conv_xproj", st, conv_xproj_bf16(T, E, P, xz, 2L * E, (const bf16*)w->conv_w, (const bf16*)w->conv_b, (const bf16*)w->x_proj_w, nullptr, xdbl, cu_clean, nseq, st,
+                                                  scratch, kSplitScratch, ncu));
       }
     } else {
       bf16* u = at<bf16>(workspace, lp.off_u);
@@ -322,11 +336,8 @@ int r2l_layer_fwd(const r2l_dims* d, r2l_dtype act, uint32_t flags, const r2l_we
     a.x = xz; a.z = xz + E; a.y = y;
     if (sp.summary) R2L_RUN("scan_summary", st, scan_summary<bf16>(a, true, st));
     R2L_RUN("scan_main", st, scan_main<bf16>(a, true, st));
-    // out_proj's K-split scratch: the part of the (dead) xz region past o
-    const size_t o_bytes = align_up((size_t)T * D * 4), xz_bytes = (size_t)T * 2 * E * 2;
     R2L_RUN("out_proj_gemm", st, gemm_bf16_nt(T, D, E, y, E, (const bf16*)w->out_proj_w, E, o, D, true, st,
-                                              xz_bytes > o_bytes ? (float*)((char*)o + o_bytes) : nullptr,
-                                              xz_bytes > o_bytes ? xz_bytes - o_bytes : 0, ncu));
+                                              scratch, kSplitScratch, ncu));
     R2L_RUN("ln_gate", st, ln_gate<bf16>(T, D, o, (const bf16*)h_in, (bf16*)h_out, w->ln_w, w->ln_b, w->s, branch_out, no_ln, R2L_LN_EPS, st));
   } else {
     float* xz = at<float>(workspace, lp.off_xz);

@@ -66,6 +66,9 @@ template hipError_t conv_silu<bf16>(int, int, const bf16*, long, const bf16*, co
 // partial [32 x P] results are summed through LDS in a fixed order (no
 // atomics, so results are deterministic).
 // ---------------------------------------------------------------------------
+// gridDim.y = KS > 1 splits the channels over blocks: block (tile, ks)
+// covers channels [ks E/KS, (ks+1) E/KS) and writes its partial sum to slab
+// ks of xdbl ([KS][T][P]); sum_slabs adds the slabs.
 template <int NCS>
 __global__ __launch_bounds__(256) void conv_xproj_kernel(int Tn, int E, int P,
                                                          const bf16* __restrict__ x, long ld_x,
@@ -83,8 +86,10 @@ __global__ __launch_bounds__(256) void conv_xproj_kernel(int Tn, int E, int P,
   const int t = t0 + tr;
   const bool tv = t < Tn;
   const int se = tv ? seq_end_of(cu, nseq, t, Tn) : 0;
-  const int Ew = E / 4;
-  const int cbeg = w * Ew;
+  const int Eb = E / gridDim.y;                 // channels of this block
+  const int Ew = Eb / 4;
+  const int cbeg = blockIdx.y * Eb + w * Ew;
+  xdbl += (long)blockIdx.y * Tn * P;
 
   f32x16 acc[NCS];
 #pragma unroll
@@ -175,22 +180,48 @@ __global__ __launch_bounds__(256) void conv_xproj_kernel(int Tn, int E, int P,
   }
 }
 
+// out[i] = sum over k < ks of slab[k][i] (slab stride n), in order of k.
+__global__ __launch_bounds__(256) void sum_slabs_kernel(long n, int ks, const float* __restrict__ slab,
+                                                        float* __restrict__ out) {
+  for (long i = blockIdx.x * 256L + threadIdx.x; i < n; i += (long)gridDim.x * 256) {
+    float v = 0.0f;
+    for (int k = 0; k < ks; ++k) v += slab[k * n + i];
+    out[i] = v;
+  }
+}
+
 hipError_t conv_xproj_bf16(int Tn, int E, int P, const bf16* x, long ld_x, const bf16* conv_w,
                            const bf16* conv_b, const bf16* x_proj_w, bf16* u_out, float* xdbl,
-                           const int32_t* cu, int nseq, hipStream_t st) {
+                           const int32_t* cu, int nseq, hipStream_t st, float* ws, size_t ws_bytes,
+                           int ncu) {
   if (Tn <= 0) return hipSuccess;
   const int ncs = (P + 31) / 32;
-  dim3 grid((Tn + 31) / 32), block(256);
+  const int ntiles = (Tn + 31) / 32;
+  // Few token tiles for the GPU: split the channels over KS blocks per tile
+  // (each wave keeps at least one 16-channel step), partial sums in ws.
+  int ks = 1;
+  if (ws != nullptr && u_out == nullptr && ncu > 0) {
+    while (ntiles * ks * 2 <= ncu && (E / (ks * 2)) % 64 == 0 &&
+           (size_t)(ks * 2) * Tn * P * sizeof(float) <= ws_bytes)
+      ks *= 2;
+  }
+  float* dst = ks > 1 ? ws : xdbl;
+  dim3 grid(ntiles, ks), block(256);
 #define R2L_CX(n)                                                                               \
   case n:                                                                                       \
     hipLaunchKernelGGL((conv_xproj_kernel<n>), grid, block, 0, st, Tn, E, P, x, ld_x, conv_w,   \
-                       conv_b, x_proj_w, u_out, xdbl, cu, nseq);                                \
+                       conv_b, x_proj_w, u_out, dst, cu, nseq);                                 \
     break;
   switch (ncs) {
     R2L_CX(1) R2L_CX(2) R2L_CX(3) R2L_CX(4) R2L_CX(5) R2L_CX(6) R2L_CX(7) R2L_CX(8)
     default: return hipErrorInvalidValue;
   }
 #undef R2L_CX
+  if (ks > 1) {
+    const long n = (long)Tn * P;
+    const long blocks = (n + 255) / 256 < 2048 ? (n + 255) / 256 : 2048;
+    hipLaunchKernelGGL(sum_slabs_kernel, dim3(blocks), dim3(256), 0, st, n, ks, (const float*)ws, xdbl);
+  }
   return hipGetLastError();
 }
 

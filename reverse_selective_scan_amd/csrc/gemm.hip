@@ -26,11 +26,17 @@
 
 namespace r2l {
 
+// splits == 0: block b computes a whole output tile into C.  splits > 0:
+// block u computes K range [s kchunk, (s+1) kchunk) (s = u % splits) of tile
+// u / splits (row-major tile order) as an fp32 partial sum into
+// part[u][BM][BN]; gemm_small_reduce_kernel adds the partials.
 template <int BM, int BN, bool OUT_F32>
 __global__ __launch_bounds__(256, 1) void gemm_bf16_nt_kernel(int M, int N, int K,
                                                               const bf16* __restrict__ A, long lda,
                                                               const bf16* __restrict__ B, long ldb,
-                                                              void* __restrict__ Cv, long ldc) {
+                                                              void* __restrict__ Cv, long ldc,
+                                                              int splits, int kchunk,
+                                                              float* __restrict__ part) {
   constexpr int BK = 64;
   constexpr int LS = BK + 8;                 // LDS row stride (bf16 elements)
   constexpr int WM = BM / 2, WN = BN / 2;    // wave tile
@@ -43,13 +49,22 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_nt_kernel(int M, int N, int 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = (wave >> 1) * WM, wn = (wave & 1) * WN;
   const int nTm = (M + BM - 1) / BM, nTn = (N + BN - 1) / BN;
-  const int lid = xcd_remap(blockIdx.x, nTm * nTn);
-  constexpr int G = 8;
-  const int per_group = G * nTn;
-  const int first_m = (lid / per_group) * G;
-  const int gsz = min(nTm - first_m, G);
-  const int tm = first_m + (lid % per_group) % gsz;
-  const int tn = (lid % per_group) / gsz;
+  int tm, tn, kbeg = 0, kend = K;
+  if (splits) {
+    const int tile = blockIdx.x / splits, sp = blockIdx.x % splits;
+    tm = tile / nTn;
+    tn = tile % nTn;
+    kbeg = sp * kchunk;
+    kend = min(K, kbeg + kchunk);
+  } else {
+    const int lid = xcd_remap(blockIdx.x, nTm * nTn);
+    constexpr int G = 8;
+    const int per_group = G * nTn;
+    const int first_m = (lid / per_group) * G;
+    const int gsz = min(nTm - first_m, G);
+    tm = first_m + (lid % per_group) % gsz;
+    tn = (lid % per_group) / gsz;
+  }
   const int m0 = tm * BM, n0 = tn * BN;
 
   i32x4 ra[AC], rb[BC];
@@ -58,13 +73,13 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_nt_kernel(int M, int N, int 
 #define R2L_GLOAD(k0)                                                              \
   _Pragma("unroll") for (int i = 0; i < AC; ++i) {                                 \
     const int c = tid + 256 * i, row = c / CPR, col = (c % CPR) * 8;               \
-    const int gm = m0 + row, gk = (k0) + col;                                      \
-    ra[i] = (gm < M && gk < K) ? *(const i32x4*)(A + (long)gm * lda + gk) : zero4; \
+    const int gm = m0 + row, gk = kbeg + (k0) + col;                               \
+    ra[i] = (gm < M && gk < kend) ? *(const i32x4*)(A + (long)gm * lda + gk) : zero4; \
   }                                                                                \
   _Pragma("unroll") for (int i = 0; i < BC; ++i) {                                 \
     const int c = tid + 256 * i, row = c / CPR, col = (c % CPR) * 8;               \
-    const int gn = n0 + row, gk = (k0) + col;                                      \
-    rb[i] = (gn < N && gk < K) ? *(const i32x4*)(B + (long)gn * ldb + gk) : zero4; \
+    const int gn = n0 + row, gk = kbeg + (k0) + col;                               \
+    rb[i] = (gn < N && gk < kend) ? *(const i32x4*)(B + (long)gn * ldb + gk) : zero4; \
   }
 #define R2L_SSTORE(buf)                                                 \
   _Pragma("unroll") for (int i = 0; i < AC; ++i) {                      \
@@ -88,7 +103,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_nt_kernel(int M, int N, int 
   // registers hold tile kt+1.  The registers go to the other LDS buffer first
   // (that buffer's last readers finished before the previous barrier), then
   // the loads of tile kt+2 are issued, then tile kt's MFMAs run.
-  const int nk = (K + BK - 1) / BK;
+  const int nk = (kend - kbeg + BK - 1) / BK;
   R2L_GLOAD(0);
   R2L_SSTORE(0);
   if (nk > 1) { R2L_GLOAD(BK); }
@@ -119,6 +134,17 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_nt_kernel(int M, int N, int 
 #undef R2L_SSTORE
 
   // D tile layout: lane holds column (lane & 31) and rows 8*(r/4) + 4*(lane/32) + r%4.
+  if (splits) {
+    float* pt = part + (long)blockIdx.x * (BM * BN);
+#pragma unroll
+    for (int i = 0; i < SM; ++i)
+#pragma unroll
+      for (int j = 0; j < SN; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          pt[(wm + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3)) * BN + wn + 32 * j + fr] = acc[i][j][r];
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < SM; ++i)
 #pragma unroll
@@ -399,16 +425,55 @@ __global__ __launch_bounds__(256) void gemm_tail_reduce_kernel(int M, int N, int
   else *(bf16x4*)((bf16*)Cv + (long)m * ldc + n) = bf16x4{(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]};
 }
 
+// C = sum over s of the 128 x 128 partial tiles part[tile * splits + s], in
+// order of s (row-major tiles); one thread per output element.
+template <int BM, int BN, bool OUT_F32>
+__global__ __launch_bounds__(256) void gemm_small_reduce_kernel(int M, int N, int splits,
+                                                                const float* __restrict__ part,
+                                                                void* __restrict__ Cv, long ldc) {
+  const int nTn = (N + BN - 1) / BN;
+  const long e = blockIdx.x * 256L + threadIdx.x;
+  const int m = (int)(e / N), n = (int)(e % N);
+  if (m >= M) return;
+  const int tile = (m / BM) * nTn + n / BN, r = m % BM, c = n % BN;
+  float v = 0.0f;
+  for (int s = 0; s < splits; ++s) v += part[((long)tile * splits + s) * (BM * BN) + r * BN + c];
+  if (OUT_F32) ((float*)Cv)[(long)m * ldc + n] = v;
+  else ((bf16*)Cv)[(long)m * ldc + n] = (bf16)v;
+}
+
 template <int BM, int BN>
 static void launch_gemm(int M, int N, int K, const bf16* A, long lda, const bf16* B, long ldb,
-                        void* C, long ldc, bool out_f32, hipStream_t st) {
+                        void* C, long ldc, bool out_f32, hipStream_t st, float* ws, size_t ws_bytes,
+                        int ncu) {
   const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+  // Few tiles for the GPU: split K over several blocks per tile (each split
+  // at least 4 of the kernel's 64-wide K steps), fp32 partials in ws.
+  int splits = 1;
+  if (ws != nullptr && ncu > 0 && tiles * 2 <= ncu) {
+    while (tiles * splits * 2 <= ncu && K / (splits * 2) >= 256 &&
+           (size_t)tiles * splits * 2 * BM * BN * sizeof(float) <= ws_bytes)
+      splits *= 2;
+  }
+  if (splits > 1) {
+    const int kchunk = ((K + splits - 1) / splits + 63) / 64 * 64;
+    hipLaunchKernelGGL((gemm_bf16_nt_kernel<BM, BN, true>), dim3(tiles * splits), dim3(256), 0, st, M,
+                       N, K, A, lda, B, ldb, C, ldc, splits, kchunk, ws);
+    const long n = (long)M * N;
+    if (out_f32)
+      hipLaunchKernelGGL((gemm_small_reduce_kernel<BM, BN, true>), dim3((n + 255) / 256), dim3(256), 0, st,
+                         M, N, splits, (const float*)ws, C, ldc);
+    else
+      hipLaunchKernelGGL((gemm_small_reduce_kernel<BM, BN, false>), dim3((n + 255) / 256), dim3(256), 0,
+                         st, M, N, splits, (const float*)ws, C, ldc);
+    return;
+  }
   if (out_f32)
     hipLaunchKernelGGL((gemm_bf16_nt_kernel<BM, BN, true>), dim3(tiles), dim3(256), 0, st, M, N, K,
-                       A, lda, B, ldb, C, ldc);
+                       A, lda, B, ldb, C, ldc, 0, 0, (float*)nullptr);
   else
     hipLaunchKernelGGL((gemm_bf16_nt_kernel<BM, BN, false>), dim3(tiles), dim3(256), 0, st, M, N,
-                       K, A, lda, B, ldb, C, ldc);
+                       K, A, lda, B, ldb, C, ldc, 0, 0, (float*)nullptr);
 }
 
 hipError_t gemm_bf16_nt(int M, int N, int K, const bf16* A, long lda, const bf16* B, long ldb,
@@ -464,7 +529,7 @@ hipError_t gemm_bf16_nt(int M, int N, int K, const bf16* A, long lda, const bf16
     return hipGetLastError();
   }
   // 128 x 128 tiles (4 waves of 64 x 64, two blocks per CU).
-  launch_gemm<128, 128>(M, N, K, A, lda, B, ldb, C, ldc, out_f32, st);
+  launch_gemm<128, 128>(M, N, K, A, lda, B, ldb, C, ldc, out_f32, st, ws, ws_bytes, ncu);
   return hipGetLastError();
 }
 

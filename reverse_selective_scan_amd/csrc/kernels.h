@@ -25,9 +25,12 @@ hipError_t conv_silu(int T_, int E, const T* x, long ld_x, const T* conv_w, cons
                      T* u, const int32_t* cu, int nseq, hipStream_t st);
 // Fused conv + SiLU + x_proj (bf16, MFMA): xdbl f32 [T, P] with P = R+2N;
 // u_out optional.  Requires E % 64 == 0 and P <= 256.
+// ws (optional, ws_bytes): scratch for splitting the channels over several
+// blocks per 32-token tile when there are few tiles (not with u_out).
 hipError_t conv_xproj_bf16(int T_, int E, int P, const bf16* x, long ld_x, const bf16* conv_w,
                            const bf16* conv_b, const bf16* x_proj_w, bf16* u_out, float* xdbl,
-                           const int32_t* cu, int nseq, hipStream_t st);
+                           const int32_t* cu, int nseq, hipStream_t st, float* ws = nullptr,
+                           size_t ws_bytes = 0, int ncu = 0);
 
 // The same for large inputs, split along K over `nblocks` blocks (one per
 // CU): xdbl = part0 + part1 (add_parts), part1 16-byte aligned.  Requires

@@ -31,6 +31,25 @@ constexpr int NS = 16;    // d_state (§4.1)
 // made non-decreasing) and the chunk table, rightmost chunk of each
 // sequence first.
 // ---------------------------------------------------------------------------
+// Exclusive block-wide scan of one value per thread (256 threads), max or sum,
+// Hillis-Steele in LDS: 8 steps.
+template <bool MAX>
+R2L_DEV int block_exclusive_scan(int v, int* buf) {
+  const int tid = threadIdx.x;
+  buf[tid] = v;
+  __syncthreads();
+#pragma unroll
+  for (int off = 1; off < 256; off <<= 1) {
+    const int o = tid >= off ? buf[tid - off] : 0;   // values are >= 0: 0 is neutral for both
+    __syncthreads();
+    if (tid >= off) buf[tid] = MAX ? max(buf[tid], o) : buf[tid] + o;
+    __syncthreads();
+  }
+  const int excl = tid > 0 ? buf[tid - 1] : 0;
+  __syncthreads();
+  return excl;
+}
+
 __global__ __launch_bounds__(256) void plan_chunks_kernel(const int32_t* __restrict__ cu, int nseq,
                                                           int Tn, int Lc, int max_chunks,
                                                           int32_t* __restrict__ cu_clean,
@@ -42,26 +61,16 @@ __global__ __launch_bounds__(256) void plan_chunks_kernel(const int32_t* __restr
   const int per = (n1 + 255) / 256;
   const int qa = min(tid * per, n1), qb = min(qa + per, n1);
   auto clampT = [&](int v) { return v < 0 ? 0 : (v > Tn ? Tn : v); };
+  // sanitised offsets: clamp into [0, T], then running maximum
   int m = 0;
   for (int q = qa; q < qb; ++q) m = max(m, clampT(cu[q]));
-  s_v[tid] = m;
-  __syncthreads();
-  if (tid == 0) {
-    int run = 0;
-    for (int i = 0; i < 256; ++i) {
-      const int v = s_v[i];
-      s_v[i] = run;  // exclusive prefix max
-      run = max(run, v);
-    }
-  }
-  __syncthreads();
-  int run = s_v[tid];
+  int run = block_exclusive_scan<true>(m, s_v);
   for (int q = qa; q < qb; ++q) {
     run = max(run, clampT(cu[q]));
     cu_clean[q] = run;
   }
   __syncthreads();
-  // chunk counts
+  // chunk counts and each sequence's first table index
   const int ps = (nseq + 255) / 256;
   const int sa = min(tid * ps, nseq), sb = min(sa + ps, nseq);
   int cnt = 0;
@@ -69,20 +78,8 @@ __global__ __launch_bounds__(256) void plan_chunks_kernel(const int32_t* __restr
     const int len = cu_clean[q + 1] - cu_clean[q];
     cnt += (len + Lc - 1) / Lc;
   }
-  __syncthreads();
-  s_v[tid] = cnt;
-  __syncthreads();
-  if (tid == 0) {
-    int acc = 0;
-    for (int i = 0; i < 256; ++i) {
-      const int v = s_v[i];
-      s_v[i] = acc;
-      acc += v;
-    }
-    *n_chunks = min(acc, max_chunks);
-  }
-  __syncthreads();
-  int base = s_v[tid];
+  int base = block_exclusive_scan<false>(cnt, s_v);
+  if (tid == 255) *n_chunks = min(base + cnt, max_chunks);
   for (int q = sa; q < sb; ++q) {
     const int slo = cu_clean[q], send = cu_clean[q + 1];
     const int nc = (send - slo + Lc - 1) / Lc;

@@ -105,6 +105,24 @@ def test_bf16_split_k_conv_path_matches_oracle():
     assert report("branch", err_rms(gr, rref), TOL_BF16_BRANCH) <= TOL_BF16_BRANCH
 
 
+@pytest.mark.parametrize("hint", ["too_small", "too_large"])
+def test_max_seqlen_hint_does_not_change_results(hint):
+    """max_seqlen only plans the scan's time chunks: a value below the true
+    longest length (one chunk per sequence, no summary pass) or far above it
+    (chunks and a carry pass) must still give the oracle's result."""
+    lens = [900, 5, 300, 1]
+    _case(f"max_seqlen {hint} lens={lens}")
+    wl = synth.custom(lens, seed=23, h_kind="rms", **SMALL)
+    W, h, cu = synth.make_weights(wl), synth.make_hidden(wl), wl.cu_seqlens()
+    ref = O.reverse_mamba_layer(h, cu, W, float(W["s"]))
+    w = B.to_device_weights(W, torch.bfloat16, DEV)
+    hd = torch.from_numpy(h).to(torch.bfloat16).to(DEV)
+    cu_d = torch.from_numpy(np.asarray(cu, np.int32)).to(DEV)
+    ms = 2 if hint == "too_small" else 100000
+    g = to_np(B.r2l_layer_fwd(hd, w, cu_d, nseq=len(lens), max_seqlen=ms))
+    assert report(f"out (max_seqlen {ms})", err_rms(g, ref), TOL_BF16) <= TOL_BF16
+
+
 def test_small_bf16_no_ln_and_in_place():
     _case("small bf16 NO_LN in place")
     wl = synth.custom([200, 57], seed=8, h_kind="rms", **SMALL)
