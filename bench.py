@@ -4,7 +4,11 @@
 
 A step is one r2l_layer_fwd call (in_proj, conv + x_proj, reverse scan,
 out_proj, LayerNorm + gated residual) over the whole synthetic batch, with
-inputs and weights already resident in HBM.  Prints one JSON line.
+inputs and weights already resident in HBM.  Prints one JSON line.  For the
+multi-hook workloads (stack7, denoise_g32, denoise_g128) a step applies every
+hook in order, and `value` counts layer-tokens (tokens x hooks) per second;
+the denoise-step workloads replay each step as one captured HIP graph
+(--graph on|off|auto) and report us_per_step.
 
 Per-kernel durations come from HIP events that the library records around
 each of its launches on the launch stream (a second timed region, so the
@@ -48,6 +52,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="serve_b8")
+    ap.add_argument("--graph", choices=("auto", "on", "off"), default="auto",
+                    help="replay each step as one captured HIP graph (auto: for the denoise-step workloads)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="approximate CPU time spent on the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -80,17 +86,26 @@ def main():
     assert wl.dtype == "bf16"
     T, D, E, N, R = wl.n_tokens, wl.d_model, wl.d_inner, wl.d_state, wl.dt_rank
     P = R + 2 * N
-    W = synth.make_weights(wl)
+    # one weight set per hook; a step applies the hooks in order (identity
+    # between hooks), ping-ponging between two hidden-state buffers
+    Ws = [synth.make_weights(wl, hook=k) for k in range(wl.n_hooks)]
+    W = Ws[0]
     h_np = synth.make_hidden(wl)
-    w = B.to_device_weights(W, torch.bfloat16, dev)
+    wd = [B.to_device_weights(Wk, torch.bfloat16, dev) for Wk in Ws]
     h = torch.from_numpy(h_np).to(torch.bfloat16).to(dev)
     out = torch.empty_like(h)
     cu, nseq, max_seqlen = B.cu_seqlens_device(wl.cu_seqlens(), T, dev)
-    ws_bytes = B.r2l_layer_workspace_bytes(B.dims_of(w), B.R2L_BF16, T, nseq, max_seqlen)
+    ws_bytes = B.r2l_layer_workspace_bytes(B.dims_of(wd[0]), B.R2L_BF16, T, nseq, max_seqlen)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    bufs = (h, out)
 
-    def step():
-        B.r2l_layer_fwd(h, w, cu, out=out, workspace=ws, nseq=nseq, max_seqlen=max_seqlen)
+    def eager_step():
+        for k, w in enumerate(wd):
+            B.r2l_layer_fwd(bufs[k % 2], w, cu, out=bufs[(k + 1) % 2], workspace=ws, nseq=nseq,
+                            max_seqlen=max_seqlen)
+
+    step = eager_step
+    use_graph = args.graph == "on" or (args.graph == "auto" and wl.name.startswith("denoise"))
 
     if args.copy_calib_mib > 0:
         # a plain copy kernel of known size, for scaling the HBM byte counters
@@ -101,10 +116,28 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    print(f"[bench] workload {wl.name}: T={T} D={D} E={E} N={N} R={R}, warmup {args.warmup}", flush=True)
+    print(f"[bench] workload {wl.name}: T={T} D={D} E={E} N={N} R={R}, hooks {wl.n_hooks}, "
+          f"warmup {args.warmup}, graph {use_graph}", flush=True)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    if use_graph:
+        # the whole step (every hook) as one HIP graph on a side stream; the
+        # library launches on the caller's current stream and allocates nothing
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            eager_step()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            eager_step()
+        torch.cuda.synchronize()
+        step = graph.replay
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -118,14 +151,14 @@ def main():
     t_wall = time.perf_counter() - t_wall
     ms_total = e0.elapsed_time(e1)
     ms_step = ms_total / args.steps
-    tok_s = T / (ms_step * 1e-3)
+    tok_s = T * wl.n_hooks / (ms_step * 1e-3)
     print(f"[bench] timed {args.steps} steps: {ms_step:.3f} ms/step (wall {t_wall:.2f}s)", flush=True)
 
     # per-kernel durations (second timed region, events inside the library)
     B.timing_reset()
     B.timing_enable(True)
     for _ in range(args.steps):
-        step()
+        eager_step()
     torch.cuda.synchronize()
     kt = B.timing_read()
     B.timing_enable(False)
@@ -188,8 +221,9 @@ def main():
         "dtype": "bf16",
         "data": "synthetic (seeded; random-init weights of the layer's shapes)",
         "config": {"workload": wl.name, "batch": nseq, "seq_len": max_seqlen, "n_tokens": T, "d_model": D,
-                   "d_inner": E, "d_state": N, "dt_rank": R, "d_conv": wl.d_conv,
-                   "state_dtype": "f32", "note": wl.note},
+                   "d_inner": E, "d_state": N, "dt_rank": R, "d_conv": wl.d_conv, "hooks": wl.n_hooks,
+                   "graph": use_graph, "state_dtype": "f32", "note": wl.note},
+        "us_per_step": round(ms_step * 1e3, 2),
         "scan_hbm_gbs": scan.get("achieved_gbs"),
         "scan_hbm_frac": scan.get("frac"),
         "roofline": roofline,

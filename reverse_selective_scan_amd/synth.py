@@ -82,7 +82,8 @@ def varlen_lengths(seed: int, count: int, lo: int, hi: int) -> List[int]:
 
 
 def workloads() -> dict:
-    """The five workload shapes (the long-context one split in two)."""
+    """The five workload shapes (the long-context one split in two) and the
+    denoise-step blocks."""
     W = {}
     W["tiny_f32"] = Workload("tiny_f32", [64], 64, 128, 16, 4, 4, "f32", 0, "normal",
                              note="B=1 L=64 D=64 E=128 N=16 R=4 K=4, fp32 throughout")
@@ -97,6 +98,11 @@ def workloads() -> dict:
                              note="16 packed sequences, lengths uniform in [512, 16384]")
     W["long32k"] = Workload("long32k", [32768], 2048, 4096, 16, 128, 4, "bf16", 4, "rms",
                             note="one sequence of L=32768")
+    # the cached-decoding inner loop: each denoise step runs the seven hooks on
+    # the masked generation block of every sequence alone
+    for g in (32, 128):
+        W[f"denoise_g{g}"] = Workload(f"denoise_g{g}", [g] * 8, 2048, 4096, 16, 128, 4, "bf16", 5, "rms",
+                                      n_hooks=7, note=f"one denoise step: 7 hooks on B=8 blocks of G={g} tokens")
     return W
 
 

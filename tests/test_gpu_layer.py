@@ -285,3 +285,82 @@ def test_long32k_matches_oracle():
     ref = _suffix_ref(h, W, float(W["s"]), 0, L, L - 6144)   # spans several scan chunks
     assert report("long32k suffix 6144", err_rms(g[L - 6144:], ref), TOL_BF16) <= TOL_BF16
     print(f"oracle {time.time() - t:.1f}s", flush=True)
+
+
+# ---------------------------------------------------------------------------
+# denoise step: seven hooks on the B=8 generation blocks alone
+# ---------------------------------------------------------------------------
+def _denoise_setup(wl):
+    h0, cu = synth.make_hidden(wl), wl.cu_seqlens()
+    Ws = [synth.make_weights(wl, hook=k) for k in range(wl.n_hooks)]
+    wd = [B.to_device_weights(W, torch.bfloat16, DEV) for W in Ws]
+    return h0, cu, Ws, wd
+
+
+@pytest.mark.parametrize("name", ["denoise_g32", "denoise_g128"])
+def test_denoise_step_matches_oracle(name):
+    """Every hook of one denoise step on the oracle's bf16 stream (strict),
+    and the GPU chain end to end (sum of the per-hook bounds, as for the
+    seven-hook stack), over all eight blocks."""
+    wl = synth.workloads()[name]
+    _case(f"{name} (7 hooks, B=8 x G={wl.lengths[0]})")
+    h0, cu, Ws, wd = _denoise_setup(wl)
+    hd = torch.from_numpy(h0).to(torch.bfloat16).to(DEV)
+    for w in wd:
+        B.r2l_layer_fwd(hd, w, cu, out=hd)
+    torch.cuda.synchronize()
+    g_chain = to_np(hd)
+    cur = h0.astype(np.float64)
+    for k, W in enumerate(Ws):
+        ref = O.reverse_mamba_layer(cur, cu, W, float(W["s"]))
+        hin = torch.from_numpy(cur.astype(np.float32)).to(torch.bfloat16).to(DEV)
+        g = to_np(B.r2l_layer_fwd(hin, wd[k], cu))
+        assert report(f"{name} hook {k}", err_rms(g, ref), TOL_BF16) <= TOL_BF16
+        cur = synth.bf16_round(ref.astype(np.float32)).astype(np.float64)
+    assert report(f"{name} end-to-end", err_rms(g_chain, ref), 7 * TOL_BF16) <= 7 * TOL_BF16
+
+
+def test_denoise_step_graph_replays_match_eager():
+    """The seven hooks captured as one HIP graph: every replay, with eager
+    work and synchronisations between replays, equals the eager step bit
+    for bit (the library launches on the caller's stream and allocates or
+    clears nothing inside the step)."""
+    wl = synth.workloads()["denoise_g32"]
+    _case("denoise_g32 graph capture, 4 replays")
+    h0, cu, Ws, wd = _denoise_setup(wl)
+    T = wl.n_tokens
+    cud, nseq, ms = B.cu_seqlens_device(cu, T, DEV)
+    ws = torch.empty(B.r2l_layer_workspace_bytes(B.dims_of(wd[0]), B.R2L_BF16, T, nseq, ms),
+                     dtype=torch.uint8, device=DEV)
+    h = torch.from_numpy(h0).to(torch.bfloat16).to(DEV)
+    bufs = [torch.empty_like(h), torch.empty_like(h)]
+
+    def step():
+        for k, w in enumerate(wd):
+            B.r2l_layer_fwd(bufs[k % 2], w, cud, out=bufs[(k + 1) % 2], workspace=ws, nseq=nseq, max_seqlen=ms)
+        return bufs[len(wd) % 2]
+
+    bufs[0].copy_(h)
+    ref = step().clone()
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        bufs[0].copy_(h)
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        out_g = step()
+    torch.cuda.synchronize()
+    other = torch.from_numpy(synth.make_hidden(wl, hook=1)).to(torch.bfloat16).to(DEV)
+    for r in range(4):
+        bufs[0].copy_(h)
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out_g, ref), f"replay {r} differs from the eager step"
+        bufs[0].copy_(other)          # eager work on different data between replays
+        step()
+        torch.cuda.synchronize()
+    print("4 replays equal to the eager step", flush=True)
