@@ -148,7 +148,9 @@ int r2l_conv_fwd(const r2l_dims* dims, r2l_dtype act, const void* x, int64_t ld_
  * ld_z) or NULL (no gate); y_out: act [n_tokens, E] contiguous.
  * u, dt, z and y_out must be 16-byte aligned, with ld_u and ld_z multiples
  * of 8 (bf16) or 4 (f32) elements and ld_dt a multiple of 4; B and C have
- * no alignment requirement.
+ * no alignment requirement.  A row stride whose 64 rows exceed 2^31 - 1
+ * bytes returns R2L_ERR_UNSUPPORTED (rows are addressed with 32-bit offsets
+ * inside windows of a few dozen rows).
  * workspace: r2l_scan_workspace_bytes(...) bytes, 256-byte aligned.
  * ---------------------------------------------------------------------- */
 size_t r2l_scan_workspace_bytes(const r2l_dims* dims, int64_t n_tokens, int32_t nseq,

@@ -177,7 +177,7 @@ ScanPlan plan_scan(int E, int64_t T, int32_t nseq, int32_t max_seqlen, size_t ba
 constexpr size_t kSplitScratch = 256ull * 256 * 256 * sizeof(float);
 
 struct LayerPlan {
-  size_t off_xz, off_xdbl, off_xdbl2, off_u, off_y, off_scratch;
+  size_t off_xz, off_xdbl, off_xdbl2, off_xdbl3, off_u, off_y, off_scratch;
   bool need_u;
   ScanPlan scan;
   size_t total;
@@ -192,8 +192,9 @@ LayerPlan plan_layer(const r2l_dims* d, r2l_dtype act, int64_t T, int32_t nseq, 
   size_t xz = Tz * 2 * E * sa, o = Tz * D * 4;  // out_proj's fp32 output reuses xz
   p.off_xz = off;   off = align_up(off + (xz > o ? xz : o));
   p.off_xdbl = off; off = align_up(off + Tz * P * 4);
-  // second partial x_proj sum of the split-K conv kernel (bf16, large T)
+  // second and third partial x_proj sums of the split-K conv kernel (bf16, large T)
   p.off_xdbl2 = off; off = align_up(off + (act == R2L_BF16 ? Tz * P * 4 : 0));
+  p.off_xdbl3 = off; off = align_up(off + (act == R2L_BF16 ? Tz * P * 4 : 0));
   p.need_u = act == R2L_F32 || P > 256;
   p.off_u = off;    off = align_up(off + (p.need_u ? Tz * E * sa : 0));
   p.off_y = off;    off = align_up(off + Tz * E * sa);
@@ -319,10 +320,11 @@ int r2l_layer_fwd(const r2l_dims* d, r2l_dtype act, uint32_t flags, const r2l_we
     if (!lp.need_u) {
       // (the split kernel counts (tile, step) pairs in 32 bits)
       if ((T + 127) / 128 >= ncu && (long)((T + 127) / 128) * (E / 32) < (1L << 31)) {
-        // large input: split-K over one block per CU, then part0 += part1
+        // large input: split-K over one or two blocks per CU, then the parts are summed
         float* xdbl2 = at<float>(workspace, lp.off_xdbl2);
-        R2L_RUN("conv_xproj", st, conv_xproj_bf16_sk(T, E, P, xz, 2L * E, (const bf16*)w->conv_w, (const bf16*)w->conv_b, (const bf16*)w->x_proj_w, xdbl, xdbl2, cu_clean, nseq, ncu, st));
-        R2L_RUN("add_parts", st, add_parts((long)T * P, xdbl, xdbl2, st));
+        float* xdbl3 = at<float>(workspace, lp.off_xdbl3);
+        R2L_RUN("conv_xproj", st, conv_xproj_bf16_sk(T, E, P, xz, 2L * E, (const bf16*)w->conv_w, (const bf16*)w->conv_b, (const bf16*)w->x_proj_w, xdbl, xdbl2, xdbl3, cu_clean, nseq, ncu, st));
+        R2L_RUN("conv_sum", st, conv_sk_sum(T, E, P, xdbl, xdbl2, xdbl3, ncu, st));
       } else {
         R2L_RUN("conv_xproj", st, conv_xproj_bf16(T, E, P, xz, 2L * E, (const bf16*)w->conv_w, (const bf16*)w->conv_b, (const bf16*)w->x_proj_w, nullptr, xdbl, cu_clean, nseq, st,
                                                   scratch, kSplitScratch, ncu));
@@ -336,9 +338,11 @@ int r2l_layer_fwd(const r2l_dims* d, r2l_dtype act, uint32_t flags, const r2l_we
     a.x = xz; a.z = xz + E; a.y = y;
     if (sp.summary) R2L_RUN("scan_summary", st, scan_summary<bf16>(a, true, st));
     R2L_RUN("scan_main", st, scan_main<bf16>(a, true, st));
+    // o stays fp32: rounding it to bf16 before the LayerNorm would add up to
+    // half a bf16 step of |o| / std(o) to r at the rows' extremes
     R2L_RUN("out_proj_gemm", st, gemm_bf16_nt(T, D, E, y, E, (const bf16*)w->out_proj_w, E, o, D, true, st,
                                               scratch, kSplitScratch, ncu));
-    R2L_RUN("ln_gate", st, ln_gate<bf16>(T, D, o, (const bf16*)h_in, (bf16*)h_out, w->ln_w, w->ln_b, w->s, branch_out, no_ln, R2L_LN_EPS, st));
+    R2L_RUN("ln_gate", st, (ln_gate<bf16, float>(T, D, o, (const bf16*)h_in, (bf16*)h_out, w->ln_w, w->ln_b, w->s, branch_out, no_ln, R2L_LN_EPS, st)));
   } else {
     float* xz = at<float>(workspace, lp.off_xz);
     float* u = at<float>(workspace, lp.off_u);
@@ -350,7 +354,7 @@ int r2l_layer_fwd(const r2l_dims* d, r2l_dtype act, uint32_t flags, const r2l_we
     if (sp.summary) R2L_RUN("scan_summary", st, scan_summary<float>(a, true, st));
     R2L_RUN("scan_main", st, scan_main<float>(a, true, st));
     R2L_RUN("out_proj_gemm", st, gemm_f32_nt(T, D, E, y, E, (const float*)w->out_proj_w, E, o, D, st));
-    R2L_RUN("ln_gate", st, ln_gate<float>(T, D, o, (const float*)h_in, (float*)h_out, w->ln_w, w->ln_b, w->s, branch_out, no_ln, R2L_LN_EPS, st));
+    R2L_RUN("ln_gate", st, (ln_gate<float, float>(T, D, o, (const float*)h_in, (float*)h_out, w->ln_w, w->ln_b, w->s, branch_out, no_ln, R2L_LN_EPS, st)));
   }
   return R2L_OK;
 }
@@ -404,6 +408,11 @@ int r2l_scan_fwd(const r2l_dims* d, r2l_dtype act, const void* u, int64_t ld_u, 
   if (!aligned16(u) || !aligned16(dt) || !aligned16(y_out) || (z && !aligned16(z)) || ld_u % vec ||
       ld_dt % 4 || (z && ld_z % vec))
     return R2L_ERR_INVALID_ARG;
+  // rows are read through 32-bit buffer windows of a few dozen rows
+  const int64_t win = 64 * (act == R2L_BF16 ? 2 : 4);
+  if (ld_u > INT32_MAX / win || ld_dt > INT32_MAX / 256 || ld_bc > INT32_MAX / 256 ||
+      (z && ld_z > INT32_MAX / win))
+    return R2L_ERR_UNSUPPORTED;
   const ScanPlan sp = plan_scan(E, n_tokens, nseq, max_seqlen, 0);
   if (!workspace || workspace_bytes < sp.total) return R2L_ERR_WORKSPACE;
   if (((uintptr_t)workspace & (kAlign - 1)) != 0) return R2L_ERR_INVALID_ARG;

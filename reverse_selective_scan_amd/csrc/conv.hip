@@ -232,17 +232,21 @@ hipError_t conv_xproj_bf16(int Tn, int E, int P, const bf16* x, long ld_x, const
 // by tile; block b of G takes the contiguous range [b W / G, (b+1) W / G) of
 // the W = tiles * E/32 steps, so every block does the same amount of work
 // whatever the token count (a plain split into 128-token tiles would leave
-// e.g. 258 tiles for 256 CUs, i.e. two rounds).  With tiles >= G every tile is
-// covered by at most two blocks: the one holding its step 0 writes its
-// partial sum to part0, the other to part1 (whole tiles zero part1); the
-// consumer adds part0 + part1, in that order, so results are deterministic.
+// e.g. 258 tiles for 256 CUs, i.e. two rounds).  With tiles >= G / 2 every
+// block holds at least half a tile's steps, so a tile is covered by at most
+// three blocks: the piece holding its step 0 writes its partial sum to part0,
+// the next to part1, a third to part2.  The summing kernel counts each
+// tile's pieces from the same step ranges and adds (part0 + part1) + part2,
+// in that order and only the parts that exist, so results are deterministic
+// and no part is ever cleared.  (Two blocks run per CU when the ring fits
+// twice in LDS; a third piece can only occur then.)
 //
 // The 4 waves of a block own 32 tokens each and walk the same steps, so one
 // copy of each W_x slice (and the conv taps) per block serves 128 tokens.
 // Every operand of a step is copied global -> LDS by buffer_load ... lds
-// into a 5-stage ring (rows past the token count read as zero through the
-// buffer descriptor's range); the barrier of step q waits for step q+1, and
-// loads run three steps ahead.  x and W_x stage rows are 64 bytes with the
+// into a ring of RS stages (rows past the token count read as zero through
+// the buffer descriptor's range); the barrier of step q waits for step q+1,
+// and loads run RS - 2 steps ahead.  x and W_x stage rows are 64 bytes with the
 // 16-byte chunk index XOR-ed by (row >> 2) & 3 against bank conflicts.
 // Lanes compute their own MFMA A-fragments (token lane & 31, 8 channels) as
 // in conv_xproj_kernel.
@@ -253,15 +257,20 @@ constexpr int kSkTok = 128, kSkK = 32;
 
 template <int NCS>
 struct SkGeo {
-  // copy instructions per step, each group padded to a multiple of the 4
-  // waves so that the m-th copy of every wave is of the same kind
-  static constexpr int NW = ((NCS * 32 * 4 + 63) / 64 + 3) / 4 * 4;       // W_x rows x 4 chunks
-  static constexpr int NX = (((kSkTok + 3) * 4 + 63) / 64 + 3) / 4 * 4;   // x rows t0 .. t0+130
-  static constexpr int NI = NW + NX + 4;                                  // + conv taps, bias, 2 spare
-  static constexpr int PER_WAVE = NI / 4;
+  // A step's operands travel as 1 KB copies (64 lanes x 16 bytes): W_x rows
+  // (16 rows of 64 bytes per copy), x rows t0 .. t0+130, the conv taps and
+  // the conv bias.  Copy i of a step is wave (i % 4)'s copy i / 4; the last
+  // few slots are padding that reads nothing (zeros land in LDS), so every
+  // wave issues the same number of copies per step.
+  static constexpr int NW = (NCS * 32 * 4 + 63) / 64;          // W_x rows
+  static constexpr int NX = ((kSkTok + 3) * 4 + 63) / 64;      // x rows t0 .. t0+130
+  static constexpr int PER_WAVE = (NW + NX + 2 + 3) / 4;       // + taps, bias
+  static constexpr int NI = 4 * PER_WAVE;
   static constexpr int SBYTES = NI * 1024;
   static constexpr int OFF_X = NW * 1024, OFF_CW = (NW + NX) * 1024, OFF_CB = OFF_CW + 1024;
-  static constexpr int RS = 5 * SBYTES <= 160 * 1024 ? 5 : 4;             // ring stages
+  // two blocks per CU with a 3-stage ring when it fits, else one with 5 (or 4)
+  static constexpr int BPC = 2 * 3 * SBYTES <= 160 * 1024 ? 2 : 1;
+  static constexpr int RS = BPC == 2 ? 3 : (5 * SBYTES <= 160 * 1024 ? 5 : 4);
 };
 
 constexpr int sk_vmcnt(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
@@ -274,20 +283,21 @@ R2L_DEV int sk_swz(int row, int chunk) { return chunk ^ ((row >> 2) & 3); }
 }  // namespace
 
 template <int NCS>
-__global__ __launch_bounds__(256, 1) void conv_xproj_sk_kernel(int Tn, int E, int P,
+__global__ __launch_bounds__(256, SkGeo<NCS>::BPC) void conv_xproj_sk_kernel(int Tn, int E, int P,
                                                                const bf16* __restrict__ x, long ld_x,
                                                                const bf16* __restrict__ cw,
                                                                const bf16* __restrict__ cb,
                                                                const bf16* __restrict__ Wx,
                                                                float* __restrict__ part0,
                                                                float* __restrict__ part1,
+                                                               long part_stride,   // part2 = part1 + part_stride
                                                                const int32_t* __restrict__ cu, int nseq) {
   using Geo = SkGeo<NCS>;
   constexpr int RS = Geo::RS, PW = Geo::PER_WAVE;
   __shared__ __attribute__((aligned(1024))) char s0[Geo::SBYTES];
   __shared__ __attribute__((aligned(1024))) char s1[Geo::SBYTES];
   __shared__ __attribute__((aligned(1024))) char s2[Geo::SBYTES];
-  __shared__ __attribute__((aligned(1024))) char s3[Geo::SBYTES];
+  __shared__ __attribute__((aligned(1024))) char s3[Geo::RS > 3 ? Geo::SBYTES : 16];
   __shared__ __attribute__((aligned(1024))) char s4[Geo::RS > 4 ? Geo::SBYTES : 16];
   auto stage = [&](int s) -> char* { return s == 0 ? s0 : s == 1 ? s1 : s == 2 ? s2 : s == 3 ? s3 : s4; };
 
@@ -304,26 +314,24 @@ __global__ __launch_bounds__(256, 1) void conv_xproj_sk_kernel(int Tn, int E, in
   const __amdgpu_buffer_rsrc_t rW = __builtin_amdgcn_make_buffer_rsrc((void*)Wx, 0, (int)((long)P * E * 2), 0x00020000);
   const __amdgpu_buffer_rsrc_t rCW = __builtin_amdgcn_make_buffer_rsrc((void*)cw, 0, (int)((long)E * 8), 0x00020000);
   const __amdgpu_buffer_rsrc_t rCB = __builtin_amdgcn_make_buffer_rsrc((void*)cb, 0, (int)((long)E * 2), 0x00020000);
-  // copy m of this wave is copy i = 4 m + w of the step; its kind depends on m only
-  constexpr int MW = Geo::NW / 4, MX = Geo::NX / 4;
+  // copy m of this wave is copy i = 4 m + w of the step; its kind depends
+  // on i, so it is uniform over the wave
   unsigned voff[PW];
 #pragma unroll
   for (int m = 0; m < PW; ++m) {
     const int i = 4 * m + w;
-    if (m < MW) {
-      const int p = i * 64 + lane, row = p >> 2;
-      // rows past P lie past the descriptor's range and read as zero
-      voff[m] = (unsigned)(((long)row * E + sk_swz(row, p & 3) * 8) * 2);
-    } else if (m < MW + MX) {
-      const int p = (i - Geo::NW) * 64 + lane, row = p >> 2;
-      voff[m] = (unsigned)(((long)row * ld_x + sk_swz(row, p & 3) * 8) * 2);
-    } else {
-      // copy NW+NX (wave 0): taps of channels c0 + 2 lane, +1; copies
-      // NW+NX+1.. (waves 1-3): bias of channels c0 + 8 lane .. +7
-      voff[m] = w == 0 ? (lane < 16 ? lane * 16 : 0) : (lane < 4 ? lane * 16 : 0);
-    }
+    // W_x rows (rows past P lie past the descriptor's range and read as zero)
+    const int pw = i * 64 + lane, roww = pw >> 2;
+    const unsigned vw = (unsigned)(((long)roww * E + sk_swz(roww, pw & 3) * 8) * 2);
+    // x rows
+    const int px = (i - Geo::NW) * 64 + lane, rowx = px >> 2;
+    const unsigned vx = (unsigned)(((long)rowx * ld_x + sk_swz(rowx, px & 3) * 8) * 2);
+    // taps of channels c0 + 2 lane, +1; bias of channels c0 + 8 lane .. +7;
+    // padding slots read past every range
+    const unsigned vt = lane < 16 ? lane * 16 : 0, vb = lane < 4 ? lane * 16 : 0;
+    voff[m] = i < Geo::NW ? vw : i < Geo::NW + Geo::NX ? vx : i == Geo::NW + Geo::NX ? vt
+            : i == Geo::NW + Geo::NX + 1 ? vb : 0x80000000u;
   }
-  const bool taps_copy = w == 0;
   // Copy position: the step RS-1 ahead of the one being computed, as
   // (tile, channel offset); it stops advancing at the block's last step
   // (later copies reload that step into stages that are never read).
@@ -333,17 +341,15 @@ __global__ __launch_bounds__(256, 1) void conv_xproj_sk_kernel(int Tn, int E, in
     const long xbytes = (long)(Tn - t0) * ld_x * 2;
     const __amdgpu_buffer_rsrc_t rX = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(x + t0 * ld_x), 0, (int)(xbytes < (1L << 30) ? xbytes : (1L << 30)), 0x00020000);
-    // taps (wave 0) and bias (waves 1-3) share the last copy slot through a
-    // uniform choice of descriptor and offset
-    const __amdgpu_buffer_rsrc_t rT = taps_copy ? rCW : rCB;
-    const unsigned soffT = taps_copy ? (unsigned)(it_c0 * 8) : (unsigned)(it_c0 * 2);
     char* base = stage(s);
 #pragma unroll
     for (int m = 0; m < PW; ++m) {
-      char* dst = base + (4 * m + w) * 1024;   // lane l lands at dst + 16 l
-      if (m < MW) sk_dma16(rW, dst, voff[m], (unsigned)(it_c0 * 2));
-      else if (m < MW + MX) sk_dma16(rX, dst, voff[m], (unsigned)(it_c0 * 2));
-      else sk_dma16(rT, dst, voff[m], soffT);
+      // (wave-uniform choices of descriptor and offset)
+      const int i = 4 * m + w;
+      const bool tap = i == Geo::NW + Geo::NX;
+      const __amdgpu_buffer_rsrc_t r = i < Geo::NW ? rW : i < Geo::NW + Geo::NX ? rX : tap ? rCW : rCB;
+      // lane l lands at base + 1024 i + 16 l
+      sk_dma16(r, base + i * 1024, voff[m], (unsigned)(it_c0 * (tap ? 8 : 2)));
     }
     if (--it_left > 0) {
       it_c0 += kSkK;
@@ -362,7 +368,11 @@ __global__ __launch_bounds__(256, 1) void conv_xproj_sk_kernel(int Tn, int E, in
 
   f32x16 acc[NCS];
   int c_tile = lo / S, c_ks = lo % S;   // step being computed
-  bool head = c_ks == 0;                // this piece holds the tile's step 0
+  // index of the piece within its tile (0: holds step 0); only a block's
+  // first piece can start inside a tile, after one or two earlier pieces
+  const int lo_prev = blockIdx.x > 0 ? (int)(W * (blockIdx.x - 1) / gridDim.x) : 0;
+  const int first_pidx = c_ks == 0 ? 0 : (blockIdx.x > 0 && lo_prev > c_tile * S ? 2 : 1);
+  int pidx = first_pidx;
   bool tv = false, ok1 = false, ok2 = false, ok3 = false, masked = false;
   auto start_piece = [&]() {
 #pragma unroll
@@ -379,8 +389,9 @@ __global__ __launch_bounds__(256, 1) void conv_xproj_sk_kernel(int Tn, int E, in
     masked = __any(tv && !(ok1 && ok2 && ok3));
   };
   auto end_piece = [&]() {
-    const bool full = head && c_ks == S - 1;
-    float* dst = (head ? part0 : part1) + ((long)c_tile * kSkTok + w * 32) * P;
+    // (part1 + stride selects part1 / part2: a three-way pointer choice here
+    // keeps the compiler from holding the block's state in registers)
+    float* dst = (pidx == 0 ? part0 : part1 + (pidx - 1) * part_stride) + ((long)c_tile * kSkTok + w * 32) * P;
     const int rows = min(32, Tn - (c_tile * kSkTok + w * 32));
 #pragma unroll
     for (int c = 0; c < NCS; ++c) {
@@ -391,7 +402,6 @@ __global__ __launch_bounds__(256, 1) void conv_xproj_sk_kernel(int Tn, int E, in
         const int row = 8 * (r >> 2) + 4 * kh + (r & 3);
         if (row < rows) {
           dst[row * P + col] = acc[c][r];
-          if (full && part1 != nullptr) part1[((long)c_tile * kSkTok + w * 32 + row) * P + col] = 0.0f;
         }
       }
     }
@@ -399,7 +409,7 @@ __global__ __launch_bounds__(256, 1) void conv_xproj_sk_kernel(int Tn, int E, in
   const bf16x8 zero8 = {};
   auto compute = [&](const char* base) {
     if (c_tile * S + c_ks == lo || c_ks == 0) {
-      head = c_ks == 0;
+      pidx = c_ks == 0 ? 0 : first_pidx;
       start_piece();
     }
     const char* wx_s = base;
@@ -485,34 +495,85 @@ __global__ __launch_bounds__(256, 1) void conv_xproj_sk_kernel(int Tn, int E, in
   __builtin_amdgcn_s_waitcnt(sk_vmcnt(0));
 }
 
-// part0 += part1 over n floats (both 16-byte aligned); the last n % 4 by the first thread.
-__global__ __launch_bounds__(256) void add_parts_kernel(long n, float* __restrict__ a,
-                                                        const float* __restrict__ b) {
-  const long n4 = n / 4;
-  for (long i = blockIdx.x * 256L + threadIdx.x; i < n4; i += (long)gridDim.x * 256)
-    ((f32x4*)a)[i] = ((f32x4*)a)[i] + ((const f32x4*)b)[i];
-  if (blockIdx.x == 0 && threadIdx.x == 0)
-    for (long i = n4 * 4; i < n; ++i) a[i] += b[i];
+// Sum of the split conv's partial x_proj outputs: row t of xdbl lies in
+// tile t / 128, whose pieces are counted from the block step ranges
+// [floor(W b / G), floor(W (b+1) / G)) exactly as the conv kernel cut them.
+// One thread per 4 consecutive floats of a row (P % 4 == 0) or per float.
+R2L_DEV int sk_pieces(long tile, long S, long W, long G) {
+  // #{b in 1 .. G-1 : floor(W b / G) < X} for X >= 1
+  auto below = [&](long X) { const long k = (X * G + W - 1) / W - 1; return k < 0 ? 0L : (k > G - 1 ? G - 1 : k); };
+  const long lo = tile * S;
+  return (int)(1 + below(lo + S) - below(lo + 1));
 }
 
-hipError_t add_parts(long n, float* part0, const float* part1, hipStream_t st) {
-  if (n <= 0) return hipSuccess;
-  const long want = (n / 4 + 255) / 256;
-  const long blocks = want < 1 ? 1 : (want < 4096 ? want : 4096);
-  hipLaunchKernelGGL(add_parts_kernel, dim3(blocks), dim3(256), 0, st, n, part0, part1);
+template <int V>
+__global__ __launch_bounds__(256) void sk_sum_kernel(long rows, int P, int S, long W, int G,
+                                                     float* __restrict__ a, const float* __restrict__ b,
+                                                     const float* __restrict__ c) {
+  const long per_row = P / V;
+  const long n = rows * per_row;
+  for (long i = blockIdx.x * 256L + threadIdx.x; i < n; i += (long)gridDim.x * 256) {
+    const long row = i / per_row;
+    const int pieces = sk_pieces(row / kSkTok, S, W, G);
+    float* pa = a + row * P + (i % per_row) * V;
+    const long off = pa - a;
+    if constexpr (V == 4) {
+      f32x4 v = *(f32x4*)pa;
+      if (pieces > 1) v = v + *(const f32x4*)(b + off);
+      if (pieces > 2) v = v + *(const f32x4*)(c + off);
+      *(f32x4*)pa = v;
+    } else {
+      float v = *pa;
+      if (pieces > 1) v = v + b[off];
+      if (pieces > 2) v = v + c[off];
+      *pa = v;
+    }
+  }
+}
+
+template <int NCS>
+static int sk_blocks(int ncu) { return ncu * SkGeo<NCS>::BPC; }
+
+static int sk_grid(int P, int ncu) {
+  switch ((P + 31) / 32) {
+    case 1: return sk_blocks<1>(ncu);
+    case 2: return sk_blocks<2>(ncu);
+    case 3: return sk_blocks<3>(ncu);
+    case 4: return sk_blocks<4>(ncu);
+    case 5: return sk_blocks<5>(ncu);
+    case 6: return sk_blocks<6>(ncu);
+    case 7: return sk_blocks<7>(ncu);
+    default: return sk_blocks<8>(ncu);
+  }
+}
+
+hipError_t conv_sk_sum(int Tn, int E, int P, float* part0, const float* part1, const float* part2, int ncu,
+                       hipStream_t st) {
+  if (Tn <= 0) return hipSuccess;
+  const int S = E / kSkK;
+  const long W = (long)((Tn + kSkTok - 1) / kSkTok) * S;
+  const int G = sk_grid(P, ncu);
+  const long n = (long)Tn * (P % 4 == 0 ? P / 4 : P);
+  const long want = (n + 255) / 256;
+  const dim3 grid((unsigned)(want < 1 ? 1 : (want < 4096 ? want : 4096)));
+  if (P % 4 == 0)
+    hipLaunchKernelGGL(sk_sum_kernel<4>, grid, dim3(256), 0, st, (long)Tn, P, S, W, G, part0, part1, part2);
+  else
+    hipLaunchKernelGGL(sk_sum_kernel<1>, grid, dim3(256), 0, st, (long)Tn, P, S, W, G, part0, part1, part2);
   return hipGetLastError();
 }
 
 hipError_t conv_xproj_bf16_sk(int Tn, int E, int P, const bf16* x, long ld_x, const bf16* conv_w,
                               const bf16* conv_b, const bf16* x_proj_w, float* part0, float* part1,
-                              const int32_t* cu, int nseq, int nblocks, hipStream_t st) {
+                              float* part2, const int32_t* cu, int nseq, int ncu, hipStream_t st) {
   if (Tn <= 0) return hipSuccess;
   const int ncs = (P + 31) / 32;
-  dim3 grid(nblocks), block(256);
+  dim3 block(256);
 #define R2L_SK(n)                                                                                \
   case n:                                                                                        \
-    hipLaunchKernelGGL((conv_xproj_sk_kernel<n>), grid, block, 0, st, Tn, E, P, x, ld_x, conv_w, \
-                       conv_b, x_proj_w, part0, part1, cu, nseq);                                \
+    hipLaunchKernelGGL((conv_xproj_sk_kernel<n>), dim3(sk_blocks<n>(ncu)), block, 0, st,        \
+                       Tn, E, P, x, ld_x, conv_w, conv_b, x_proj_w, part0, part1, part2 - part1, \
+                       cu, nseq);                                                               \
     break;
   switch (ncs) {
     R2L_SK(1) R2L_SK(2) R2L_SK(3) R2L_SK(4) R2L_SK(5) R2L_SK(6) R2L_SK(7) R2L_SK(8)

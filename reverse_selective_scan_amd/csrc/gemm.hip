@@ -188,8 +188,8 @@ R2L_DEV int big_swz(int row, int chunk) { return chunk ^ ((row >> kBigSH) & (kBi
 // Linear tile index -> (row tile, column tile): group-M raster, G row tiles
 // sweep all column tiles; narrow outputs (few column tiles) use taller groups
 // (measured best: 8 for <= 8 column tiles).
+template <int G>
 R2L_DEV void big_tile(int lid, int nTm, int nTn, int& tm, int& tn) {
-  const int G = nTn <= 8 ? 8 : 4;
   const int per_group = G * nTn;
   const int first_m = (lid / per_group) * G;
   const int gsz = min(nTm - first_m, G);
@@ -204,7 +204,7 @@ R2L_DEV void big_tile(int lid, int nTm, int nTn, int& tm, int& tn) {
 // (the tail launch): block u computes K-steps [s ksteps, (s+1) ksteps) with
 // s = u % splits of tile n_dp + u / splits, as an fp32 partial sum into
 // part[u][256][256].
-template <bool OUT_F32>
+template <bool OUT_F32, int G>
 __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(int M, int N, int K,
                                                                const bf16* __restrict__ A, long lda,
                                                                const bf16* __restrict__ B, long ldb,
@@ -226,7 +226,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(int M, int N, int
   const int lid = splits ? n_dp + (int)blockIdx.x / splits : xcd_remap(blockIdx.x, n_dp);
   const int kbeg = splits ? ((int)blockIdx.x % splits) * ksteps : 0;
   int tm, tn;
-  big_tile(lid, nTm, nTn, tm, tn);
+  big_tile<G>(lid, nTm, nTn, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
 
   // Buffer descriptors over this tile's rows: reads past row M (N) return 0.
@@ -408,7 +408,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(int M, int N, int
 
 // C tile n_dp + t = sum over s of part[t * splits + s], in order of s.
 // Block: 4 rows of 256 columns of one tail tile; thread: 4 consecutive columns.
-template <bool OUT_F32>
+template <bool OUT_F32, int G>
 __global__ __launch_bounds__(256) void gemm_tail_reduce_kernel(int M, int N, int n_dp, int splits,
                                                                const float* __restrict__ part,
                                                                void* __restrict__ Cv, long ldc) {
@@ -416,7 +416,7 @@ __global__ __launch_bounds__(256) void gemm_tail_reduce_kernel(int M, int N, int
   const int t = blockIdx.x / (kBigBM / 4), r = (blockIdx.x % (kBigBM / 4)) * 4 + (threadIdx.x >> 6);
   const int c = (threadIdx.x & 63) * 4;
   int tm, tn;
-  big_tile(n_dp + t, nTm, nTn, tm, tn);
+  big_tile<G>(n_dp + t, nTm, nTn, tm, tn);
   const int m = tm * kBigBM + r, n = tn * kBigBN + c;
   if (m >= M || n >= N) return;
   f32x4 v = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -476,6 +476,30 @@ static void launch_gemm(int M, int N, int K, const bf16* A, long lda, const bf16
                        K, A, lda, B, ldb, C, ldc, 0, 0, (float*)nullptr);
 }
 
+template <int G>
+static void launch_big(int M, int N, int K, const bf16* A, long lda, const bf16* B, long ldb, void* C,
+                       long ldc, bool out_f32, int n_dp, int rem, int splits, int nk, float* ws,
+                       hipStream_t st) {
+  if (out_f32)
+    hipLaunchKernelGGL((gemm_bf16_big_kernel<true, G>), dim3(n_dp), dim3(256), 0, st, M, N, K, A, lda,
+                       B, ldb, C, ldc, n_dp, 0, 0, (float*)nullptr);
+  else
+    hipLaunchKernelGGL((gemm_bf16_big_kernel<false, G>), dim3(n_dp), dim3(256), 0, st, M, N, K, A, lda,
+                       B, ldb, C, ldc, n_dp, 0, 0, (float*)nullptr);
+  if (splits) {
+    const int ksteps = nk / splits;
+    // (the kernel's OUT_F32 only shapes the direct epilogue; partials are fp32)
+    hipLaunchKernelGGL((gemm_bf16_big_kernel<true, G>), dim3(rem * splits), dim3(256), 0, st, M, N, K,
+                       A, lda, B, ldb, C, ldc, n_dp, splits, ksteps, ws);
+    if (out_f32)
+      hipLaunchKernelGGL((gemm_tail_reduce_kernel<true, G>), dim3(rem * (kBigBM / 4)), dim3(256), 0, st, M,
+                         N, n_dp, splits, (const float*)ws, C, ldc);
+    else
+      hipLaunchKernelGGL((gemm_tail_reduce_kernel<false, G>), dim3(rem * (kBigBM / 4)), dim3(256), 0, st, M,
+                         N, n_dp, splits, (const float*)ws, C, ldc);
+  }
+}
+
 hipError_t gemm_bf16_nt(int M, int N, int K, const bf16* A, long lda, const bf16* B, long ldb,
                         void* C, long ldc, bool out_f32, hipStream_t st, float* ws, size_t ws_bytes,
                         int ncu) {
@@ -508,24 +532,11 @@ hipError_t gemm_bf16_nt(int M, int N, int K, const bf16* A, long lda, const bf16
         }
     }
     const int n_dp = (int)big_tiles - (splits ? rem : 0);
-    if (out_f32)
-      hipLaunchKernelGGL((gemm_bf16_big_kernel<true>), dim3(n_dp), dim3(256), 0, st, M, N, K, A, lda,
-                         B, ldb, C, ldc, n_dp, 0, 0, (float*)nullptr);
-    else
-      hipLaunchKernelGGL((gemm_bf16_big_kernel<false>), dim3(n_dp), dim3(256), 0, st, M, N, K, A, lda,
-                         B, ldb, C, ldc, n_dp, 0, 0, (float*)nullptr);
-    if (splits) {
-      const int ksteps = nk / splits;
-      // (the kernel's OUT_F32 only shapes the direct epilogue; partials are fp32)
-      hipLaunchKernelGGL((gemm_bf16_big_kernel<true>), dim3(rem * splits), dim3(256), 0, st, M, N, K,
-                         A, lda, B, ldb, C, ldc, n_dp, splits, ksteps, ws);
-      if (out_f32)
-        hipLaunchKernelGGL((gemm_tail_reduce_kernel<true>), dim3(rem * (kBigBM / 4)), dim3(256), 0, st, M,
-                           N, n_dp, splits, (const float*)ws, C, ldc);
-      else
-        hipLaunchKernelGGL((gemm_tail_reduce_kernel<false>), dim3(rem * (kBigBM / 4)), dim3(256), 0, st, M,
-                           N, n_dp, splits, (const float*)ws, C, ldc);
-    }
+    // groups of G tile rows walk the tile columns: 8 rows for narrow
+    // outputs (<= 8 tile columns), else 4
+    const int nTn = (N + kBigBN - 1) / kBigBN;
+    if (nTn <= 8) launch_big<8>(M, N, K, A, lda, B, ldb, C, ldc, out_f32, n_dp, rem, splits, nk, ws, st);
+    else launch_big<4>(M, N, K, A, lda, B, ldb, C, ldc, out_f32, n_dp, rem, splits, nk, ws, st);
     return hipGetLastError();
   }
   // 128 x 128 tiles (4 waves of 64 x 64, two blocks per CU).

@@ -32,14 +32,15 @@ hipError_t conv_xproj_bf16(int T_, int E, int P, const bf16* x, long ld_x, const
                            const int32_t* cu, int nseq, hipStream_t st, float* ws = nullptr,
                            size_t ws_bytes = 0, int ncu = 0);
 
-// The same for large inputs, split along K over `nblocks` blocks (one per
-// CU): xdbl = part0 + part1 (add_parts), part1 16-byte aligned.  Requires
-// E % 64 == 0, P <= 256 and ceil(T / 128) >= nblocks.
+// The same for large inputs, split along K over one or two blocks per CU
+// (`ncu` CUs) into up to three partial sums; conv_sk_sum (same T, E, P, ncu)
+// then leaves xdbl in part0.  Parts [T, P] fp32, 16-byte aligned.  Requires
+// E % 64 == 0, P <= 256 and ceil(T / 128) >= ncu.
 hipError_t conv_xproj_bf16_sk(int T_, int E, int P, const bf16* x, long ld_x, const bf16* conv_w,
                               const bf16* conv_b, const bf16* x_proj_w, float* part0, float* part1,
-                              const int32_t* cu, int nseq, int nblocks, hipStream_t st);
-// part0[i] += part1[i] for i < n (both 16-byte aligned).
-hipError_t add_parts(long n, float* part0, const float* part1, hipStream_t st);
+                              float* part2, const int32_t* cu, int nseq, int ncu, hipStream_t st);
+hipError_t conv_sk_sum(int T_, int E, int P, float* part0, const float* part1, const float* part2, int ncu,
+                       hipStream_t st);
 
 // Chunk planning for the scan: sanitised cu_seqlens and the chunk table.
 hipError_t plan_chunks(const int32_t* cu, int nseq, int T_, int Lc, int max_chunks,
@@ -72,8 +73,8 @@ hipError_t scan_summary(const ScanArgs& a, bool fused, hipStream_t st);
 template <typename T>
 hipError_t scan_main(const ScanArgs& a, bool fused, hipStream_t st);
 
-template <typename T>
-hipError_t ln_gate(int T_, int D, const float* o, const T* h_in, T* h_out, const float* gamma,
+template <typename T, typename O>
+hipError_t ln_gate(int T_, int D, const O* o, const T* h_in, T* h_out, const float* gamma,
                    const float* beta, const float* s, float* branch, bool no_ln, float eps,
                    hipStream_t st);
 

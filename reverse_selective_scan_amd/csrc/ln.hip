@@ -8,7 +8,8 @@
 // also keeps -0.0 inputs and non-finite branch values from leaking through.
 //
 // One wave per token row; the row (D <= 64 * VPL floats) stays in registers
-// between the two reductions (mean, then centred second moment).
+// between the two reductions (mean, then centred second moment).  o, the
+// out_proj output, is read as fp32 (also for bf16 activations).
 #include "kernels.h"
 
 namespace r2l {
@@ -40,8 +41,8 @@ template <typename T> struct Raw8h;
 template <> struct Raw8h<bf16> { bf16x8 v; };
 template <> struct Raw8h<float> { f32x4 a, b; };
 
-template <typename T, int NCH>
-__global__ __launch_bounds__(256) void ln_gate_kernel(int Tn, int D, const float* __restrict__ o,
+template <typename T, typename O, int NCH>
+__global__ __launch_bounds__(256) void ln_gate_kernel(int Tn, int D, const O* __restrict__ o,
                                                       const T* h_in, T* h_out,  // may alias
                                                       const float* __restrict__ gamma,
                                                       const float* __restrict__ beta,
@@ -52,7 +53,7 @@ __global__ __launch_bounds__(256) void ln_gate_kernel(int Tn, int D, const float
   const int row = blockIdx.x * 4 + wave_id();
   if (row >= Tn) return;
   const int nch = D / 512;  // D % 512 == 0 here (other widths use the generic kernel)
-  const float* orow = o + (long)row * D;
+  const O* orow = o + (long)row * D;
   float v[NCH][8];
   float sum = 0.0f;
 #pragma unroll
@@ -112,8 +113,8 @@ __global__ __launch_bounds__(256) void ln_gate_kernel(int Tn, int D, const float
 }
 
 // Generic widths (D a multiple of 64): lane l holds elements 64 i + l.
-template <typename T, int VPL>
-__global__ __launch_bounds__(256) void ln_gate_generic_kernel(int Tn, int D, const float* __restrict__ o,
+template <typename T, typename O, int VPL>
+__global__ __launch_bounds__(256) void ln_gate_generic_kernel(int Tn, int D, const O* __restrict__ o,
                                                               const T* h_in, T* h_out,  // may alias
                                                               const float* __restrict__ gamma,
                                                               const float* __restrict__ beta,
@@ -124,12 +125,12 @@ __global__ __launch_bounds__(256) void ln_gate_generic_kernel(int Tn, int D, con
   const int row = blockIdx.x * 4 + wave_id();
   if (row >= Tn) return;
   const int cnt = D / 64;
-  const float* orow = o + (long)row * D;
+  const O* orow = o + (long)row * D;
   float v[VPL];
   float sum = 0.0f;
 #pragma unroll
   for (int i = 0; i < VPL; ++i) {
-    v[i] = (i < cnt) ? orow[i * 64 + lane] : 0.0f;
+    v[i] = (i < cnt) ? to_f32(orow[i * 64 + lane]) : 0.0f;
     sum += v[i];
   }
   const float invD = 1.0f / (float)D;
@@ -163,8 +164,8 @@ __global__ __launch_bounds__(256) void ln_gate_generic_kernel(int Tn, int D, con
     }
 }
 
-template <typename T>
-hipError_t ln_gate(int Tn, int D, const float* o, const T* h_in, T* h_out, const float* gamma,
+template <typename T, typename O>
+hipError_t ln_gate(int Tn, int D, const O* o, const T* h_in, T* h_out, const float* gamma,
                    const float* beta, const float* s, float* branch, bool no_ln, float eps,
                    hipStream_t st) {
   if (Tn <= 0) return hipSuccess;
@@ -172,7 +173,7 @@ hipError_t ln_gate(int Tn, int D, const float* o, const T* h_in, T* h_out, const
   const int nl = no_ln ? 1 : 0;
   if (D % 512 == 0 && D <= 8192) {
 #define R2L_LNV(C) \
-  hipLaunchKernelGGL((ln_gate_kernel<T, C>), grid, block, 0, st, Tn, D, o, h_in, h_out, gamma, beta, s, branch, nl, eps)
+  hipLaunchKernelGGL((ln_gate_kernel<T, O, C>), grid, block, 0, st, Tn, D, o, h_in, h_out, gamma, beta, s, branch, nl, eps)
     if (D <= 1024) R2L_LNV(2);
     else if (D <= 2048) R2L_LNV(4);
     else if (D <= 4096) R2L_LNV(8);
@@ -182,7 +183,7 @@ hipError_t ln_gate(int Tn, int D, const float* o, const T* h_in, T* h_out, const
   }
   const int cnt = D / 64;
 #define R2L_LN(V)                                                                                      \
-  hipLaunchKernelGGL((ln_gate_generic_kernel<T, V>), grid, block, 0, st, Tn, D, o, h_in, h_out, gamma, \
+  hipLaunchKernelGGL((ln_gate_generic_kernel<T, O, V>), grid, block, 0, st, Tn, D, o, h_in, h_out, gamma, \
                      beta, s, branch, nl, eps)
   if (cnt <= 4) R2L_LN(4);
   else if (cnt <= 16) R2L_LN(16);
@@ -192,9 +193,9 @@ hipError_t ln_gate(int Tn, int D, const float* o, const T* h_in, T* h_out, const
 #undef R2L_LN
   return hipGetLastError();
 }
-template hipError_t ln_gate<float>(int, int, const float*, const float*, float*, const float*,
-                                   const float*, const float*, float*, bool, float, hipStream_t);
-template hipError_t ln_gate<bf16>(int, int, const float*, const bf16*, bf16*, const float*,
-                                  const float*, const float*, float*, bool, float, hipStream_t);
+template hipError_t ln_gate<float, float>(int, int, const float*, const float*, float*, const float*,
+                                          const float*, const float*, float*, bool, float, hipStream_t);
+template hipError_t ln_gate<bf16, float>(int, int, const float*, const bf16*, bf16*, const float*,
+                                         const float*, const float*, float*, bool, float, hipStream_t);
 
 }  // namespace r2l

@@ -108,24 +108,52 @@ hipError_t plan_chunks(const int32_t* cu, int nseq, int Tn, int Lc, int max_chun
 }
 
 // ---------------------------------------------------------------------------
-// 8-channel vector helpers (16-byte accesses for bf16, 2 x 16 for fp32)
+// Row-window buffer resources.  Every per-token input is read through a
+// buffer resource that covers exactly the rows a block may use: reads past
+// its end return zeros without touching memory (rows past a sequence end for
+// the conv window, rows past the block for the rest) and stores past its end
+// are dropped, so no row index is clamped or selected per lane.  Offsets are
+// relative to the window's first row and stay far below 2^31 (the host
+// limits row pitches accordingly).
 // ---------------------------------------------------------------------------
-template <typename T> struct Raw8;
-template <> struct Raw8<bf16> { bf16x8 v; };
-template <> struct Raw8<float> { f32x4 a, b; };
-R2L_DEV void raw_load(Raw8<bf16>& r, const bf16* p) { r.v = *(const bf16x8*)p; }
-R2L_DEV void raw_load(Raw8<float>& r, const float* p) { r.a = *(const f32x4*)p; r.b = *(const f32x4*)(p + 4); }
-R2L_DEV float raw_at(const Raw8<bf16>& r, int i) { return (float)r.v[i]; }
-R2L_DEV float raw_at(const Raw8<float>& r, int i) { return i < 4 ? r.a[i] : r.b[i - 4]; }
-R2L_DEV void store8(bf16* p, const float v[8]) {
-  bf16x8 q;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) q[i] = (bf16)v[i];
-  *(bf16x8*)p = q;
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+R2L_DEV Rsrc row_window(const void* base, long row0, long pitch_bytes, int rows) {
+  const long bytes = rows > 0 ? rows * pitch_bytes : 0;
+  return __builtin_amdgcn_make_buffer_rsrc((void*)((const char*)base + row0 * pitch_bytes), 0, (int)bytes,
+                                           0x00020000);
 }
-R2L_DEV void store8(float* p, const float v[8]) {
-  *(f32x4*)p = f32x4{v[0], v[1], v[2], v[3]};
-  *(f32x4*)(p + 4) = f32x4{v[4], v[5], v[6], v[7]};
+R2L_DEV u32x4 bload16(Rsrc r, unsigned off) { return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0); }
+R2L_DEV float bload4(Rsrc r, unsigned off) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+}
+R2L_DEV void bstore16(Rsrc r, unsigned off, u32x4 v) { __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, 0); }
+constexpr unsigned kOutside = 0x80000000u;   // an offset past every window
+
+// 8 channels of one row: one 16-byte load (bf16) or two (fp32)
+template <typename T> struct Raw8;
+template <> struct Raw8<bf16> { u32x4 v; };
+template <> struct Raw8<float> { u32x4 a, b; };
+R2L_DEV void raw_load(Raw8<bf16>& r, Rsrc s, unsigned off) { r.v = bload16(s, off); }
+R2L_DEV void raw_load(Raw8<float>& r, Rsrc s, unsigned off) { r.a = bload16(s, off); r.b = bload16(s, off + 16); }
+R2L_DEV float raw_at(const Raw8<bf16>& r, int i) {
+  const unsigned w = r.v[i >> 1];
+  return __builtin_bit_cast(float, (i & 1) ? (w & 0xffff0000u) : (w << 16));
+}
+R2L_DEV float raw_at(const Raw8<float>& r, int i) { return __builtin_bit_cast(float, i < 4 ? r.a[i] : r.b[i - 4]); }
+R2L_DEV void store8(Rsrc s, unsigned off, const float v[8], bf16*) {
+  u32x4 q;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const bf16x2 p = {(bf16)v[2 * i], (bf16)v[2 * i + 1]};
+    q[i] = __builtin_bit_cast(unsigned, p);
+  }
+  bstore16(s, off, q);
+}
+R2L_DEV void store8(Rsrc s, unsigned off, const float v[8], float*) {
+  bstore16(s, off, __builtin_bit_cast(u32x4, f32x4{v[0], v[1], v[2], v[3]}));
+  bstore16(s, off + 16, __builtin_bit_cast(u32x4, f32x4{v[4], v[5], v[6], v[7]}));
 }
 
 // softplus for dt.  bf16 activations: log2(1 + 2^(-|v| log2 e)) ln 2 on the
@@ -147,19 +175,21 @@ template <> R2L_DEV float softplus_dt<bf16>(float v) {
 // A block of 4 waves owns 64 channels of one time chunk; time is walked right
 // to left in blocks of TB = 32 tokens:
 //   A  thread (r8 = tid / 8, c8 = tid % 8): token row r8, channels 8 c8 .. +7:
-//      consumes the registers prefetched for this block (conv + SiLU -> u,
+//      consumes the registers loaded for this block (conv + SiLU -> u,
 //      SiLU(z), Dskip u, delta -> LDS in bf16, B and C -> LDS), then issues
 //      the next block's loads;
 //   M  wave w: dt = softplus(delta . W_dt^T + b) for channels 16 w .. +15 of
 //      all 32 rows on MFMA (16x16x32 bf16); fp32 uses the VALU;
 //   B  wave w, lane c: channel c, states 4 w .. 4 w + 3 in registers, the
-//      recurrence over the block's tokens; the LDS operands run 4 tokens ahead
-//      of the arithmetic;
+//      recurrence over the block's tokens.  Per token the decay is applied
+//      on the VALU (h <- exp(dt A) h) and the input term dt u B is added by
+//      one 4x4x1 fp32 MFMA over 16 blocks, whose accumulator layout is
+//      exactly this one: block b = lanes 4b..4b+3, lane 4b+j holds column j
+//      in its 4 result registers (rows = states), with A operand B_t[4w + i]
+//      in lane 4b+i and B operand dt u of the lane's own channel.  The LDS
+//      operands run 4 tokens ahead of the arithmetic;
 //   C  same layout as A: y = (sum of the 4 partial C.h + Dskip u) SiLU(z),
 //      one 16-byte store per thread.
-// Prefetch loads are unconditional, from clamped rows, with validity applied
-// when consumed: a per-lane branch around a load makes both paths write the
-// same registers and forces an immediate wait for the load.
 // ---------------------------------------------------------------------------
 template <typename T, bool FUSED, bool SUMMARY, int KS>
 __global__ __launch_bounds__(256, 2) void scan_kernel(ScanArgs a) {
@@ -168,13 +198,13 @@ __global__ __launch_bounds__(256, 2) void scan_kernel(ScanArgs a) {
   constexpr int RP = MFMA_DT ? KS * 32 : 32;   // padded dt_rank for the MFMA k loop
   constexpr int DLS = RP + 8;                   // delta row stride in LDS (bf16)
   constexpr int DPT = RP / 8;                   // delta floats per thread per row (4..32)
-  static_assert(TB * DLS * 2 <= 3 * TB * 64 * 4, "delta must fit in yp_s[1..3]");
-  // yp_s (partial C.h sums of B/C) also hosts u and delta between A and M
-  __shared__ __attribute__((aligned(16))) float yp_s[4][TB][64];
-  __shared__ __attribute__((aligned(16))) float2 pre_s[TB][64];   // (dt, dt*u)
-  __shared__ __attribute__((aligned(16))) f32x4 bc_s[TB][8];      // B[0..16) C[0..16)
-  float (*u_s)[64] = yp_s[0];
-  bf16* dl_s = (bf16*)&yp_s[1][0][0];
+  constexpr bool BF = std::is_same<T, bf16>::value;
+  constexpr unsigned SZ = sizeof(T);
+  __shared__ __attribute__((aligned(16))) float yp_s[4][TB][64];   // partial C.h of each wave
+  __shared__ __attribute__((aligned(16))) float2 pre_s[TB][64];    // (dt, dt*u)
+  __shared__ __attribute__((aligned(16))) f32x4 bc_s[TB][8];       // B[0..16) C[0..16)
+  __shared__ __attribute__((aligned(16))) float u_s[FUSED ? TB : 1][64];
+  __shared__ __attribute__((aligned(16))) bf16 dl_s[MFMA_DT ? TB * DLS : 8];
 
   const int E = a.E;
   const int NB = E / 64;
@@ -197,13 +227,31 @@ __global__ __launch_bounds__(256, 2) void scan_kernel(ScanArgs a) {
   float A2[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) A2[i] = -expf(a.A_log[(long)e * NS + 4 * w + i]) * kLog2e;
-  float cwr[8][4], cb8[8], dsk8[8];
+  float dsk8[8], cb8[8];
+  float cwr[BF ? 1 : 8][4];        // fp32 conv taps
+  unsigned w10[8], w32[8];         // bf16 conv taps as pairs (tap for row t | row t+1), (t+2 | t+3)
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     dsk8[i] = a.Dskip ? a.Dskip[ea + i] : 0.0f;
     cb8[i] = FUSED ? to_f32(((const T*)a.conv_b)[ea + i]) : 0.0f;
+  }
+  if constexpr (FUSED) {
+    if constexpr (BF) {
+      // taps k = 0..3 of channel i as two dwords (k0|k1), (k2|k3); the conv
+      // weight for row t + j is tap 3 - j
+      const unsigned* cw = (const unsigned*)a.conv_w;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) cwr[i][k] = FUSED ? to_f32(((const T*)a.conv_w)[(long)(ea + i) * 4 + k]) : 0.0f;
+      for (int i = 0; i < 8; ++i) {
+        const unsigned k01 = cw[(long)(ea + i) * 2], k23 = cw[(long)(ea + i) * 2 + 1];
+        w10[i] = __builtin_amdgcn_alignbit(k23, k23, 16);   // (tap 3 | tap 2)
+        w32[i] = __builtin_amdgcn_alignbit(k01, k01, 16);   // (tap 1 | tap 0)
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) cwr[i][k] = ((const float*)a.conv_w)[(long)(ea + i) * 4 + k];
+    }
   }
   // dt_proj fragments (B operand of the 16x16x32 MFMA): channel
   // e0 + 16 w + (lane & 15), k = 32 ks + 8 (lane >> 4) .. +7.
@@ -225,7 +273,7 @@ __global__ __launch_bounds__(256, 2) void scan_kernel(ScanArgs a) {
   }
 
   // carry into this chunk from the chunks to its right
-  float h[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  f32x4 h = {0.0f, 0.0f, 0.0f, 0.0f};
   if (!SUMMARY) {
     for (int jj = 0; jj < d.j; ++jj) {
       const long base = (long)(d.first + jj) * NS * E;
@@ -238,58 +286,55 @@ __global__ __launch_bounds__(256, 2) void scan_kernel(ScanArgs a) {
   }
   float sdt = 0.0f;
 
-  // ---------------- prefetch registers ----------------
-  const T* xin = FUSED ? (const T*)a.x : (const T*)a.u;
-  const long ldx = FUSED ? a.ld_x : a.ld_u;
-  const T* zin = (const T*)a.z;
+  // ---------------- per-thread window offsets (constant over blocks) ----------------
+  const void* xin = FUSED ? a.x : a.u;
+  const long ldx_b = (FUSED ? a.ld_x : a.ld_u) * (long)SZ;     // x or u row pitch, bytes
+  const long ldz_b = a.ld_z * (long)SZ;
+  const long ldp_b = (long)a.ldp * 4;
+  const long lddt_b = a.ld_dt * 4, ldbc_b = a.ld_bc * 4;
+  const long ldy_b = (long)E * SZ;
+  const void* zin = a.z;
   const bool has_z = zin != nullptr;
+  const unsigned offX = (unsigned)(r8 * ldx_b) + (unsigned)ea * SZ;
+  const unsigned offZ = (unsigned)(r8 * ldz_b) + (unsigned)ea * SZ;
+  const unsigned offY = (unsigned)(r8 * ldy_b) + (unsigned)ea * SZ;
+  const unsigned offD = (unsigned)(r8 * ldp_b) + (unsigned)(c8 * DPT) * 4;         // delta (fused)
+  const unsigned offBC = (unsigned)(r8 * ldp_b) + (unsigned)(a.R + 4 * c8) * 4;   // B then C (fused)
+  const unsigned offDT = (unsigned)(r8 * lddt_b) + (unsigned)ea * 4;               // dt (standalone)
+  const unsigned offB = c8 < 4 ? (unsigned)(r8 * ldbc_b) + 16u * c8 : kOutside;    // B (standalone)
+  const unsigned offC = c8 < 4 ? kOutside : (unsigned)(r8 * ldbc_b) + 16u * (c8 - 4);
+
+  // ---------------- prefetch registers ----------------
   Raw8<T> px[FUSED ? 4 : 1];   // x rows r8 .. r8+3 (fused) or the u row r8
   Raw8<T> pz;                  // z row r8
-  float pd[FUSED ? DPT : 8];   // delta (fused) or dt (standalone) of row r8
+  u32x4 pd[FUSED ? (MFMA_DT ? DPT / 4 : 1) : 2];   // delta (fused) or dt (standalone) of row r8
   float pbc[4];                // 4 of the row's 32 B/C floats
-  const bool vec_d = FUSED ? ((a.R & 3) == 0 && (a.ldp & 3) == 0) : true;
 
   auto issue = [&](int blo, int bhi) {
-    const int t = min(blo + r8, bhi - 1);        // clamped: always a valid row
+    const int rows = bhi - blo;
     if constexpr (FUSED) {
+      // the conv window reaches 3 rows past the block, never past the sequence
+      const Rsrc rX = row_window(xin, blo, ldx_b, min(d.seq_end, bhi + 3) - blo);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) raw_load(px[j], xin + (long)min(t + j, d.seq_end - 1) * ldx + ea);
+      for (int j = 0; j < 4; ++j) raw_load(px[j], rX, offX + (unsigned)(j * ldx_b));
+      const Rsrc rD = row_window(a.xdbl, blo, ldp_b, rows);
       if constexpr (MFMA_DT) {
-        // c8 * DPT + DPT <= RP <= R + 31 < ldp: always inside row t
-        const float* src = a.xdbl + (long)t * a.ldp + c8 * DPT;
-        if (vec_d) {
 #pragma unroll
-          for (int q = 0; q < DPT / 4; ++q) {
-            const f32x4 v = *(const f32x4*)(src + 4 * q);
-#pragma unroll
-            for (int p = 0; p < 4; ++p) pd[4 * q + p] = v[p];
-          }
-        } else {
-#pragma unroll
-          for (int p = 0; p < DPT; ++p) pd[p] = src[p];
-        }
+        for (int q = 0; q < DPT / 4; ++q) pd[q] = bload16(rD, offD + 16u * q);
       }
-      const float* bsrc = a.xdbl + (long)t * a.ldp + a.R + 4 * c8;   // B then C, contiguous
-      if (vec_d) {
-        const f32x4 v = *(const f32x4*)bsrc;
 #pragma unroll
-        for (int p = 0; p < 4; ++p) pbc[p] = v[p];
-      } else {
-#pragma unroll
-        for (int p = 0; p < 4; ++p) pbc[p] = bsrc[p];
-      }
+      for (int p = 0; p < 4; ++p) pbc[p] = bload4(rD, offBC + 4u * p);
     } else {
-      raw_load(px[0], xin + (long)t * ldx + ea);
-      const f32x4 v0 = *(const f32x4*)(a.dt + (long)t * a.ld_dt + ea);
-      const f32x4 v1 = *(const f32x4*)(a.dt + (long)t * a.ld_dt + ea + 4);
+      raw_load(px[0], row_window(xin, blo, ldx_b, rows), offX);
+      const Rsrc rT = row_window(a.dt, blo, lddt_b, rows);
+      pd[0] = bload16(rT, offDT);
+      pd[1] = bload16(rT, offDT + 16);
+      const Rsrc rB = row_window(a.Bm, blo, ldbc_b, rows), rC = row_window(a.Cm, blo, ldbc_b, rows);
 #pragma unroll
-      for (int p = 0; p < 4; ++p) { pd[p] = v0[p]; pd[4 + p] = v1[p]; }
-      const float* src = (c8 < 4 ? a.Bm + 4 * c8 : a.Cm + 4 * (c8 - 4)) + (long)t * a.ld_bc;
-#pragma unroll
-      for (int p = 0; p < 4; ++p) pbc[p] = src[p];
+      for (int p = 0; p < 4; ++p) pbc[p] = bload4(rB, offB + 4u * p) + bload4(rC, offC + 4u * p);
     }
     if constexpr (!SUMMARY) {
-      if (has_z) raw_load(pz, zin + (long)t * a.ld_z + ea);
+      if (has_z) raw_load(pz, row_window(zin, blo, ldz_b, rows), offZ);
     }
   };
 
@@ -301,49 +346,66 @@ __global__ __launch_bounds__(256, 2) void scan_kernel(ScanArgs a) {
   for (; bhi > d.lo; bhi -= TB) {
     const int blo = max(d.lo, bhi - TB);
     const int nt = bhi - blo;
-    const int tr = blo + r8;
-    const bool rv = tr < bhi;
     // ---------------- A: consume this block's prefetched inputs ----------------
+    // (rows past the block read as zeros, or as the real rows of the conv
+    // window; either way their results are never used)
     {
       float uu[8];
       if constexpr (FUSED) {
-        bool xv[4];
+        if constexpr (BF) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) xv[j] = tr + j < d.seq_end;   // zero past the sequence end
+          for (int q = 0; q < 4; ++q) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          float c = cb8[i];
+            for (int hh = 0; hh < 2; ++hh) {
+              const int i = 2 * q + hh;
+              const unsigned sel = hh ? 0x07060302u : 0x05040100u;   // high / low bf16 of each row
+              const unsigned x10 = __builtin_amdgcn_perm(px[1].v[q], px[0].v[q], sel);   // (row t | row t+1)
+              const unsigned x32 = __builtin_amdgcn_perm(px[3].v[q], px[2].v[q], sel);   // (row t+2 | row t+3)
+              float c = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w10[i]),
+                                                        __builtin_bit_cast(bf16x2, x10), cb8[i], false);
+              c = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w32[i]),
+                                                  __builtin_bit_cast(bf16x2, x32), c, false);
+              uu[i] = silu_fast(c);
+            }
+          }
+        } else {
 #pragma unroll
-          for (int j = 0; j < 4; ++j) c = fmaf(cwr[i][3 - j], xv[j] ? raw_at(px[j], i) : 0.0f, c);
-          uu[i] = silu_fast(c);
+          for (int i = 0; i < 8; ++i) {
+            float c = cb8[i];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) c = fmaf(cwr[i][3 - j], raw_at(px[j], i), c);
+            uu[i] = silu_fast(c);
+          }
         }
         if constexpr (MFMA_DT) {
+          // delta -> bf16; columns at or past dt_rank meet zero rows of W_dt
+          // (they hold finite B/C values of the same row)
 #pragma unroll
           for (int q = 0; q < DPT / 4; ++q) {
-            bf16x4 pk;
-#pragma unroll
-            for (int p = 0; p < 4; ++p) pk[p] = (rv && c8 * DPT + 4 * q + p < a.R) ? (bf16)pd[4 * q + p] : (bf16)0.0f;
+            const f32x4 v = __builtin_bit_cast(f32x4, pd[q]);
+            const bf16x4 pk = {(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]};
             *(bf16x4*)(dl_s + r8 * DLS + c8 * DPT + 4 * q) = pk;
           }
         }
+        *(f32x4*)&u_s[r8][8 * c8] = f32x4{uu[0], uu[1], uu[2], uu[3]};
+        *(f32x4*)&u_s[r8][8 * c8 + 4] = f32x4{uu[4], uu[5], uu[6], uu[7]};
       } else {
+        const f32x4 d0 = __builtin_bit_cast(f32x4, pd[0]), d1 = __builtin_bit_cast(f32x4, pd[1]);
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-          uu[i] = rv ? raw_at(px[0], i) : 0.0f;
-          const float dtv = rv ? pd[i] : 0.0f;
+          uu[i] = raw_at(px[0], i);
+          const float dtv = i < 4 ? d0[i] : d1[i - 4];
           pre_s[r8][8 * c8 + i] = make_float2(dtv, dtv * uu[i]);
         }
       }
-      *(f32x4*)&u_s[r8][8 * c8] = f32x4{uu[0], uu[1], uu[2], uu[3]};
-      *(f32x4*)&u_s[r8][8 * c8 + 4] = f32x4{uu[4], uu[5], uu[6], uu[7]};
       if constexpr (!SUMMARY) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-          g8[i] = has_z ? silu_fast(rv ? raw_at(pz, i) : 0.0f) : 1.0f;
+          g8[i] = has_z ? silu_fast(raw_at(pz, i)) : 1.0f;
           du8[i] = dsk8[i] * uu[i];
         }
       }
-      bc_s[r8][c8] = rv ? f32x4{pbc[0], pbc[1], pbc[2], pbc[3]} : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+      bc_s[r8][c8] = f32x4{pbc[0], pbc[1], pbc[2], pbc[3]};
     }
     // the next block's loads go out now and land during this block's compute
     if (bhi - TB > d.lo) issue(max(d.lo, bhi - 2 * TB), bhi - TB);
@@ -384,63 +446,64 @@ __global__ __launch_bounds__(256, 2) void scan_kernel(ScanArgs a) {
       __syncthreads();
     }
     // ---------------- B: the recurrence, right to left ----------------
-    auto compute = [&](int r, float2 p, f32x4 Bv, f32x4 Cv) {
-      float av[4];
+    auto compute = [&](int r, float2 p, float bsel, f32x4 Cv) __attribute__((always_inline)) {
+      f32x4 hd;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) av[i] = exp2_fast(p.x * A2[i]);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) h[i] = fmaf(av[i], h[i], p.y * Bv[i]);
+      for (int i = 0; i < 4; ++i) hd[i] = exp2_fast(p.x * A2[i]) * h[i];
+      h = __builtin_amdgcn_mfma_f32_4x4x1f32(bsel, p.y, hd, 0, 0, 0);
       if constexpr (SUMMARY) {
         sdt += p.x;
       } else {
-        yp_s[w][r][lane] = fmaf(Cv[1], h[1], Cv[0] * h[0]) + fmaf(Cv[3], h[3], Cv[2] * h[2]);
+        yp_s[w][r][lane] = fmaf(Cv[3], h[3], fmaf(Cv[2], h[2], fmaf(Cv[1], h[1], Cv[0] * h[0])));
       }
     };
+    const float* bsrc = (const float*)&bc_s[0][w] + (lane & 3);   // B_t[4 w + (lane & 3)] at row 0
     if (nt == TB) {
       // 4-deep ring of LDS operands (indices are constants after unrolling)
       constexpr int LA = 4;
       float2 Pq[LA];
-      f32x4 Bq[LA], Cq[LA];
+      float Bq[LA];
+      f32x4 Cq[LA];
 #pragma unroll
       for (int k = 0; k < LA; ++k) {
         Pq[k] = pre_s[TB - 1 - k][lane];
-        Bq[k] = bc_s[TB - 1 - k][w];
-        Cq[k] = SUMMARY ? Bq[k] : bc_s[TB - 1 - k][4 + w];
+        Bq[k] = bsrc[(TB - 1 - k) * 32];
+        Cq[k] = SUMMARY ? f32x4{} : bc_s[TB - 1 - k][4 + w];
       }
 #pragma unroll
       for (int k = 0; k < TB; ++k) {
         const int r = TB - 1 - k, sl = k % LA;
         const float2 p = Pq[sl];
-        const f32x4 Bv = Bq[sl], Cv = Cq[sl];
+        const float bv = Bq[sl];
+        const f32x4 Cv = Cq[sl];
         if (k + LA < TB) {
           Pq[sl] = pre_s[r - LA][lane];
-          Bq[sl] = bc_s[r - LA][w];
+          Bq[sl] = bsrc[(r - LA) * 32];
           if constexpr (!SUMMARY) Cq[sl] = bc_s[r - LA][4 + w];
         }
-        compute(r, p, Bv, Cv);
+        compute(r, p, bv, Cv);
       }
     } else {
-      for (int r = nt - 1; r >= 0; --r) compute(r, pre_s[r][lane], bc_s[r][w], bc_s[r][4 + w]);
+      for (int r = nt - 1; r >= 0; --r) compute(r, pre_s[r][lane], bsrc[r * 32], bc_s[r][4 + w]);
     }
     __syncthreads();
     // ---------------- C: combine and store ----------------
+    // (rows past the block fall outside the store window and are dropped)
     if constexpr (!SUMMARY) {
-      if (rv) {
-        float v[8];
+      float v[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) v[i] = du8[i];
+      for (int i = 0; i < 8; ++i) v[i] = du8[i];
 #pragma unroll
-        for (int ww = 0; ww < 4; ++ww) {
-          const f32x4 p0 = *(const f32x4*)&yp_s[ww][r8][8 * c8];
-          const f32x4 p1 = *(const f32x4*)&yp_s[ww][r8][8 * c8 + 4];
+      for (int ww = 0; ww < 4; ++ww) {
+        const f32x4 p0 = *(const f32x4*)&yp_s[ww][r8][8 * c8];
+        const f32x4 p1 = *(const f32x4*)&yp_s[ww][r8][8 * c8 + 4];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) { v[i] += p0[i]; v[4 + i] += p1[i]; }
-        }
-#pragma unroll
-        for (int i = 0; i < 8; ++i) v[i] *= g8[i];
-        store8((T*)a.y + (long)tr * E + ea, v);
+        for (int i = 0; i < 4; ++i) { v[i] += p0[i]; v[4 + i] += p1[i]; }
       }
-      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] *= g8[i];
+      store8(row_window(a.y, blo, ldy_b, nt), offY, v, (T*)nullptr);
+      // the next block's phase B rewrites yp_s only after two more barriers
     }
   }
   if constexpr (SUMMARY) {
