@@ -178,73 +178,91 @@ def _seq_bounds(cu_seqlens, n_tokens):
 # --------------------------------------------------------------------------
 # the layer, literally: flip -> Mamba-1 -> flip -> LN -> gated residual
 # --------------------------------------------------------------------------
-def reverse_mamba_layer(h, cu_seqlens, W, s, use_ln=True, eps=1e-5, return_branch=False):
+def _check_direction(direction):
+    assert direction in ("r2l", "l2r"), "direction is 'r2l' or 'l2r'"
+    return direction == "r2l"
+
+
+def reverse_mamba_layer(h, cu_seqlens, W, s, use_ln=True, eps=1e-5, return_branch=False,
+                        direction="r2l"):
     """ReverseMambaLayer forward over packed sequences (§3.4 steps ❶-❹).
 
     h: [T, D] hidden states, sequences packed back to back; cu_seqlens:
     [nseq+1] offsets.  Each sequence is flipped, run through the Mamba-1
     block, flipped back, layer-normalised (unless use_ln is False) and added
     to h with weight tanh(s).  Returns h+ (and the branch r if asked).
+
+    direction="l2r" is the ablation control of §4.4 (Table 4, "L2R Mamba"):
+    the same block run in the original direction, i.e. with no flips.
     """
+    flip = _check_direction(direction)
     h = np.asarray(h, np.float64)
     T, D = h.shape
     r = np.zeros((T, D))
     for t0, t1 in _seq_bounds(cu_seqlens, T):
         if t1 == t0:
             continue
-        F = h[t0:t1][::-1]                      # ❶ flip
-        m = mamba_block(F, W)                   # ❷ Mamba-1 over the flipped sequence
-        M = m[::-1]                             # ❸ unflip ...
+        F = h[t0:t1][::-1] if flip else h[t0:t1]        # ❶ flip
+        m = mamba_block(F, W)                           # ❷ Mamba-1 over the flipped sequence
+        M = m[::-1] if flip else m                      # ❸ unflip ...
         r[t0:t1] = layer_norm(M, W["ln_w"], W["ln_b"], eps) if use_ln else M  # ... and LN
     out = gated_residual(h, r, s)               # ❹ gated residual
     return (out, r) if return_branch else out
 
 
-def hook_stack(h, cu_seqlens, layers, use_ln=True, eps=1e-5):
+def hook_stack(h, cu_seqlens, layers, use_ln=True, eps=1e-5, direction="r2l"):
     """Apply several hooks in sequence (§4.1: a hook after every 4th decoder
     layer; the decoder layers between hooks are taken as identity here).
     layers: list of (W, s)."""
     cur = np.asarray(h, np.float64)
     for W, s in layers:
-        cur = reverse_mamba_layer(cur, cu_seqlens, W, s, use_ln=use_ln, eps=eps)
+        cur = reverse_mamba_layer(cur, cu_seqlens, W, s, use_ln=use_ln, eps=eps, direction=direction)
     return cur
 
 
 # --------------------------------------------------------------------------
 # sub-operations exposed by the library, stated the same literal way
 # --------------------------------------------------------------------------
-def reverse_conv_silu(x, cu_seqlens, conv_w, conv_b, x_proj_w=None):
+def reverse_conv_silu(x, cu_seqlens, conv_w, conv_b, x_proj_w=None, direction="r2l"):
     """Conv + SiLU (+ x_proj) of the flipped Mamba block, returned in the
     original token order: per sequence, u = flip(SiLU(causal_conv(flip(x)))).
+    direction="l2r": u = SiLU(causal_conv(x)) (no flips).
     Returns u [T, E] and, if x_proj_w is given, xdbl = u @ x_proj_w.T."""
+    flip = _check_direction(direction)
     x = np.asarray(x, np.float64)
     T, E = x.shape
     u = np.zeros((T, E))
     for t0, t1 in _seq_bounds(cu_seqlens, T):
         if t1 == t0:
             continue
-        u[t0:t1] = silu(causal_depthwise_conv(x[t0:t1][::-1], conv_w, conv_b))[::-1]
+        if flip:
+            u[t0:t1] = silu(causal_depthwise_conv(x[t0:t1][::-1], conv_w, conv_b))[::-1]
+        else:
+            u[t0:t1] = silu(causal_depthwise_conv(x[t0:t1], conv_w, conv_b))
     if x_proj_w is None:
         return u, None
     return u, u @ np.asarray(x_proj_w, np.float64).T
 
 
-def reverse_selective_scan(u, dt, A_log, Bm, Cm, cu_seqlens, Dskip=None, z=None):
+def reverse_selective_scan(u, dt, A_log, Bm, Cm, cu_seqlens, Dskip=None, z=None, direction="r2l"):
     """Selective scan run right to left per sequence, stated as
     flip -> causal scan -> flip; optional Dskip term and SiLU(z) gate.
+    direction="l2r": the causal scan itself (no flips).
     u, dt, z: [T, E]; Bm, Cm: [T, N]; A_log: [E, N]."""
+    flip = _check_direction(direction)
     u = np.asarray(u, np.float64)
     T, E = u.shape
     A = -np.exp(np.asarray(A_log, np.float64))
     y = np.zeros((T, E))
+    o = (lambda a: a[::-1]) if flip else (lambda a: a)  # noqa: E731
     for t0, t1 in _seq_bounds(cu_seqlens, T):
         if t1 == t0:
             continue
         sl = slice(t0, t1)
-        y[sl] = selective_scan_causal(
-            u[sl][::-1], np.asarray(dt, np.float64)[sl][::-1], A,
-            np.asarray(Bm, np.float64)[sl][::-1], np.asarray(Cm, np.float64)[sl][::-1], Dskip,
-        )[::-1]
+        y[sl] = o(selective_scan_causal(
+            o(u[sl]), o(np.asarray(dt, np.float64)[sl]), A,
+            o(np.asarray(Bm, np.float64)[sl]), o(np.asarray(Cm, np.float64)[sl]), Dskip,
+        ))
     if z is not None:
         y = y * silu(z)
     return y

@@ -435,3 +435,86 @@ def test_synthetic_recipe_statistics():
     np.testing.assert_allclose(np.exp(W["A_log"][0]), np.arange(1, 17), rtol=1e-6)
     lens = synth.workloads()["varlen16"].lengths
     assert len(lens) == 16 and min(lens) >= 512 and max(lens) <= 16384
+
+
+# ---------------------------------------------------------------------------
+# L2R control (§4.4, Table 4: the same block run left to right)
+# ---------------------------------------------------------------------------
+def _closed_form_forward_scan(u, dt, A_log, Bm, Cm, Dskip):
+    """y_t[e] = sum_{v <= t} sum_n C_t[n] (prod_{v < k <= t} exp(dt_k[e] A[e,n]))
+    dt_v[e] B_v[n] u_v[e] + D[e] u_t[e], written with scalar loops."""
+    L, E = u.shape
+    N = Bm.shape[1]
+    y = np.zeros((L, E))
+    for t in range(L):
+        for e in range(E):
+            acc = 0.0
+            for v in range(0, t + 1):
+                for n in range(N):
+                    A = -math.exp(A_log[e][n])
+                    prod = 1.0
+                    for k in range(v + 1, t + 1):
+                        prod *= math.exp(dt[k][e] * A)
+                    acc += Cm[t][n] * prod * dt[v][e] * Bm[v][n] * u[v][e]
+            y[t][e] = acc + Dskip[e] * u[t][e]
+    return y
+
+
+@pytest.mark.parametrize("L", [1, 2, 5, 8])
+def test_l2r_scan_matches_brute_force_closed_form(L):
+    rng = _rng(300 + L)
+    u, dt, A_log, Bm, Cm, Dskip = _scan_inputs(rng, L, 3, 4)
+    got = O.reverse_selective_scan(u, dt, A_log, Bm, Cm, [0, L], Dskip=Dskip, direction="l2r")
+    ref = _closed_form_forward_scan(u, dt, A_log, Bm, Cm, Dskip)
+    np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-12)
+
+
+def test_l2r_conv_impulse_orientation():
+    E, K, L, t0 = 3, 4, 10, 3
+    rng = _rng(301)
+    w = rng.standard_normal((E, K))
+    b = rng.standard_normal(E)
+    x = np.zeros((L, E))
+    x[t0] = 1.0
+    u, _ = O.reverse_conv_silu(x, [0, L], w, b, direction="l2r")
+    c = np.tile(b, (L, 1))
+    for j in range(K):                           # token t0+j sees x[t0] through tap K-1-j
+        c[t0 + j] = b + w[:, K - 1 - j]
+    np.testing.assert_allclose(u, c / (1 + np.exp(-c)), rtol=1e-14, atol=1e-15)
+
+
+def test_l2r_conv_sequence_start_is_zero_padded():
+    E, K = 2, 4
+    rng = _rng(302)
+    w = rng.standard_normal((E, K))
+    b = rng.standard_normal(E)
+    x = rng.standard_normal((5, E))
+    u, _ = O.reverse_conv_silu(x, [0, 2, 5], w, b, direction="l2r")
+    # first token of sequence 1 (t=2) only sees itself through tap K-1
+    c = b + w[:, K - 1] * x[2]
+    np.testing.assert_allclose(u[2], c / (1 + np.exp(-c)), rtol=1e-14)
+    # t=3 sees t=3 (tap K-1) and t=2 (tap K-2), not t=1 (other sequence)
+    c = b + w[:, K - 1] * x[3] + w[:, K - 2] * x[2]
+    np.testing.assert_allclose(u[3], c / (1 + np.exp(-c)), rtol=1e-14)
+
+
+def test_l2r_layer_left_context_only():
+    rng, W, h, cu = _layer_case(41)
+    base = O.reverse_mamba_layer(h, cu, W, 0.9, direction="l2r")
+    j = 5                                        # inside sequence 0 = [0, 13)
+    h2 = h.copy()
+    h2[j] += rng.standard_normal(h.shape[1])
+    pert = O.reverse_mamba_layer(h2, cu, W, 0.9, direction="l2r")
+    assert np.array_equal(pert[:j], base[:j])    # positions left of j untouched
+    assert np.all(np.abs(pert[j:cu[1]] - base[j:cu[1]]).max(axis=1) > 0)   # right of j sees it
+    assert np.array_equal(pert[cu[1]:], base[cu[1]:])
+
+
+def test_l2r_of_flipped_sequences_is_flipped_r2l():
+    """Reversing every sequence turns one direction into the other."""
+    _, W, h, cu = _layer_case(42)
+    flip = np.concatenate([np.arange(a, b)[::-1] for a, b in zip(cu[:-1], cu[1:])])
+    r2l = O.reverse_mamba_layer(h, cu, W, 0.7)
+    l2r = O.reverse_mamba_layer(h[flip], cu, W, 0.7, direction="l2r")
+    np.testing.assert_allclose(l2r[flip], r2l, rtol=1e-12, atol=1e-12)
+    assert np.max(np.abs(O.reverse_mamba_layer(h, cu, W, 0.7, direction="l2r") - r2l)) > 1e-3
