@@ -67,8 +67,14 @@ enum {
   R2L_ERR_HIP = -4           /* a HIP launch or runtime call failed */
 };
 
-/* Flags for r2l_layer_fwd. */
+/* Flags for r2l_layer_fwd (both), r2l_conv_fwd and r2l_scan_fwd (R2L_FLAG_L2R). */
 #define R2L_FLAG_NO_LN 0x1u  /* skip the stream LayerNorm: r = unflipped Mamba output */
+/* Run the conv and the scan left to right instead (a causal conv and a forward
+ * scan over each sequence, no flips): the "L2R Mamba" control of the pages'
+ * ablation (§4.4, Table 4), the same block in the original direction.  Every
+ * other step is unchanged; results are those of the default direction on
+ * each sequence reversed, reversed back. */
+#define R2L_FLAG_L2R 0x2u
 
 /* LayerNorm epsilon used by r2l_layer_fwd (biased variance over d_model). */
 #define R2L_LN_EPS 1e-5f
@@ -128,9 +134,11 @@ int r2l_layer_fwd(const r2l_dims* dims, r2l_dtype act, uint32_t flags, const r2l
  * x half of an in_proj output has ld_x = 2E).  u_out: act [n_tokens, E]
  * (contiguous) or NULL when only xdbl is wanted; xdbl_out: f32
  * [n_tokens, R+2N] (contiguous), required iff x_proj_w != NULL.  At least
- * one output must be requested.  Needs no workspace.
+ * one output must be requested.  Needs no workspace.  flags: 0 or
+ * R2L_FLAG_L2R (causal taps x[t-j], x before the sequence start taken as 0);
+ * other bits return R2L_ERR_INVALID_ARG.
  * ---------------------------------------------------------------------- */
-int r2l_conv_fwd(const r2l_dims* dims, r2l_dtype act, const void* x, int64_t ld_x,
+int r2l_conv_fwd(const r2l_dims* dims, r2l_dtype act, uint32_t flags, const void* x, int64_t ld_x,
                  const void* conv_w, const void* conv_b, const void* x_proj_w, void* u_out,
                  float* xdbl_out, const int32_t* cu_seqlens, int32_t nseq, int64_t n_tokens,
                  int32_t max_seqlen, void* stream);
@@ -151,12 +159,15 @@ int r2l_conv_fwd(const r2l_dims* dims, r2l_dtype act, const void* x, int64_t ld_
  * no alignment requirement.  A row stride whose 64 rows exceed 2^31 - 1
  * bytes returns R2L_ERR_UNSUPPORTED (rows are addressed with 32-bit offsets
  * inside windows of a few dozen rows).
+ * flags: 0 or R2L_FLAG_L2R (the recurrence run left to right,
+ * h_t = exp(dt_t A) h_{t-1} + ..., h = 0 before the sequence start); other
+ * bits return R2L_ERR_INVALID_ARG.
  * workspace: r2l_scan_workspace_bytes(...) bytes, 256-byte aligned.
  * ---------------------------------------------------------------------- */
 size_t r2l_scan_workspace_bytes(const r2l_dims* dims, int64_t n_tokens, int32_t nseq,
                                 int32_t max_seqlen);
 
-int r2l_scan_fwd(const r2l_dims* dims, r2l_dtype act, const void* u, int64_t ld_u,
+int r2l_scan_fwd(const r2l_dims* dims, r2l_dtype act, uint32_t flags, const void* u, int64_t ld_u,
                  const float* dt, int64_t ld_dt, const float* A_log, const float* B,
                  const float* C, int64_t ld_bc, const float* Dskip, const void* z, int64_t ld_z,
                  void* y_out, const int32_t* cu_seqlens, int32_t nseq, int64_t n_tokens,

@@ -20,6 +20,7 @@ LIB_PATH = os.path.join(_PKG, "libr2l.so")
 R2L_OK, R2L_ERR_INVALID_ARG, R2L_ERR_UNSUPPORTED, R2L_ERR_WORKSPACE, R2L_ERR_HIP = 0, -1, -2, -3, -4
 R2L_F32, R2L_BF16 = 0, 1
 R2L_FLAG_NO_LN = 0x1
+R2L_FLAG_L2R = 0x2
 
 
 class R2LError(RuntimeError):
@@ -47,11 +48,11 @@ _SIGS = {
     "r2l_layer_workspace_bytes": (_SZ, [C.POINTER(Dims), C.c_int, _I64, _I32, _I32]),
     "r2l_layer_fwd": (C.c_int, [C.POINTER(Dims), C.c_int, C.c_uint32, C.POINTER(Weights), _P, _P, _P,
                                 _I32, _I64, _I32, _P, _SZ, _P, _P]),
-    "r2l_conv_fwd": (C.c_int, [C.POINTER(Dims), C.c_int, _P, _I64, _P, _P, _P, _P, _P, _P, _I32, _I64,
-                               _I32, _P]),
+    "r2l_conv_fwd": (C.c_int, [C.POINTER(Dims), C.c_int, C.c_uint32, _P, _I64, _P, _P, _P, _P, _P, _P, _I32,
+                               _I64, _I32, _P]),
     "r2l_scan_workspace_bytes": (_SZ, [C.POINTER(Dims), _I64, _I32, _I32]),
-    "r2l_scan_fwd": (C.c_int, [C.POINTER(Dims), C.c_int, _P, _I64, _P, _I64, _P, _P, _P, _I64, _P, _P,
-                               _I64, _P, _P, _I32, _I64, _I32, _P, _SZ, _P]),
+    "r2l_scan_fwd": (C.c_int, [C.POINTER(Dims), C.c_int, C.c_uint32, _P, _I64, _P, _I64, _P, _P, _P, _I64, _P,
+                               _P, _I64, _P, _P, _I32, _I64, _I32, _P, _SZ, _P]),
     "r2l_gemm_nt": (C.c_int, [C.c_int, _I64, _I64, _I64, _P, _I64, _P, _I64, _P, _I64, C.c_int, _P, C.c_size_t, _P]),
     "r2l_timing_enable": (C.c_int, [C.c_int]),
     "r2l_timing_reset": (C.c_int, []),
@@ -175,10 +176,10 @@ def r2l_layer_fwd(h: torch.Tensor, w: Dict[str, torch.Tensor], cu_seqlens, *, ou
 
 def r2l_conv_fwd(x: torch.Tensor, conv_w: torch.Tensor, conv_b: torch.Tensor, cu_seqlens, *,
                  x_proj_w: Optional[torch.Tensor] = None, d_state: int = 16, dt_rank: Optional[int] = None,
-                 want_u: bool = True):
-    """Anti-causal conv + SiLU (+ x_proj).  x may be a strided view whose
-    rows are contiguous (e.g. the x half of in_proj's output).  Returns
-    (u or None, xdbl or None)."""
+                 want_u: bool = True, flags: int = 0):
+    """Anti-causal conv + SiLU (+ x_proj); causal with flags=R2L_FLAG_L2R.
+    x may be a strided view whose rows are contiguous (e.g. the x half of
+    in_proj's output).  Returns (u or None, xdbl or None)."""
     _need(x, "x", contiguous=False)
     if x.stride(1) != 1:
         raise ValueError("x rows must be contiguous")
@@ -190,16 +191,17 @@ def r2l_conv_fwd(x: torch.Tensor, conv_w: torch.Tensor, conv_b: torch.Tensor, cu
     u = torch.empty(T, E, dtype=x.dtype, device=x.device) if want_u else None
     xdbl = torch.empty(T, R + 2 * d_state, dtype=torch.float32, device=x.device) if x_proj_w is not None else None
     _check("r2l_conv_fwd", lib().r2l_conv_fwd(
-        C.byref(d), act, _ptr(x), x.stride(0), _ptr(conv_w), _ptr(conv_b), _ptr(x_proj_w), _ptr(u),
+        C.byref(d), act, flags, _ptr(x), x.stride(0), _ptr(conv_w), _ptr(conv_b), _ptr(x_proj_w), _ptr(u),
         _ptr(xdbl), _ptr(cu_dev), nseq, T, max_seqlen, _stream()))
     return u, xdbl
 
 
 def r2l_scan_fwd(u: torch.Tensor, dt: torch.Tensor, A_log: torch.Tensor, B: torch.Tensor, C_: torch.Tensor,
                  cu_seqlens, *, Dskip: Optional[torch.Tensor] = None, z: Optional[torch.Tensor] = None,
-                 dt_rank: int = 1) -> torch.Tensor:
-    """Reverse selective scan with the Dskip term and SiLU(z) gate.
-    B and C may be strided column slices (row stride shared)."""
+                 dt_rank: int = 1, flags: int = 0) -> torch.Tensor:
+    """Reverse selective scan with the Dskip term and SiLU(z) gate (left to
+    right with flags=R2L_FLAG_L2R).  B and C may be strided column slices
+    (row stride shared)."""
     _need(u, "u", contiguous=False)
     act = _act(u)
     T, E = u.shape
@@ -216,7 +218,7 @@ def r2l_scan_fwd(u: torch.Tensor, dt: torch.Tensor, A_log: torch.Tensor, B: torc
     wsb = int(lib().r2l_scan_workspace_bytes(C.byref(d), T, nseq, max_seqlen))
     ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=u.device)
     _check("r2l_scan_fwd", lib().r2l_scan_fwd(
-        C.byref(d), act, _ptr(u), u.stride(0), _ptr(dt), dt.stride(0), _ptr(A_log), _ptr(B), _ptr(C_),
+        C.byref(d), act, flags, _ptr(u), u.stride(0), _ptr(dt), dt.stride(0), _ptr(A_log), _ptr(B), _ptr(C_),
         B.stride(0), _ptr(Dskip), _ptr(z), z.stride(0) if z is not None else 0, _ptr(y), _ptr(cu_dev), nseq, T,
         max_seqlen, _ptr(ws), ws.numel(), _stream()))
     return y

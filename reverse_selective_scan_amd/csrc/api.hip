@@ -212,7 +212,7 @@ Tp* at(void* ws, size_t off) {
 template <typename T>
 int run_scan(const ScanArgs& a, const ScanPlan& sp, bool fused, const int32_t* cu, int nseq,
              int64_t Tn, int32_t* cu_clean, ChunkDesc* chunks, int32_t* nch, hipStream_t st) {
-  R2L_RUN("plan_chunks", st, plan_chunks(cu, nseq, (int)Tn, sp.Lc, sp.max_chunks, cu_clean, chunks, nch, st));
+  R2L_RUN("plan_chunks", st, plan_chunks(cu, nseq, (int)Tn, sp.Lc, sp.max_chunks, a.l2r, cu_clean, chunks, nch, st));
   if (sp.summary) R2L_RUN("scan_summary", st, scan_summary<T>(a, fused, st));
   R2L_RUN("scan_main", st, scan_main<T>(a, fused, st));
   return R2L_OK;
@@ -267,7 +267,8 @@ int r2l_layer_fwd(const r2l_dims* d, r2l_dtype act, uint32_t flags, const r2l_we
   int rc = check_dims(d);
   if (rc != R2L_OK) return rc;
   if ((rc = check_tokens(act, n_tokens, nseq, max_seqlen)) != R2L_OK) return rc;
-  if (flags & ~R2L_FLAG_NO_LN) return R2L_ERR_INVALID_ARG;
+  if (flags & ~(R2L_FLAG_NO_LN | R2L_FLAG_L2R)) return R2L_ERR_INVALID_ARG;
+  const bool l2r = flags & R2L_FLAG_L2R;
   if (!w || !h_in || !h_out || !cu_seqlens) return R2L_ERR_INVALID_ARG;
   if (!w->in_proj_w || !w->conv_w || !w->conv_b || !w->x_proj_w || !w->dt_proj_w ||
       !w->out_proj_w || !w->dt_proj_b || !w->A_log || !w->Dskip || !w->s)
@@ -306,9 +307,10 @@ int r2l_layer_fwd(const r2l_dims* d, r2l_dtype act, uint32_t flags, const r2l_we
   a.chunks = chunks; a.n_chunks = nch; a.max_chunks = sp.max_chunks;
   a.sumS = at<float>(workspace, sp.off_sumS);
   a.sumP = at<float>(workspace, sp.off_sumP);
+  a.l2r = l2r;
 
   // chunk table first: the conv kernel also reads the sanitised offsets
-  R2L_RUN("plan_chunks", st, plan_chunks(cu_seqlens, nseq, T, sp.Lc, sp.max_chunks, cu_clean, chunks, nch, st));
+  R2L_RUN("plan_chunks", st, plan_chunks(cu_seqlens, nseq, T, sp.Lc, sp.max_chunks, l2r, cu_clean, chunks, nch, st));
 
   if (act == R2L_BF16) {
     bf16* xz = at<bf16>(workspace, lp.off_xz);
@@ -323,15 +325,15 @@ int r2l_layer_fwd(const r2l_dims* d, r2l_dtype act, uint32_t flags, const r2l_we
         // large input: split-K over one or two blocks per CU, then the parts are summed
         float* xdbl2 = at<float>(workspace, lp.off_xdbl2);
         float* xdbl3 = at<float>(workspace, lp.off_xdbl3);
-        R2L_RUN("conv_xproj", st, conv_xproj_bf16_sk(T, E, P, xz, 2L * E, (const bf16*)w->conv_w, (const bf16*)w->conv_b, (const bf16*)w->x_proj_w, xdbl, xdbl2, xdbl3, cu_clean, nseq, ncu, st));
+        R2L_RUN("conv_xproj", st, conv_xproj_bf16_sk(T, E, P, xz, 2L * E, (const bf16*)w->conv_w, (const bf16*)w->conv_b, (const bf16*)w->x_proj_w, xdbl, xdbl2, xdbl3, cu_clean, nseq, ncu, l2r, st));
         R2L_RUN("conv_sum", st, conv_sk_sum(T, E, P, xdbl, xdbl2, xdbl3, ncu, st));
       } else {
-        R2L_RUN("conv_xproj", st, conv_xproj_bf16(T, E, P, xz, 2L * E, (const bf16*)w->conv_w, (const bf16*)w->conv_b, (const bf16*)w->x_proj_w, nullptr, xdbl, cu_clean, nseq, st,
+        R2L_RUN("conv_xproj", st, conv_xproj_bf16(T, E, P, xz, 2L * E, (const bf16*)w->conv_w, (const bf16*)w->conv_b, (const bf16*)w->x_proj_w, nullptr, xdbl, cu_clean, nseq, l2r, st,
                                                   scratch, kSplitScratch, ncu));
       }
     } else {
       bf16* u = at<bf16>(workspace, lp.off_u);
-      R2L_RUN("conv_silu", st, conv_silu<bf16>(T, E, xz, 2L * E, (const bf16*)w->conv_w, (const bf16*)w->conv_b, u, cu_clean, nseq, st));
+      R2L_RUN("conv_silu", st, conv_silu<bf16>(T, E, xz, 2L * E, (const bf16*)w->conv_w, (const bf16*)w->conv_b, u, cu_clean, nseq, l2r, st));
       // x_proj with a bf16 output would lose precision; run it through the fp32-out MFMA GEMM
       R2L_RUN("x_proj_gemm", st, gemm_bf16_nt(T, P, E, u, E, (const bf16*)w->x_proj_w, E, xdbl, P, true, st));
     }
@@ -348,7 +350,7 @@ int r2l_layer_fwd(const r2l_dims* d, r2l_dtype act, uint32_t flags, const r2l_we
     float* u = at<float>(workspace, lp.off_u);
     float* y = at<float>(workspace, lp.off_y);
     R2L_RUN("in_proj_gemm", st, gemm_f32_nt(T, 2 * E, D, (const float*)h_in, D, (const float*)w->in_proj_w, D, xz, 2L * E, st));
-    R2L_RUN("conv_silu", st, conv_silu<float>(T, E, xz, 2L * E, (const float*)w->conv_w, (const float*)w->conv_b, u, cu_clean, nseq, st));
+    R2L_RUN("conv_silu", st, conv_silu<float>(T, E, xz, 2L * E, (const float*)w->conv_w, (const float*)w->conv_b, u, cu_clean, nseq, l2r, st));
     R2L_RUN("x_proj_gemm", st, gemm_f32_nt(T, P, E, u, E, (const float*)w->x_proj_w, E, xdbl, P, st));
     a.x = xz; a.z = xz + E; a.y = y;
     if (sp.summary) R2L_RUN("scan_summary", st, scan_summary<float>(a, true, st));
@@ -359,12 +361,14 @@ int r2l_layer_fwd(const r2l_dims* d, r2l_dtype act, uint32_t flags, const r2l_we
   return R2L_OK;
 }
 
-int r2l_conv_fwd(const r2l_dims* d, r2l_dtype act, const void* x, int64_t ld_x, const void* conv_w,
-                 const void* conv_b, const void* x_proj_w, void* u_out, float* xdbl_out,
-                 const int32_t* cu_seqlens, int32_t nseq, int64_t n_tokens, int32_t max_seqlen,
-                 void* stream) {
+int r2l_conv_fwd(const r2l_dims* d, r2l_dtype act, uint32_t flags, const void* x, int64_t ld_x,
+                 const void* conv_w, const void* conv_b, const void* x_proj_w, void* u_out,
+                 float* xdbl_out, const int32_t* cu_seqlens, int32_t nseq, int64_t n_tokens,
+                 int32_t max_seqlen, void* stream) {
   int rc = check_dims(d);
   if (rc != R2L_OK) return rc;
+  if (flags & ~R2L_FLAG_L2R) return R2L_ERR_INVALID_ARG;
+  const bool l2r = flags & R2L_FLAG_L2R;
   if ((rc = check_tokens(act, n_tokens, nseq, max_seqlen)) != R2L_OK) return rc;
   const int E = d->d_inner, P = d->dt_rank + 2 * d->d_state;
   if (!x || !conv_w || !conv_b || !cu_seqlens || ld_x < E) return R2L_ERR_INVALID_ARG;
@@ -380,25 +384,26 @@ int r2l_conv_fwd(const r2l_dims* d, r2l_dtype act, const void* x, int64_t ld_x, 
   const int T = (int)n_tokens;
   if (act == R2L_BF16) {
     if (fused) {
-      R2L_RUN("conv_xproj", st, conv_xproj_bf16(T, E, P, (const bf16*)x, ld_x, (const bf16*)conv_w, (const bf16*)conv_b, (const bf16*)x_proj_w, (bf16*)u_out, xdbl_out, cu_seqlens, nseq, st));
+      R2L_RUN("conv_xproj", st, conv_xproj_bf16(T, E, P, (const bf16*)x, ld_x, (const bf16*)conv_w, (const bf16*)conv_b, (const bf16*)x_proj_w, (bf16*)u_out, xdbl_out, cu_seqlens, nseq, l2r, st));
     } else {
-      R2L_RUN("conv_silu", st, conv_silu<bf16>(T, E, (const bf16*)x, ld_x, (const bf16*)conv_w, (const bf16*)conv_b, (bf16*)u_out, cu_seqlens, nseq, st));
+      R2L_RUN("conv_silu", st, conv_silu<bf16>(T, E, (const bf16*)x, ld_x, (const bf16*)conv_w, (const bf16*)conv_b, (bf16*)u_out, cu_seqlens, nseq, l2r, st));
       if (x_proj_w) R2L_RUN("x_proj_gemm", st, gemm_bf16_nt(T, P, E, (const bf16*)u_out, E, (const bf16*)x_proj_w, E, xdbl_out, P, true, st));
     }
   } else {
-    R2L_RUN("conv_silu", st, conv_silu<float>(T, E, (const float*)x, ld_x, (const float*)conv_w, (const float*)conv_b, (float*)u_out, cu_seqlens, nseq, st));
+    R2L_RUN("conv_silu", st, conv_silu<float>(T, E, (const float*)x, ld_x, (const float*)conv_w, (const float*)conv_b, (float*)u_out, cu_seqlens, nseq, l2r, st));
     if (x_proj_w) R2L_RUN("x_proj_gemm", st, gemm_f32_nt(T, P, E, (const float*)u_out, E, (const float*)x_proj_w, E, xdbl_out, P, st));
   }
   return R2L_OK;
 }
 
-int r2l_scan_fwd(const r2l_dims* d, r2l_dtype act, const void* u, int64_t ld_u, const float* dt,
-                 int64_t ld_dt, const float* A_log, const float* B, const float* C, int64_t ld_bc,
-                 const float* Dskip, const void* z, int64_t ld_z, void* y_out,
+int r2l_scan_fwd(const r2l_dims* d, r2l_dtype act, uint32_t flags, const void* u, int64_t ld_u,
+                 const float* dt, int64_t ld_dt, const float* A_log, const float* B, const float* C,
+                 int64_t ld_bc, const float* Dskip, const void* z, int64_t ld_z, void* y_out,
                  const int32_t* cu_seqlens, int32_t nseq, int64_t n_tokens, int32_t max_seqlen,
                  void* workspace, size_t workspace_bytes, void* stream) {
   int rc = check_dims(d);
   if (rc != R2L_OK) return rc;
+  if (flags & ~R2L_FLAG_L2R) return R2L_ERR_INVALID_ARG;
   if ((rc = check_tokens(act, n_tokens, nseq, max_seqlen)) != R2L_OK) return rc;
   const int E = d->d_inner;
   if (!u || !dt || !A_log || !B || !C || !y_out || !cu_seqlens) return R2L_ERR_INVALID_ARG;
@@ -429,6 +434,7 @@ int r2l_scan_fwd(const r2l_dims* d, r2l_dtype act, const void* u, int64_t ld_u, 
   a.max_chunks = sp.max_chunks;
   a.sumS = at<float>(workspace, sp.off_sumS);
   a.sumP = at<float>(workspace, sp.off_sumP);
+  a.l2r = flags & R2L_FLAG_L2R;
   int32_t* cu_clean = at<int32_t>(workspace, sp.off_cu);
   if (act == R2L_BF16)
     return run_scan<bf16>(a, sp, false, cu_seqlens, nseq, n_tokens, cu_clean, (ChunkDesc*)a.chunks, (int32_t*)a.n_chunks, st);

@@ -77,9 +77,21 @@ R2L_DEV int seq_end_of(const int32_t* cu, int nseq, int t, int n_tokens) {
   return e > n_tokens ? n_tokens : e;
 }
 
+// The start of the sequence containing token t, clamped into [0, t].
+R2L_DEV int seq_start_of(const int32_t* cu, int nseq, int t) {
+  int lo = 0, hi = nseq;  // the last q in [0, nseq) with cu[q] <= t
+  while (hi - lo > 1) {
+    int mid = (lo + hi) >> 1;
+    if (cu[mid] <= t) lo = mid; else hi = mid;
+  }
+  const int s = cu[lo];
+  return s > t ? t : (s < 0 ? 0 : s);
+}
+
 // ---- chunk table used by the scan ----------------------------------------------
-// One time chunk of one sequence; chunks of a sequence are stored contiguously,
-// the rightmost first (j = 0).
+// One time chunk of one sequence; chunks of a sequence are stored contiguously
+// in scan order: the rightmost first (j = 0) for the right-to-left scan, the
+// leftmost first for the left-to-right one.
 struct ChunkDesc {
   int lo, hi;        // token range [lo, hi)
   int seq_lo, seq_end;

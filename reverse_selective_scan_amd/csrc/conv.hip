@@ -3,7 +3,9 @@
 // causal conv run over the flipped sequence is, in the original order, a
 // conv that looks at a token and the K-1 tokens to its right):
 //   u[t,e] = SiLU(b[e] + sum_{j=0}^{K-1} w[e,K-1-j] * x[t+j,e]),
-// with x past the end of t's sequence taken as 0.
+// with x past the end of t's sequence taken as 0.  With L2R (the left-to-
+// right control of §4.4, Table 4) the taps look left instead: x[t-j], with
+// x before the start of t's sequence taken as 0.
 #include "kernels.h"
 
 namespace r2l {
@@ -15,7 +17,7 @@ constexpr int KC = 4;  // d_conv (§4.1)
 // lane = channel, so every load/store instruction touches 64 consecutive
 // channels of one token row.
 // ---------------------------------------------------------------------------
-template <typename T>
+template <typename T, bool L2R>
 __global__ __launch_bounds__(256) void conv_silu_kernel(int Tn, int E, const T* __restrict__ x,
                                                         long ld_x, const T* __restrict__ cw,
                                                         const T* __restrict__ cb, T* __restrict__ u,
@@ -30,28 +32,35 @@ __global__ __launch_bounds__(256) void conv_silu_kernel(int Tn, int E, const T* 
   for (int i = 0; i < 8; ++i) {
     const int t = tb + i;
     if (t >= Tn) break;
-    const int se = seq_end_of(cu, nseq, t, Tn);
+    // the sequence end (R2L) or start (L2R) bounds the taps
+    const int sb = L2R ? seq_start_of(cu, nseq, t) : seq_end_of(cu, nseq, t, Tn);
     float c = b;
 #pragma unroll
-    for (int j = 0; j < KC; ++j)
-      if (t + j < se) c = fmaf(wt[KC - 1 - j], to_f32(x[(long)(t + j) * ld_x + e]), c);
+    for (int j = 0; j < KC; ++j) {
+      const int row = L2R ? t - j : t + j;
+      if (L2R ? row >= sb : row < sb) c = fmaf(wt[KC - 1 - j], to_f32(x[(long)row * ld_x + e]), c);
+    }
     u[(long)t * E + e] = from_f32<T>(silu_fast(c));
   }
 }
 
 template <typename T>
 hipError_t conv_silu(int Tn, int E, const T* x, long ld_x, const T* conv_w, const T* conv_b, T* u,
-                     const int32_t* cu, int nseq, hipStream_t st) {
+                     const int32_t* cu, int nseq, bool l2r, hipStream_t st) {
   if (Tn <= 0) return hipSuccess;
   dim3 grid((Tn + 31) / 32, E / 64);
-  hipLaunchKernelGGL((conv_silu_kernel<T>), grid, dim3(256), 0, st, Tn, E, x, ld_x, conv_w, conv_b,
-                     u, cu, nseq);
+  if (l2r)
+    hipLaunchKernelGGL((conv_silu_kernel<T, true>), grid, dim3(256), 0, st, Tn, E, x, ld_x, conv_w,
+                       conv_b, u, cu, nseq);
+  else
+    hipLaunchKernelGGL((conv_silu_kernel<T, false>), grid, dim3(256), 0, st, Tn, E, x, ld_x, conv_w,
+                       conv_b, u, cu, nseq);
   return hipGetLastError();
 }
 template hipError_t conv_silu<float>(int, int, const float*, long, const float*, const float*,
-                                     float*, const int32_t*, int, hipStream_t);
+                                     float*, const int32_t*, int, bool, hipStream_t);
 template hipError_t conv_silu<bf16>(int, int, const bf16*, long, const bf16*, const bf16*, bf16*,
-                                    const int32_t*, int, hipStream_t);
+                                    const int32_t*, int, bool, hipStream_t);
 
 // ---------------------------------------------------------------------------
 // Fused conv + SiLU + x_proj, bf16 on MFMA.
@@ -69,7 +78,7 @@ template hipError_t conv_silu<bf16>(int, int, const bf16*, long, const bf16*, co
 // gridDim.y = KS > 1 splits the channels over blocks: block (tile, ks)
 // covers channels [ks E/KS, (ks+1) E/KS) and writes its partial sum to slab
 // ks of xdbl ([KS][T][P]); sum_slabs adds the slabs.
-template <int NCS>
+template <int NCS, bool L2R>
 __global__ __launch_bounds__(256) void conv_xproj_kernel(int Tn, int E, int P,
                                                          const bf16* __restrict__ x, long ld_x,
                                                          const bf16* __restrict__ cw,
@@ -85,7 +94,8 @@ __global__ __launch_bounds__(256) void conv_xproj_kernel(int Tn, int E, int P,
   const int t0 = blockIdx.x * 32;
   const int t = t0 + tr;
   const bool tv = t < Tn;
-  const int se = tv ? seq_end_of(cu, nseq, t, Tn) : 0;
+  // the sequence end (R2L) or start (L2R) bounds the conv window
+  const int sb = tv ? (L2R ? seq_start_of(cu, nseq, t) : seq_end_of(cu, nseq, t, Tn)) : 0;
   const int Eb = E / gridDim.y;                 // channels of this block
   const int Ew = Eb / 4;
   const int cbeg = blockIdx.y * Eb + w * Ew;
@@ -107,17 +117,21 @@ __global__ __launch_bounds__(256) void conv_xproj_kernel(int Tn, int E, int P,
   // when the values are used.  (A per-lane branch around a load makes both
   // paths write the same registers and forces an immediate wait.)
   const int tt = min(t, Tn - 1);
-  const int xlast = (tv ? se : tt + 1) - 1;   // last row this lane may read
+  // the last (R2L) or first (L2R) row this lane may read
+  const int xlim = L2R ? (tv ? sb : tt) : (tv ? sb : tt + 1) - 1;
   bool xok[KC];
 #pragma unroll
-  for (int j = 0; j < KC; ++j) xok[j] = tv && t + j < se;
+  for (int j = 0; j < KC; ++j) xok[j] = tv && (L2R ? t - j >= sb : t + j < sb);
   auto load_step = [&](Step& s, int k0) {
     const int c0 = k0 + kh * 8;
 #pragma unroll
     for (int q = 0; q < 4; ++q) s.wv[q] = *(const bf16x8*)(cw + (long)c0 * KC + 8 * q);
     s.bv = *(const bf16x8*)(cb + c0);
 #pragma unroll
-    for (int j = 0; j < KC; ++j) s.xv[j] = *(const bf16x8*)(x + (long)min(tt + j, xlast) * ld_x + c0);
+    for (int j = 0; j < KC; ++j) {
+      const int row = L2R ? max(tt - j, xlim) : min(tt + j, xlim);   // x[t -+ j]
+      s.xv[j] = *(const bf16x8*)(x + (long)row * ld_x + c0);
+    }
 #pragma unroll
     for (int c = 0; c < NCS; ++c) {
       const int row = min(c * 32 + tr, P - 1);
@@ -192,8 +206,8 @@ __global__ __launch_bounds__(256) void sum_slabs_kernel(long n, int ks, const fl
 
 hipError_t conv_xproj_bf16(int Tn, int E, int P, const bf16* x, long ld_x, const bf16* conv_w,
                            const bf16* conv_b, const bf16* x_proj_w, bf16* u_out, float* xdbl,
-                           const int32_t* cu, int nseq, hipStream_t st, float* ws, size_t ws_bytes,
-                           int ncu) {
+                           const int32_t* cu, int nseq, bool l2r, hipStream_t st, float* ws,
+                           size_t ws_bytes, int ncu) {
   if (Tn <= 0) return hipSuccess;
   const int ncs = (P + 31) / 32;
   const int ntiles = (Tn + 31) / 32;
@@ -207,10 +221,14 @@ hipError_t conv_xproj_bf16(int Tn, int E, int P, const bf16* x, long ld_x, const
   }
   float* dst = ks > 1 ? ws : xdbl;
   dim3 grid(ntiles, ks), block(256);
-#define R2L_CX(n)                                                                               \
-  case n:                                                                                       \
-    hipLaunchKernelGGL((conv_xproj_kernel<n>), grid, block, 0, st, Tn, E, P, x, ld_x, conv_w,   \
-                       conv_b, x_proj_w, u_out, dst, cu, nseq);                                 \
+#define R2L_CX(n)                                                                                 \
+  case n:                                                                                         \
+    if (l2r)                                                                                      \
+      hipLaunchKernelGGL((conv_xproj_kernel<n, true>), grid, block, 0, st, Tn, E, P, x, ld_x,     \
+                         conv_w, conv_b, x_proj_w, u_out, dst, cu, nseq);                         \
+    else                                                                                          \
+      hipLaunchKernelGGL((conv_xproj_kernel<n, false>), grid, block, 0, st, Tn, E, P, x, ld_x,    \
+                         conv_w, conv_b, x_proj_w, u_out, dst, cu, nseq);                         \
     break;
   switch (ncs) {
     R2L_CX(1) R2L_CX(2) R2L_CX(3) R2L_CX(4) R2L_CX(5) R2L_CX(6) R2L_CX(7) R2L_CX(8)
@@ -258,12 +276,12 @@ constexpr int kSkTok = 128, kSkK = 32;
 template <int NCS>
 struct SkGeo {
   // A step's operands travel as 1 KB copies (64 lanes x 16 bytes): W_x rows
-  // (16 rows of 64 bytes per copy), x rows t0 .. t0+130, the conv taps and
+  // (16 rows of 64 bytes per copy), the tile's x rows with the conv halo (131), the conv taps and
   // the conv bias.  Copy i of a step is wave (i % 4)'s copy i / 4; the last
   // few slots are padding that reads nothing (zeros land in LDS), so every
   // wave issues the same number of copies per step.
   static constexpr int NW = (NCS * 32 * 4 + 63) / 64;          // W_x rows
-  static constexpr int NX = ((kSkTok + 3) * 4 + 63) / 64;      // x rows t0 .. t0+130
+  static constexpr int NX = ((kSkTok + 3) * 4 + 63) / 64;      // x rows of the tile and its halo
   static constexpr int PER_WAVE = (NW + NX + 2 + 3) / 4;       // + taps, bias
   static constexpr int NI = 4 * PER_WAVE;
   static constexpr int SBYTES = NI * 1024;
@@ -282,7 +300,7 @@ R2L_DEV int sk_swz(int row, int chunk) { return chunk ^ ((row >> 2) & 3); }
 
 }  // namespace
 
-template <int NCS>
+template <int NCS, bool L2R>
 __global__ __launch_bounds__(256, SkGeo<NCS>::BPC) void conv_xproj_sk_kernel(int Tn, int E, int P,
                                                                const bf16* __restrict__ x, long ld_x,
                                                                const bf16* __restrict__ cw,
@@ -337,19 +355,25 @@ __global__ __launch_bounds__(256, SkGeo<NCS>::BPC) void conv_xproj_sk_kernel(int
   // (later copies reload that step into stages that are never read).
   int it_tile = lo / S, it_c0 = (lo % S) * kSkK, it_left = n;
   auto issue = [&](int s) {
+    // stage rows: tokens t0 .. t0+130 (R2L) or t0-3 .. t0+127 (L2R); the
+    // descriptor starts at a real row, and rows before it (L2R, first tile)
+    // get a negative offset that wraps past the range and reads as zero
     const long t0 = (long)it_tile * kSkTok;
-    const long xbytes = (long)(Tn - t0) * ld_x * 2;
+    const long r0 = L2R ? (t0 >= 3 ? t0 - 3 : 0) : t0;
+    const unsigned xshift = L2R ? (unsigned)((t0 - 3 - r0) * ld_x * 2) : 0u;
+    const long xbytes = (long)(Tn - r0) * ld_x * 2;
     const __amdgpu_buffer_rsrc_t rX = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(x + t0 * ld_x), 0, (int)(xbytes < (1L << 30) ? xbytes : (1L << 30)), 0x00020000);
+        (void*)(x + r0 * ld_x), 0, (int)(xbytes < (1L << 30) ? xbytes : (1L << 30)), 0x00020000);
     char* base = stage(s);
 #pragma unroll
     for (int m = 0; m < PW; ++m) {
       // (wave-uniform choices of descriptor and offset)
       const int i = 4 * m + w;
       const bool tap = i == Geo::NW + Geo::NX;
-      const __amdgpu_buffer_rsrc_t r = i < Geo::NW ? rW : i < Geo::NW + Geo::NX ? rX : tap ? rCW : rCB;
+      const bool xcopy = i >= Geo::NW && i < Geo::NW + Geo::NX;
+      const __amdgpu_buffer_rsrc_t r = i < Geo::NW ? rW : xcopy ? rX : tap ? rCW : rCB;
       // lane l lands at base + 1024 i + 16 l
-      sk_dma16(r, base + i * 1024, voff[m], (unsigned)(it_c0 * (tap ? 8 : 2)));
+      sk_dma16(r, base + i * 1024, voff[m] + (xcopy ? xshift : 0u), (unsigned)(it_c0 * (tap ? 8 : 2)));
     }
     if (--it_left > 0) {
       it_c0 += kSkK;
@@ -363,8 +387,12 @@ __global__ __launch_bounds__(256, SkGeo<NCS>::BPC) void conv_xproj_sk_kernel(int
   // up when they start.
   const int tileA = lo / S, tileB = (hi - 1) / S;
   const int tA = tileA * kSkTok + w * 32 + tr, tB = tileB * kSkTok + w * 32 + tr;
-  const int seA = tA < Tn ? seq_end_of(cu, nseq, tA, Tn) : 0;
-  const int seB = tB < Tn ? seq_end_of(cu, nseq, tB, Tn) : 0;
+  // the sequence end (R2L) or start (L2R) bounds each lane's conv window
+  auto bound_of = [&](int t) __attribute__((always_inline)) {
+    return L2R ? seq_start_of(cu, nseq, t) : seq_end_of(cu, nseq, t, Tn);
+  };
+  const int seA = tA < Tn ? bound_of(tA) : 0;
+  const int seB = tB < Tn ? bound_of(tB) : 0;
 
   f32x16 acc[NCS];
   int c_tile = lo / S, c_ks = lo % S;   // step being computed
@@ -381,10 +409,10 @@ __global__ __launch_bounds__(256, SkGeo<NCS>::BPC) void conv_xproj_sk_kernel(int
       for (int r = 0; r < 16; ++r) acc[c][r] = 0.0f;
     const int t = c_tile * kSkTok + w * 32 + tr;
     tv = t < Tn;
-    const int se = c_tile == tileA ? seA : c_tile == tileB ? seB : (tv ? seq_end_of(cu, nseq, t, Tn) : 0);
-    ok1 = t + 1 < se;
-    ok2 = t + 2 < se;
-    ok3 = t + 3 < se;
+    const int se = c_tile == tileA ? seA : c_tile == tileB ? seB : (tv ? bound_of(t) : 0);
+    ok1 = L2R ? t - 1 >= se : t + 1 < se;
+    ok2 = L2R ? t - 2 >= se : t + 2 < se;
+    ok3 = L2R ? t - 3 >= se : t + 3 < se;
     // taps past a sequence end are zeroed only in waves that have such a lane
     masked = __any(tv && !(ok1 && ok2 && ok3));
   };
@@ -423,7 +451,7 @@ __global__ __launch_bounds__(256, SkGeo<NCS>::BPC) void conv_xproj_sk_kernel(int
       i32x4 xr[KC], wt[4];
 #pragma unroll
       for (int j = 0; j < KC; ++j) {
-        const int row = w * 32 + tr + j;
+        const int row = w * 32 + tr + (L2R ? 3 - j : j);   // x[t -+ j]
         xr[j] = *(const i32x4*)(x_s + row * 64 + sk_swz(row, kc) * 16);
       }
 #pragma unroll
@@ -565,15 +593,20 @@ hipError_t conv_sk_sum(int Tn, int E, int P, float* part0, const float* part1, c
 
 hipError_t conv_xproj_bf16_sk(int Tn, int E, int P, const bf16* x, long ld_x, const bf16* conv_w,
                               const bf16* conv_b, const bf16* x_proj_w, float* part0, float* part1,
-                              float* part2, const int32_t* cu, int nseq, int ncu, hipStream_t st) {
+                              float* part2, const int32_t* cu, int nseq, int ncu, bool l2r, hipStream_t st) {
   if (Tn <= 0) return hipSuccess;
   const int ncs = (P + 31) / 32;
   dim3 block(256);
-#define R2L_SK(n)                                                                                \
-  case n:                                                                                        \
-    hipLaunchKernelGGL((conv_xproj_sk_kernel<n>), dim3(sk_blocks<n>(ncu)), block, 0, st,        \
-                       Tn, E, P, x, ld_x, conv_w, conv_b, x_proj_w, part0, part1, part2 - part1, \
-                       cu, nseq);                                                               \
+#define R2L_SK(n)                                                                                 \
+  case n:                                                                                         \
+    if (l2r)                                                                                      \
+      hipLaunchKernelGGL((conv_xproj_sk_kernel<n, true>), dim3(sk_blocks<n>(ncu)), block, 0, st,  \
+                         Tn, E, P, x, ld_x, conv_w, conv_b, x_proj_w, part0, part1,               \
+                         part2 - part1, cu, nseq);                                                \
+    else                                                                                          \
+      hipLaunchKernelGGL((conv_xproj_sk_kernel<n, false>), dim3(sk_blocks<n>(ncu)), block, 0, st, \
+                         Tn, E, P, x, ld_x, conv_w, conv_b, x_proj_w, part0, part1,               \
+                         part2 - part1, cu, nseq);                                                \
     break;
   switch (ncs) {
     R2L_SK(1) R2L_SK(2) R2L_SK(3) R2L_SK(4) R2L_SK(5) R2L_SK(6) R2L_SK(7) R2L_SK(8)

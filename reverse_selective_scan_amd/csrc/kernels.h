@@ -19,17 +19,22 @@ hipError_t gemm_bf16_nt(int M, int N, int K, const bf16* A, long lda, const bf16
 hipError_t gemm_f32_nt(int M, int N, int K, const float* A, long lda, const float* B, long ldb,
                        float* C, long ldc, hipStream_t st);
 
-// Anti-causal depthwise conv + bias + SiLU -> u (act, contiguous [T,E]).
+// Direction of the conv and the scan: l2r = false runs the block over the
+// flipped sequence (anti-causal conv, right-to-left scan: the layer of the
+// pages), l2r = true in the original order (causal conv, left-to-right
+// scan: the L2R control of the pages' ablation).
+
+// Depthwise conv + bias + SiLU -> u (act, contiguous [T,E]).
 template <typename T>
 hipError_t conv_silu(int T_, int E, const T* x, long ld_x, const T* conv_w, const T* conv_b,
-                     T* u, const int32_t* cu, int nseq, hipStream_t st);
+                     T* u, const int32_t* cu, int nseq, bool l2r, hipStream_t st);
 // Fused conv + SiLU + x_proj (bf16, MFMA): xdbl f32 [T, P] with P = R+2N;
 // u_out optional.  Requires E % 64 == 0 and P <= 256.
 // ws (optional, ws_bytes): scratch for splitting the channels over several
 // blocks per 32-token tile when there are few tiles (not with u_out).
 hipError_t conv_xproj_bf16(int T_, int E, int P, const bf16* x, long ld_x, const bf16* conv_w,
                            const bf16* conv_b, const bf16* x_proj_w, bf16* u_out, float* xdbl,
-                           const int32_t* cu, int nseq, hipStream_t st, float* ws = nullptr,
+                           const int32_t* cu, int nseq, bool l2r, hipStream_t st, float* ws = nullptr,
                            size_t ws_bytes = 0, int ncu = 0);
 
 // The same for large inputs, split along K over one or two blocks per CU
@@ -38,12 +43,13 @@ hipError_t conv_xproj_bf16(int T_, int E, int P, const bf16* x, long ld_x, const
 // E % 64 == 0, P <= 256 and ceil(T / 128) >= ncu.
 hipError_t conv_xproj_bf16_sk(int T_, int E, int P, const bf16* x, long ld_x, const bf16* conv_w,
                               const bf16* conv_b, const bf16* x_proj_w, float* part0, float* part1,
-                              float* part2, const int32_t* cu, int nseq, int ncu, hipStream_t st);
+                              float* part2, const int32_t* cu, int nseq, int ncu, bool l2r, hipStream_t st);
 hipError_t conv_sk_sum(int T_, int E, int P, float* part0, const float* part1, const float* part2, int ncu,
                        hipStream_t st);
 
-// Chunk planning for the scan: sanitised cu_seqlens and the chunk table.
-hipError_t plan_chunks(const int32_t* cu, int nseq, int T_, int Lc, int max_chunks,
+// Chunk planning for the scan: sanitised cu_seqlens and the chunk table
+// (chunks cut from the end the scan starts at).
+hipError_t plan_chunks(const int32_t* cu, int nseq, int T_, int Lc, int max_chunks, bool l2r,
                        int32_t* cu_clean, ChunkDesc* chunks, int32_t* n_chunks, hipStream_t st);
 
 struct ScanArgs {
@@ -63,11 +69,12 @@ struct ScanArgs {
   void* y;
   const ChunkDesc* chunks; const int32_t* n_chunks; int max_chunks;
   float* sumS; float* sumP;    // [max_chunks][16][E] each
+  bool l2r;                    // scan direction (see above)
 };
 
 // Pass 1 (only when some sequence spans several chunks): per-chunk decay
 // product and local state.  Pass 2: outputs, with the carry-in of each chunk
-// combined from the summaries of the chunks to its right.
+// combined from the summaries of the chunks before it in scan order.
 template <typename T>
 hipError_t scan_summary(const ScanArgs& a, bool fused, hipStream_t st);
 template <typename T>

@@ -11,6 +11,9 @@
 // blocks of 32 tokens whose per-(token, channel) inputs are prepared
 // cooperatively (conv + SiLU from x, SiLU(z), dt on MFMA) one block at a time,
 // with the next block's global loads in flight meanwhile.
+// With L2R (the left-to-right control of §4.4, Table 4) everything runs
+// mirrored: causal conv, time walked left to right, chunks cut from the
+// sequence start.
 // Long sequences are cut into chunks so that enough blocks exist to fill the
 // GPU.  A first pass computes, per chunk, the state at its left edge from a
 // zero carry (S) and the decay across it (P = exp(A * sum dt)); the main pass
@@ -28,8 +31,8 @@ constexpr int NS = 16;    // d_state (§4.1)
 
 // ---------------------------------------------------------------------------
 // chunk planning (one block): sanitised cu_seqlens (clamped to [0, T] and
-// made non-decreasing) and the chunk table, rightmost chunk of each
-// sequence first.
+// made non-decreasing) and the chunk table, each sequence's chunks in scan
+// order (the chunk the scan starts in first).
 // ---------------------------------------------------------------------------
 // Exclusive block-wide scan of one value per thread (256 threads), max or sum,
 // Hillis-Steele in LDS: 8 steps.
@@ -51,7 +54,7 @@ R2L_DEV int block_exclusive_scan(int v, int* buf) {
 }
 
 __global__ __launch_bounds__(256) void plan_chunks_kernel(const int32_t* __restrict__ cu, int nseq,
-                                                          int Tn, int Lc, int max_chunks,
+                                                          int Tn, int Lc, int max_chunks, int l2r,
                                                           int32_t* __restrict__ cu_clean,
                                                           ChunkDesc* __restrict__ chunks,
                                                           int32_t* __restrict__ n_chunks) {
@@ -86,8 +89,13 @@ __global__ __launch_bounds__(256) void plan_chunks_kernel(const int32_t* __restr
     for (int j = 0; j < nc; ++j) {
       if (base + j >= max_chunks) break;
       ChunkDesc d;
-      d.hi = send - j * Lc;
-      d.lo = max(slo, d.hi - Lc);
+      if (l2r) {            // cut from the sequence start, leftmost first
+        d.lo = slo + j * Lc;
+        d.hi = min(send, d.lo + Lc);
+      } else {              // cut from the sequence end, rightmost first
+        d.hi = send - j * Lc;
+        d.lo = max(slo, d.hi - Lc);
+      }
       d.seq_lo = slo;
       d.seq_end = send;
       d.first = base;
@@ -100,10 +108,10 @@ __global__ __launch_bounds__(256) void plan_chunks_kernel(const int32_t* __restr
   }
 }
 
-hipError_t plan_chunks(const int32_t* cu, int nseq, int Tn, int Lc, int max_chunks,
+hipError_t plan_chunks(const int32_t* cu, int nseq, int Tn, int Lc, int max_chunks, bool l2r,
                        int32_t* cu_clean, ChunkDesc* chunks, int32_t* n_chunks, hipStream_t st) {
   hipLaunchKernelGGL(plan_chunks_kernel, dim3(1), dim3(256), 0, st, cu, nseq, Tn, Lc, max_chunks,
-                     cu_clean, chunks, n_chunks);
+                     l2r ? 1 : 0, cu_clean, chunks, n_chunks);
   return hipGetLastError();
 }
 
@@ -191,7 +199,7 @@ template <> R2L_DEV float softplus_dt<bf16>(float v) {
 //   C  same layout as A: y = (sum of the 4 partial C.h + Dskip u) SiLU(z),
 //      one 16-byte store per thread.
 // ---------------------------------------------------------------------------
-template <typename T, bool FUSED, bool SUMMARY, int KS>
+template <typename T, bool FUSED, bool SUMMARY, int KS, bool L2R>
 __global__ __launch_bounds__(256, 2) void scan_kernel(ScanArgs a) {
   constexpr int TB = 32;
   constexpr bool MFMA_DT = FUSED && KS > 0;
@@ -216,7 +224,7 @@ __global__ __launch_bounds__(256, 2) void scan_kernel(ScanArgs a) {
   const int ci = blockIdx.x / NB, cblk = blockIdx.x % NB;
   if (ci >= *a.n_chunks) return;
   const ChunkDesc d = a.chunks[ci];
-  if (SUMMARY && d.j == d.n_in_seq - 1) return;  // leftmost chunk: its summary is never used
+  if (SUMMARY && d.j == d.n_in_seq - 1) return;  // last chunk in scan order: its summary is never used
   const int tid = threadIdx.x;
   const int lane = lane_id(), w = wave_id();
   const int e0 = cblk * 64;
@@ -272,7 +280,7 @@ __global__ __launch_bounds__(256, 2) void scan_kernel(ScanArgs a) {
     dtb_col = a.dt_b[e0 + dcol];
   }
 
-  // carry into this chunk from the chunks to its right
+  // carry into this chunk from the chunks before it in scan order
   f32x4 h = {0.0f, 0.0f, 0.0f, 0.0f};
   if (!SUMMARY) {
     for (int jj = 0; jj < d.j; ++jj) {
@@ -313,10 +321,15 @@ __global__ __launch_bounds__(256, 2) void scan_kernel(ScanArgs a) {
   auto issue = [&](int blo, int bhi) {
     const int rows = bhi - blo;
     if constexpr (FUSED) {
-      // the conv window reaches 3 rows past the block, never past the sequence
-      const Rsrc rX = row_window(xin, blo, ldx_b, min(d.seq_end, bhi + 3) - blo);
+      // the conv window reaches 3 rows past the block (R2L) or before it
+      // (L2R), never out of the sequence; px[j] = x[t + j] (R2L) or x[t - j]
+      // (L2R), rows outside the window reading as zero (a negative L2R
+      // offset wraps past the window's end)
+      const int wb = L2R ? max(d.seq_lo, blo - 3) : blo;
+      const Rsrc rX = row_window(xin, wb, ldx_b, (L2R ? bhi : min(d.seq_end, bhi + 3)) - wb);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) raw_load(px[j], rX, offX + (unsigned)(j * ldx_b));
+      for (int j = 0; j < 4; ++j)
+        raw_load(px[j], rX, offX + (unsigned)((L2R ? blo - wb - j : j) * ldx_b));
       const Rsrc rD = row_window(a.xdbl, blo, ldp_b, rows);
       if constexpr (MFMA_DT) {
 #pragma unroll
@@ -341,10 +354,13 @@ __global__ __launch_bounds__(256, 2) void scan_kernel(ScanArgs a) {
   // SiLU(z) and Dskip*u of this thread's (row, 8 channels): phase A makes
   // them, phase C of the same block uses them.
   float g8[8], du8[8];
-  int bhi = d.hi;
-  if (bhi > d.lo) issue(max(d.lo, bhi - TB), bhi);
-  for (; bhi > d.lo; bhi -= TB) {
-    const int blo = max(d.lo, bhi - TB);
+  // the chunk's blocks of TB tokens in scan order; only the last is partial
+  const int nblk = (d.hi - d.lo + TB - 1) / TB;
+  auto blo_of = [&](int k) { return L2R ? d.lo + k * TB : max(d.lo, d.hi - (k + 1) * TB); };
+  auto bhi_of = [&](int k) { return L2R ? min(d.hi, d.lo + (k + 1) * TB) : d.hi - k * TB; };
+  if (nblk > 0) issue(blo_of(0), bhi_of(0));
+  for (int kb = 0; kb < nblk; ++kb) {
+    const int blo = blo_of(kb), bhi = bhi_of(kb);
     const int nt = bhi - blo;
     // ---------------- A: consume this block's prefetched inputs ----------------
     // (rows past the block read as zeros, or as the real rows of the conv
@@ -408,7 +424,7 @@ __global__ __launch_bounds__(256, 2) void scan_kernel(ScanArgs a) {
       bc_s[r8][c8] = f32x4{pbc[0], pbc[1], pbc[2], pbc[3]};
     }
     // the next block's loads go out now and land during this block's compute
-    if (bhi - TB > d.lo) issue(max(d.lo, bhi - 2 * TB), bhi - TB);
+    if (kb + 1 < nblk) issue(blo_of(kb + 1), bhi_of(kb + 1));
     __syncthreads();
     // ---------------- M: dt = softplus(delta . W_dt^T + b) ----------------
     if constexpr (FUSED) {
@@ -445,7 +461,7 @@ __global__ __launch_bounds__(256, 2) void scan_kernel(ScanArgs a) {
       }
       __syncthreads();
     }
-    // ---------------- B: the recurrence, right to left ----------------
+    // ---------------- B: the recurrence, in scan order ----------------
     auto compute = [&](int r, float2 p, float bsel, f32x4 Cv) __attribute__((always_inline)) {
       f32x4 hd;
 #pragma unroll
@@ -464,27 +480,32 @@ __global__ __launch_bounds__(256, 2) void scan_kernel(ScanArgs a) {
       float2 Pq[LA];
       float Bq[LA];
       f32x4 Cq[LA];
+      auto row = [](int k) { return L2R ? k : TB - 1 - k; };   // k-th row in scan order
 #pragma unroll
       for (int k = 0; k < LA; ++k) {
-        Pq[k] = pre_s[TB - 1 - k][lane];
-        Bq[k] = bsrc[(TB - 1 - k) * 32];
-        Cq[k] = SUMMARY ? f32x4{} : bc_s[TB - 1 - k][4 + w];
+        Pq[k] = pre_s[row(k)][lane];
+        Bq[k] = bsrc[row(k) * 32];
+        Cq[k] = SUMMARY ? f32x4{} : bc_s[row(k)][4 + w];
       }
 #pragma unroll
       for (int k = 0; k < TB; ++k) {
-        const int r = TB - 1 - k, sl = k % LA;
+        const int r = row(k), sl = k % LA;
         const float2 p = Pq[sl];
         const float bv = Bq[sl];
         const f32x4 Cv = Cq[sl];
         if (k + LA < TB) {
-          Pq[sl] = pre_s[r - LA][lane];
-          Bq[sl] = bsrc[(r - LA) * 32];
-          if constexpr (!SUMMARY) Cq[sl] = bc_s[r - LA][4 + w];
+          const int rn = row(k + LA);
+          Pq[sl] = pre_s[rn][lane];
+          Bq[sl] = bsrc[rn * 32];
+          if constexpr (!SUMMARY) Cq[sl] = bc_s[rn][4 + w];
         }
         compute(r, p, bv, Cv);
       }
     } else {
-      for (int r = nt - 1; r >= 0; --r) compute(r, pre_s[r][lane], bsrc[r * 32], bc_s[r][4 + w]);
+      for (int k = 0; k < nt; ++k) {
+        const int r = L2R ? k : nt - 1 - k;
+        compute(r, pre_s[r][lane], bsrc[r * 32], bc_s[r][4 + w]);
+      }
     }
     __syncthreads();
     // ---------------- C: combine and store ----------------
@@ -517,23 +538,28 @@ __global__ __launch_bounds__(256, 2) void scan_kernel(ScanArgs a) {
   }
 }
 
-template <typename T, bool SUMMARY>
-static hipError_t launch_scan(const ScanArgs& a, bool fused, hipStream_t st) {
-  const int nblocks = a.max_chunks * (a.E / 64);
-  if (nblocks <= 0) return hipSuccess;
-  dim3 grid(nblocks), block(256);
+template <typename T, bool SUMMARY, bool L2R>
+static void launch_scan_dir(const ScanArgs& a, bool fused, hipStream_t st) {
+  dim3 grid(a.max_chunks * (a.E / 64)), block(256);
   if (!fused) {
-    hipLaunchKernelGGL((scan_kernel<T, false, SUMMARY, 0>), grid, block, 0, st, a);
+    hipLaunchKernelGGL((scan_kernel<T, false, SUMMARY, 0, L2R>), grid, block, 0, st, a);
   } else if constexpr (std::is_same<T, float>::value) {
-    hipLaunchKernelGGL((scan_kernel<T, true, SUMMARY, 0>), grid, block, 0, st, a);
+    hipLaunchKernelGGL((scan_kernel<T, true, SUMMARY, 0, L2R>), grid, block, 0, st, a);
   } else {
     const int ks = (a.R + 31) / 32;
-    if (ks > 8) hipLaunchKernelGGL((scan_kernel<T, true, SUMMARY, 0>), grid, block, 0, st, a);
-    else if (ks <= 1) hipLaunchKernelGGL((scan_kernel<T, true, SUMMARY, 1>), grid, block, 0, st, a);
-    else if (ks <= 2) hipLaunchKernelGGL((scan_kernel<T, true, SUMMARY, 2>), grid, block, 0, st, a);
-    else if (ks <= 4) hipLaunchKernelGGL((scan_kernel<T, true, SUMMARY, 4>), grid, block, 0, st, a);
-    else hipLaunchKernelGGL((scan_kernel<T, true, SUMMARY, 8>), grid, block, 0, st, a);
+    if (ks > 8) hipLaunchKernelGGL((scan_kernel<T, true, SUMMARY, 0, L2R>), grid, block, 0, st, a);
+    else if (ks <= 1) hipLaunchKernelGGL((scan_kernel<T, true, SUMMARY, 1, L2R>), grid, block, 0, st, a);
+    else if (ks <= 2) hipLaunchKernelGGL((scan_kernel<T, true, SUMMARY, 2, L2R>), grid, block, 0, st, a);
+    else if (ks <= 4) hipLaunchKernelGGL((scan_kernel<T, true, SUMMARY, 4, L2R>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((scan_kernel<T, true, SUMMARY, 8, L2R>), grid, block, 0, st, a);
   }
+}
+
+template <typename T, bool SUMMARY>
+static hipError_t launch_scan(const ScanArgs& a, bool fused, hipStream_t st) {
+  if (a.max_chunks * (a.E / 64) <= 0) return hipSuccess;
+  if (a.l2r) launch_scan_dir<T, SUMMARY, true>(a, fused, st);
+  else launch_scan_dir<T, SUMMARY, false>(a, fused, st);
   return hipGetLastError();
 }
 

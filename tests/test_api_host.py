@@ -111,6 +111,12 @@ def test_layer_fwd_rejects_bad_arguments():
     assert _layer(wsb=1024) == B.R2L_ERR_WORKSPACE                 # smaller than the query
 
 
+def test_layer_fwd_accepts_the_direction_flag():
+    assert _layer(flags=B.R2L_FLAG_L2R, wsb=16) == B.R2L_ERR_WORKSPACE
+    assert _layer(flags=B.R2L_FLAG_L2R | B.R2L_FLAG_NO_LN, wsb=16) == B.R2L_ERR_WORKSPACE
+    assert _layer(flags=0x4) == B.R2L_ERR_INVALID_ARG
+
+
 def test_layer_fwd_no_ln_needs_no_ln_weights():
     # with the flag, missing LN weights are fine: the call then only fails at the workspace check
     assert _layer(flags=B.R2L_FLAG_NO_LN, w=_weights(ln_w=None, ln_b=None), wsb=16) == B.R2L_ERR_WORKSPACE
@@ -128,21 +134,29 @@ def test_conv_scan_gemm_reject_bad_arguments():
     lib = B.lib()
     d = _dims()
     # conv: no output requested / xdbl without x_proj / ld_x < E
-    assert lib.r2l_conv_fwd(C.byref(d), B.R2L_BF16, FAKE, 8192, FAKE, FAKE, None, None, None, FAKE, 1, 10, 10,
+    assert lib.r2l_conv_fwd(C.byref(d), B.R2L_BF16, 0, FAKE, 8192, FAKE, FAKE, None, None, None, FAKE, 1, 10, 10,
                             None) == B.R2L_ERR_INVALID_ARG
-    assert lib.r2l_conv_fwd(C.byref(d), B.R2L_BF16, FAKE, 8192, FAKE, FAKE, None, FAKE, FAKE, FAKE, 1, 10, 10,
+    assert lib.r2l_conv_fwd(C.byref(d), B.R2L_BF16, 0, FAKE, 8192, FAKE, FAKE, None, FAKE, FAKE, FAKE, 1, 10, 10,
                             None) == B.R2L_ERR_INVALID_ARG
-    assert lib.r2l_conv_fwd(C.byref(d), B.R2L_BF16, FAKE, 100, FAKE, FAKE, None, FAKE, None, FAKE, 1, 10, 10,
+    assert lib.r2l_conv_fwd(C.byref(d), B.R2L_BF16, 0, FAKE, 100, FAKE, FAKE, None, FAKE, None, FAKE, 1, 10, 10,
                             None) == B.R2L_ERR_INVALID_ARG
-    assert lib.r2l_conv_fwd(C.byref(d), B.R2L_BF16, FAKE, 8190, FAKE, FAKE, None, FAKE, None, FAKE, 1, 10, 10,
+    assert lib.r2l_conv_fwd(C.byref(d), B.R2L_BF16, 0, FAKE, 8190, FAKE, FAKE, None, FAKE, None, FAKE, 1, 10, 10,
                             None) == B.R2L_ERR_INVALID_ARG   # bf16 rows must stay 16-byte aligned
     # scan: missing dt / small ld / missing workspace
-    assert lib.r2l_scan_fwd(C.byref(d), B.R2L_F32, FAKE, 4096, None, 4096, FAKE, FAKE, FAKE, 16, None, None, 0,
+    assert lib.r2l_scan_fwd(C.byref(d), B.R2L_F32, 0, FAKE, 4096, None, 4096, FAKE, FAKE, FAKE, 16, None, None, 0,
                             FAKE, FAKE, 1, 10, 10, FAKE, 1 << 30, None) == B.R2L_ERR_INVALID_ARG
-    assert lib.r2l_scan_fwd(C.byref(d), B.R2L_F32, FAKE, 4000, FAKE, 4096, FAKE, FAKE, FAKE, 16, None, None, 0,
+    assert lib.r2l_scan_fwd(C.byref(d), B.R2L_F32, 0, FAKE, 4000, FAKE, 4096, FAKE, FAKE, FAKE, 16, None, None, 0,
                             FAKE, FAKE, 1, 10, 10, FAKE, 1 << 30, None) == B.R2L_ERR_INVALID_ARG
-    assert lib.r2l_scan_fwd(C.byref(d), B.R2L_F32, FAKE, 4096, FAKE, 4096, FAKE, FAKE, FAKE, 16, None, None, 0,
+    assert lib.r2l_scan_fwd(C.byref(d), B.R2L_F32, 0, FAKE, 4096, FAKE, 4096, FAKE, FAKE, FAKE, 16, None, None, 0,
                             FAKE, FAKE, 1, 10, 10, None, 0, None) == B.R2L_ERR_WORKSPACE
+    # unknown flag bits (R2L_FLAG_NO_LN means nothing to the conv or the scan)
+    assert lib.r2l_conv_fwd(C.byref(d), B.R2L_BF16, B.R2L_FLAG_NO_LN, FAKE, 8192, FAKE, FAKE, None, FAKE, None,
+                            FAKE, 1, 10, 10, None) == B.R2L_ERR_INVALID_ARG
+    assert lib.r2l_scan_fwd(C.byref(d), B.R2L_F32, 0x8, FAKE, 4096, FAKE, 4096, FAKE, FAKE, FAKE, 16, None, None,
+                            0, FAKE, FAKE, 1, 10, 10, FAKE, 1 << 30, None) == B.R2L_ERR_INVALID_ARG
+    # the direction flag passes validation (then fails at the workspace check)
+    assert lib.r2l_scan_fwd(C.byref(d), B.R2L_F32, B.R2L_FLAG_L2R, FAKE, 4096, FAKE, 4096, FAKE, FAKE, FAKE, 16,
+                            None, None, 0, FAKE, FAKE, 1, 10, 10, None, 0, None) == B.R2L_ERR_WORKSPACE
     # gemm
     assert lib.r2l_gemm_nt(B.R2L_BF16, 10, 10, 12, FAKE, 12, FAKE, 12, FAKE, 10, 0, None, 0, None) == B.R2L_ERR_UNSUPPORTED
     assert lib.r2l_gemm_nt(B.R2L_BF16, 10, 10, 16, FAKE, 8, FAKE, 16, FAKE, 10, 0, None, 0, None) == B.R2L_ERR_INVALID_ARG
