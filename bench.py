@@ -234,13 +234,16 @@ def main():
 
 
 KERNEL_SOURCES = {  # the source file that defines each timed kernel
-    "in_proj_gemm": "gemm.hip", "out_proj_gemm": "gemm.hip", "conv_xproj": "conv.hip", "conv_sum": "conv.hip",
+    "in_proj_gemm": "gemm.hip", "out_proj_gemm": "gemm.hip", "out_proj_tail": "gemm.hip",
+    "out_proj_reduce": "gemm.hip", "conv_xproj": "conv.hip", "conv_sum": "conv.hip",
     "scan_main": "scan.hip", "scan_summary": "scan.hip", "ln_gate": "ln.hip", "plan_chunks": "scan.hip",
 }
 ROCPROF_NAMES = {  # substring of the demangled kernel name in rocprofv3 output
-    "in_proj_gemm": "gemm_bf16_big_kernel<false, 4>", "out_proj_gemm": "gemm_bf16_big_kernel<true, 8>",
-    "conv_xproj": "conv_xproj_sk_kernel", "conv_sum": "sk_sum_kernel", "scan_main": "false, 4>(r2l::ScanArgs)",
-    "scan_summary": "true, 4>(r2l::ScanArgs)", "ln_gate": "ln_gate_kernel",
+    "in_proj_gemm": "gemm_bf16_big_kernel<false, 4, false>", "out_proj_gemm": "gemm_bf16_big_kernel<true, 8, false>",
+    "out_proj_tail": "gemm_bf16_big_kernel<true, 8, true>", "out_proj_reduce": "gemm_tail_reduce_kernel<true, 8>",
+    "conv_xproj": "conv_xproj_sk_kernel<5, false>", "conv_sum": "sk_sum_kernel",
+    "scan_main": "E, false, 4, false>(r2l::ScanArgs)", "scan_summary": "E, true, 4, false>(r2l::ScanArgs)",
+    "ln_gate": "ln_gate_kernel",
 }
 PROFILE_JSON = os.path.join(ROOT, "profiles", "traffic_serve_b8.json")
 

@@ -199,12 +199,12 @@ R2L_DEV void big_tile(int lid, int nTm, int nTn, int& tm, int& tn) {
 
 }  // namespace
 
-// n_dp = number of whole tiles of the main launch.  splits == 0: block b
-// computes tile xcd_remap(b) of those, over all of K, into C.  splits > 0
-// (the tail launch): block u computes K-steps [s ksteps, (s+1) ksteps) with
+// n_dp = number of whole tiles of the main launch.  !TAIL: block b
+// computes tile xcd_remap(b) of those, over all of K, into C.  TAIL (the
+// tail launch, splits > 0): block u computes K-steps [s ksteps, (s+1) ksteps) with
 // s = u % splits of tile n_dp + u / splits, as an fp32 partial sum into
 // part[u][256][256].
-template <bool OUT_F32, int G>
+template <bool OUT_F32, int G, bool TAIL>
 __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(int M, int N, int K,
                                                                const bf16* __restrict__ A, long lda,
                                                                const bf16* __restrict__ B, long ldb,
@@ -223,8 +223,8 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(int M, int N, int
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int wm = (wave >> 1) * 128, wn = (wave & 1) * 128;
   const int nTm = (M + BM - 1) / BM, nTn = (N + BN - 1) / BN;
-  const int lid = splits ? n_dp + (int)blockIdx.x / splits : xcd_remap(blockIdx.x, n_dp);
-  const int kbeg = splits ? ((int)blockIdx.x % splits) * ksteps : 0;
+  const int lid = TAIL ? n_dp + (int)blockIdx.x / splits : xcd_remap(blockIdx.x, n_dp);
+  const int kbeg = TAIL ? ((int)blockIdx.x % splits) * ksteps : 0;
   int tm, tn;
   big_tile<G>(lid, nTm, nTn, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
@@ -245,7 +245,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(int M, int N, int
     voff[i] = i < LPT / 2 ? (unsigned)(((long)row * lda + kc * 8) * 2)
                           : (unsigned)(((long)(row - BM) * ldb + kc * 8) * 2);
   }
-  const int nk = splits ? ksteps : K / BK;
+  const int nk = TAIL ? ksteps : K / BK;
   auto issue = [&](int s, int kt) {  // k-step kt -> stage s (past the end: reload the last step)
     char* base = stage(s);
     const unsigned kb = (unsigned)((kbeg + min(kt, nk - 1)) * BK * 2);
@@ -347,7 +347,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(int M, int N, int
 
   // acc[i][j] register 4q+e holds C[m][n] with m = m0+wm+32i+(lane&31) and
   // n = n0+wn+32j+8q+4*(lane>>5)+e: four consecutive columns per store.
-  if (splits) {
+  if constexpr (TAIL) {
     float* pt = part + (long)blockIdx.x * (BM * BN);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -481,15 +481,15 @@ static void launch_big(int M, int N, int K, const bf16* A, long lda, const bf16*
                        long ldc, bool out_f32, int n_dp, int rem, int splits, int nk, float* ws,
                        hipStream_t st) {
   if (out_f32)
-    hipLaunchKernelGGL((gemm_bf16_big_kernel<true, G>), dim3(n_dp), dim3(256), 0, st, M, N, K, A, lda,
+    hipLaunchKernelGGL((gemm_bf16_big_kernel<true, G, false>), dim3(n_dp), dim3(256), 0, st, M, N, K, A, lda,
                        B, ldb, C, ldc, n_dp, 0, 0, (float*)nullptr);
   else
-    hipLaunchKernelGGL((gemm_bf16_big_kernel<false, G>), dim3(n_dp), dim3(256), 0, st, M, N, K, A, lda,
+    hipLaunchKernelGGL((gemm_bf16_big_kernel<false, G, false>), dim3(n_dp), dim3(256), 0, st, M, N, K, A, lda,
                        B, ldb, C, ldc, n_dp, 0, 0, (float*)nullptr);
   if (splits) {
     const int ksteps = nk / splits;
     // (the kernel's OUT_F32 only shapes the direct epilogue; partials are fp32)
-    hipLaunchKernelGGL((gemm_bf16_big_kernel<true, G>), dim3(rem * splits), dim3(256), 0, st, M, N, K,
+    hipLaunchKernelGGL((gemm_bf16_big_kernel<true, G, true>), dim3(rem * splits), dim3(256), 0, st, M, N, K,
                        A, lda, B, ldb, C, ldc, n_dp, splits, ksteps, ws);
     if (out_f32)
       hipLaunchKernelGGL((gemm_tail_reduce_kernel<true, G>), dim3(rem * (kBigBM / 4)), dim3(256), 0, st, M,
