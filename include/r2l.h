@@ -174,6 +174,34 @@ int r2l_scan_fwd(const r2l_dims* dims, r2l_dtype act, uint32_t flags, const void
                  int32_t max_seqlen, void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * r2l_scan_bwd -- the gradient of r2l_scan_fwd (the backward of the
+ * reverse selective scan, for training the sidecar: §3.5, plug-in mode).
+ * Given dy, the gradient of a loss with respect to y_out of r2l_scan_fwd on
+ * the same inputs, it writes the gradients with respect to every input:
+ *   du, ddt: f32 [n_tokens, E] contiguous;  dA_log: f32 [E, N] (w.r.t.
+ *   A_log, summed over tokens);  dB, dC: f32 [n_tokens, N] contiguous;
+ *   dDskip: f32 [E] (required iff Dskip != NULL);  dz: f32 [n_tokens, E]
+ *   contiguous (required iff z != NULL).
+ * Inputs as in r2l_scan_fwd; dy: act [n_tokens, E] (row stride ld_dy, the
+ * same alignment rules as u).  flags: 0 (R2L_FLAG_L2R returns
+ * R2L_ERR_UNSUPPORTED: the backward runs the default direction only).
+ * Method: a first sweep recomputes the states right to left and keeps the
+ * state entering every 16-token sub-block; a second sweep runs the adjoint
+ * recurrence left to right, recomputing each sub-block's states; sums over
+ * channels and sequences are taken in a fixed order (deterministic).  Each
+ * sequence is walked by one block per 64 channels (no time chunks).
+ * workspace: r2l_scan_bwd_workspace_bytes(...) bytes, 256-byte aligned.
+ * ---------------------------------------------------------------------- */
+size_t r2l_scan_bwd_workspace_bytes(const r2l_dims* dims, int64_t n_tokens, int32_t nseq);
+
+int r2l_scan_bwd(const r2l_dims* dims, r2l_dtype act, uint32_t flags, const void* u, int64_t ld_u,
+                 const float* dt, int64_t ld_dt, const float* A_log, const float* B, const float* C,
+                 int64_t ld_bc, const float* Dskip, const void* z, int64_t ld_z, const void* dy,
+                 int64_t ld_dy, float* du, float* ddt, float* dA_log, float* dB, float* dC,
+                 float* dDskip, float* dz, const int32_t* cu_seqlens, int32_t nseq, int64_t n_tokens,
+                 void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
  * r2l_gemm_nt -- the dense projection used by the layer (in_proj, out_proj):
  *   C[m, n] = sum_k A[m, k] * B[n, k]      (C = A @ B^T, fp32 accumulate).
  * A: act [M, K] (row stride lda); B: act [N, K] (row stride ldb);

@@ -53,6 +53,9 @@ _SIGS = {
     "r2l_scan_workspace_bytes": (_SZ, [C.POINTER(Dims), _I64, _I32, _I32]),
     "r2l_scan_fwd": (C.c_int, [C.POINTER(Dims), C.c_int, C.c_uint32, _P, _I64, _P, _I64, _P, _P, _P, _I64, _P,
                                _P, _I64, _P, _P, _I32, _I64, _I32, _P, _SZ, _P]),
+    "r2l_scan_bwd_workspace_bytes": (_SZ, [C.POINTER(Dims), _I64, _I32]),
+    "r2l_scan_bwd": (C.c_int, [C.POINTER(Dims), C.c_int, C.c_uint32, _P, _I64, _P, _I64, _P, _P, _P, _I64, _P,
+                               _P, _I64, _P, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _I64, _P, _SZ, _P]),
     "r2l_gemm_nt": (C.c_int, [C.c_int, _I64, _I64, _I64, _P, _I64, _P, _I64, _P, _I64, C.c_int, _P, C.c_size_t, _P]),
     "r2l_timing_enable": (C.c_int, [C.c_int]),
     "r2l_timing_reset": (C.c_int, []),
@@ -222,6 +225,42 @@ def r2l_scan_fwd(u: torch.Tensor, dt: torch.Tensor, A_log: torch.Tensor, B: torc
         B.stride(0), _ptr(Dskip), _ptr(z), z.stride(0) if z is not None else 0, _ptr(y), _ptr(cu_dev), nseq, T,
         max_seqlen, _ptr(ws), ws.numel(), _stream()))
     return y
+
+
+def r2l_scan_bwd(u: torch.Tensor, dt: torch.Tensor, A_log: torch.Tensor, B: torch.Tensor, C_: torch.Tensor,
+                 cu_seqlens, dy: torch.Tensor, *, Dskip: Optional[torch.Tensor] = None,
+                 z: Optional[torch.Tensor] = None, dt_rank: int = 1) -> Dict[str, torch.Tensor]:
+    """Gradient of r2l_scan_fwd: given dy = dL/dy_out, returns fp32 tensors
+    du, ddt, dA_log, dB, dC (and dDskip, dz when Dskip, z are given)."""
+    _need(u, "u", contiguous=False)
+    act = _act(u)
+    T, E = u.shape
+    for t, n in ((u, "u"), (dt, "dt"), (B, "B"), (C_, "C"), (dy, "dy")):
+        if t.stride(1) != 1:
+            raise ValueError(f"{n} rows must be contiguous")
+    if B.stride(0) != C_.stride(0):
+        raise ValueError("B and C must share a row stride")
+    _need(dt, "dt", torch.float32, contiguous=False)
+    _need(dy, "dy", u.dtype, contiguous=False)
+    _need(A_log, "A_log", torch.float32)
+    N = A_log.shape[1]
+    cu_dev, nseq, _ = cu_seqlens_device(cu_seqlens, T, u.device)
+    d = Dims(d_model=64, d_inner=E, d_state=N, dt_rank=dt_rank, d_conv=4)
+    f32 = dict(dtype=torch.float32, device=u.device)
+    out = {"du": torch.empty(T, E, **f32), "ddt": torch.empty(T, E, **f32), "dA_log": torch.empty(E, N, **f32),
+           "dB": torch.empty(T, N, **f32), "dC": torch.empty(T, N, **f32)}
+    if Dskip is not None:
+        out["dDskip"] = torch.empty(E, **f32)
+    if z is not None:
+        out["dz"] = torch.empty(T, E, **f32)
+    wsb = int(lib().r2l_scan_bwd_workspace_bytes(C.byref(d), T, nseq))
+    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=u.device)
+    _check("r2l_scan_bwd", lib().r2l_scan_bwd(
+        C.byref(d), act, 0, _ptr(u), u.stride(0), _ptr(dt), dt.stride(0), _ptr(A_log), _ptr(B), _ptr(C_),
+        B.stride(0), _ptr(Dskip), _ptr(z), z.stride(0) if z is not None else 0, _ptr(dy), dy.stride(0),
+        _ptr(out["du"]), _ptr(out["ddt"]), _ptr(out["dA_log"]), _ptr(out["dB"]), _ptr(out["dC"]),
+        _ptr(out.get("dDskip")), _ptr(out.get("dz")), _ptr(cu_dev), nseq, T, _ptr(ws), ws.numel(), _stream()))
+    return out
 
 
 def r2l_gemm_nt(A: torch.Tensor, B: torch.Tensor, *, out_f32: bool = False,

@@ -172,6 +172,30 @@ ScanPlan plan_scan(int E, int64_t T, int32_t nseq, int32_t max_seqlen, size_t ba
   return p;
 }
 
+// Workspace of the scan backward: one chunk per sequence (no carries), the
+// state entering every 16-token sub-block, the per-channel-block dB | dC
+// partials and the per-sequence dA_log / dDskip partials.
+struct ScanBwdPlan {
+  int max_chunks;
+  size_t off_cu, off_chunks, off_n, off_hc, off_dbc, off_dA, off_dD, total;
+};
+
+ScanBwdPlan plan_scan_bwd(int E, int64_t T, int32_t nseq) {
+  ScanBwdPlan p{};
+  p.max_chunks = nseq;
+  const size_t slots = (size_t)(T / 16) + (size_t)nseq + 1;   // sum over sequences of ceil(L / 16)
+  size_t off = 0;
+  p.off_cu = off;     off = align_up(off + sizeof(int32_t) * ((size_t)nseq + 1));
+  p.off_chunks = off; off = align_up(off + sizeof(ChunkDesc) * (size_t)nseq);
+  p.off_n = off;      off = align_up(off + sizeof(int32_t));
+  p.off_hc = off;     off = align_up(off + sizeof(float) * 16 * (size_t)E * slots);
+  p.off_dbc = off;    off = align_up(off + sizeof(float) * 32 * (size_t)(E / 64) * (size_t)T);
+  p.off_dA = off;     off = align_up(off + sizeof(float) * 16 * (size_t)E * (size_t)nseq);
+  p.off_dD = off;     off = align_up(off + sizeof(float) * (size_t)E * (size_t)nseq);
+  p.total = off;
+  return p;
+}
+
 // Scratch for K-split partial sums (GEMM tiles, conv channel splits): up to
 // one 256 x 256 fp32 tile per compute unit of a 256-CU device.
 constexpr size_t kSplitScratch = 256ull * 256 * 256 * sizeof(float);
@@ -258,6 +282,11 @@ size_t r2l_scan_workspace_bytes(const r2l_dims* dims, int64_t n_tokens, int32_t 
   if (check_dims(dims) != R2L_OK || check_tokens(R2L_F32, n_tokens, nseq, max_seqlen) != R2L_OK)
     return 0;
   return plan_scan(dims->d_inner, n_tokens, nseq, max_seqlen, 0).total;
+}
+
+size_t r2l_scan_bwd_workspace_bytes(const r2l_dims* dims, int64_t n_tokens, int32_t nseq) {
+  if (check_dims(dims) != R2L_OK || check_tokens(R2L_F32, n_tokens, nseq, 0) != R2L_OK) return 0;
+  return plan_scan_bwd(dims->d_inner, n_tokens, nseq).total;
 }
 
 int r2l_layer_fwd(const r2l_dims* d, r2l_dtype act, uint32_t flags, const r2l_weights* w,
@@ -439,6 +468,75 @@ int r2l_scan_fwd(const r2l_dims* d, r2l_dtype act, uint32_t flags, const void* u
   if (act == R2L_BF16)
     return run_scan<bf16>(a, sp, false, cu_seqlens, nseq, n_tokens, cu_clean, (ChunkDesc*)a.chunks, (int32_t*)a.n_chunks, st);
   return run_scan<float>(a, sp, false, cu_seqlens, nseq, n_tokens, cu_clean, (ChunkDesc*)a.chunks, (int32_t*)a.n_chunks, st);
+}
+
+int r2l_scan_bwd(const r2l_dims* d, r2l_dtype act, uint32_t flags, const void* u, int64_t ld_u,
+                 const float* dt, int64_t ld_dt, const float* A_log, const float* B, const float* C,
+                 int64_t ld_bc, const float* Dskip, const void* z, int64_t ld_z, const void* dy,
+                 int64_t ld_dy, float* du, float* ddt, float* dA_log, float* dB, float* dC,
+                 float* dDskip, float* dz, const int32_t* cu_seqlens, int32_t nseq, int64_t n_tokens,
+                 void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = check_dims(d);
+  if (rc != R2L_OK) return rc;
+  if ((rc = check_tokens(act, n_tokens, nseq, 0)) != R2L_OK) return rc;
+  if (flags & R2L_FLAG_L2R) return R2L_ERR_UNSUPPORTED;   // the backward runs the default direction only
+  if (flags) return R2L_ERR_INVALID_ARG;
+  const int E = d->d_inner;
+  if (!u || !dt || !A_log || !B || !C || !dy || !du || !ddt || !dA_log || !dB || !dC || !cu_seqlens)
+    return R2L_ERR_INVALID_ARG;
+  if ((Dskip != nullptr) != (dDskip != nullptr) || (z != nullptr) != (dz != nullptr)) return R2L_ERR_INVALID_ARG;
+  if (ld_u < E || ld_dt < E || ld_bc < d->d_state || ld_dy < E || (z && ld_z < E)) return R2L_ERR_INVALID_ARG;
+  // u, z, dy and dt rows are read with 16-byte vectors, the outputs written with them
+  const int64_t vec = act == R2L_BF16 ? 8 : 4;
+  if (!aligned16(u) || !aligned16(dy) || (z && !aligned16(z)) || !aligned16(dt) || !aligned16(du) ||
+      !aligned16(ddt) || (dz && !aligned16(dz)) || ld_u % vec || ld_dy % vec || (z && ld_z % vec) || ld_dt % 4)
+    return R2L_ERR_INVALID_ARG;
+  const int64_t win = 64 * (act == R2L_BF16 ? 2 : 4);
+  if (ld_u > INT32_MAX / win || ld_dy > INT32_MAX / win || ld_dt > INT32_MAX / 256 || ld_bc > INT32_MAX / 256 ||
+      (z && ld_z > INT32_MAX / win) || (int64_t)E * 256 > INT32_MAX)
+    return R2L_ERR_UNSUPPORTED;
+  const ScanBwdPlan bp = plan_scan_bwd(E, n_tokens, nseq);
+  if (!workspace || workspace_bytes < bp.total) return R2L_ERR_WORKSPACE;
+  if (((uintptr_t)workspace & (kAlign - 1)) != 0) return R2L_ERR_INVALID_ARG;
+  if (n_tokens == 0) return R2L_OK;
+  hipStream_t st = (hipStream_t)stream;
+  const int T = (int)n_tokens;
+  int32_t* cu_clean = at<int32_t>(workspace, bp.off_cu);
+  ChunkDesc* chunks = at<ChunkDesc>(workspace, bp.off_chunks);
+  int32_t* nch = at<int32_t>(workspace, bp.off_n);
+  float* hc = at<float>(workspace, bp.off_hc);
+  // one chunk per sequence: the adjoint sweep carries lambda along a whole sequence
+  R2L_RUN("plan_chunks", st, plan_chunks(cu_seqlens, nseq, T, T, bp.max_chunks, false, cu_clean, chunks, nch, st));
+  // sweep 1: states every 16 tokens, and dz
+  ScanArgs a{};
+  a.T = T; a.E = E; a.R = d->dt_rank; a.ldp = 0;
+  a.u = u; a.ld_u = ld_u; a.dt = dt; a.ld_dt = ld_dt;
+  a.Bm = B; a.Cm = C; a.ld_bc = ld_bc;
+  a.z = z; a.ld_z = ld_z;
+  a.A_log = A_log; a.Dskip = Dskip;
+  a.chunks = chunks; a.n_chunks = nch; a.max_chunks = bp.max_chunks;
+  a.l2r = false;
+  a.dy = dy; a.ld_dy = ld_dy; a.dz = dz; a.hc = hc;
+  // sweep 2: the adjoint, then the sums over channel blocks and sequences
+  ScanBwdArgs b{};
+  b.T = T; b.E = E;
+  b.u = u; b.ld_u = ld_u; b.dt = dt; b.ld_dt = ld_dt;
+  b.Bm = B; b.Cm = C; b.ld_bc = ld_bc;
+  b.A_log = A_log; b.Dskip = Dskip;
+  b.z = z; b.ld_z = ld_z; b.dy = dy; b.ld_dy = ld_dy;
+  b.chunks = chunks; b.n_chunks = nch;
+  b.hc = hc; b.du = du; b.ddt = ddt;
+  b.dbc = at<float>(workspace, bp.off_dbc);
+  b.dA = at<float>(workspace, bp.off_dA);
+  b.dD = at<float>(workspace, bp.off_dD);
+  if (act == R2L_BF16) {
+    R2L_RUN("scan_bwd_states", st, scan_bwd_states<bf16>(a, st));
+    R2L_RUN("scan_bwd_adjoint", st, scan_bwd_adjoint<bf16>(b, bp.max_chunks, dA_log, dB, dC, dDskip, st));
+  } else {
+    R2L_RUN("scan_bwd_states", st, scan_bwd_states<float>(a, st));
+    R2L_RUN("scan_bwd_adjoint", st, scan_bwd_adjoint<float>(b, bp.max_chunks, dA_log, dB, dC, dDskip, st));
+  }
+  return R2L_OK;
 }
 
 int r2l_gemm_nt(r2l_dtype act, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,

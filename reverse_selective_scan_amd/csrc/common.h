@@ -98,5 +98,5 @@ struct ChunkDesc {
   int first;         // table index of the sequence's rightmost chunk
   int j;             // position counted from the right (0 = rightmost)
   int n_in_seq;      // number of chunks of this sequence
-  int pad;
+  int slot0;         // first 16-token state slot of this chunk (scan backward)
 };

@@ -70,6 +70,12 @@ struct ScanArgs {
   const ChunkDesc* chunks; const int32_t* n_chunks; int max_chunks;
   float* sumS; float* sumP;    // [max_chunks][16][E] each
   bool l2r;                    // scan direction (see above)
+  // backward, first sweep: the gradient of the scan's output, dz (f32
+  // [T, E]) and the state entering every 16-token sub-block from the right
+  // (f32 [slots][16][E], slot ChunkDesc::slot0 + q for sub-block q counted
+  // from the chunk's right end)
+  const void* dy; long ld_dy;
+  float* dz; float* hc;
 };
 
 // Pass 1 (only when some sequence spans several chunks): per-chunk decay
@@ -79,6 +85,31 @@ template <typename T>
 hipError_t scan_summary(const ScanArgs& a, bool fused, hipStream_t st);
 template <typename T>
 hipError_t scan_main(const ScanArgs& a, bool fused, hipStream_t st);
+// Backward of the standalone scan (right to left, one chunk per sequence):
+// sweep 1 recomputes the states (kept every 16 tokens in a.hc) and writes dz;
+// the adjoint sweep and the reductions live in scan_bwd.hip.
+template <typename T>
+hipError_t scan_bwd_states(const ScanArgs& a, hipStream_t st);
+struct ScanBwdArgs {
+  int T, E;
+  const void* u; long ld_u;
+  const float* dt; long ld_dt;
+  const float* Bm; const float* Cm; long ld_bc;
+  const float* A_log; const float* Dskip;
+  const void* z; long ld_z;
+  const void* dy; long ld_dy;
+  const ChunkDesc* chunks; const int32_t* n_chunks;
+  const float* hc;          // [slots][16][E] from the first sweep
+  float* du; float* ddt;    // [T, E]
+  float* dbc;               // [E/64][T][32]: dB | dC partial sums of each channel block
+  float* dA;                // [max_chunks][E][16] (d/dA_log)
+  float* dD;                // [max_chunks][E]
+};
+// The adjoint sweep and the reductions into dA_log [E,16], dB, dC [T,16]
+// and dDskip [E] (may be null).
+template <typename T>
+hipError_t scan_bwd_adjoint(const ScanBwdArgs& a, int max_chunks, float* dA_log, float* dB, float* dC,
+                            float* dDskip, hipStream_t st);
 
 template <typename T, typename O>
 hipError_t ln_gate(int T_, int D, const O* o, const T* h_in, T* h_out, const float* gamma,

@@ -76,12 +76,17 @@ __global__ __launch_bounds__(256) void plan_chunks_kernel(const int32_t* __restr
   // chunk counts and each sequence's first table index
   const int ps = (nseq + 255) / 256;
   const int sa = min(tid * ps, nseq), sb = min(sa + ps, nseq);
-  int cnt = 0;
+  // (and the number of 16-token state slots of the chunks: only the last
+  // chunk of a sequence can be partial)
+  int cnt = 0, slots = 0;
   for (int q = sa; q < sb; ++q) {
     const int len = cu_clean[q + 1] - cu_clean[q];
-    cnt += (len + Lc - 1) / Lc;
+    const int nc = (len + Lc - 1) / Lc;
+    cnt += nc;
+    slots += nc > 0 ? (nc - 1) * ((Lc + 15) / 16) + (len - (nc - 1) * Lc + 15) / 16 : 0;
   }
   int base = block_exclusive_scan<false>(cnt, s_v);
+  int slot = block_exclusive_scan<false>(slots, s_v);
   if (tid == 255) *n_chunks = min(base + cnt, max_chunks);
   for (int q = sa; q < sb; ++q) {
     const int slo = cu_clean[q], send = cu_clean[q + 1];
@@ -101,7 +106,8 @@ __global__ __launch_bounds__(256) void plan_chunks_kernel(const int32_t* __restr
       d.first = base;
       d.j = j;
       d.n_in_seq = nc;
-      d.pad = 0;
+      d.slot0 = slot;
+      slot += (d.hi - d.lo + 15) / 16;
       chunks[base + j] = d;
     }
     base += nc;
@@ -142,14 +148,20 @@ constexpr unsigned kOutside = 0x80000000u;   // an offset past every window
 // 8 channels of one row: one 16-byte load (bf16) or two (fp32)
 template <typename T> struct Raw8;
 template <> struct Raw8<bf16> { u32x4 v; };
-template <> struct Raw8<float> { u32x4 a, b; };
+template <> struct Raw8<float> { f32x4 a, b; };
 R2L_DEV void raw_load(Raw8<bf16>& r, Rsrc s, unsigned off) { r.v = bload16(s, off); }
-R2L_DEV void raw_load(Raw8<float>& r, Rsrc s, unsigned off) { r.a = bload16(s, off); r.b = bload16(s, off + 16); }
+// (fp32 lanes are reinterpreted as a whole vector: extracting one 32-bit
+// element of a 16-byte buffer load and reinterpreting it as a float makes
+// this compiler narrow the load to its first dword)
+R2L_DEV void raw_load(Raw8<float>& r, Rsrc s, unsigned off) {
+  r.a = __builtin_bit_cast(f32x4, bload16(s, off));
+  r.b = __builtin_bit_cast(f32x4, bload16(s, off + 16));
+}
 R2L_DEV float raw_at(const Raw8<bf16>& r, int i) {
   const unsigned w = r.v[i >> 1];
   return __builtin_bit_cast(float, (i & 1) ? (w & 0xffff0000u) : (w << 16));
 }
-R2L_DEV float raw_at(const Raw8<float>& r, int i) { return __builtin_bit_cast(float, i < 4 ? r.a[i] : r.b[i - 4]); }
+R2L_DEV float raw_at(const Raw8<float>& r, int i) { return i < 4 ? r.a[i] : r.b[i - 4]; }
 R2L_DEV void store8(Rsrc s, unsigned off, const float v[8], bf16*) {
   u32x4 q;
 #pragma unroll
@@ -199,8 +211,14 @@ template <> R2L_DEV float softplus_dt<bf16>(float v) {
 //   C  same layout as A: y = (sum of the 4 partial C.h + Dskip u) SiLU(z),
 //      one 16-byte store per thread.
 // ---------------------------------------------------------------------------
-template <typename T, bool FUSED, bool SUMMARY, int KS, bool L2R>
+//
+// BWD (standalone, right to left, no chunk carries): the first sweep of the
+// backward pass.  The recurrence runs as above; before each 16-token
+// sub-block it stores the state entering it from the right into a.hc, and
+// phase C writes dz = dy SiLU'(z) (C.h + Dskip u) instead of y.
+template <typename T, bool FUSED, bool SUMMARY, int KS, bool L2R, bool BWD = false>
 __global__ __launch_bounds__(256, 2) void scan_kernel(ScanArgs a) {
+  static_assert(!BWD || (!FUSED && !SUMMARY && !L2R), "the backward sweep is standalone and right to left");
   constexpr int TB = 32;
   constexpr bool MFMA_DT = FUSED && KS > 0;
   constexpr int RP = MFMA_DT ? KS * 32 : 32;   // padded dt_rank for the MFMA k loop
@@ -311,10 +329,14 @@ __global__ __launch_bounds__(256, 2) void scan_kernel(ScanArgs a) {
   const unsigned offDT = (unsigned)(r8 * lddt_b) + (unsigned)ea * 4;               // dt (standalone)
   const unsigned offB = c8 < 4 ? (unsigned)(r8 * ldbc_b) + 16u * c8 : kOutside;    // B (standalone)
   const unsigned offC = c8 < 4 ? kOutside : (unsigned)(r8 * ldbc_b) + 16u * (c8 - 4);
+  const long lddy_b = a.ld_dy * (long)SZ;
+  const unsigned offDY = (unsigned)(r8 * lddy_b) + (unsigned)ea * SZ;               // dy (backward)
+  const unsigned offDZ = (unsigned)(r8 * (long)E * 4) + (unsigned)ea * 4;          // dz (backward)
 
   // ---------------- prefetch registers ----------------
   Raw8<T> px[FUSED ? 4 : 1];   // x rows r8 .. r8+3 (fused) or the u row r8
   Raw8<T> pz;                  // z row r8
+  Raw8<T> pdy;                 // dy row r8 (backward)
   u32x4 pd[FUSED ? (MFMA_DT ? DPT / 4 : 1) : 2];   // delta (fused) or dt (standalone) of row r8
   float pbc[4];                // 4 of the row's 32 B/C floats
 
@@ -348,6 +370,9 @@ __global__ __launch_bounds__(256, 2) void scan_kernel(ScanArgs a) {
     }
     if constexpr (!SUMMARY) {
       if (has_z) raw_load(pz, row_window(zin, blo, ldz_b, rows), offZ);
+    }
+    if constexpr (BWD) {
+      if (has_z) raw_load(pdy, row_window(a.dy, blo, lddy_b, rows), offDY);
     }
   };
 
@@ -414,7 +439,16 @@ __global__ __launch_bounds__(256, 2) void scan_kernel(ScanArgs a) {
           pre_s[r8][8 * c8 + i] = make_float2(dtv, dtv * uu[i]);
         }
       }
-      if constexpr (!SUMMARY) {
+      if constexpr (BWD) {
+        // g8 = dy SiLU'(z), SiLU'(z) = sig(z) (1 + z (1 - sig(z)))
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const float zv = has_z ? raw_at(pz, i) : 0.0f;
+          const float sg = sigmoid_fast(zv);
+          g8[i] = has_z ? raw_at(pdy, i) * (sg * fmaf(zv, 1.0f - sg, 1.0f)) : 0.0f;
+          du8[i] = dsk8[i] * uu[i];
+        }
+      } else if constexpr (!SUMMARY) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
           g8[i] = has_z ? silu_fast(raw_at(pz, i)) : 1.0f;
@@ -474,6 +508,15 @@ __global__ __launch_bounds__(256, 2) void scan_kernel(ScanArgs a) {
       }
     };
     const float* bsrc = (const float*)&bc_s[0][w] + (lane & 3);   // B_t[4 w + (lane & 3)] at row 0
+    // (backward) the state entering the block's sub-blocks: before its
+    // first token and, for a block of more than 16, before its 17th
+    auto keep_state = [&](int half) __attribute__((always_inline)) {
+      if constexpr (BWD) {
+        const long slot = (long)d.slot0 + 2 * kb + half;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) a.hc[(slot * NS + 4 * w + i) * E + e] = h[i];
+      }
+    };
     if (nt == TB) {
       // 4-deep ring of LDS operands (indices are constants after unrolling)
       constexpr int LA = 4;
@@ -489,6 +532,7 @@ __global__ __launch_bounds__(256, 2) void scan_kernel(ScanArgs a) {
       }
 #pragma unroll
       for (int k = 0; k < TB; ++k) {
+        if (k == 0 || k == 16) keep_state(k / 16);
         const int r = row(k), sl = k % LA;
         const float2 p = Pq[sl];
         const float bv = Bq[sl];
@@ -503,6 +547,7 @@ __global__ __launch_bounds__(256, 2) void scan_kernel(ScanArgs a) {
       }
     } else {
       for (int k = 0; k < nt; ++k) {
+        if (k == 0 || k == 16) keep_state(k / 16);
         const int r = L2R ? k : nt - 1 - k;
         compute(r, pre_s[r][lane], bsrc[r * 32], bc_s[r][4 + w]);
       }
@@ -523,7 +568,11 @@ __global__ __launch_bounds__(256, 2) void scan_kernel(ScanArgs a) {
       }
 #pragma unroll
       for (int i = 0; i < 8; ++i) v[i] *= g8[i];
-      store8(row_window(a.y, blo, ldy_b, nt), offY, v, (T*)nullptr);
+      if constexpr (BWD) {
+        if (has_z) store8(row_window(a.dz, blo, (long)E * 4, nt), offDZ, v, (float*)nullptr);
+      } else {
+        store8(row_window(a.y, blo, ldy_b, nt), offY, v, (T*)nullptr);
+      }
       // the next block's phase B rewrites yp_s only after two more barriers
     }
   }
@@ -571,6 +620,15 @@ template <typename T>
 hipError_t scan_main(const ScanArgs& a, bool fused, hipStream_t st) {
   return launch_scan<T, false>(a, fused, st);
 }
+template <typename T>
+hipError_t scan_bwd_states(const ScanArgs& a, hipStream_t st) {
+  if (a.max_chunks * (a.E / 64) <= 0) return hipSuccess;
+  hipLaunchKernelGGL((scan_kernel<T, false, false, 0, false, true>), dim3(a.max_chunks * (a.E / 64)), dim3(256),
+                     0, st, a);
+  return hipGetLastError();
+}
+template hipError_t scan_bwd_states<float>(const ScanArgs&, hipStream_t);
+template hipError_t scan_bwd_states<bf16>(const ScanArgs&, hipStream_t);
 template hipError_t scan_summary<float>(const ScanArgs&, bool, hipStream_t);
 template hipError_t scan_summary<bf16>(const ScanArgs&, bool, hipStream_t);
 template hipError_t scan_main<float>(const ScanArgs&, bool, hipStream_t);

@@ -178,3 +178,23 @@ def test_binding_fails_loudly_without_library(monkeypatch):
     monkeypatch.setattr(B, "LIB_PATH", "/nonexistent/libr2l.so")
     with pytest.raises(RuntimeError, match="not built"):
         B.lib()
+
+
+def test_scan_bwd_rejects_bad_arguments():
+    lib = B.lib()
+    d = _dims()
+    need = lib.r2l_scan_bwd_workspace_bytes(C.byref(d), 10, 1)
+    assert need > 0
+
+    def call(flags=0, dy=FAKE, dD=None, dz=None, Dskip=None, z=None, ws=FAKE * 256, wsb=need, ld_u=4096):
+        return lib.r2l_scan_bwd(C.byref(d), B.R2L_F32, flags, FAKE, ld_u, FAKE, 4096, FAKE, FAKE, FAKE, 16, Dskip,
+                                z, 4096, dy, 4096, FAKE, FAKE, FAKE, FAKE, FAKE, dD, dz, FAKE, 1, 10, ws, wsb,
+                                None)
+    assert call(flags=B.R2L_FLAG_L2R) == B.R2L_ERR_UNSUPPORTED
+    assert call(flags=0x8) == B.R2L_ERR_INVALID_ARG
+    assert call(dy=None) == B.R2L_ERR_INVALID_ARG
+    assert call(Dskip=FAKE) == B.R2L_ERR_INVALID_ARG            # dDskip required with Dskip
+    assert call(z=FAKE) == B.R2L_ERR_INVALID_ARG                # dz required with z
+    assert call(ld_u=4000) == B.R2L_ERR_INVALID_ARG
+    assert call(ws=None, wsb=0) == B.R2L_ERR_WORKSPACE
+    assert call(wsb=need - 1) == B.R2L_ERR_WORKSPACE

@@ -1,0 +1,86 @@
+"""GPU parity of the backward pass against the gradient oracle (torch CPU
+float64 autograd of the scan's definition, pinned by finite differences in
+test_oracle_grad.py), on the same exactly representable inputs.  The
+gradients come out in fp32 from fp32 arithmetic on both activation types,
+so both are held to the fp32 bound."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import r2l_oracle_grad as G
+from parity import err_f32, report, to_np
+from reverse_selective_scan_amd import binding as B
+from reverse_selective_scan_amd import synth
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+TOL_GRAD = 2e-4
+
+
+def _err(g, ref):
+    """err_f32, or the largest |g| where the reference is identically zero
+    (e.g. dA_log of one-token sequences: no state reaches a later token)."""
+    if not np.any(ref):
+        return float(np.max(np.abs(g))) if g.size else 0.0
+    return err_f32(g, ref)
+
+
+def _case(name):
+    print(f"\n[case] {name}", flush=True)
+
+
+def _dev(a, act):
+    t = torch.from_numpy(np.ascontiguousarray(a, np.float32))
+    return (t.to(torch.bfloat16) if act == "bf16" else t).to(DEV)
+
+
+def _q(a, act):
+    return synth.bf16_round(a) if act == "bf16" else np.asarray(a, np.float32)
+
+
+def _scan_case(T, E, act, seed):
+    N = 16
+    u = _q(synth.make_aux(seed, (T, E)), act)
+    dt = synth.make_aux(seed + 1, (T, E), kind="uniform", lo=1e-3, hi=0.2)
+    A_log = synth.make_aux(seed + 2, (E, N), kind="uniform", lo=-1.0, hi=2.5)
+    bcx = synth.make_aux(seed + 3, (T, 40))          # B at columns 8..23, C at 24..39
+    Dskip = synth.make_aux(seed + 4, (E,), kind="uniform", lo=0.5, hi=1.5)
+    z = _q(synth.make_aux(seed + 5, (T, E)), act)
+    dy = _q(synth.make_aux(seed + 6, (T, E)), act)
+    return u, dt, A_log, bcx, Dskip, z, dy
+
+
+@pytest.mark.parametrize("act", ["f32", "bf16"])
+@pytest.mark.parametrize("lens,E", [([1], 64), ([17], 64), ([5, 0, 130, 1, 300], 128), ([700, 2, 129], 192),
+                                    ([2048], 64)])
+@pytest.mark.parametrize("gated", [True, False])
+def test_scan_bwd_matches_oracle(act, lens, E, gated):
+    _case(f"scan bwd {act} lens={lens} E={E} gated={gated}")
+    T = sum(lens)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    u, dt, A_log, bcx, Dskip, z, dy = _scan_case(T, E, act, 80 + len(lens) + E)
+    Dk, zz = (Dskip, z) if gated else (None, None)
+    ref = G.scan_grads(u, dt, A_log, bcx[:, 8:24], bcx[:, 24:40], cu, dy, Dskip=Dk, z=zz)
+    bc_d = _dev(bcx, "f32")
+    got = B.r2l_scan_bwd(_dev(u, act), _dev(dt, "f32"), _dev(A_log, "f32"), bc_d[:, 8:24], bc_d[:, 24:40], cu,
+                         _dev(dy, act), Dskip=_dev(Dk, "f32") if gated else None,
+                         z=_dev(zz, act) if gated else None)
+    pairs = [("du", "u"), ("ddt", "dt"), ("dA_log", "A_log"), ("dB", "B"), ("dC", "C")]
+    if gated:
+        pairs += [("dDskip", "Dskip"), ("dz", "z")]
+    for gk, rk in pairs:
+        assert report(f"scan bwd {gk}", _err(to_np(got[gk]), ref[rk]), TOL_GRAD) <= TOL_GRAD
+
+
+def test_scan_bwd_is_deterministic():
+    _case("scan bwd determinism")
+    lens, E = [300, 41, 5], 256
+    T = sum(lens)
+    u, dt, A_log, bcx, Dskip, z, dy = _scan_case(T, E, "bf16", 90)
+    bc_d = _dev(bcx, "f32")
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    args = (_dev(u, "bf16"), _dev(dt, "f32"), _dev(A_log, "f32"), bc_d[:, 8:24], bc_d[:, 24:40], cu, _dev(dy, "bf16"))
+    g1 = B.r2l_scan_bwd(*args, Dskip=_dev(Dskip, "f32"), z=_dev(z, "bf16"))
+    g2 = B.r2l_scan_bwd(*args, Dskip=_dev(Dskip, "f32"), z=_dev(z, "bf16"))
+    for k in g1:
+        assert torch.equal(g1[k], g2[k]), k
