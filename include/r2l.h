@@ -103,6 +103,24 @@ typedef struct {
   const float* s;          /* f32  [1]   scalar gate s (device) */
 } r2l_weights;
 
+/* Gradients of one hook's parameters (device pointers, f32, same shapes as
+ * r2l_weights; written, not accumulated).  ln_w and ln_b may be NULL under
+ * R2L_FLAG_NO_LN. */
+typedef struct {
+  float* in_proj_w;   /* [2E, D] */
+  float* conv_w;      /* [E, K] */
+  float* conv_b;      /* [E] */
+  float* x_proj_w;    /* [R+2N, E] */
+  float* dt_proj_w;   /* [E, R] */
+  float* out_proj_w;  /* [D, E] */
+  float* dt_proj_b;   /* [E] */
+  float* A_log;       /* [E, N] */
+  float* Dskip;       /* [E] */
+  float* ln_w;        /* [D] */
+  float* ln_b;        /* [D] */
+  float* s;           /* [1] */
+} r2l_grads;
+
 /* ------------------------------------------------------------------------
  * r2l_layer_fwd -- one ReverseMambaLayer hook (§3.4 steps 1-4):
  *   h_out = h_in + tanh(s) * LN(flip(Mamba1(flip(h_in))))   per sequence.
@@ -123,6 +141,34 @@ int r2l_layer_fwd(const r2l_dims* dims, r2l_dtype act, uint32_t flags, const r2l
                   const void* h_in, void* h_out, const int32_t* cu_seqlens, int32_t nseq,
                   int64_t n_tokens, int32_t max_seqlen, void* workspace, size_t workspace_bytes,
                   float* branch_out, void* stream);
+
+/* ------------------------------------------------------------------------
+ * r2l_layer_bwd -- the gradient of r2l_layer_fwd for training the sidecar
+ * (§3.5, plug-in mode: the backbone is frozen, the Mamba block, the stream
+ * LayerNorm and the gate s are trained).  Given g_out = dL/dh+ for the
+ * output of r2l_layer_fwd on h_in, it writes dh = dL/dh_in (act [n_tokens,
+ * D]; may equal g_out) and every parameter gradient (r2l_grads, f32).
+ * The forward is recomputed inside (activation checkpointing): in_proj, the
+ * conv + SiLU + x_proj, dt, the scan and out_proj; then, in reverse: the
+ * LayerNorm + gate, out_proj, the scan (r2l_scan_bwd's two sweeps), dt_proj
+ * and softplus, x_proj, the conv + SiLU and in_proj.  Products go through
+ * the same GEMM as the forward (bf16 operands on MFMA, fp32 accumulation
+ * and fp32 results for bf16 activations; the fp32 kernel for fp32), with
+ * the transposed operands materialised.  Sums over tokens run in a fixed
+ * order: results are deterministic.
+ * flags: 0 or R2L_FLAG_NO_LN (R2L_FLAG_L2R returns R2L_ERR_UNSUPPORTED).
+ * bf16 activations need dt_rank a multiple of 8.  Other arguments as in
+ * r2l_layer_fwd.  workspace: r2l_layer_bwd_workspace_bytes(...) bytes,
+ * 256-byte aligned (several times the forward's: every recomputed
+ * activation and its transpose is kept).
+ * ---------------------------------------------------------------------- */
+size_t r2l_layer_bwd_workspace_bytes(const r2l_dims* dims, r2l_dtype act, int64_t n_tokens, int32_t nseq,
+                                     int32_t max_seqlen);
+
+int r2l_layer_bwd(const r2l_dims* dims, r2l_dtype act, uint32_t flags, const r2l_weights* w,
+                  const void* h_in, const void* g_out, void* dh, const r2l_grads* grads,
+                  const int32_t* cu_seqlens, int32_t nseq, int64_t n_tokens, int32_t max_seqlen,
+                  void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
  * r2l_conv_fwd -- the anti-causal depthwise conv1d + bias + SiLU of the

@@ -34,6 +34,12 @@ class Dims(C.Structure):
                 ("dt_rank", C.c_int32), ("d_conv", C.c_int32)]
 
 
+class Grads(C.Structure):
+    _fields_ = [(n, C.c_void_p) for n in (
+        "in_proj_w", "conv_w", "conv_b", "x_proj_w", "dt_proj_w", "out_proj_w",
+        "dt_proj_b", "A_log", "Dskip", "ln_w", "ln_b", "s")]
+
+
 class Weights(C.Structure):
     _fields_ = [(n, C.c_void_p) for n in (
         "in_proj_w", "conv_w", "conv_b", "x_proj_w", "dt_proj_w", "out_proj_w",
@@ -54,6 +60,9 @@ _SIGS = {
     "r2l_scan_fwd": (C.c_int, [C.POINTER(Dims), C.c_int, C.c_uint32, _P, _I64, _P, _I64, _P, _P, _P, _I64, _P,
                                _P, _I64, _P, _P, _I32, _I64, _I32, _P, _SZ, _P]),
     "r2l_scan_bwd_workspace_bytes": (_SZ, [C.POINTER(Dims), _I64, _I32]),
+    "r2l_layer_bwd_workspace_bytes": (_SZ, [C.POINTER(Dims), C.c_int, _I64, _I32, _I32]),
+    "r2l_layer_bwd": (C.c_int, [C.POINTER(Dims), C.c_int, C.c_uint32, C.POINTER(Weights), _P, _P, _P,
+                                C.POINTER(Grads), _P, _I32, _I64, _I32, _P, _SZ, _P]),
     "r2l_scan_bwd": (C.c_int, [C.POINTER(Dims), C.c_int, C.c_uint32, _P, _I64, _P, _I64, _P, _P, _P, _I64, _P,
                                _P, _I64, _P, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _I64, _P, _SZ, _P]),
     "r2l_gemm_nt": (C.c_int, [C.c_int, _I64, _I64, _I64, _P, _I64, _P, _I64, _P, _I64, C.c_int, _P, C.c_size_t, _P]),
@@ -175,6 +184,31 @@ def r2l_layer_fwd(h: torch.Tensor, w: Dict[str, torch.Tensor], cu_seqlens, *, ou
         C.byref(d), act, flags, C.byref(W), _ptr(h), _ptr(out), _ptr(cu_dev), nseq, T, max_seqlen,
         _ptr(workspace), workspace.numel(), _ptr(branch_out), _stream()))
     return out
+
+
+def r2l_layer_bwd(h: torch.Tensor, w: Dict[str, torch.Tensor], cu_seqlens, g_out: torch.Tensor, *,
+                  dh: Optional[torch.Tensor] = None, flags: int = 0,
+                  workspace: Optional[torch.Tensor] = None):
+    """Gradient of r2l_layer_fwd: given g_out = dL/dh+, returns (dh, grads)
+    with grads a dict of fp32 device tensors named like the weights."""
+    _need(h, "h")
+    act = _act(h)
+    T = h.shape[0]
+    _need(g_out, "g_out", h.dtype)
+    cu_dev, nseq, max_seqlen = cu_seqlens_device(cu_seqlens, T, h.device)
+    d = dims_of(w)
+    if dh is None:
+        dh = torch.empty_like(h)
+    grads = {k: torch.empty(w[k].shape, dtype=torch.float32, device=h.device) for k, _ in Grads._fields_}
+    need = int(lib().r2l_layer_bwd_workspace_bytes(C.byref(d), act, T, nseq, max_seqlen))
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=h.device)
+    W = Weights(**{f[0]: _ptr(w[f[0]]) for f in Weights._fields_})
+    G = Grads(**{f[0]: _ptr(grads[f[0]]) for f in Grads._fields_})
+    _check("r2l_layer_bwd", lib().r2l_layer_bwd(
+        C.byref(d), act, flags, C.byref(W), _ptr(h), _ptr(g_out), _ptr(dh), C.byref(G), _ptr(cu_dev), nseq, T,
+        max_seqlen, _ptr(workspace), workspace.numel(), _stream()))
+    return dh, grads
 
 
 def r2l_conv_fwd(x: torch.Tensor, conv_w: torch.Tensor, conv_b: torch.Tensor, cu_seqlens, *,

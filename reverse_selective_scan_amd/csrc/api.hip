@@ -242,6 +242,263 @@ int run_scan(const ScanArgs& a, const ScanPlan& sp, bool fused, const int32_t* c
   return R2L_OK;
 }
 
+// Both sweeps of the scan backward and its reductions; ws laid out by
+// plan_scan_bwd(E, T, nseq).
+int run_scan_bwd(r2l_dtype act, int E, int R, int T, int nseq, const void* u, int64_t ld_u, const float* dt,
+                 int64_t ld_dt, const float* A_log, const float* B, const float* C, int64_t ld_bc,
+                 const float* Dskip, const void* z, int64_t ld_z, const void* dy, int64_t ld_dy, float* du,
+                 float* ddt, float* dA_log, float* dB, float* dC, float* dDskip, float* dz,
+                 const int32_t* cu_seqlens, void* workspace, hipStream_t st) {
+  const ScanBwdPlan bp = plan_scan_bwd(E, T, nseq);
+  int32_t* cu_clean = at<int32_t>(workspace, bp.off_cu);
+  ChunkDesc* chunks = at<ChunkDesc>(workspace, bp.off_chunks);
+  int32_t* nch = at<int32_t>(workspace, bp.off_n);
+  float* hc = at<float>(workspace, bp.off_hc);
+  // one chunk per sequence: the adjoint sweep carries lambda along a whole sequence
+  R2L_RUN("plan_chunks", st, plan_chunks(cu_seqlens, nseq, T, T, bp.max_chunks, false, cu_clean, chunks, nch, st));
+  // sweep 1: states every 16 tokens, and dz
+  ScanArgs a{};
+  a.T = T; a.E = E; a.R = R; a.ldp = 0;
+  a.u = u; a.ld_u = ld_u; a.dt = dt; a.ld_dt = ld_dt;
+  a.Bm = B; a.Cm = C; a.ld_bc = ld_bc;
+  a.z = z; a.ld_z = ld_z;
+  a.A_log = A_log; a.Dskip = Dskip;
+  a.chunks = chunks; a.n_chunks = nch; a.max_chunks = bp.max_chunks;
+  a.l2r = false;
+  a.dy = dy; a.ld_dy = ld_dy; a.dz = dz; a.hc = hc;
+  // sweep 2: the adjoint, then the sums over channel blocks and sequences
+  ScanBwdArgs b{};
+  b.T = T; b.E = E;
+  b.u = u; b.ld_u = ld_u; b.dt = dt; b.ld_dt = ld_dt;
+  b.Bm = B; b.Cm = C; b.ld_bc = ld_bc;
+  b.A_log = A_log; b.Dskip = Dskip;
+  b.z = z; b.ld_z = ld_z; b.dy = dy; b.ld_dy = ld_dy;
+  b.chunks = chunks; b.n_chunks = nch;
+  b.hc = hc; b.du = du; b.ddt = ddt;
+  b.dbc = at<float>(workspace, bp.off_dbc);
+  b.dA = at<float>(workspace, bp.off_dA);
+  b.dD = at<float>(workspace, bp.off_dD);
+  if (act == R2L_BF16) {
+    R2L_RUN("scan_bwd_states", st, scan_bwd_states<bf16>(a, st));
+    R2L_RUN("scan_bwd_adjoint", st, scan_bwd_adjoint<bf16>(b, bp.max_chunks, dA_log, dB, dC, dDskip, st));
+  } else {
+    R2L_RUN("scan_bwd_states", st, scan_bwd_states<float>(a, st));
+    R2L_RUN("scan_bwd_adjoint", st, scan_bwd_adjoint<float>(b, bp.max_chunks, dA_log, dB, dC, dDskip, st));
+  }
+  return R2L_OK;
+}
+
+// Workspace of the layer backward: every recomputed activation, the
+// gradient buffers and the transposed GEMM operands (tokens padded to Tp, a
+// multiple of 128, in the transposes), the forward scan's and the scan
+// backward's own regions, and the GEMM split scratch.
+struct LayerBwdPlan {
+  size_t xz, u, xdbl, delta, dt, yg, o, scanf, dout, gx, gr, do_a, doT, ygT, wT, dyg, du, ddt, dz, dB, dC, scanb,
+      ddt_a, ddtT, deltaT, ddelta, dxdbl_a, dxdblT, uT, dux, dc, dx, convp, dxz_a, dxzT, hT, dhb, colp, scratch;
+  ScanPlan sp;
+  int Tp;
+  size_t total;
+};
+
+LayerBwdPlan plan_layer_bwd(const r2l_dims* d, r2l_dtype act, int64_t T, int32_t nseq, int32_t max_seqlen) {
+  LayerBwdPlan p{};
+  const size_t sa = act == R2L_BF16 ? 2 : 4, f = 4;
+  const size_t D = d->d_model, E = d->d_inner, N = d->d_state, R = d->dt_rank, P = R + 2 * N;
+  const size_t Tz = (size_t)T;
+  p.Tp = (int)(((T + 127) / 128) * 128);
+  const size_t Tp = (size_t)p.Tp;
+  size_t off = 0;
+  auto take = [&](size_t bytes) { const size_t o = off; off = align_up(off + bytes); return o; };
+  p.xz = take(Tz * 2 * E * sa);
+  p.u = take(Tz * E * sa);
+  p.xdbl = take(Tz * P * f);
+  p.delta = take(Tz * R * sa);
+  p.dt = take(Tz * E * f);
+  p.yg = take(Tz * E * sa);
+  p.o = take(Tz * D * f);
+  p.sp = plan_scan((int)E, T, nseq, max_seqlen, 0);
+  p.scanf = take(p.sp.total);
+  p.dout = take(Tz * D * f);
+  p.gx = take(Tz * 2 * D * f);
+  p.gr = take(Tz * f);
+  p.do_a = take(Tz * D * sa);
+  p.doT = take(D * Tp * sa);
+  p.ygT = take(E * Tp * sa);
+  // W_out^T [E, D], W_dt^T [R, E], W_x^T [E, P], W_in^T [D, 2E] share one region
+  p.wT = take((E * D > 2 * E * D ? E * D : 2 * E * D) * sa);
+  p.dyg = take(Tz * E * sa);
+  p.du = take(Tz * E * f);
+  p.ddt = take(Tz * E * f);
+  p.dz = take(Tz * E * f);
+  p.dB = take(Tz * N * f);
+  p.dC = take(Tz * N * f);
+  p.scanb = take(plan_scan_bwd((int)E, T, nseq).total);
+  p.ddt_a = take(Tz * E * sa);
+  p.ddtT = take(E * Tp * sa);
+  p.deltaT = take(R * Tp * sa);
+  p.ddelta = take(Tz * R * f);
+  p.dxdbl_a = take(Tz * P * sa);
+  p.dxdblT = take(P * Tp * sa);
+  p.uT = take(E * Tp * sa);
+  p.dux = take(Tz * E * f);
+  p.dc = take(Tz * E * f);
+  p.dx = take(Tz * E * f);
+  p.convp = take((size_t)conv_bwd_parts((int)T) * E * 5 * f);
+  p.dxz_a = take(Tz * 2 * E * sa);
+  p.dxzT = take(2 * E * Tp * sa);
+  p.hT = take(D * Tp * sa);
+  p.dhb = take(Tz * D * f);
+  p.colp = take((size_t)colsum_parts((int)T) * (E > D ? E : D) * f);
+  p.scratch = take(act == R2L_BF16 ? kSplitScratch : 0);
+  p.total = off;
+  return p;
+}
+
+template <typename A>
+int run_layer_bwd(const r2l_dims* d, r2l_dtype act, bool no_ln, const r2l_weights* w, const A* h, const A* g,
+                  A* dh, const r2l_grads* gr, const int32_t* cu_seqlens, int nseq, int T, int32_t max_seqlen,
+                  void* ws, hipStream_t st) {
+  const LayerBwdPlan p = plan_layer_bwd(d, act, T, nseq, max_seqlen);
+  const int D = d->d_model, E = d->d_inner, N = d->d_state, R = d->dt_rank, P = R + 2 * N, Tp = p.Tp;
+  const bool bf = act == R2L_BF16;
+  const int ncu = bf ? num_cus() : 0;
+  float* scratch = at<float>(ws, p.scratch);
+  // C = A B^T: bf16 operands on MFMA (act-typed or f32 result), or the fp32 kernel
+  auto gemm = [&](int M, int Nn, int K, const A* a, long lda, const A* b, long ldb, void* c, long ldc,
+                  bool out_f32) -> hipError_t {
+    if constexpr (std::is_same<A, bf16>::value)
+      return gemm_bf16_nt(M, Nn, K, a, lda, b, ldb, c, ldc, out_f32, st, scratch, kSplitScratch, ncu);
+    else
+      return gemm_f32_nt(M, Nn, K, a, lda, b, ldb, (float*)c, ldc, st);
+  };
+  A* xz = at<A>(ws, p.xz);
+  A* u = at<A>(ws, p.u);
+  float* xdbl = at<float>(ws, p.xdbl);
+  A* delta = at<A>(ws, p.delta);
+  float* dt = at<float>(ws, p.dt);
+  A* yg = at<A>(ws, p.yg);
+  float* o = at<float>(ws, p.o);
+  A* wT = at<A>(ws, p.wT);
+  const A* Win = (const A*)w->in_proj_w;
+  const A* Wx = (const A*)w->x_proj_w;
+  const A* Wdt = (const A*)w->dt_proj_w;
+  const A* Wout = (const A*)w->out_proj_w;
+  const A* cw = (const A*)w->conv_w;
+  const A* cb = (const A*)w->conv_b;
+
+  // ---------------- forward recompute ----------------
+  void* sfw = at<char>(ws, p.scanf);
+  int32_t* cu_clean = at<int32_t>(sfw, p.sp.off_cu);
+  ChunkDesc* chunks = at<ChunkDesc>(sfw, p.sp.off_chunks);
+  int32_t* nch = at<int32_t>(sfw, p.sp.off_n);
+  R2L_RUN("plan_chunks", st, plan_chunks(cu_seqlens, nseq, T, p.sp.Lc, p.sp.max_chunks, false, cu_clean, chunks, nch, st));
+  R2L_RUN("bwd_in_proj", st, gemm(T, 2 * E, D, h, D, Win, D, xz, 2L * E, false));
+  if constexpr (std::is_same<A, bf16>::value) {
+    if (P <= 256) {
+      R2L_RUN("bwd_conv", st, conv_xproj_bf16(T, E, P, xz, 2L * E, cw, cb, Wx, u, xdbl, cu_clean, nseq, false, st));
+    } else {
+      R2L_RUN("bwd_conv", st, conv_silu<bf16>(T, E, xz, 2L * E, cw, cb, u, cu_clean, nseq, false, st));
+      R2L_RUN("bwd_x_proj", st, gemm(T, P, E, u, E, Wx, E, xdbl, P, true));
+    }
+  } else {
+    R2L_RUN("bwd_conv", st, conv_silu<float>(T, E, xz, 2L * E, cw, cb, u, cu_clean, nseq, false, st));
+    R2L_RUN("bwd_x_proj", st, gemm(T, P, E, u, E, Wx, E, xdbl, P, true));
+  }
+  R2L_RUN("bwd_delta", st, (elementwise<kConvert, float, A>(T, R, xdbl, P, nullptr, 0, nullptr, delta, R, st)));
+  R2L_RUN("bwd_dt_proj", st, gemm(T, E, R, delta, R, Wdt, R, dt, E, true));
+  R2L_RUN("bwd_softplus", st, (elementwise<kSoftplusBias, float, float>(T, E, dt, E, nullptr, 0, w->dt_proj_b, dt, E, st)));
+  {
+    ScanArgs a{};
+    a.T = T; a.E = E; a.R = R; a.ldp = 0;
+    a.u = u; a.ld_u = E; a.dt = dt; a.ld_dt = E;
+    a.Bm = xdbl + R; a.Cm = xdbl + R + N; a.ld_bc = P;
+    a.z = xz + E; a.ld_z = 2L * E;
+    a.A_log = w->A_log; a.Dskip = w->Dskip; a.y = yg;
+    a.chunks = chunks; a.n_chunks = nch; a.max_chunks = p.sp.max_chunks;
+    a.sumS = at<float>(sfw, p.sp.off_sumS); a.sumP = at<float>(sfw, p.sp.off_sumP);
+    a.l2r = false;
+    if (p.sp.summary) R2L_RUN("bwd_scan_summary", st, scan_summary<A>(a, false, st));
+    R2L_RUN("bwd_scan", st, scan_main<A>(a, false, st));
+  }
+  R2L_RUN("bwd_out_proj", st, gemm(T, D, E, yg, E, Wout, E, o, D, true));
+
+  // ---------------- backward ----------------
+  float* dout = at<float>(ws, p.dout);
+  float* gx = at<float>(ws, p.gx);
+  float* grr = at<float>(ws, p.gr);
+  float* colp = at<float>(ws, p.colp);
+  R2L_RUN("bwd_ln_gate", st, ln_gate_bwd<A>(T, D, g, o, w->ln_w, w->ln_b, w->s, no_ln, R2L_LN_EPS, dout, gx, grr, st));
+  if (!no_ln) {
+    R2L_RUN("bwd_ln_w", st, colsum(T, D, gx, 2L * D, colp, 1.0f, gr->ln_w, st));
+    R2L_RUN("bwd_ln_b", st, colsum(T, D, gx + D, 2L * D, colp, 1.0f, gr->ln_b, st));
+  }
+  R2L_RUN("bwd_s", st, colsum(T, 1, grr, 1, colp, 1.0f, gr->s, st));
+  // out_proj: dyg = do W_out, dW_out = do^T yg
+  A* do_a = at<A>(ws, p.do_a);
+  A* dyg = at<A>(ws, p.dyg);
+  R2L_RUN("bwd_do", st, (elementwise<kConvert, float, A>(T, D, dout, D, nullptr, 0, nullptr, do_a, D, st)));
+  R2L_RUN("bwd_WoutT", st, (transpose<A, A>(D, E, D, Wout, E, wT, st)));
+  R2L_RUN("bwd_dyg", st, gemm(T, E, D, do_a, D, wT, D, dyg, E, !bf));
+  A* doT = at<A>(ws, p.doT);
+  A* ygT = at<A>(ws, p.ygT);
+  R2L_RUN("bwd_doT", st, (transpose<float, A>(T, D, Tp, dout, D, doT, st)));
+  R2L_RUN("bwd_ygT", st, (transpose<A, A>(T, E, Tp, yg, E, ygT, st)));
+  R2L_RUN("bwd_dWout", st, gemm(D, E, Tp, doT, Tp, ygT, Tp, gr->out_proj_w, E, true));
+  // the scan
+  float* du = at<float>(ws, p.du);
+  float* ddt = at<float>(ws, p.ddt);
+  float* dz = at<float>(ws, p.dz);
+  float* dB = at<float>(ws, p.dB);
+  float* dC = at<float>(ws, p.dC);
+  {
+    const int rc = run_scan_bwd(act, E, R, T, nseq, u, E, dt, E, w->A_log, xdbl + R, xdbl + R + N, P, w->Dskip,
+                                xz + E, 2L * E, dyg, E, du, ddt, gr->A_log, dB, dC, gr->Dskip, dz, cu_seqlens,
+                                at<char>(ws, p.scanb), st);
+    if (rc != R2L_OK) return rc;
+  }
+  // dt_proj + softplus: ddt_pre = ddt sigmoid(pre); d b_dt = sum ddt_pre; d delta = ddt_pre W_dt; dW_dt = ddt_pre^T delta
+  R2L_RUN("bwd_dt_pre", st, (elementwise<kDtPre, float, float>(T, E, ddt, E, dt, E, nullptr, ddt, E, st)));
+  R2L_RUN("bwd_dt_b", st, colsum(T, E, ddt, E, colp, 1.0f, gr->dt_proj_b, st));
+  A* ddt_a = at<A>(ws, p.ddt_a);
+  float* ddelta = at<float>(ws, p.ddelta);
+  R2L_RUN("bwd_ddt_a", st, (elementwise<kConvert, float, A>(T, E, ddt, E, nullptr, 0, nullptr, ddt_a, E, st)));
+  R2L_RUN("bwd_WdtT", st, (transpose<A, A>(E, R, E, Wdt, R, wT, st)));
+  R2L_RUN("bwd_ddelta", st, gemm(T, R, E, ddt_a, E, wT, E, ddelta, R, true));
+  A* ddtT = at<A>(ws, p.ddtT);
+  A* deltaT = at<A>(ws, p.deltaT);
+  R2L_RUN("bwd_ddtT", st, (transpose<float, A>(T, E, Tp, ddt, E, ddtT, st)));
+  R2L_RUN("bwd_deltaT", st, (transpose<A, A>(T, R, Tp, delta, R, deltaT, st)));
+  R2L_RUN("bwd_dWdt", st, gemm(E, R, Tp, ddtT, Tp, deltaT, Tp, gr->dt_proj_w, R, true));
+  // x_proj: dxdbl = [d delta | dB | dC]; du += dxdbl W_x; dW_x = dxdbl^T u
+  A* dxdbl_a = at<A>(ws, p.dxdbl_a);
+  float* dux = at<float>(ws, p.dux);
+  R2L_RUN("bwd_dxdbl", st, concat3<A>(T, R, N, N, ddelta, dB, dC, dxdbl_a, P, st));
+  R2L_RUN("bwd_WxT", st, (transpose<A, A>(P, E, P, Wx, E, wT, st)));
+  R2L_RUN("bwd_dux", st, gemm(T, E, P, dxdbl_a, P, wT, P, dux, E, true));
+  A* dxdblT = at<A>(ws, p.dxdblT);
+  A* uT = at<A>(ws, p.uT);
+  R2L_RUN("bwd_dxdblT", st, (transpose<A, A>(T, P, Tp, dxdbl_a, P, dxdblT, st)));
+  R2L_RUN("bwd_uT", st, (transpose<A, A>(T, E, Tp, u, E, uT, st)));
+  R2L_RUN("bwd_dWx", st, gemm(P, E, Tp, dxdblT, Tp, uT, Tp, gr->x_proj_w, E, true));
+  // conv + SiLU
+  float* dx = at<float>(ws, p.dx);
+  R2L_RUN("bwd_conv_bwd", st, conv_bwd<A>(T, E, xz, 2L * E, cw, cb, du, dux, at<float>(ws, p.dc), dx,
+                                          at<float>(ws, p.convp), gr->conv_w, gr->conv_b, cu_clean, nseq, st));
+  // in_proj: dxz = [dx | dz]; dh = g + dxz W_in; dW_in = dxz^T h
+  A* dxz_a = at<A>(ws, p.dxz_a);
+  float* dhb = at<float>(ws, p.dhb);
+  R2L_RUN("bwd_dxz", st, concat3<A>(T, E, E, 0, dx, dz, nullptr, dxz_a, 2L * E, st));
+  R2L_RUN("bwd_WinT", st, (transpose<A, A>(2 * E, D, 2 * E, Win, D, wT, st)));
+  R2L_RUN("bwd_dh_branch", st, gemm(T, D, 2 * E, dxz_a, 2L * E, wT, 2L * E, dhb, D, true));
+  A* dxzT = at<A>(ws, p.dxzT);
+  A* hT = at<A>(ws, p.hT);
+  R2L_RUN("bwd_dxzT", st, (transpose<A, A>(T, 2 * E, Tp, dxz_a, 2L * E, dxzT, st)));
+  R2L_RUN("bwd_hT", st, (transpose<A, A>(T, D, Tp, h, D, hT, st)));
+  R2L_RUN("bwd_dWin", st, gemm(2 * E, D, Tp, dxzT, Tp, hT, Tp, gr->in_proj_w, D, true));
+  R2L_RUN("bwd_dh", st, (elementwise<kAddTo, A, A>(T, D, g, D, dhb, D, nullptr, dh, D, st)));
+  return R2L_OK;
+}
+
 }  // namespace
 
 // ===========================================================================
@@ -499,44 +756,50 @@ int r2l_scan_bwd(const r2l_dims* d, r2l_dtype act, uint32_t flags, const void* u
   if (!workspace || workspace_bytes < bp.total) return R2L_ERR_WORKSPACE;
   if (((uintptr_t)workspace & (kAlign - 1)) != 0) return R2L_ERR_INVALID_ARG;
   if (n_tokens == 0) return R2L_OK;
-  hipStream_t st = (hipStream_t)stream;
-  const int T = (int)n_tokens;
-  int32_t* cu_clean = at<int32_t>(workspace, bp.off_cu);
-  ChunkDesc* chunks = at<ChunkDesc>(workspace, bp.off_chunks);
-  int32_t* nch = at<int32_t>(workspace, bp.off_n);
-  float* hc = at<float>(workspace, bp.off_hc);
-  // one chunk per sequence: the adjoint sweep carries lambda along a whole sequence
-  R2L_RUN("plan_chunks", st, plan_chunks(cu_seqlens, nseq, T, T, bp.max_chunks, false, cu_clean, chunks, nch, st));
-  // sweep 1: states every 16 tokens, and dz
-  ScanArgs a{};
-  a.T = T; a.E = E; a.R = d->dt_rank; a.ldp = 0;
-  a.u = u; a.ld_u = ld_u; a.dt = dt; a.ld_dt = ld_dt;
-  a.Bm = B; a.Cm = C; a.ld_bc = ld_bc;
-  a.z = z; a.ld_z = ld_z;
-  a.A_log = A_log; a.Dskip = Dskip;
-  a.chunks = chunks; a.n_chunks = nch; a.max_chunks = bp.max_chunks;
-  a.l2r = false;
-  a.dy = dy; a.ld_dy = ld_dy; a.dz = dz; a.hc = hc;
-  // sweep 2: the adjoint, then the sums over channel blocks and sequences
-  ScanBwdArgs b{};
-  b.T = T; b.E = E;
-  b.u = u; b.ld_u = ld_u; b.dt = dt; b.ld_dt = ld_dt;
-  b.Bm = B; b.Cm = C; b.ld_bc = ld_bc;
-  b.A_log = A_log; b.Dskip = Dskip;
-  b.z = z; b.ld_z = ld_z; b.dy = dy; b.ld_dy = ld_dy;
-  b.chunks = chunks; b.n_chunks = nch;
-  b.hc = hc; b.du = du; b.ddt = ddt;
-  b.dbc = at<float>(workspace, bp.off_dbc);
-  b.dA = at<float>(workspace, bp.off_dA);
-  b.dD = at<float>(workspace, bp.off_dD);
-  if (act == R2L_BF16) {
-    R2L_RUN("scan_bwd_states", st, scan_bwd_states<bf16>(a, st));
-    R2L_RUN("scan_bwd_adjoint", st, scan_bwd_adjoint<bf16>(b, bp.max_chunks, dA_log, dB, dC, dDskip, st));
-  } else {
-    R2L_RUN("scan_bwd_states", st, scan_bwd_states<float>(a, st));
-    R2L_RUN("scan_bwd_adjoint", st, scan_bwd_adjoint<float>(b, bp.max_chunks, dA_log, dB, dC, dDskip, st));
+  return run_scan_bwd(act, E, d->dt_rank, (int)n_tokens, nseq, u, ld_u, dt, ld_dt, A_log, B, C, ld_bc, Dskip, z,
+                      ld_z, dy, ld_dy, du, ddt, dA_log, dB, dC, dDskip, dz, cu_seqlens, workspace,
+                      (hipStream_t)stream);
+}
+
+size_t r2l_layer_bwd_workspace_bytes(const r2l_dims* dims, r2l_dtype act, int64_t n_tokens, int32_t nseq,
+                                     int32_t max_seqlen) {
+  if (check_dims(dims) != R2L_OK || check_tokens(act, n_tokens, nseq, max_seqlen) != R2L_OK) return 0;
+  return plan_layer_bwd(dims, act, n_tokens, nseq, max_seqlen).total;
+}
+
+int r2l_layer_bwd(const r2l_dims* d, r2l_dtype act, uint32_t flags, const r2l_weights* w, const void* h_in,
+                  const void* g_out, void* dh, const r2l_grads* gr, const int32_t* cu_seqlens, int32_t nseq,
+                  int64_t n_tokens, int32_t max_seqlen, void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = check_dims(d);
+  if (rc != R2L_OK) return rc;
+  if ((rc = check_tokens(act, n_tokens, nseq, max_seqlen)) != R2L_OK) return rc;
+  if (flags & R2L_FLAG_L2R) return R2L_ERR_UNSUPPORTED;   // the backward runs the default direction only
+  if (flags & ~R2L_FLAG_NO_LN) return R2L_ERR_INVALID_ARG;
+  const bool no_ln = flags & R2L_FLAG_NO_LN;
+  if (!w || !gr || !h_in || !g_out || !dh || !cu_seqlens) return R2L_ERR_INVALID_ARG;
+  if (!w->in_proj_w || !w->conv_w || !w->conv_b || !w->x_proj_w || !w->dt_proj_w || !w->out_proj_w ||
+      !w->dt_proj_b || !w->A_log || !w->Dskip || !w->s || (!no_ln && (!w->ln_w || !w->ln_b)))
+    return R2L_ERR_INVALID_ARG;
+  if (!gr->in_proj_w || !gr->conv_w || !gr->conv_b || !gr->x_proj_w || !gr->dt_proj_w || !gr->out_proj_w ||
+      !gr->dt_proj_b || !gr->A_log || !gr->Dskip || !gr->s || (!no_ln && (!gr->ln_w || !gr->ln_b)))
+    return R2L_ERR_INVALID_ARG;
+  {
+    const void* ptrs[] = {h_in, g_out, dh, w->in_proj_w, w->conv_w, w->conv_b, w->x_proj_w, w->dt_proj_w,
+                          w->out_proj_w};
+    for (const void* q : ptrs)
+      if (!aligned16(q)) return R2L_ERR_INVALID_ARG;
   }
-  return R2L_OK;
+  if (act == R2L_BF16 && d->dt_rank % 8) return R2L_ERR_UNSUPPORTED;   // bf16 GEMMs over K = R and R + 2N
+  const LayerBwdPlan p = plan_layer_bwd(d, act, n_tokens, nseq, max_seqlen);
+  if (!workspace || workspace_bytes < p.total) return R2L_ERR_WORKSPACE;
+  if (((uintptr_t)workspace & (kAlign - 1)) != 0) return R2L_ERR_INVALID_ARG;
+  if (n_tokens == 0) return R2L_OK;
+  hipStream_t st = (hipStream_t)stream;
+  if (act == R2L_BF16)
+    return run_layer_bwd<bf16>(d, act, no_ln, w, (const bf16*)h_in, (const bf16*)g_out, (bf16*)dh, gr, cu_seqlens,
+                               nseq, (int)n_tokens, max_seqlen, workspace, st);
+  return run_layer_bwd<float>(d, act, no_ln, w, (const float*)h_in, (const float*)g_out, (float*)dh, gr, cu_seqlens,
+                              nseq, (int)n_tokens, max_seqlen, workspace, st);
 }
 
 int r2l_gemm_nt(r2l_dtype act, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,

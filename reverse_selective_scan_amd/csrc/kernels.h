@@ -111,6 +111,30 @@ template <typename T>
 hipError_t scan_bwd_adjoint(const ScanBwdArgs& a, int max_chunks, float* dA_log, float* dB, float* dC,
                             float* dDskip, hipStream_t st);
 
+// ---- backward of the layer (layer_bwd.hip) ----
+// out [cols, rows_pad] = in [rows, cols]^T, zero columns past rows.
+template <typename Tin, typename Tout>
+hipError_t transpose(int rows, int cols, int rows_pad, const Tin* in, long ld_in, Tout* out, hipStream_t st);
+enum EwOp { kConvert = 0, kSoftplusBias = 1, kDtPre = 2, kAddTo = 3 };
+template <int OP, typename Tin, typename Tout>
+hipError_t elementwise(int rows, int cols, const Tin* in, long ld_in, const float* aux, long ld_aux,
+                       const float* vec, Tout* out, long ld_out, hipStream_t st);
+// out[c] = scale * sum_r in[r][c]; part: colsum_parts(rows) * cols floats.
+int colsum_parts(int rows);
+hipError_t colsum(int rows, int cols, const float* in, long ld, float* part, float scale, float* out, hipStream_t st);
+template <typename T>
+hipError_t ln_gate_bwd(int T_, int D, const T* g, const float* o, const float* gamma, const float* beta,
+                       const float* s, bool no_ln, float eps, float* dout, float* gx, float* gr, hipStream_t st);
+// part: conv_bwd_parts(T) * E * 5 floats.
+int conv_bwd_parts(int T_);
+template <typename T>
+hipError_t conv_bwd(int T_, int E, const T* x, long ld_x, const T* cw, const T* cb, const float* du, const float* du2,
+                    float* dc, float* dx, float* part, float* dw, float* db, const int32_t* cu, int nseq,
+                    hipStream_t st);
+template <typename Tout>
+hipError_t concat3(int T_, int na, int nb, int nc, const float* a, const float* b, const float* c, Tout* out,
+                   long ld_out, hipStream_t st);
+
 template <typename T, typename O>
 hipError_t ln_gate(int T_, int D, const O* o, const T* h_in, T* h_out, const float* gamma,
                    const float* beta, const float* s, float* branch, bool no_ln, float eps,
