@@ -57,6 +57,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="approximate CPU time spent on the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--backward", action="store_true",
+                    help="time r2l_layer_bwd (forward recompute + gradients) instead of the forward")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB first (counter calibration)")
     ap.add_argument("--calib-mib", type=float, default=0.0,
@@ -74,6 +76,10 @@ def main():
               "(sequences shard across GPUs with no communication; see DESIGN.md). "
               f"--gpus {args.gpus} is not supported.", file=sys.stderr)
         sys.exit(2)
+
+    if args.backward:
+        bench_backward(args)
+        return
 
     import torch
 
@@ -229,6 +235,96 @@ def main():
         "roofline": roofline,
         "kernels": kernels,
         "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+def bench_backward(args):
+    """One step = one r2l_layer_bwd call over the whole batch: the forward
+    recomputed into the workspace, then every gradient (h, the Mamba block's
+    weights, the LayerNorm's and s).  GEMM work per step, with TDE = T*D*E:
+    recompute 6 TDE (in_proj 4, out_proj 2), backward 12 TDE (out_proj input
+    2 and weight 2, in_proj input 4 and weight 4), plus the x_proj/dt_proj
+    products, which are small."""
+    import torch
+
+    from reverse_selective_scan_amd import binding as B
+    from reverse_selective_scan_amd import synth
+
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    wl = synth.workloads()[args.workload]
+    T, D, E, N, R = wl.n_tokens, wl.d_model, wl.d_inner, wl.d_state, wl.dt_rank
+    P = R + 2 * N
+    W = synth.make_weights(wl, affine_ln=True)
+    w = B.to_device_weights(W, torch.bfloat16, dev)
+    h = torch.from_numpy(synth.make_hidden(wl)).to(torch.bfloat16).to(dev)
+    g = torch.from_numpy(synth.make_hidden(wl, hook=9)).to(torch.bfloat16).to(dev)
+    cu, nseq, max_seqlen = B.cu_seqlens_device(wl.cu_seqlens(), T, dev)
+    need = B.r2l_layer_bwd_workspace_bytes(B.dims_of(w), B.R2L_BF16, T, nseq, max_seqlen)
+    ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    dh = torch.empty_like(h)
+    grads = {k: torch.empty(w[k].shape, dtype=torch.float32, device=dev) for k, _ in B.Grads._fields_}
+
+    def step():
+        B.r2l_layer_bwd(h, w, cu, g, dh=dh, workspace=ws, grads=grads, nseq=nseq, max_seqlen=max_seqlen)
+
+    print(f"[bench] backward {wl.name}: T={T} D={D} E={E} N={N} R={R}, workspace {need / 2**30:.2f} GiB, "
+          f"warmup {args.warmup}", flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = e0.elapsed_time(e1) / args.steps
+    print(f"[bench] timed {args.steps} backward steps: {ms_step:.3f} ms/step", flush=True)
+
+    B.timing_reset()
+    B.timing_enable(True)
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    kt = B.timing_read()
+    B.timing_enable(False)
+    TDE = float(T) * D * E
+    flops = {"bwd_in_proj": 4 * TDE, "bwd_out_proj": 2 * TDE, "bwd_dyg": 2 * TDE, "bwd_dWout": 2 * TDE,
+             "bwd_dh_branch": 4 * TDE, "bwd_dWin": 4 * TDE, "bwd_dt_proj": 2.0 * T * R * E,
+             "bwd_ddelta": 2.0 * T * R * E, "bwd_dWdt": 2.0 * T * R * E, "bwd_dux": 2.0 * T * P * E,
+             "bwd_dWx": 2.0 * T * P * E}
+    kernels = {}
+    for name, (tot_ms, cnt) in sorted(kt.items(), key=lambda kv: -kv[1][0]):
+        avg = tot_ms / max(cnt, 1)
+        k = {"avg_ms": round(avg, 4), "launches": int(cnt), "share": round(tot_ms / args.steps / ms_step, 4)}
+        if name in flops:
+            tf = flops[name] / (avg * 1e-3) / 1e12
+            k.update(bound="mfma", achieved_tflops=round(tf, 1), frac=round(tf / MFMA_BF16_PEAK_TFLOPS, 4))
+        kernels[name] = k
+    gemm_ms = sum(kernels[n]["avg_ms"] for n in flops if n in kernels)
+    gemm_tflops = sum(flops.values()) / (gemm_ms * 1e-3) / 1e12 if gemm_ms else None
+    rec = {
+        "metric": "R2L layer backward tokens/sec (forward recompute + all gradients) at B=8,L=4096,D=2048",
+        "value": round(T / (ms_step * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded; random-init weights of the layer's shapes)",
+        "config": {"workload": wl.name, "pass": "backward", "batch": nseq, "seq_len": max_seqlen, "n_tokens": T,
+                   "d_model": D, "d_inner": E, "d_state": N, "dt_rank": R, "d_conv": wl.d_conv},
+        "gemm_ms": round(gemm_ms, 4),
+        "gemm_tflops": None if gemm_tflops is None else round(gemm_tflops, 1),
+        "gemm_frac": None if gemm_tflops is None else round(gemm_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+        "kernels": kernels,
     }
     print(json.dumps(rec), flush=True)
 

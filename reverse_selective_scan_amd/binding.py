@@ -146,6 +146,10 @@ def r2l_layer_workspace_bytes(dims: Dims, act: int, n_tokens: int, nseq: int, ma
     return int(lib().r2l_layer_workspace_bytes(C.byref(dims), act, n_tokens, nseq, max_seqlen))
 
 
+def r2l_layer_bwd_workspace_bytes(dims: Dims, act: int, n_tokens: int, nseq: int, max_seqlen: int) -> int:
+    return int(lib().r2l_layer_bwd_workspace_bytes(C.byref(dims), act, n_tokens, nseq, max_seqlen))
+
+
 def r2l_layer_fwd(h: torch.Tensor, w: Dict[str, torch.Tensor], cu_seqlens, *, out: Optional[torch.Tensor] = None,
                   flags: int = 0, branch_out: Optional[torch.Tensor] = None,
                   workspace: Optional[torch.Tensor] = None, max_seqlen: Optional[int] = None,
@@ -188,19 +192,34 @@ def r2l_layer_fwd(h: torch.Tensor, w: Dict[str, torch.Tensor], cu_seqlens, *, ou
 
 def r2l_layer_bwd(h: torch.Tensor, w: Dict[str, torch.Tensor], cu_seqlens, g_out: torch.Tensor, *,
                   dh: Optional[torch.Tensor] = None, flags: int = 0,
-                  workspace: Optional[torch.Tensor] = None):
+                  workspace: Optional[torch.Tensor] = None,
+                  grads: Optional[Dict[str, torch.Tensor]] = None,
+                  max_seqlen: Optional[int] = None, nseq: Optional[int] = None):
     """Gradient of r2l_layer_fwd: given g_out = dL/dh+, returns (dh, grads)
-    with grads a dict of fp32 device tensors named like the weights."""
+    with grads a dict of fp32 device tensors named like the weights (plus
+    "s"); pass `grads` (and `dh`, `workspace`) to reuse buffers.  cu_seqlens
+    as for r2l_layer_fwd."""
     _need(h, "h")
     act = _act(h)
     T = h.shape[0]
     _need(g_out, "g_out", h.dtype)
-    cu_dev, nseq, max_seqlen = cu_seqlens_device(cu_seqlens, T, h.device)
+    if isinstance(cu_seqlens, torch.Tensor) and cu_seqlens.is_cuda:
+        _need(cu_seqlens, "cu_seqlens", torch.int32)
+        if nseq is None or max_seqlen is None:
+            raise ValueError("device cu_seqlens needs nseq and max_seqlen")
+        cu_dev = cu_seqlens
+    else:
+        cu_dev, nseq, max_seqlen = cu_seqlens_device(cu_seqlens, T, h.device)
     d = dims_of(w)
     if dh is None:
         dh = torch.empty_like(h)
-    grads = {k: torch.empty(w[k].shape, dtype=torch.float32, device=h.device) for k, _ in Grads._fields_}
-    need = int(lib().r2l_layer_bwd_workspace_bytes(C.byref(d), act, T, nseq, max_seqlen))
+    if grads is None:
+        grads = {k: torch.empty(w[k].shape, dtype=torch.float32, device=h.device) for k, _ in Grads._fields_}
+    for k, _ in Grads._fields_:
+        _need(grads[k], "grads[" + k + "]", torch.float32)
+        if grads[k].numel() != w[k].numel():
+            raise ValueError(f"grads[{k}] has {grads[k].numel()} elements, the weight {w[k].numel()}")
+    need = r2l_layer_bwd_workspace_bytes(d, act, T, nseq, max_seqlen)
     if workspace is None or workspace.numel() < need:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=h.device)
     W = Weights(**{f[0]: _ptr(w[f[0]]) for f in Weights._fields_})
@@ -325,8 +344,14 @@ def timing_reset() -> None:
     lib().r2l_timing_reset()
 
 
-def timing_read(max_names: int = 32) -> Dict[str, tuple]:
-    """{kernel name: (total ms, launches)} since the last read/reset."""
+def timing_read(max_names: Optional[int] = None) -> Dict[str, tuple]:
+    """{kernel name: (total ms, launches)} since the last reset (every name
+    unless max_names is given)."""
+    if max_names is None:
+        max_names = int(lib().r2l_timing_read(None, None, None, 0))
+        if max_names < 0:
+            _check("r2l_timing_read", max_names)
+    max_names = max(max_names, 1)
     names = (C.c_char_p * max_names)()
     tot = (C.c_double * max_names)()
     cnt = (C.c_int64 * max_names)()
