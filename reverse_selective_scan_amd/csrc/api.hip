@@ -293,8 +293,8 @@ int run_scan_bwd(r2l_dtype act, int E, int R, int T, int nseq, const void* u, in
 // multiple of 128, in the transposes), the forward scan's and the scan
 // backward's own regions, and the GEMM split scratch.
 struct LayerBwdPlan {
-  size_t xz, u, xdbl, delta, dt, yg, o, scanf, dout, gx, gr, do_a, doT, ygT, wT, dyg, du, ddt, dz, dB, dC, scanb,
-      ddt_a, ddtT, deltaT, ddelta, dxdbl_a, dxdblT, uT, dux, dc, dx, convp, dxz_a, dxzT, hT, dhb, colp, scratch;
+  size_t xz, u, xdbl, xdbl2, xdbl3, delta, dt, yg, o, scanf, dout, gx, gr, do_a, doT, ygT, wT, dyg, du, ddt, dz, dB,
+      dC, scanb, ddt_a, ddtT, deltaT, ddelta, dxdbl_a, dxdblT, uT, dux, convp, dxz_a, dxzT, hT, dhb, colp, scratch;
   ScanPlan sp;
   int Tp;
   size_t total;
@@ -312,6 +312,8 @@ LayerBwdPlan plan_layer_bwd(const r2l_dims* d, r2l_dtype act, int64_t T, int32_t
   p.xz = take(Tz * 2 * E * sa);
   p.u = take(Tz * E * sa);
   p.xdbl = take(Tz * P * f);
+  p.xdbl2 = take(act == R2L_BF16 ? Tz * P * f : 0);
+  p.xdbl3 = take(act == R2L_BF16 ? Tz * P * f : 0);
   p.delta = take(Tz * R * sa);
   p.dt = take(Tz * E * f);
   p.yg = take(Tz * E * sa);
@@ -319,7 +321,7 @@ LayerBwdPlan plan_layer_bwd(const r2l_dims* d, r2l_dtype act, int64_t T, int32_t
   p.sp = plan_scan((int)E, T, nseq, max_seqlen, 0);
   p.scanf = take(p.sp.total);
   p.dout = take(Tz * D * f);
-  p.gx = take(Tz * 2 * D * f);
+  p.gx = take((size_t)ln_bwd_parts((int)T) * 2 * D * f);
   p.gr = take(Tz * f);
   p.do_a = take(Tz * D * sa);
   p.doT = take(D * Tp * sa);
@@ -341,8 +343,6 @@ LayerBwdPlan plan_layer_bwd(const r2l_dims* d, r2l_dtype act, int64_t T, int32_t
   p.dxdblT = take(P * Tp * sa);
   p.uT = take(E * Tp * sa);
   p.dux = take(Tz * E * f);
-  p.dc = take(Tz * E * f);
-  p.dx = take(Tz * E * f);
   p.convp = take((size_t)conv_bwd_parts((int)T) * E * 5 * f);
   p.dxz_a = take(Tz * 2 * E * sa);
   p.dxzT = take(2 * E * Tp * sa);
@@ -395,7 +395,18 @@ int run_layer_bwd(const r2l_dims* d, r2l_dtype act, bool no_ln, const r2l_weight
   R2L_RUN("bwd_in_proj", st, gemm(T, 2 * E, D, h, D, Win, D, xz, 2L * E, false));
   if constexpr (std::is_same<A, bf16>::value) {
     if (P <= 256) {
-      R2L_RUN("bwd_conv", st, conv_xproj_bf16(T, E, P, xz, 2L * E, cw, cb, Wx, u, xdbl, cu_clean, nseq, false, st));
+      // xdbl as the forward computes it (the split-K kernel for large inputs), u on its own
+      R2L_RUN("bwd_u", st, conv_silu<bf16>(T, E, xz, 2L * E, cw, cb, u, cu_clean, nseq, false, st));
+      if ((T + 127) / 128 >= ncu && (long)((T + 127) / 128) * (E / 32) < (1L << 31)) {
+        float* xdbl2 = at<float>(ws, p.xdbl2);
+        float* xdbl3 = at<float>(ws, p.xdbl3);
+        R2L_RUN("bwd_conv", st, conv_xproj_bf16_sk(T, E, P, xz, 2L * E, cw, cb, Wx, xdbl, xdbl2, xdbl3, cu_clean,
+                                                   nseq, ncu, false, st));
+        R2L_RUN("bwd_conv_sum", st, conv_sk_sum(T, E, P, xdbl, xdbl2, xdbl3, ncu, st));
+      } else {
+        R2L_RUN("bwd_conv", st, conv_xproj_bf16(T, E, P, xz, 2L * E, cw, cb, Wx, nullptr, xdbl, cu_clean, nseq, false,
+                                                st, scratch, kSplitScratch, ncu));
+      }
     } else {
       R2L_RUN("bwd_conv", st, conv_silu<bf16>(T, E, xz, 2L * E, cw, cb, u, cu_clean, nseq, false, st));
       R2L_RUN("bwd_x_proj", st, gemm(T, P, E, u, E, Wx, E, xdbl, P, true));
@@ -429,8 +440,9 @@ int run_layer_bwd(const r2l_dims* d, r2l_dtype act, bool no_ln, const r2l_weight
   float* colp = at<float>(ws, p.colp);
   R2L_RUN("bwd_ln_gate", st, ln_gate_bwd<A>(T, D, g, o, w->ln_w, w->ln_b, w->s, no_ln, R2L_LN_EPS, dout, gx, grr, st));
   if (!no_ln) {
-    R2L_RUN("bwd_ln_w", st, colsum(T, D, gx, 2L * D, colp, 1.0f, gr->ln_w, st));
-    R2L_RUN("bwd_ln_b", st, colsum(T, D, gx + D, 2L * D, colp, 1.0f, gr->ln_b, st));
+    const int np = ln_bwd_parts(T);
+    R2L_RUN("bwd_ln_w", st, colsum(np, D, gx, 2L * D, colp, 1.0f, gr->ln_w, st));
+    R2L_RUN("bwd_ln_b", st, colsum(np, D, gx + D, 2L * D, colp, 1.0f, gr->ln_b, st));
   }
   R2L_RUN("bwd_s", st, colsum(T, 1, grr, 1, colp, 1.0f, gr->s, st));
   // out_proj: dyg = do W_out, dW_out = do^T yg
@@ -480,14 +492,13 @@ int run_layer_bwd(const r2l_dims* d, r2l_dtype act, bool no_ln, const r2l_weight
   R2L_RUN("bwd_dxdblT", st, (transpose<A, A>(T, P, Tp, dxdbl_a, P, dxdblT, st)));
   R2L_RUN("bwd_uT", st, (transpose<A, A>(T, E, Tp, u, E, uT, st)));
   R2L_RUN("bwd_dWx", st, gemm(P, E, Tp, dxdblT, Tp, uT, Tp, gr->x_proj_w, E, true));
-  // conv + SiLU
-  float* dx = at<float>(ws, p.dx);
-  R2L_RUN("bwd_conv_bwd", st, conv_bwd<A>(T, E, xz, 2L * E, cw, cb, du, dux, at<float>(ws, p.dc), dx,
-                                          at<float>(ws, p.convp), gr->conv_w, gr->conv_b, cu_clean, nseq, st));
-  // in_proj: dxz = [dx | dz]; dh = g + dxz W_in; dW_in = dxz^T h
+  // conv + SiLU: dx goes straight into the x half of dxz = [dx | dz]
   A* dxz_a = at<A>(ws, p.dxz_a);
+  R2L_RUN("bwd_conv_bwd", st, conv_bwd<A>(T, E, xz, 2L * E, cw, cb, du, dux, dxz_a, 2L * E, at<float>(ws, p.convp),
+                                          gr->conv_w, gr->conv_b, cu_clean, nseq, st));
+  // in_proj: dh = g + dxz W_in; dW_in = dxz^T h
   float* dhb = at<float>(ws, p.dhb);
-  R2L_RUN("bwd_dxz", st, concat3<A>(T, E, E, 0, dx, dz, nullptr, dxz_a, 2L * E, st));
+  R2L_RUN("bwd_dz", st, (elementwise<kConvert, float, A>(T, E, dz, E, nullptr, 0, nullptr, dxz_a + E, 2L * E, st)));
   R2L_RUN("bwd_WinT", st, (transpose<A, A>(2 * E, D, 2 * E, Win, D, wT, st)));
   R2L_RUN("bwd_dh_branch", st, gemm(T, D, 2 * E, dxz_a, 2L * E, wT, 2L * E, dhb, D, true));
   A* dxzT = at<A>(ws, p.dxzT);

@@ -22,23 +22,41 @@ __global__ __launch_bounds__(256) void conv_silu_kernel(int Tn, int E, const T* 
                                                         long ld_x, const T* __restrict__ cw,
                                                         const T* __restrict__ cb, T* __restrict__ u,
                                                         const int32_t* __restrict__ cu, int nseq) {
-  const int lane = lane_id(), w = wave_id();
+  const int lane = lane_id();
   const int e = blockIdx.y * 64 + lane;
-  const int tb = blockIdx.x * 32 + w * 8;
+  // a wave owns 8 consecutive tokens of 64 channels (the token index is
+  // wave-uniform, so the sequence lookups are too)
+  const int t0 = __builtin_amdgcn_readfirstlane(blockIdx.x * 32 + wave_id() * 8);
+  if (t0 >= Tn) return;
   float wt[KC];
 #pragma unroll
   for (int k = 0; k < KC; ++k) wt[k] = to_f32(cw[(long)e * KC + k]);
   const float b = to_f32(cb[e]);
+  // rows t0 .. t0+10 (R2L) or t0-3 .. t0+7 (L2R), all loads first
+  constexpr int NR = 8 + KC - 1;
+  const int rbase = L2R ? t0 - (KC - 1) : t0;
+  float xv[NR];
+#pragma unroll
+  for (int i = 0; i < NR; ++i) {
+    const int row = rbase + i;
+    xv[i] = row >= 0 && row < Tn ? to_f32(x[(long)row * ld_x + e]) : 0.0f;
+  }
+  // the current sequence [sl, se); looked up again only past its end
+  int sl = seq_start_of(cu, nseq, t0), se = seq_end_of(cu, nseq, t0, Tn);
+#pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const int t = tb + i;
+    const int t = t0 + i;
     if (t >= Tn) break;
-    // the sequence end (R2L) or start (L2R) bounds the taps
-    const int sb = L2R ? seq_start_of(cu, nseq, t) : seq_end_of(cu, nseq, t, Tn);
+    if (t >= se) {
+      sl = seq_start_of(cu, nseq, t);
+      se = seq_end_of(cu, nseq, t, Tn);
+    }
     float c = b;
 #pragma unroll
     for (int j = 0; j < KC; ++j) {
-      const int row = L2R ? t - j : t + j;
-      if (L2R ? row >= sb : row < sb) c = fmaf(wt[KC - 1 - j], to_f32(x[(long)row * ld_x + e]), c);
+      const int row = L2R ? t - j : t + j;     // rbase + (L2R ? i + KC - 1 - j : i + j)
+      const float xr = xv[L2R ? i + KC - 1 - j : i + j];
+      if (L2R ? row >= sl : row < se) c = fmaf(wt[KC - 1 - j], xr, c);
     }
     u[(long)t * E + e] = from_f32<T>(silu_fast(c));
   }

@@ -480,10 +480,10 @@ template <int G>
 static void launch_big(int M, int N, int K, const bf16* A, long lda, const bf16* B, long ldb, void* C,
                        long ldc, bool out_f32, int n_dp, int rem, int splits, int nk, float* ws,
                        hipStream_t st) {
-  if (out_f32)
+  if (n_dp > 0 && out_f32)
     hipLaunchKernelGGL((gemm_bf16_big_kernel<true, G, false>), dim3(n_dp), dim3(256), 0, st, M, N, K, A, lda,
                        B, ldb, C, ldc, n_dp, 0, 0, (float*)nullptr);
-  else
+  else if (n_dp > 0)
     hipLaunchKernelGGL((gemm_bf16_big_kernel<false, G, false>), dim3(n_dp), dim3(256), 0, st, M, N, K, A, lda,
                        B, ldb, C, ldc, n_dp, 0, 0, (float*)nullptr);
   if (splits) {
@@ -520,10 +520,12 @@ hipError_t gemm_bf16_nt(int M, int N, int K, const bf16* A, long lda, const bf16
     // instead, and their fp32 partial sums added in a fixed order.  The split
     // costs two launches and the partials' traffic, so it is used only for a
     // small leftover (measured: a gain at 1/32 of a round, a loss at 1/8).
+    // Fewer tiles than CUs (a long K over a small output, e.g. a weight
+    // gradient summed over tokens): every tile is split along K the same way.
     const int nk = K / kBigBK;
     const int rem = ncu > 0 ? (int)(big_tiles % ncu) : 0;
     int splits = 0;
-    if (ws != nullptr && rem > 0 && rem * 16 <= ncu && big_tiles > ncu) {
+    if (ws != nullptr && rem > 0 && (rem * 16 <= ncu || big_tiles * 2 <= ncu)) {
       for (int s = 64; s >= 2; s /= 2)
         if ((long)rem * s <= ncu && nk % (s * kBigST) == 0 &&
             (size_t)rem * s * kBigBM * kBigBN * sizeof(float) <= ws_bytes && ((uintptr_t)ws & 15) == 0) {

@@ -122,14 +122,17 @@ hipError_t elementwise(int rows, int cols, const Tin* in, long ld_in, const floa
 // out[c] = scale * sum_r in[r][c]; part: colsum_parts(rows) * cols floats.
 int colsum_parts(int rows);
 hipError_t colsum(int rows, int cols, const float* in, long ld, float* part, float scale, float* out, hipStream_t st);
+// part: ln_bwd_parts(T) * 2D floats (per-wave sums of th [g xhat | g]).
+int ln_bwd_parts(int T_);
 template <typename T>
 hipError_t ln_gate_bwd(int T_, int D, const T* g, const float* o, const float* gamma, const float* beta,
-                       const float* s, bool no_ln, float eps, float* dout, float* gx, float* gr, hipStream_t st);
-// part: conv_bwd_parts(T) * E * 5 floats.
+                       const float* s, bool no_ln, float eps, float* dout, float* part, float* gr, hipStream_t st);
+// dx (act, row stride ld_dx) from du (+ du2); dw, db summed over tokens.
+// cu: sanitised offsets.  part: conv_bwd_parts(T) * E * 5 floats.
 int conv_bwd_parts(int T_);
 template <typename T>
 hipError_t conv_bwd(int T_, int E, const T* x, long ld_x, const T* cw, const T* cb, const float* du, const float* du2,
-                    float* dc, float* dx, float* part, float* dw, float* db, const int32_t* cu, int nseq,
+                    T* dx, long ld_dx, float* part, float* dw, float* db, const int32_t* cu, int nseq,
                     hipStream_t st);
 template <typename Tout>
 hipError_t concat3(int T_, int na, int nb, int nc, const float* a, const float* b, const float* c, Tout* out,

@@ -120,93 +120,137 @@ hipError_t colsum(int rows, int cols, const float* in, long ld, float* part, flo
 }
 
 // ---------------------------------------------------------------------------
-// LayerNorm + gate backward, one wave per token row (D a multiple of 64).
+// LayerNorm + gate backward (D a multiple of 64).
 //   h+ = h + th r, r = gamma xhat + beta, xhat = (o - mu) / sigma, th = tanh(s):
 //   do = th / sigma (gamma g - mean(gamma g) - xhat mean(gamma g xhat));
-//   gx[t] = th [g xhat | g] (f32 [T, 2D]: summed over t, d gamma and d beta);
+//   part[block] = sum over the block's rows of th [g xhat | g] (f32 [2D]; the
+//   partials, summed over blocks in order, are d gamma and d beta);
 //   gr[t] = (1 - th^2) sum_d g r (summed over t, d s).
-// Without the LayerNorm r = o: do = th g.
+// Without the LayerNorm r = o: do = th g, and part is not written.
+// A block walks kLnRowsPerBlock rows; each of its waves owns a quarter of
+// the columns (lane: columns q + 64 i + lane), so the per-column sums stay in
+// a few registers.  The row statistics are summed over the lanes, then over
+// the four waves through LDS in a fixed order (three rounds per row).
 // ---------------------------------------------------------------------------
+constexpr int kLnRowsPerBlock = 16;
+
 template <typename T, int VPL>
 __global__ __launch_bounds__(256) void ln_gate_bwd_kernel(int Tn, int D, const T* __restrict__ g, const float* __restrict__ o,
                                                           const float* __restrict__ gamma, const float* __restrict__ beta,
                                                           const float* __restrict__ s, int no_ln, float eps,
-                                                          float* __restrict__ dout, float* __restrict__ gx,
+                                                          float* __restrict__ dout, float* __restrict__ part,
                                                           float* __restrict__ gr) {
-  const int lane = lane_id();
-  const int row = blockIdx.x * 4 + wave_id();
-  if (row >= Tn) return;
-  const int cnt = D / 64;
+  __shared__ float red[3][4][4];
+  const int lane = lane_id(), w = wave_id();
+  const int cw = D / 4;                       // columns per wave (a multiple of 16)
+  const int q0 = w * cw;                      // this wave's first column
+  const int row0 = blockIdx.x * kLnRowsPerBlock;
   const float th = tanhf(s[0]);
-  float x[VPL], gg[VPL];
-  float sum = 0.0f;
-#pragma unroll
-  for (int i = 0; i < VPL; ++i) {
-    const int dd = i * 64 + lane;
-    x[i] = i < cnt ? o[(long)row * D + dd] : 0.0f;
-    gg[i] = i < cnt ? to_f32(g[(long)row * D + dd]) : 0.0f;
-    sum += x[i];
-  }
   const float invD = 1.0f / (float)D;
-  if (no_ln) {
-    float p = 0.0f;
-#pragma unroll
-    for (int i = 0; i < VPL; ++i)
-      if (i < cnt) {
-        const int dd = i * 64 + lane;
-        dout[(long)row * D + dd] = th * gg[i];
-        p = fmaf(gg[i], x[i], p);
-      }
-    p = wave_sum(p);
-    if (lane == 0) gr[row] = (1.0f - th * th) * p;
-    return;
-  }
-  const float mu = wave_sum(sum) * invD;
-  float sq = 0.0f;
+  float gm[VPL], bt[VPL], ax[VPL], ag[VPL];
 #pragma unroll
   for (int i = 0; i < VPL; ++i) {
-    x[i] = i < cnt ? x[i] - mu : 0.0f;
-    sq = fmaf(x[i], x[i], sq);
+    const int dd = q0 + i * 64 + lane;
+    const bool ok = !no_ln && i * 64 + lane < cw;
+    gm[i] = ok ? gamma[dd] : 0.0f;
+    bt[i] = ok ? beta[dd] : 0.0f;
+    ax[i] = ag[i] = 0.0f;
   }
-  const float rstd = 1.0f / sqrtf(wave_sum(sq) * invD + eps);
-  float m1 = 0.0f, m2 = 0.0f, p = 0.0f;
+  // the four waves' partial sums of one statistic, added in wave order
+  auto block_sum = [&](int slot, int k, float v) __attribute__((always_inline)) {
+    v = wave_sum(v);
+    if (lane == 0) red[slot][w][k] = v;
+    __syncthreads();
+    return ((red[slot][0][k] + red[slot][1][k]) + red[slot][2][k]) + red[slot][3][k];
+  };
+  const int nrows = min(kLnRowsPerBlock, Tn - row0);
+  for (int k = 0; k < nrows; ++k) {
+    const int row = row0 + k;
+    float x[VPL], gg[VPL];
 #pragma unroll
-  for (int i = 0; i < VPL; ++i)
-    if (i < cnt) {
-      const int dd = i * 64 + lane;
+    for (int i = 0; i < VPL; ++i) {
+      const int dd = q0 + i * 64 + lane;
+      const bool ok = i * 64 + lane < cw;
+      x[i] = ok ? o[(long)row * D + dd] : 0.0f;
+      gg[i] = ok ? to_f32(g[(long)row * D + dd]) : 0.0f;
+    }
+    if (no_ln) {
+      float p = 0.0f;
+#pragma unroll
+      for (int i = 0; i < VPL; ++i)
+        if (i * 64 + lane < cw) {
+          dout[(long)row * D + q0 + i * 64 + lane] = th * gg[i];
+          p = fmaf(gg[i], x[i], p);
+        }
+      p = block_sum(0, 0, p);
+      if (threadIdx.x == 0) gr[row] = (1.0f - th * th) * p;
+      __syncthreads();   // red is rewritten by the next row
+      continue;
+    }
+    float sum = 0.0f;
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) sum += x[i];
+    const float mu = block_sum(0, 0, sum) * invD;
+    float sq = 0.0f;
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) {
+      x[i] = i * 64 + lane < cw ? x[i] - mu : 0.0f;
+      sq = fmaf(x[i], x[i], sq);
+    }
+    const float rstd = 1.0f / sqrtf(block_sum(1, 0, sq) * invD + eps);
+    float m1 = 0.0f, m2 = 0.0f, p = 0.0f;
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) {
       x[i] *= rstd;                                    // xhat
-      const float gg_gamma = gg[i] * gamma[dd];
+      const float gg_gamma = gg[i] * gm[i];
       m1 += gg_gamma;
       m2 = fmaf(gg_gamma, x[i], m2);
-      p = fmaf(gg[i], fmaf(gamma[dd], x[i], beta[dd]), p);
-      gx[(long)row * 2 * D + dd] = th * gg[i] * x[i];
-      gx[(long)row * 2 * D + D + dd] = th * gg[i];
+      p = fmaf(gg[i], fmaf(gm[i], x[i], bt[i]), p);
+      ax[i] = fmaf(th * gg[i], x[i], ax[i]);
+      ag[i] = fmaf(th, gg[i], ag[i]);
     }
-  m1 = wave_sum(m1) * invD;
-  m2 = wave_sum(m2) * invD;
-  p = wave_sum(p);
-  if (lane == 0) gr[row] = (1.0f - th * th) * p;
+    // three statistics in one round: slot 2, entries 0..2
+    m1 = wave_sum(m1);
+    m2 = wave_sum(m2);
+    p = wave_sum(p);
+    if (lane == 0) { red[2][w][0] = m1; red[2][w][1] = m2; red[2][w][2] = p; }
+    __syncthreads();
+    m1 = (((red[2][0][0] + red[2][1][0]) + red[2][2][0]) + red[2][3][0]) * invD;
+    m2 = (((red[2][0][1] + red[2][1][1]) + red[2][2][1]) + red[2][3][1]) * invD;
+    p = ((red[2][0][2] + red[2][1][2]) + red[2][2][2]) + red[2][3][2];
+    if (threadIdx.x == 0) gr[row] = (1.0f - th * th) * p;
 #pragma unroll
-  for (int i = 0; i < VPL; ++i)
-    if (i < cnt) {
-      const int dd = i * 64 + lane;
-      dout[(long)row * D + dd] = th * rstd * (gg[i] * gamma[dd] - m1 - x[i] * m2);
-    }
+    for (int i = 0; i < VPL; ++i)
+      if (i * 64 + lane < cw) dout[(long)row * D + q0 + i * 64 + lane] = th * rstd * (gg[i] * gm[i] - m1 - x[i] * m2);
+    // (slot 0 is rewritten by the next row only after every wave has passed
+    // that row's first round, i.e. after all reads of this row's slot 2)
+  }
+  if (!no_ln && nrows > 0) {
+#pragma unroll
+    for (int i = 0; i < VPL; ++i)
+      if (i * 64 + lane < cw) {
+        const int dd = q0 + i * 64 + lane;
+        part[(long)blockIdx.x * 2 * D + dd] = ax[i];
+        part[(long)blockIdx.x * 2 * D + D + dd] = ag[i];
+      }
+  }
 }
+
+int ln_bwd_parts(int Tn) { return (Tn + kLnRowsPerBlock - 1) / kLnRowsPerBlock; }
 
 template <typename T>
 hipError_t ln_gate_bwd(int Tn, int D, const T* g, const float* o, const float* gamma, const float* beta,
-                       const float* s, bool no_ln, float eps, float* dout, float* gx, float* gr, hipStream_t st) {
+                       const float* s, bool no_ln, float eps, float* dout, float* part, float* gr, hipStream_t st) {
   if (Tn <= 0) return hipSuccess;
-  dim3 grid((Tn + 3) / 4), block(256);
-  const int cnt = D / 64, nl = no_ln ? 1 : 0;
+  dim3 grid(ln_bwd_parts(Tn)), block(256);
+  const int cnt = (D / 4 + 63) / 64, nl = no_ln ? 1 : 0;   // columns per lane
 #define R2L_LNB(V) \
-  hipLaunchKernelGGL((ln_gate_bwd_kernel<T, V>), grid, block, 0, st, Tn, D, g, o, gamma, beta, s, nl, eps, dout, gx, gr)
-  if (cnt <= 4) R2L_LNB(4);
+  hipLaunchKernelGGL((ln_gate_bwd_kernel<T, V>), grid, block, 0, st, Tn, D, g, o, gamma, beta, s, nl, eps, dout, part, gr)
+  if (cnt <= 1) R2L_LNB(1);
+  else if (cnt <= 4) R2L_LNB(4);
+  else if (cnt <= 8) R2L_LNB(8);
   else if (cnt <= 16) R2L_LNB(16);
-  else if (cnt <= 32) R2L_LNB(32);
-  else if (cnt <= 64) R2L_LNB(64);
-  else R2L_LNB(128);
+  else R2L_LNB(32);
 #undef R2L_LNB
   return hipGetLastError();
 }
@@ -220,57 +264,118 @@ template hipError_t ln_gate_bwd<bf16>(int, int, const bf16*, const float*, const
 //   c_t = b + sum_j w[K-1-j] x_{t+j} (x past t's sequence end = 0), u = SiLU(c).
 // dc_t = du_t SiLU'(c_t) (c recomputed from x);  dx_s = sum_j w[K-1-j] dc_{s-j}
 // over s-j at or after s's sequence start;  dw[K-1-j] = sum_t dc_t x_{t+j},
-// db = sum_t dc_t, as per-(row block) partials [nb][E][K+1].
+// db = sum_t dc_t.
+//
+// A block owns 64 channels (lane = channel) of a contiguous range of rows,
+// split into four consecutive runs, one per wave.  Each wave walks its run
+// top to bottom with the conv window (x_t .. x_{t+3}) and the last three dc
+// values in registers: dx_t needs dc_t .. dc_{t-3}, so dc is never stored.
+// The three dc values before the run are recomputed.  The current sequence's
+// bounds advance with the walk (offsets are sanitised: non-decreasing, from 0
+// to the token count).  The tap and bias gradients are summed per lane, then
+// over the four waves in a fixed order, into per-block partials [nb][E][K+1]
+// that a second kernel adds in block order.
 // ---------------------------------------------------------------------------
-template <typename T>
-__global__ __launch_bounds__(256) void conv_dc_kernel(int Tn, int E, const T* __restrict__ x, long ld_x,
-                                                      const T* __restrict__ cw, const T* __restrict__ cb,
-                                                      const float* __restrict__ du, const float* __restrict__ du2,
-                                                      float* __restrict__ dc, const int32_t* __restrict__ cu, int nseq) {
-  const long n = (long)Tn * E;
-  for (long i = blockIdx.x * 256L + threadIdx.x; i < n; i += (long)gridDim.x * 256) {
-    const int t = (int)(i / E), e = (int)(i % E);
-    const int se = seq_end_of(cu, nseq, t, Tn);
-    float c = to_f32(cb[e]);
-    for (int j = 0; j < KC_; ++j)
-      if (t + j < se) c = fmaf(to_f32(cw[(long)e * KC_ + KC_ - 1 - j]), to_f32(x[(long)(t + j) * ld_x + e]), c);
-    const float sg = 1.0f / (1.0f + expf(-c));
-    const float g = du[i] + (du2 ? du2[i] : 0.0f);
-    dc[i] = g * sg * (1.0f + c * (1.0f - sg));
-  }
-}
-
-template <typename T>
-__global__ __launch_bounds__(256) void conv_dx_kernel(int Tn, int E, const T* __restrict__ x, long ld_x,
-                                                      const T* __restrict__ cw, const float* __restrict__ dc,
-                                                      float* __restrict__ dx, float* __restrict__ part,
-                                                      const int32_t* __restrict__ cu, int nseq) {
-  // block: 64 channels x a contiguous range of rows; thread = (channel, row phase)
+template <typename T, typename TO>
+__global__ __launch_bounds__(256) void conv_bwd_kernel(int Tn, int E, const T* __restrict__ x, long ld_x,
+                                                       const T* __restrict__ cw, const T* __restrict__ cb,
+                                                       const float* __restrict__ du, const float* __restrict__ du2,
+                                                       TO* __restrict__ dx, long ld_dx, float* __restrict__ part,
+                                                       const int32_t* __restrict__ cu, int nseq) {
   const int nb = gridDim.y, b = blockIdx.y;
-  const int e = blockIdx.x * 64 + (threadIdx.x & 63), ph = threadIdx.x >> 6;
-  __shared__ float red[4][64][KC_ + 1];
-  float acc[KC_ + 1] = {};
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int e = blockIdx.x * 64 + lane;
   const long r0 = (long)Tn * b / nb, r1 = (long)Tn * (b + 1) / nb;
+  const int ra = (int)(r0 + (r1 - r0) * wv / 4), rz = (int)(r0 + (r1 - r0) * (wv + 1) / 4);
   float w[KC_];
+#pragma unroll
   for (int k = 0; k < KC_; ++k) w[k] = to_f32(cw[(long)e * KC_ + k]);
-  for (long s = r0 + ph; s < r1; s += 4) {
-    const int t = (int)s;
-    const int sl = seq_start_of(cu, nseq, t), se = seq_end_of(cu, nseq, t, Tn);
-    float v = 0.0f;
-    for (int j = 0; j < KC_; ++j)
-      if (t - j >= sl) v = fmaf(w[KC_ - 1 - j], dc[(long)(t - j) * E + e], v);
-    dx[(long)t * E + e] = v;
-    const float d = dc[(long)t * E + e];
-    for (int j = 0; j < KC_; ++j)
-      if (t + j < se) acc[KC_ - 1 - j] = fmaf(d, to_f32(x[(long)(t + j) * ld_x + e]), acc[KC_ - 1 - j]);
-    acc[KC_] += d;
+  const float bias = to_f32(cb[e]);
+  auto xat = [&](int t) __attribute__((always_inline)) {
+    return t < Tn ? to_f32(x[(long)t * ld_x + e]) : 0.0f;
+  };
+  auto gat = [&](int t) __attribute__((always_inline)) {
+    const long i = (long)t * E + e;
+    return du2 ? du[i] + du2[i] : du[i];
+  };
+  // dc_t from the window x_t .. x_{t+3}, n = rows of it inside the sequence (>= 1)
+  auto dc_of = [&](float g, float x0, float x1, float x2, float x3, int n) __attribute__((always_inline)) {
+    float c = fmaf(w[KC_ - 1], x0, bias);
+    c = fmaf(w[KC_ - 2], n > 1 ? x1 : 0.0f, c);
+    c = fmaf(w[KC_ - 3], n > 2 ? x2 : 0.0f, c);
+    c = fmaf(w[KC_ - 4], n > 3 ? x3 : 0.0f, c);
+    const float sg = sigmoid_fast(c);
+    return g * sg * fmaf(c, 1.0f - sg, 1.0f);
+  };
+  float acc[KC_ + 1] = {};
+  if (ra < rz) {
+    int q = 0;
+    {
+      int lo = 0, hi = nseq;   // the last q with cu[q] <= ra
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (cu[mid] <= ra) lo = mid; else hi = mid;
+      }
+      q = lo;
+    }
+    int sl = cu[q], se = max(cu[q + 1], ra + 1);
+    // dc of the three rows before the run, when they are in the same sequence
+    float d1 = 0.0f, d2 = 0.0f, d3 = 0.0f;
+    {
+      float xs[6];
+#pragma unroll
+      for (int i = 0; i < 6; ++i) xs[i] = ra - 3 + i >= sl ? xat(ra - 3 + i) : 0.0f;
+      if (ra - 1 >= sl) d1 = dc_of(gat(ra - 1), xs[2], xs[3], xs[4], xs[5], se - (ra - 1));
+      if (ra - 2 >= sl) d2 = dc_of(gat(ra - 2), xs[1], xs[2], xs[3], xs[4], se - (ra - 2));
+      if (ra - 3 >= sl) d3 = dc_of(gat(ra - 3), xs[0], xs[1], xs[2], xs[3], se - (ra - 3));
+    }
+    float x0 = xat(ra), x1 = xat(ra + 1), x2 = xat(ra + 2);
+    auto step = [&](int t, float g, float x3) __attribute__((always_inline)) {
+      const int n = se - t;
+      const float d = dc_of(g, x0, x1, x2, x3, n);
+      const float v = fmaf(w[KC_ - 1], d, fmaf(w[KC_ - 2], d1, fmaf(w[KC_ - 3], d2, w[KC_ - 4] * d3)));
+      dx[(long)t * ld_dx + e] = from_f32<TO>(v);
+      acc[KC_ - 1] = fmaf(d, x0, acc[KC_ - 1]);
+      acc[KC_ - 2] = fmaf(d, n > 1 ? x1 : 0.0f, acc[KC_ - 2]);
+      acc[KC_ - 3] = fmaf(d, n > 2 ? x2 : 0.0f, acc[KC_ - 3]);
+      acc[KC_ - 4] = fmaf(d, n > 3 ? x3 : 0.0f, acc[KC_ - 4]);
+      acc[KC_] += d;
+      d3 = d2; d2 = d1; d1 = d;
+      x0 = x1; x1 = x2; x2 = x3;
+    };
+    int t = ra;
+    while (t < rz) {
+      if (t >= se) {   // next non-empty sequence; the dc history starts over
+        while (q + 1 < nseq && cu[q + 1] <= t) ++q;
+        sl = cu[q];
+        // (rows past the last offset, which valid offsets never leave, are
+        // taken one at a time)
+        se = max(cu[q + 1], t + 1);
+        d1 = d2 = d3 = 0.0f;
+      }
+      if (t + 4 <= rz && t + 4 <= se) {
+        // four rows of one sequence: every load first
+        float xn[4], gn[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) { xn[i] = xat(t + 3 + i); gn[i] = gat(t + i); }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) step(t + i, gn[i], xn[i]);
+        t += 4;
+      } else {
+        step(t, gat(t), xat(t + 3));
+        t += 1;
+      }
+    }
   }
-  for (int k = 0; k <= KC_; ++k) red[ph][threadIdx.x & 63][k] = acc[k];
+  __shared__ float red[4][KC_ + 1][64];
+#pragma unroll
+  for (int k = 0; k <= KC_; ++k) red[wv][k][lane] = acc[k];
   __syncthreads();
-  if (ph == 0)
+  if (wv == 0) {
+#pragma unroll
     for (int k = 0; k <= KC_; ++k)
-      part[((long)b * E + e) * (KC_ + 1) + k] =
-          ((red[0][threadIdx.x][k] + red[1][threadIdx.x][k]) + red[2][threadIdx.x][k]) + red[3][threadIdx.x][k];
+      part[((long)b * E + e) * (KC_ + 1) + k] = ((red[0][k][lane] + red[1][k][lane]) + red[2][k][lane]) + red[3][k][lane];
+  }
 }
 
 __global__ __launch_bounds__(256) void conv_wsum_kernel(int E, int nb, const float* __restrict__ part,
@@ -285,29 +390,26 @@ __global__ __launch_bounds__(256) void conv_wsum_kernel(int E, int nb, const flo
   else db[e] = s;
 }
 
-int conv_bwd_parts(int Tn) { return Tn < 256 ? 1 : (Tn / 256 < 128 ? Tn / 256 : 128); }
+// row blocks: about 64 rows per wave, at most 1024 blocks of rows
+int conv_bwd_parts(int Tn) { return Tn < 256 ? 1 : (Tn / 256 < 1024 ? Tn / 256 : 1024); }
 
 template <typename T>
 hipError_t conv_bwd(int Tn, int E, const T* x, long ld_x, const T* cw, const T* cb, const float* du, const float* du2,
-                    float* dc, float* dx, float* part, float* dw, float* db, const int32_t* cu, int nseq,
+                    T* dx, long ld_dx, float* part, float* dw, float* db, const int32_t* cu, int nseq,
                     hipStream_t st) {
   if (Tn <= 0) return hipSuccess;
-  const long n = (long)Tn * E;
-  const long want = (n + 255) / 256;
-  hipLaunchKernelGGL((conv_dc_kernel<T>), dim3((unsigned)(want < 8192 ? want : 8192)), dim3(256), 0, st, Tn, E, x,
-                     ld_x, cw, cb, du, du2, dc, cu, nseq);
   const int nb = conv_bwd_parts(Tn);
-  hipLaunchKernelGGL((conv_dx_kernel<T>), dim3(E / 64, nb), dim3(256), 0, st, Tn, E, x, ld_x, cw, (const float*)dc,
-                     dx, part, cu, nseq);
+  hipLaunchKernelGGL((conv_bwd_kernel<T, T>), dim3(E / 64, nb), dim3(256), 0, st, Tn, E, x, ld_x, cw, cb, du, du2,
+                     dx, ld_dx, part, cu, nseq);
   hipLaunchKernelGGL(conv_wsum_kernel, dim3((E * (KC_ + 1) + 255) / 256), dim3(256), 0, st, E, nb,
                      (const float*)part, dw, db);
   return hipGetLastError();
 }
 template hipError_t conv_bwd<float>(int, int, const float*, long, const float*, const float*, const float*,
-                                    const float*, float*, float*, float*, float*, float*, const int32_t*, int,
+                                    const float*, float*, long, float*, float*, float*, const int32_t*, int,
                                     hipStream_t);
 template hipError_t conv_bwd<bf16>(int, int, const bf16*, long, const bf16*, const bf16*, const float*, const float*,
-                                   float*, float*, float*, float*, float*, const int32_t*, int, hipStream_t);
+                                   bf16*, long, float*, float*, float*, const int32_t*, int, hipStream_t);
 
 // out[t] (act, ld_out) = [a (f32 [T, na]) | b (f32 [T, nb]) | c (f32 [T, nc])]
 template <typename Tout>

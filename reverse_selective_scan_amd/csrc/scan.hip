@@ -226,10 +226,14 @@ __global__ __launch_bounds__(256, 2) void scan_kernel(ScanArgs a) {
   constexpr int DPT = RP / 8;                   // delta floats per thread per row (4..32)
   constexpr bool BF = std::is_same<T, bf16>::value;
   constexpr unsigned SZ = sizeof(T);
-  __shared__ __attribute__((aligned(16))) float yp_s[4][TB][64];   // partial C.h of each wave
-  __shared__ __attribute__((aligned(16))) float2 pre_s[TB][64];    // (dt, dt*u)
+  // Rows of yp_s, pre_s and u_s are padded by 4 words: the accesses that
+  // touch several rows at once (16 lanes over rows 4 apart in the dt phase,
+  // 8 lanes per row over 2 rows in phases A and C) then fall in distinct banks.
+  constexpr int RW = 64 + 4;
+  __shared__ __attribute__((aligned(16))) float yp_s[4][TB][RW];   // partial C.h of each wave
+  __shared__ __attribute__((aligned(16))) float2 pre_s[TB][RW];    // (dt, dt*u)
   __shared__ __attribute__((aligned(16))) f32x4 bc_s[TB][8];       // B[0..16) C[0..16)
-  __shared__ __attribute__((aligned(16))) float u_s[FUSED ? TB : 1][64];
+  __shared__ __attribute__((aligned(16))) float u_s[FUSED ? TB : 1][RW];
   __shared__ __attribute__((aligned(16))) bf16 dl_s[MFMA_DT ? TB * DLS : 8];
 
   const int E = a.E;
