@@ -294,7 +294,8 @@ int run_scan_bwd(r2l_dtype act, int E, int R, int T, int nseq, const void* u, in
 // backward's own regions, and the GEMM split scratch.
 struct LayerBwdPlan {
   size_t xz, u, xdbl, xdbl2, xdbl3, delta, dt, yg, o, scanf, dout, gx, gr, do_a, doT, ygT, wT, dyg, du, ddt, dz, dB,
-      dC, scanb, ddt_a, ddtT, deltaT, ddelta, dxdbl_a, dxdblT, uT, dux, convp, dxz_a, dxzT, hT, dhb, colp, scratch;
+      dC, scanb, ddt_a, ddtT, deltaT, ddelta, dxdbl_a, dxdblT, uT, dux, convp, dxz_a, dxzT, hT, dhb, colp, dtpart,
+      scratch;
   ScanPlan sp;
   int Tp;
   size_t total;
@@ -349,6 +350,7 @@ LayerBwdPlan plan_layer_bwd(const r2l_dims* d, r2l_dtype act, int64_t T, int32_t
   p.hT = take(D * Tp * sa);
   p.dhb = take(Tz * D * f);
   p.colp = take((size_t)colsum_parts((int)T) * (E > D ? E : D) * f);
+  p.dtpart = take((size_t)((T + 63) / 64) * E * f);
   p.scratch = take(act == R2L_BF16 ? kSplitScratch : 0);
   p.total = off;
   return p;
@@ -448,12 +450,11 @@ int run_layer_bwd(const r2l_dims* d, r2l_dtype act, bool no_ln, const r2l_weight
   // out_proj: dyg = do W_out, dW_out = do^T yg
   A* do_a = at<A>(ws, p.do_a);
   A* dyg = at<A>(ws, p.dyg);
-  R2L_RUN("bwd_do", st, (elementwise<kConvert, float, A>(T, D, dout, D, nullptr, 0, nullptr, do_a, D, st)));
-  R2L_RUN("bwd_WoutT", st, (transpose<A, A>(D, E, D, Wout, E, wT, st)));
-  R2L_RUN("bwd_dyg", st, gemm(T, E, D, do_a, D, wT, D, dyg, E, !bf));
   A* doT = at<A>(ws, p.doT);
   A* ygT = at<A>(ws, p.ygT);
-  R2L_RUN("bwd_doT", st, (transpose<float, A>(T, D, Tp, dout, D, doT, st)));
+  R2L_RUN("bwd_do", st, (fused_t<kConvert, float, A>(T, D, Tp, dout, D, nullptr, 0, do_a, D, doT, nullptr, st)));
+  R2L_RUN("bwd_WoutT", st, (transpose<A, A>(D, E, D, Wout, E, wT, st)));
+  R2L_RUN("bwd_dyg", st, gemm(T, E, D, do_a, D, wT, D, dyg, E, !bf));
   R2L_RUN("bwd_ygT", st, (transpose<A, A>(T, E, Tp, yg, E, ygT, st)));
   R2L_RUN("bwd_dWout", st, gemm(D, E, Tp, doT, Tp, ygT, Tp, gr->out_proj_w, E, true));
   // the scan
@@ -469,16 +470,16 @@ int run_layer_bwd(const r2l_dims* d, r2l_dtype act, bool no_ln, const r2l_weight
     if (rc != R2L_OK) return rc;
   }
   // dt_proj + softplus: ddt_pre = ddt sigmoid(pre); d b_dt = sum ddt_pre; d delta = ddt_pre W_dt; dW_dt = ddt_pre^T delta
-  R2L_RUN("bwd_dt_pre", st, (elementwise<kDtPre, float, float>(T, E, ddt, E, dt, E, nullptr, ddt, E, st)));
-  R2L_RUN("bwd_dt_b", st, colsum(T, E, ddt, E, colp, 1.0f, gr->dt_proj_b, st));
+  // (one pass: ddt_pre, its activation-typed copy, its transpose and column sums)
   A* ddt_a = at<A>(ws, p.ddt_a);
+  A* ddtT = at<A>(ws, p.ddtT);
+  float* dtpart = at<float>(ws, p.dtpart);
+  R2L_RUN("bwd_dt_pre", st, (fused_t<kDtPre, float, A>(T, E, Tp, ddt, E, dt, E, ddt_a, E, ddtT, dtpart, st)));
+  R2L_RUN("bwd_dt_b", st, colsum((T + 63) / 64, E, dtpart, E, colp, 1.0f, gr->dt_proj_b, st));
   float* ddelta = at<float>(ws, p.ddelta);
-  R2L_RUN("bwd_ddt_a", st, (elementwise<kConvert, float, A>(T, E, ddt, E, nullptr, 0, nullptr, ddt_a, E, st)));
   R2L_RUN("bwd_WdtT", st, (transpose<A, A>(E, R, E, Wdt, R, wT, st)));
   R2L_RUN("bwd_ddelta", st, gemm(T, R, E, ddt_a, E, wT, E, ddelta, R, true));
-  A* ddtT = at<A>(ws, p.ddtT);
   A* deltaT = at<A>(ws, p.deltaT);
-  R2L_RUN("bwd_ddtT", st, (transpose<float, A>(T, E, Tp, ddt, E, ddtT, st)));
   R2L_RUN("bwd_deltaT", st, (transpose<A, A>(T, R, Tp, delta, R, deltaT, st)));
   R2L_RUN("bwd_dWdt", st, gemm(E, R, Tp, ddtT, Tp, deltaT, Tp, gr->dt_proj_w, R, true));
   // x_proj: dxdbl = [d delta | dB | dC]; du += dxdbl W_x; dW_x = dxdbl^T u
@@ -498,12 +499,14 @@ int run_layer_bwd(const r2l_dims* d, r2l_dtype act, bool no_ln, const r2l_weight
                                           gr->conv_w, gr->conv_b, cu_clean, nseq, st));
   // in_proj: dh = g + dxz W_in; dW_in = dxz^T h
   float* dhb = at<float>(ws, p.dhb);
-  R2L_RUN("bwd_dz", st, (elementwise<kConvert, float, A>(T, E, dz, E, nullptr, 0, nullptr, dxz_a + E, 2L * E, st)));
+  A* dxzT = at<A>(ws, p.dxzT);
+  // dz into the z half of dxz and of its transpose; the x half is transposed from dx
+  R2L_RUN("bwd_dz", st, (fused_t<kConvert, float, A>(T, E, Tp, dz, E, nullptr, 0, dxz_a + E, 2L * E,
+                                                      dxzT + (size_t)E * Tp, nullptr, st)));
   R2L_RUN("bwd_WinT", st, (transpose<A, A>(2 * E, D, 2 * E, Win, D, wT, st)));
   R2L_RUN("bwd_dh_branch", st, gemm(T, D, 2 * E, dxz_a, 2L * E, wT, 2L * E, dhb, D, true));
-  A* dxzT = at<A>(ws, p.dxzT);
   A* hT = at<A>(ws, p.hT);
-  R2L_RUN("bwd_dxzT", st, (transpose<A, A>(T, 2 * E, Tp, dxz_a, 2L * E, dxzT, st)));
+  R2L_RUN("bwd_dxT", st, (transpose<A, A>(T, E, Tp, dxz_a, 2L * E, dxzT, st)));
   R2L_RUN("bwd_hT", st, (transpose<A, A>(T, D, Tp, h, D, hT, st)));
   R2L_RUN("bwd_dWin", st, gemm(2 * E, D, Tp, dxzT, Tp, hT, Tp, gr->in_proj_w, D, true));
   R2L_RUN("bwd_dh", st, (elementwise<kAddTo, A, A>(T, D, g, D, dhb, D, nullptr, dh, D, st)));

@@ -119,6 +119,13 @@ enum EwOp { kConvert = 0, kSoftplusBias = 1, kDtPre = 2, kAddTo = 3 };
 template <int OP, typename Tin, typename Tout>
 hipError_t elementwise(int rows, int cols, const Tin* in, long ld_in, const float* aux, long ld_aux,
                        const float* vec, Tout* out, long ld_out, hipStream_t st);
+// One pass of v = op(in, aux) over [rows, cols] (kConvert or kDtPre): the
+// row-major copy out_rm, the transposed copy out_t [cols, rows_pad] (zeros
+// past rows) and column sums of each 64-row band colpart
+// [ceil(rows/64)][cols], each optional (null).
+template <int OP, typename Tin, typename Tout>
+hipError_t fused_t(int rows, int cols, int rows_pad, const Tin* in, long ld_in, const float* aux, long ld_aux,
+                   Tout* out_rm, long ld_rm, Tout* out_t, float* colpart, hipStream_t st);
 // out[c] = scale * sum_r in[r][c]; part: colsum_parts(rows) * cols floats.
 int colsum_parts(int rows);
 hipError_t colsum(int rows, int cols, const float* in, long ld, float* part, float scale, float* out, hipStream_t st);

@@ -48,35 +48,95 @@ template hipError_t transpose<float, float>(int, int, int, const float*, long, f
 // kSoftplusBias: out = softplus(in + vec[col])              (dt from dt_proj's product)
 // kDtPre:        out = in (1 - exp(-aux))                   (ddt through softplus: sigmoid(pre) = 1 - e^-dt)
 // kAddTo:        out = in + aux                             (dh = g + the branch's gradient)
+template <int OP>
+R2L_DEV float ew_op(float v, const float* aux, long ai, const float* vec, int c) {
+  if (OP == kConvert) return v;
+  if (OP == kSoftplusBias) return softplus_f(v + vec[c]);
+  if (OP == kDtPre) return v * (1.0f - expf(-aux[ai]));
+  return v + aux[ai];
+}
+
+// grid (column blocks of 256, row groups); each block walks its rows
 template <int OP, typename Tin, typename Tout>
 __global__ __launch_bounds__(256) void elementwise_kernel(int rows, int cols, const Tin* __restrict__ in, long ld_in,
                                                           const float* __restrict__ aux, long ld_aux,
                                                           const float* __restrict__ vec, Tout* __restrict__ out,
                                                           long ld_out) {
-  const long n = (long)rows * cols;
-  for (long i = blockIdx.x * 256L + threadIdx.x; i < n; i += (long)gridDim.x * 256) {
-    const long r = i / cols;
-    const int c = (int)(i % cols);
-    const float v = to_f32(in[r * ld_in + c]);
-    float o;
-    if (OP == kConvert) o = v;
-    else if (OP == kSoftplusBias) o = softplus_f(v + vec[c]);
-    else if (OP == kDtPre) o = v * (1.0f - expf(-aux[r * ld_aux + c]));
-    else o = v + aux[r * ld_aux + c];
-    out[r * ld_out + c] = from_f32<Tout>(o);
+  const int c = blockIdx.x * 256 + threadIdx.x;
+  if (c >= cols) return;
+  for (int r = blockIdx.y; r < rows; r += gridDim.y) {
+    const float v = to_f32(in[(long)r * ld_in + c]);
+    out[(long)r * ld_out + c] = from_f32<Tout>(ew_op<OP>(v, aux, (long)r * ld_aux + c, vec, c));
   }
 }
 
 template <int OP, typename Tin, typename Tout>
 hipError_t elementwise(int rows, int cols, const Tin* in, long ld_in, const float* aux, long ld_aux,
                        const float* vec, Tout* out, long ld_out, hipStream_t st) {
-  const long n = (long)rows * cols;
-  if (n <= 0) return hipSuccess;
-  const long want = (n + 255) / 256;
-  hipLaunchKernelGGL((elementwise_kernel<OP, Tin, Tout>), dim3((unsigned)(want < 8192 ? want : 8192)), dim3(256), 0,
-                     st, rows, cols, in, ld_in, aux, ld_aux, vec, out, ld_out);
+  if (rows <= 0 || cols <= 0) return hipSuccess;
+  const int cb = (cols + 255) / 256;
+  const int rg = rows < 65535 ? rows : 65535;
+  const int ry = cb * rg > 16384 ? (16384 + cb - 1) / cb : rg;   // about 16K blocks
+  hipLaunchKernelGGL((elementwise_kernel<OP, Tin, Tout>), dim3(cb, ry > 0 ? ry : 1), dim3(256), 0, st, rows, cols,
+                     in, ld_in, aux, ld_aux, vec, out, ld_out);
   return hipGetLastError();
 }
+
+// ---------------------------------------------------------------------------
+// One pass over 64 x 64 tiles of [rows, cols]: v = op(in, aux); optional
+// row-major copy out_rm (row stride ld_rm), transposed copy out_t
+// [cols, rows_pad] (zeros past rows) and per-tile-row column sums
+// colpart [ceil(rows / 64)][cols] (each the sum of 64 rows, four row phases
+// added in order).
+// ---------------------------------------------------------------------------
+template <int OP, typename Tin, typename Tout>
+__global__ __launch_bounds__(256) void fused_t_kernel(int rows, int cols, int rows_pad, const Tin* __restrict__ in,
+                                                      long ld_in, const float* __restrict__ aux, long ld_aux,
+                                                      Tout* __restrict__ out_rm, long ld_rm, Tout* __restrict__ out_t,
+                                                      float* __restrict__ colpart) {
+  __shared__ float tile[64][65];
+  __shared__ float cs[4][64];
+  const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  const int c = c0 + tx;
+  float sum = 0.0f;
+  for (int i = ty; i < 64; i += 4) {
+    const int r = r0 + i;
+    float v = 0.0f;
+    if (r < rows && c < cols) {
+      v = ew_op<OP>(to_f32(in[(long)r * ld_in + c]), aux, (long)r * ld_aux + c, nullptr, c);
+      if (out_rm) out_rm[(long)r * ld_rm + c] = from_f32<Tout>(v);
+    }
+    tile[i][tx] = v;
+    sum += v;
+  }
+  cs[ty][tx] = sum;
+  __syncthreads();
+  if (colpart && ty == 0 && c < cols && r0 < rows)
+    colpart[(long)blockIdx.y * cols + c] = ((cs[0][tx] + cs[1][tx]) + cs[2][tx]) + cs[3][tx];
+  if (out_t) {
+    for (int i = ty; i < 64; i += 4) {
+      const int cc = c0 + i, r = r0 + tx;
+      if (cc < cols && r < rows_pad) out_t[(long)cc * rows_pad + r] = from_f32<Tout>(tile[tx][i]);
+    }
+  }
+}
+
+template <int OP, typename Tin, typename Tout>
+hipError_t fused_t(int rows, int cols, int rows_pad, const Tin* in, long ld_in, const float* aux, long ld_aux,
+                   Tout* out_rm, long ld_rm, Tout* out_t, float* colpart, hipStream_t st) {
+  if (rows <= 0 || cols <= 0) return hipSuccess;
+  const int ry = ((out_t ? rows_pad : rows) + 63) / 64;
+  hipLaunchKernelGGL((fused_t_kernel<OP, Tin, Tout>), dim3((cols + 63) / 64, ry), dim3(256), 0, st, rows, cols,
+                     rows_pad, in, ld_in, aux, ld_aux, out_rm, ld_rm, out_t, colpart);
+  return hipGetLastError();
+}
+#define R2L_FT(OP, TI, TO)                                                                                     \
+  template hipError_t fused_t<OP, TI, TO>(int, int, int, const TI*, long, const float*, long, TO*, long, TO*, \
+                                          float*, hipStream_t);
+R2L_FT(kConvert, float, bf16) R2L_FT(kConvert, float, float) R2L_FT(kDtPre, float, bf16) R2L_FT(kDtPre, float, float)
+#undef R2L_FT
+
 #define R2L_EW(OP, TI, TO)                                                                                \
   template hipError_t elementwise<OP, TI, TO>(int, int, const TI*, long, const float*, long, const float*, \
                                               TO*, long, hipStream_t);
