@@ -213,12 +213,28 @@ __global__ __launch_bounds__(256) void conv_xproj_kernel(int Tn, int E, int P,
 }
 
 // out[i] = sum over k < ks of slab[k][i] (slab stride n), in order of k.
+// A thread owns 4 consecutive elements and loads all of its slabs (up to
+// 16) before adding, so the loads are in flight together.
 __global__ __launch_bounds__(256) void sum_slabs_kernel(long n, int ks, const float* __restrict__ slab,
                                                         float* __restrict__ out) {
-  for (long i = blockIdx.x * 256L + threadIdx.x; i < n; i += (long)gridDim.x * 256) {
-    float v = 0.0f;
-    for (int k = 0; k < ks; ++k) v += slab[k * n + i];
-    out[i] = v;
+  const long i = (blockIdx.x * 256L + threadIdx.x) * 4;
+  if (i >= n) return;
+  if (i + 4 <= n && (n & 3) == 0) {
+    f32x4 v[16];
+#pragma unroll
+    for (int k = 0; k < 16; ++k)
+      if (k < ks) v[k] = *(const f32x4*)(slab + k * n + i);
+    f32x4 acc = v[0];
+#pragma unroll
+    for (int k = 1; k < 16; ++k)
+      if (k < ks) acc += v[k];
+    *(f32x4*)(out + i) = acc;
+  } else {
+    for (long j = i; j < i + 4 && j < n; ++j) {
+      float v = 0.0f;
+      for (int k = 0; k < ks; ++k) v += slab[k * n + j];
+      out[j] = v;
+    }
   }
 }
 
@@ -233,7 +249,7 @@ hipError_t conv_xproj_bf16(int Tn, int E, int P, const bf16* x, long ld_x, const
   // (each wave keeps at least one 16-channel step), partial sums in ws.
   int ks = 1;
   if (ws != nullptr && u_out == nullptr && ncu > 0) {
-    while (ntiles * ks * 2 <= ncu && (E / (ks * 2)) % 64 == 0 &&
+    while (ks < 16 && ntiles * ks * 2 <= ncu && (E / (ks * 2)) % 64 == 0 &&
            (size_t)(ks * 2) * Tn * P * sizeof(float) <= ws_bytes)
       ks *= 2;
   }
@@ -253,10 +269,10 @@ hipError_t conv_xproj_bf16(int Tn, int E, int P, const bf16* x, long ld_x, const
     default: return hipErrorInvalidValue;
   }
 #undef R2L_CX
-  if (ks > 1) {
+  if (ks > 1) {   // (ks <= 16, as sum_slabs_kernel needs)
     const long n = (long)Tn * P;
-    const long blocks = (n + 255) / 256 < 2048 ? (n + 255) / 256 : 2048;
-    hipLaunchKernelGGL(sum_slabs_kernel, dim3(blocks), dim3(256), 0, st, n, ks, (const float*)ws, xdbl);
+    hipLaunchKernelGGL(sum_slabs_kernel, dim3((unsigned)((n / 4 + 255) / 256 + 1)), dim3(256), 0, st, n, ks,
+                       (const float*)ws, xdbl);
   }
   return hipGetLastError();
 }
