@@ -66,9 +66,11 @@ def main():
     ap.add_argument("--summarize", nargs="+", metavar=("OUT_MD", "DIR"),
                     help="write a profile summary from rocprofv3 outputs instead of benchmarking: "
                          "OUT_MD TRACE_DIR [FETCH_DIR WRITE_DIR]")
+    ap.add_argument("--summarize-args", default="",
+                    help="with --summarize: the bench.py arguments of the profiled runs (for the header)")
     args = ap.parse_args()
     if args.summarize:
-        summarize_profiles(args.summarize, args.calib_mib * 1024.0)
+        summarize_profiles(args.summarize, args.calib_mib * 1024.0, args.summarize_args)
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -338,7 +340,8 @@ ROCPROF_NAMES = {  # substring of the demangled kernel name in rocprofv3 output
     "in_proj_gemm": "gemm_bf16_big_kernel<false, 4, false>", "out_proj_gemm": "gemm_bf16_big_kernel<true, 8, false>",
     "out_proj_tail": "gemm_bf16_big_kernel<true, 8, true>", "out_proj_reduce": "gemm_tail_reduce_kernel<true, 8>",
     "conv_xproj": "conv_xproj_sk_kernel<5, false>", "conv_sum": "sk_sum_kernel",
-    "scan_main": "E, false, 4, false>(r2l::ScanArgs)", "scan_summary": "E, true, 4, false>(r2l::ScanArgs)",
+    "scan_main": "E, false, 4, false, false>(r2l::ScanArgs)",
+    "scan_summary": "E, true, 4, false, false>(r2l::ScanArgs)",
     "ln_gate": "ln_gate_kernel",
 }
 PROFILE_JSON = os.path.join(ROOT, "profiles", "traffic_serve_b8.json")
@@ -373,20 +376,24 @@ def _rocprof_rows(d, name):
     return rows
 
 
-def summarize_profiles(argv, size_kib=0.0):
+def summarize_profiles(argv, size_kib=0.0, bench_args=""):
     """OUT_MD TRACE_DIR [FETCH_DIR WRITE_DIR]: kernel-trace stats and, when
-    counter runs are given, HBM bytes per dispatch scaled by the copy kernel."""
+    counter runs are given, HBM bytes per dispatch scaled by the copy kernel
+    (written to the traffic JSON only for the default forward workload)."""
     out_md, trace_dir = argv[0], argv[1]
+    extra = (" " + bench_args.strip()) if bench_args.strip() else ""
     lines = ["# Kernel profile: " + os.path.basename(out_md), "",
              "Commands (from the repository root, TMPDIR=/tmp):", "",
-             "    rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/prof_trace -o run -- "
-             "python -u bench.py --steps 10 --warmup 3 --no-cpu-baseline",
-             "    rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/prof_fetch -o run -- "
-             "python -u bench.py --steps 2 --warmup 1 --no-cpu-baseline --copy-calib-mib 1024",
-             "    rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/prof_write -o run -- "
-             "python -u bench.py --steps 2 --warmup 1 --no-cpu-baseline --copy-calib-mib 1024",
-             "    python bench.py --summarize " + out_md + " gpurun_out/prof_trace gpurun_out/prof_fetch "
-             "gpurun_out/prof_write --calib-mib 1024", ""]
+             f"    rocprofv3 --kernel-trace --stats --output-format csv -d {trace_dir} -o run -- "
+             "python -u bench.py --steps 10 --warmup 3 --no-cpu-baseline" + extra]
+    if len(argv) >= 4:
+        lines += [f"    rocprofv3 --pmc FETCH_SIZE --output-format csv -d {argv[2]} -o run -- "
+                  "python -u bench.py --steps 2 --warmup 1 --no-cpu-baseline --copy-calib-mib 1024" + extra,
+                  f"    rocprofv3 --pmc WRITE_SIZE --output-format csv -d {argv[3]} -o run -- "
+                  "python -u bench.py --steps 2 --warmup 1 --no-cpu-baseline --copy-calib-mib 1024" + extra]
+    lines += ["    python bench.py --summarize " + " ".join(argv) +
+              (" --calib-mib 1024" if len(argv) >= 4 else "") +
+              (f' --summarize-args="{bench_args.strip()}"' if extra else ""), ""]
     stats = _rocprof_rows(trace_dir, "*kernel_stats.csv")
     if stats:
         lines += ["## rocprofv3 --kernel-trace --stats", "", "| kernel | calls | avg us | total ms | % |",
@@ -428,7 +435,8 @@ def summarize_profiles(argv, size_kib=0.0):
                                         "write_bytes": round(wb), "copy_scale": [round(rs, 5), round(ws, 5)],
                                         "source_sha256": _source_hash(ours)}
                 lines.append(f"| {ours} | {f:.0f} | {wr:.0f} | {rb / 1e6:.1f} | {wb / 1e6:.1f} |")
-            json.dump(rec, open(PROFILE_JSON, "w"), indent=1)
+            if not extra:
+                json.dump(rec, open(PROFILE_JSON, "w"), indent=1)
         lines.append("")
     open(out_md, "w").write("\n".join(lines) + "\n")
     print("\n".join(lines))
