@@ -59,6 +59,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--backward", action="store_true",
                     help="time r2l_layer_bwd (forward recompute + gradients) instead of the forward")
+    ap.add_argument("--saved", action="store_true",
+                    help="with --backward: the forward runs with R2L_FLAG_TRAIN and the backward reads its "
+                         "activations instead of recomputing them")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB first (counter calibration)")
     ap.add_argument("--calib-mib", type=float, default=0.0,
@@ -267,12 +270,34 @@ def bench_backward(args):
     ws = torch.empty(need, dtype=torch.uint8, device=dev)
     dh = torch.empty_like(h)
     grads = {k: torch.empty(w[k].shape, dtype=torch.float32, device=dev) for k, _ in B.Grads._fields_}
+    saved = None
+    out = torch.empty_like(h)
+    if args.saved:
+        saved = torch.empty(B.r2l_layer_train_workspace_bytes(B.dims_of(w), B.R2L_BF16, T, nseq, max_seqlen),
+                            dtype=torch.uint8, device=dev)
+
+    def fwd_train():
+        B.r2l_layer_fwd(h, w, cu, out=out, flags=B.R2L_FLAG_TRAIN, workspace=saved, nseq=nseq,
+                        max_seqlen=max_seqlen)
 
     def step():
-        B.r2l_layer_bwd(h, w, cu, g, dh=dh, workspace=ws, grads=grads, nseq=nseq, max_seqlen=max_seqlen)
+        B.r2l_layer_bwd(h, w, cu, g, dh=dh, workspace=ws, grads=grads, nseq=nseq, max_seqlen=max_seqlen,
+                        saved=saved)
 
     print(f"[bench] backward {wl.name}: T={T} D={D} E={E} N={N} R={R}, workspace {need / 2**30:.2f} GiB, "
-          f"warmup {args.warmup}", flush=True)
+          f"saved activations {args.saved}, warmup {args.warmup}", flush=True)
+    fwd_ms = None
+    if args.saved:
+        for _ in range(args.warmup):
+            fwd_train()
+        torch.cuda.synchronize()
+        f0, f1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        f0.record(torch.cuda.current_stream())
+        for _ in range(args.steps):
+            fwd_train()
+        f1.record(torch.cuda.current_stream())
+        torch.cuda.synchronize()
+        fwd_ms = f0.elapsed_time(f1) / args.steps   # (the saved buffer holds the last call's activations)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -308,8 +333,9 @@ def bench_backward(args):
         kernels[name] = k
     gemm_ms = sum(kernels[n]["avg_ms"] for n in flops if n in kernels)
     gemm_tflops = sum(flops.values()) / (gemm_ms * 1e-3) / 1e12 if gemm_ms else None
+    what = "saved forward activations" if args.saved else "forward recompute"
     rec = {
-        "metric": "R2L layer backward tokens/sec (forward recompute + all gradients) at B=8,L=4096,D=2048",
+        "metric": f"R2L layer backward tokens/sec ({what} + all gradients) at B=8,L=4096,D=2048",
         "value": round(T / (ms_step * 1e-3), 1),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -321,8 +347,11 @@ def bench_backward(args):
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded; random-init weights of the layer's shapes)",
-        "config": {"workload": wl.name, "pass": "backward", "batch": nseq, "seq_len": max_seqlen, "n_tokens": T,
-                   "d_model": D, "d_inner": E, "d_state": N, "dt_rank": R, "d_conv": wl.d_conv},
+        "config": {"workload": wl.name, "pass": "backward", "saved_activations": bool(args.saved), "batch": nseq,
+                   "seq_len": max_seqlen, "n_tokens": T, "d_model": D, "d_inner": E, "d_state": N, "dt_rank": R,
+                   "d_conv": wl.d_conv},
+        "train_forward_ms": None if fwd_ms is None else round(fwd_ms, 4),
+        "train_step_ms": None if fwd_ms is None else round(fwd_ms + ms_step, 4),
         "gemm_ms": round(gemm_ms, 4),
         "gemm_tflops": None if gemm_tflops is None else round(gemm_tflops, 1),
         "gemm_frac": None if gemm_tflops is None else round(gemm_tflops / MFMA_BF16_PEAK_TFLOPS, 4),

@@ -67,7 +67,7 @@ enum {
   R2L_ERR_HIP = -4           /* a HIP launch or runtime call failed */
 };
 
-/* Flags for r2l_layer_fwd (both), r2l_conv_fwd and r2l_scan_fwd (R2L_FLAG_L2R). */
+/* Flags for r2l_layer_fwd (all three), r2l_conv_fwd and r2l_scan_fwd (R2L_FLAG_L2R). */
 #define R2L_FLAG_NO_LN 0x1u  /* skip the stream LayerNorm: r = unflipped Mamba output */
 /* Run the conv and the scan left to right instead (a causal conv and a forward
  * scan over each sequence, no flips): the "L2R Mamba" control of the pages'
@@ -75,6 +75,12 @@ enum {
  * other step is unchanged; results are those of the default direction on
  * each sequence reversed, reversed back. */
 #define R2L_FLAG_L2R 0x2u
+/* r2l_layer_fwd only: keep the activations r2l_layer_bwd reads (the in_proj
+ * output, the x_proj output, the gated scan output and the out_proj output)
+ * in the workspace, each in a region of its own, so that the backward need
+ * not recompute the forward.  The workspace is then
+ * r2l_layer_train_workspace_bytes(...) bytes; the results are the same. */
+#define R2L_FLAG_TRAIN 0x4u
 
 /* LayerNorm epsilon used by r2l_layer_fwd (biased variance over d_model). */
 #define R2L_LN_EPS 1e-5f
@@ -136,6 +142,10 @@ typedef struct {
  * ---------------------------------------------------------------------- */
 size_t r2l_layer_workspace_bytes(const r2l_dims* dims, r2l_dtype act, int64_t n_tokens,
                                  int32_t nseq, int32_t max_seqlen);
+/* The workspace of r2l_layer_fwd with R2L_FLAG_TRAIN (the "saved" buffer of
+ * r2l_layer_bwd). */
+size_t r2l_layer_train_workspace_bytes(const r2l_dims* dims, r2l_dtype act, int64_t n_tokens,
+                                       int32_t nseq, int32_t max_seqlen);
 
 int r2l_layer_fwd(const r2l_dims* dims, r2l_dtype act, uint32_t flags, const r2l_weights* w,
                   const void* h_in, void* h_out, const int32_t* cu_seqlens, int32_t nseq,
@@ -148,8 +158,12 @@ int r2l_layer_fwd(const r2l_dims* dims, r2l_dtype act, uint32_t flags, const r2l
  * LayerNorm and the gate s are trained).  Given g_out = dL/dh+ for the
  * output of r2l_layer_fwd on h_in, it writes dh = dL/dh_in (act [n_tokens,
  * D]; may equal g_out) and every parameter gradient (r2l_grads, f32).
- * The forward is recomputed inside (activation checkpointing): in_proj, the
- * conv + SiLU + x_proj, dt, the scan and out_proj; then, in reverse: the
+ * With saved == NULL the forward is recomputed inside (activation
+ * checkpointing): in_proj, the conv + SiLU + x_proj, dt, the scan and
+ * out_proj.  saved (read only): the workspace of an r2l_layer_fwd call with
+ * R2L_FLAG_TRAIN on the same h_in, Mamba-block weights, direction,
+ * offsets and sizes, untouched since; then only the conv + SiLU output and
+ * dt are recomputed (the forward keeps neither).  Then, in reverse: the
  * LayerNorm + gate, out_proj, the scan (r2l_scan_bwd's two sweeps), dt_proj
  * and softplus, x_proj, the conv + SiLU and in_proj.  Products go through
  * the same GEMM as the forward (bf16 operands on MFMA, fp32 accumulation
@@ -168,7 +182,7 @@ size_t r2l_layer_bwd_workspace_bytes(const r2l_dims* dims, r2l_dtype act, int64_
 int r2l_layer_bwd(const r2l_dims* dims, r2l_dtype act, uint32_t flags, const r2l_weights* w,
                   const void* h_in, const void* g_out, void* dh, const r2l_grads* grads,
                   const int32_t* cu_seqlens, int32_t nseq, int64_t n_tokens, int32_t max_seqlen,
-                  void* workspace, size_t workspace_bytes, void* stream);
+                  const void* saved, void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
  * r2l_conv_fwd -- the anti-causal depthwise conv1d + bias + SiLU of the

@@ -21,6 +21,7 @@ R2L_OK, R2L_ERR_INVALID_ARG, R2L_ERR_UNSUPPORTED, R2L_ERR_WORKSPACE, R2L_ERR_HIP
 R2L_F32, R2L_BF16 = 0, 1
 R2L_FLAG_NO_LN = 0x1
 R2L_FLAG_L2R = 0x2
+R2L_FLAG_TRAIN = 0x4
 
 
 class R2LError(RuntimeError):
@@ -61,8 +62,9 @@ _SIGS = {
                                _P, _I64, _P, _P, _I32, _I64, _I32, _P, _SZ, _P]),
     "r2l_scan_bwd_workspace_bytes": (_SZ, [C.POINTER(Dims), _I64, _I32]),
     "r2l_layer_bwd_workspace_bytes": (_SZ, [C.POINTER(Dims), C.c_int, _I64, _I32, _I32]),
+    "r2l_layer_train_workspace_bytes": (_SZ, [C.POINTER(Dims), C.c_int, _I64, _I32, _I32]),
     "r2l_layer_bwd": (C.c_int, [C.POINTER(Dims), C.c_int, C.c_uint32, C.POINTER(Weights), _P, _P, _P,
-                                C.POINTER(Grads), _P, _I32, _I64, _I32, _P, _SZ, _P]),
+                                C.POINTER(Grads), _P, _I32, _I64, _I32, _P, _P, _SZ, _P]),
     "r2l_scan_bwd": (C.c_int, [C.POINTER(Dims), C.c_int, C.c_uint32, _P, _I64, _P, _I64, _P, _P, _P, _I64, _P,
                                _P, _I64, _P, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _I64, _P, _SZ, _P]),
     "r2l_gemm_nt": (C.c_int, [C.c_int, _I64, _I64, _I64, _P, _I64, _P, _I64, _P, _I64, C.c_int, _P, C.c_size_t, _P]),
@@ -150,6 +152,10 @@ def r2l_layer_bwd_workspace_bytes(dims: Dims, act: int, n_tokens: int, nseq: int
     return int(lib().r2l_layer_bwd_workspace_bytes(C.byref(dims), act, n_tokens, nseq, max_seqlen))
 
 
+def r2l_layer_train_workspace_bytes(dims: Dims, act: int, n_tokens: int, nseq: int, max_seqlen: int) -> int:
+    return int(lib().r2l_layer_train_workspace_bytes(C.byref(dims), act, n_tokens, nseq, max_seqlen))
+
+
 def r2l_layer_fwd(h: torch.Tensor, w: Dict[str, torch.Tensor], cu_seqlens, *, out: Optional[torch.Tensor] = None,
                   flags: int = 0, branch_out: Optional[torch.Tensor] = None,
                   workspace: Optional[torch.Tensor] = None, max_seqlen: Optional[int] = None,
@@ -180,8 +186,12 @@ def r2l_layer_fwd(h: torch.Tensor, w: Dict[str, torch.Tensor], cu_seqlens, *, ou
     _need(out, "out", h.dtype)
     if branch_out is not None:
         _need(branch_out, "branch_out", torch.float32)
-    need = r2l_layer_workspace_bytes(d, act, T, nseq, max_seqlen)
+    need = (r2l_layer_train_workspace_bytes if flags & R2L_FLAG_TRAIN else r2l_layer_workspace_bytes)(
+        d, act, T, nseq, max_seqlen)
     if workspace is None or workspace.numel() < need:
+        if flags & R2L_FLAG_TRAIN:
+            raise ValueError("R2L_FLAG_TRAIN needs a caller workspace of r2l_layer_train_workspace_bytes "
+                             "(it is the backward's saved buffer)")
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=h.device)
     W = Weights(**{f[0]: _ptr(w[f[0]]) for f in Weights._fields_})
     _check("r2l_layer_fwd", lib().r2l_layer_fwd(
@@ -194,11 +204,14 @@ def r2l_layer_bwd(h: torch.Tensor, w: Dict[str, torch.Tensor], cu_seqlens, g_out
                   dh: Optional[torch.Tensor] = None, flags: int = 0,
                   workspace: Optional[torch.Tensor] = None,
                   grads: Optional[Dict[str, torch.Tensor]] = None,
-                  max_seqlen: Optional[int] = None, nseq: Optional[int] = None):
+                  max_seqlen: Optional[int] = None, nseq: Optional[int] = None,
+                  saved: Optional[torch.Tensor] = None):
     """Gradient of r2l_layer_fwd: given g_out = dL/dh+, returns (dh, grads)
     with grads a dict of fp32 device tensors named like the weights (plus
     "s"); pass `grads` (and `dh`, `workspace`) to reuse buffers.  cu_seqlens
-    as for r2l_layer_fwd."""
+    as for r2l_layer_fwd.  saved: the workspace of r2l_layer_fwd(...,
+    flags=R2L_FLAG_TRAIN, workspace=saved) on the same h and weights (None:
+    the forward is recomputed)."""
     _need(h, "h")
     act = _act(h)
     T = h.shape[0]
@@ -224,9 +237,13 @@ def r2l_layer_bwd(h: torch.Tensor, w: Dict[str, torch.Tensor], cu_seqlens, g_out
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=h.device)
     W = Weights(**{f[0]: _ptr(w[f[0]]) for f in Weights._fields_})
     G = Grads(**{f[0]: _ptr(grads[f[0]]) for f in Grads._fields_})
+    if saved is not None:
+        _need(saved, "saved", torch.uint8)
+        if saved.numel() < r2l_layer_train_workspace_bytes(d, act, T, nseq, max_seqlen):
+            raise ValueError("saved is smaller than r2l_layer_train_workspace_bytes")
     _check("r2l_layer_bwd", lib().r2l_layer_bwd(
         C.byref(d), act, flags, C.byref(W), _ptr(h), _ptr(g_out), _ptr(dh), C.byref(G), _ptr(cu_dev), nseq, T,
-        max_seqlen, _ptr(workspace), workspace.numel(), _stream()))
+        max_seqlen, _ptr(saved), _ptr(workspace), workspace.numel(), _stream()))
     return dh, grads
 
 

@@ -201,20 +201,25 @@ ScanBwdPlan plan_scan_bwd(int E, int64_t T, int32_t nseq) {
 constexpr size_t kSplitScratch = 256ull * 256 * 256 * sizeof(float);
 
 struct LayerPlan {
-  size_t off_xz, off_xdbl, off_xdbl2, off_xdbl3, off_u, off_y, off_scratch;
+  size_t off_xz, off_xdbl, off_xdbl2, off_xdbl3, off_u, off_y, off_scratch, off_o;
   bool need_u;
   ScanPlan scan;
   size_t total;
 };
 
-LayerPlan plan_layer(const r2l_dims* d, r2l_dtype act, int64_t T, int32_t nseq, int32_t max_seqlen) {
+// train: out_proj's output gets a region of its own (the backward reads both
+// it and the in_proj output); otherwise it reuses the in_proj output's.
+LayerPlan plan_layer(const r2l_dims* d, r2l_dtype act, int64_t T, int32_t nseq, int32_t max_seqlen,
+                     bool train = false) {
   LayerPlan p{};
   const size_t sa = act == R2L_BF16 ? 2 : 4;
   const size_t D = d->d_model, E = d->d_inner, P = d->dt_rank + 2 * d->d_state;
   const size_t Tz = (size_t)T;
   size_t off = 0;
-  size_t xz = Tz * 2 * E * sa, o = Tz * D * 4;  // out_proj's fp32 output reuses xz
-  p.off_xz = off;   off = align_up(off + (xz > o ? xz : o));
+  size_t xz = Tz * 2 * E * sa, o = Tz * D * 4;
+  p.off_xz = off;   off = align_up(off + (train ? xz : (xz > o ? xz : o)));
+  p.off_o = train ? off : p.off_xz;
+  if (train) off = align_up(off + o);
   p.off_xdbl = off; off = align_up(off + Tz * P * 4);
   // second and third partial x_proj sums of the split-K conv kernel (bf16, large T)
   p.off_xdbl2 = off; off = align_up(off + (act == R2L_BF16 ? Tz * P * 4 : 0));
@@ -359,7 +364,7 @@ LayerBwdPlan plan_layer_bwd(const r2l_dims* d, r2l_dtype act, int64_t T, int32_t
 template <typename A>
 int run_layer_bwd(const r2l_dims* d, r2l_dtype act, bool no_ln, const r2l_weights* w, const A* h, const A* g,
                   A* dh, const r2l_grads* gr, const int32_t* cu_seqlens, int nseq, int T, int32_t max_seqlen,
-                  void* ws, hipStream_t st) {
+                  const void* saved, void* ws, hipStream_t st) {
   const LayerBwdPlan p = plan_layer_bwd(d, act, T, nseq, max_seqlen);
   const int D = d->d_model, E = d->d_inner, N = d->d_state, R = d->dt_rank, P = R + 2 * N, Tp = p.Tp;
   const bool bf = act == R2L_BF16;
@@ -387,40 +392,50 @@ int run_layer_bwd(const r2l_dims* d, r2l_dtype act, bool no_ln, const r2l_weight
   const A* Wout = (const A*)w->out_proj_w;
   const A* cw = (const A*)w->conv_w;
   const A* cb = (const A*)w->conv_b;
+  if (saved) {
+    // the forward's activations, laid out by its training plan (read only)
+    const LayerPlan fp = plan_layer(d, act, T, nseq, max_seqlen, true);
+    void* sv = const_cast<void*>(saved);
+    xz = at<A>(sv, fp.off_xz);
+    xdbl = at<float>(sv, fp.off_xdbl);
+    yg = at<A>(sv, fp.off_y);
+    o = at<float>(sv, fp.off_o);
+  }
 
-  // ---------------- forward recompute ----------------
+  // ---------------- forward recompute (u and dt only, with saved activations) ----------------
   void* sfw = at<char>(ws, p.scanf);
   int32_t* cu_clean = at<int32_t>(sfw, p.sp.off_cu);
   ChunkDesc* chunks = at<ChunkDesc>(sfw, p.sp.off_chunks);
   int32_t* nch = at<int32_t>(sfw, p.sp.off_n);
   R2L_RUN("plan_chunks", st, plan_chunks(cu_seqlens, nseq, T, p.sp.Lc, p.sp.max_chunks, false, cu_clean, chunks, nch, st));
-  R2L_RUN("bwd_in_proj", st, gemm(T, 2 * E, D, h, D, Win, D, xz, 2L * E, false));
+  if (!saved) R2L_RUN("bwd_in_proj", st, gemm(T, 2 * E, D, h, D, Win, D, xz, 2L * E, false));
   if constexpr (std::is_same<A, bf16>::value) {
     if (P <= 256) {
       // xdbl as the forward computes it (the split-K kernel for large inputs), u on its own
       R2L_RUN("bwd_u", st, conv_silu<bf16>(T, E, xz, 2L * E, cw, cb, u, cu_clean, nseq, false, st));
-      if ((T + 127) / 128 >= ncu && (long)((T + 127) / 128) * (E / 32) < (1L << 31)) {
+      const bool sk = (T + 127) / 128 >= ncu && (long)((T + 127) / 128) * (E / 32) < (1L << 31);
+      if (!saved && sk) {
         float* xdbl2 = at<float>(ws, p.xdbl2);
         float* xdbl3 = at<float>(ws, p.xdbl3);
         R2L_RUN("bwd_conv", st, conv_xproj_bf16_sk(T, E, P, xz, 2L * E, cw, cb, Wx, xdbl, xdbl2, xdbl3, cu_clean,
                                                    nseq, ncu, false, st));
         R2L_RUN("bwd_conv_sum", st, conv_sk_sum(T, E, P, xdbl, xdbl2, xdbl3, ncu, st));
-      } else {
+      } else if (!saved) {
         R2L_RUN("bwd_conv", st, conv_xproj_bf16(T, E, P, xz, 2L * E, cw, cb, Wx, nullptr, xdbl, cu_clean, nseq, false,
                                                 st, scratch, kSplitScratch, ncu));
       }
     } else {
       R2L_RUN("bwd_conv", st, conv_silu<bf16>(T, E, xz, 2L * E, cw, cb, u, cu_clean, nseq, false, st));
-      R2L_RUN("bwd_x_proj", st, gemm(T, P, E, u, E, Wx, E, xdbl, P, true));
+      if (!saved) R2L_RUN("bwd_x_proj", st, gemm(T, P, E, u, E, Wx, E, xdbl, P, true));
     }
   } else {
     R2L_RUN("bwd_conv", st, conv_silu<float>(T, E, xz, 2L * E, cw, cb, u, cu_clean, nseq, false, st));
-    R2L_RUN("bwd_x_proj", st, gemm(T, P, E, u, E, Wx, E, xdbl, P, true));
+    if (!saved) R2L_RUN("bwd_x_proj", st, gemm(T, P, E, u, E, Wx, E, xdbl, P, true));
   }
   R2L_RUN("bwd_delta", st, (elementwise<kConvert, float, A>(T, R, xdbl, P, nullptr, 0, nullptr, delta, R, st)));
   R2L_RUN("bwd_dt_proj", st, gemm(T, E, R, delta, R, Wdt, R, dt, E, true));
   R2L_RUN("bwd_softplus", st, (elementwise<kSoftplusBias, float, float>(T, E, dt, E, nullptr, 0, w->dt_proj_b, dt, E, st)));
-  {
+  if (!saved) {
     ScanArgs a{};
     a.T = T; a.E = E; a.R = R; a.ldp = 0;
     a.u = u; a.ld_u = E; a.dt = dt; a.ld_dt = E;
@@ -432,8 +447,8 @@ int run_layer_bwd(const r2l_dims* d, r2l_dtype act, bool no_ln, const r2l_weight
     a.l2r = false;
     if (p.sp.summary) R2L_RUN("bwd_scan_summary", st, scan_summary<A>(a, false, st));
     R2L_RUN("bwd_scan", st, scan_main<A>(a, false, st));
+    R2L_RUN("bwd_out_proj", st, gemm(T, D, E, yg, E, Wout, E, o, D, true));
   }
-  R2L_RUN("bwd_out_proj", st, gemm(T, D, E, yg, E, Wout, E, o, D, true));
 
   // ---------------- backward ----------------
   float* dout = at<float>(ws, p.dout);
@@ -548,6 +563,13 @@ size_t r2l_layer_workspace_bytes(const r2l_dims* dims, r2l_dtype act, int64_t n_
   return plan_layer(dims, act, n_tokens, nseq, max_seqlen).total;
 }
 
+size_t r2l_layer_train_workspace_bytes(const r2l_dims* dims, r2l_dtype act, int64_t n_tokens,
+                                       int32_t nseq, int32_t max_seqlen) {
+  if (check_dims(dims) != R2L_OK || check_tokens(act, n_tokens, nseq, max_seqlen) != R2L_OK)
+    return 0;
+  return plan_layer(dims, act, n_tokens, nseq, max_seqlen, true).total;
+}
+
 size_t r2l_scan_workspace_bytes(const r2l_dims* dims, int64_t n_tokens, int32_t nseq,
                                 int32_t max_seqlen) {
   if (check_dims(dims) != R2L_OK || check_tokens(R2L_F32, n_tokens, nseq, max_seqlen) != R2L_OK)
@@ -567,7 +589,7 @@ int r2l_layer_fwd(const r2l_dims* d, r2l_dtype act, uint32_t flags, const r2l_we
   int rc = check_dims(d);
   if (rc != R2L_OK) return rc;
   if ((rc = check_tokens(act, n_tokens, nseq, max_seqlen)) != R2L_OK) return rc;
-  if (flags & ~(R2L_FLAG_NO_LN | R2L_FLAG_L2R)) return R2L_ERR_INVALID_ARG;
+  if (flags & ~(R2L_FLAG_NO_LN | R2L_FLAG_L2R | R2L_FLAG_TRAIN)) return R2L_ERR_INVALID_ARG;
   const bool l2r = flags & R2L_FLAG_L2R;
   if (!w || !h_in || !h_out || !cu_seqlens) return R2L_ERR_INVALID_ARG;
   if (!w->in_proj_w || !w->conv_w || !w->conv_b || !w->x_proj_w || !w->dt_proj_w ||
@@ -582,7 +604,7 @@ int r2l_layer_fwd(const r2l_dims* d, r2l_dtype act, uint32_t flags, const r2l_we
     for (const void* p : ptrs)
       if (p && !aligned16(p)) return R2L_ERR_INVALID_ARG;
   }
-  const LayerPlan lp = plan_layer(d, act, n_tokens, nseq, max_seqlen);
+  const LayerPlan lp = plan_layer(d, act, n_tokens, nseq, max_seqlen, (flags & R2L_FLAG_TRAIN) != 0);
   if (!workspace || workspace_bytes < lp.total) return R2L_ERR_WORKSPACE;
   if (((uintptr_t)workspace & (kAlign - 1)) != 0) return R2L_ERR_INVALID_ARG;
   if (n_tokens == 0) return R2L_OK;
@@ -595,7 +617,7 @@ int r2l_layer_fwd(const r2l_dims* d, r2l_dtype act, uint32_t flags, const r2l_we
   ChunkDesc* chunks = at<ChunkDesc>(workspace, sp.off_chunks);
   int32_t* nch = at<int32_t>(workspace, sp.off_n);
   float* xdbl = at<float>(workspace, lp.off_xdbl);
-  float* o = at<float>(workspace, lp.off_xz);  // aliases xz, which is dead by then
+  float* o = at<float>(workspace, lp.off_o);  // xz's region unless training: xz is dead by then
 
   ScanArgs a{};
   a.T = T; a.E = E; a.R = R; a.ldp = P;
@@ -783,7 +805,8 @@ size_t r2l_layer_bwd_workspace_bytes(const r2l_dims* dims, r2l_dtype act, int64_
 
 int r2l_layer_bwd(const r2l_dims* d, r2l_dtype act, uint32_t flags, const r2l_weights* w, const void* h_in,
                   const void* g_out, void* dh, const r2l_grads* gr, const int32_t* cu_seqlens, int32_t nseq,
-                  int64_t n_tokens, int32_t max_seqlen, void* workspace, size_t workspace_bytes, void* stream) {
+                  int64_t n_tokens, int32_t max_seqlen, const void* saved, void* workspace,
+                  size_t workspace_bytes, void* stream) {
   int rc = check_dims(d);
   if (rc != R2L_OK) return rc;
   if ((rc = check_tokens(act, n_tokens, nseq, max_seqlen)) != R2L_OK) return rc;
@@ -807,13 +830,14 @@ int r2l_layer_bwd(const r2l_dims* d, r2l_dtype act, uint32_t flags, const r2l_we
   const LayerBwdPlan p = plan_layer_bwd(d, act, n_tokens, nseq, max_seqlen);
   if (!workspace || workspace_bytes < p.total) return R2L_ERR_WORKSPACE;
   if (((uintptr_t)workspace & (kAlign - 1)) != 0) return R2L_ERR_INVALID_ARG;
+  if (saved && ((uintptr_t)saved & (kAlign - 1)) != 0) return R2L_ERR_INVALID_ARG;
   if (n_tokens == 0) return R2L_OK;
   hipStream_t st = (hipStream_t)stream;
   if (act == R2L_BF16)
     return run_layer_bwd<bf16>(d, act, no_ln, w, (const bf16*)h_in, (const bf16*)g_out, (bf16*)dh, gr, cu_seqlens,
-                               nseq, (int)n_tokens, max_seqlen, workspace, st);
+                               nseq, (int)n_tokens, max_seqlen, saved, workspace, st);
   return run_layer_bwd<float>(d, act, no_ln, w, (const float*)h_in, (const float*)g_out, (float*)dh, gr, cu_seqlens,
-                              nseq, (int)n_tokens, max_seqlen, workspace, st);
+                              nseq, (int)n_tokens, max_seqlen, saved, workspace, st);
 }
 
 int r2l_gemm_nt(r2l_dtype act, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,

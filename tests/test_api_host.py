@@ -114,7 +114,41 @@ def test_layer_fwd_rejects_bad_arguments():
 def test_layer_fwd_accepts_the_direction_flag():
     assert _layer(flags=B.R2L_FLAG_L2R, wsb=16) == B.R2L_ERR_WORKSPACE
     assert _layer(flags=B.R2L_FLAG_L2R | B.R2L_FLAG_NO_LN, wsb=16) == B.R2L_ERR_WORKSPACE
-    assert _layer(flags=0x4) == B.R2L_ERR_INVALID_ARG
+    assert _layer(flags=0x8) == B.R2L_ERR_INVALID_ARG
+
+
+def test_train_flag_needs_the_train_workspace():
+    lib = B.lib()
+    d = _dims()
+    T = 33024
+    ws = lib.r2l_layer_workspace_bytes(C.byref(d), B.R2L_BF16, T, 8, 4128)
+    tws = lib.r2l_layer_train_workspace_bytes(C.byref(d), B.R2L_BF16, T, 8, 4128)
+    # the out_proj output gets a region of its own instead of reusing the in_proj output's
+    assert tws >= ws + T * 2048 * 4 - 4096
+    assert lib.r2l_layer_train_workspace_bytes(C.byref(_dims(N=8)), B.R2L_BF16, T, 8, 4128) == 0
+    assert _layer(flags=B.R2L_FLAG_TRAIN, T=T, nseq=8, maxlen=4128, wsb=ws) == B.R2L_ERR_WORKSPACE
+    # with the train workspace the call passes every check (and then launches nothing: T = 0)
+    assert _layer(flags=B.R2L_FLAG_TRAIN, T=0, nseq=1, maxlen=0, ws=FAKE * 256,
+                  wsb=lib.r2l_layer_train_workspace_bytes(C.byref(d), B.R2L_BF16, 0, 1, 0)) == B.R2L_OK
+
+
+def _layer_bwd(flags=0, saved=None, T=100, wsb=None, ws=FAKE * 256):
+    lib = B.lib()
+    d = _dims()
+    w = _weights()
+    g = B.Grads(**{f[0]: FAKE for f in B.Grads._fields_})
+    if wsb is None:
+        wsb = lib.r2l_layer_bwd_workspace_bytes(C.byref(d), B.R2L_BF16, T, 2, 60)
+    return lib.r2l_layer_bwd(C.byref(d), B.R2L_BF16, flags, C.byref(w), FAKE, FAKE, FAKE, C.byref(g), FAKE, 2, T, 60,
+                             saved, ws, wsb, None)
+
+
+def test_layer_bwd_rejects_bad_arguments():
+    assert _layer_bwd(flags=B.R2L_FLAG_L2R) == B.R2L_ERR_UNSUPPORTED
+    assert _layer_bwd(flags=B.R2L_FLAG_TRAIN) == B.R2L_ERR_INVALID_ARG    # a forward-only flag
+    assert _layer_bwd(wsb=1024) == B.R2L_ERR_WORKSPACE
+    assert _layer_bwd(saved=FAKE * 256 + 16) == B.R2L_ERR_INVALID_ARG     # saved must be 256-byte aligned
+    assert _layer_bwd(T=0, saved=FAKE * 256) == B.R2L_OK                  # nothing to do, nothing launched
 
 
 def test_layer_fwd_no_ln_needs_no_ln_weights():

@@ -98,11 +98,24 @@ GRAD_NAMES = ("in_proj_w", "conv_w", "conv_b", "x_proj_w", "dt_proj_w", "dt_proj
               "out_proj_w", "ln_w", "ln_b")
 
 
-def _layer_bwd_case(wl, W, h, cu, g, dtype, flags):
+def _layer_bwd_case(wl, W, h, cu, g, dtype, flags, saved=False):
+    """The backward on the GPU; saved: run the forward with R2L_FLAG_TRAIN
+    first and hand its workspace to the backward (no recompute), checking
+    on the way that the training forward's output equals the plain one."""
     w = B.to_device_weights(W, dtype, DEV)
     hd = torch.from_numpy(np.ascontiguousarray(h, np.float32)).to(dtype).to(DEV)
     gd = torch.from_numpy(np.ascontiguousarray(g, np.float32)).to(dtype).to(DEV)
-    dh, grads = B.r2l_layer_bwd(hd, w, cu, gd, flags=flags)
+    sv = None
+    if saved:
+        T = hd.shape[0]
+        cu_np = np.asarray(cu)
+        need = B.r2l_layer_train_workspace_bytes(B.dims_of(w), B._act(hd), T, len(cu_np) - 1,
+                                                 int(np.diff(cu_np).max()))
+        sv = torch.empty(need, dtype=torch.uint8, device=DEV)
+        out_t = B.r2l_layer_fwd(hd, w, cu, flags=flags | B.R2L_FLAG_TRAIN, workspace=sv)
+        out_p = B.r2l_layer_fwd(hd, w, cu, flags=flags)
+        assert torch.equal(out_t, out_p), "the training forward changed the output"
+    dh, grads = B.r2l_layer_bwd(hd, w, cu, gd, flags=flags, saved=sv)
     torch.cuda.synchronize()
     return to_np(dh), {k: to_np(v) for k, v in grads.items()}
 
@@ -116,14 +129,15 @@ def _layer_err(f, got, ref, names, tol, tag):
     return worst
 
 
+@pytest.mark.parametrize("saved", [False, True])
 @pytest.mark.parametrize("use_ln", [True, False])
-def test_tiny_f32_layer_bwd_matches_oracle(use_ln):
+def test_tiny_f32_layer_bwd_matches_oracle(use_ln, saved):
     wl = synth.workloads()["tiny_f32"]
-    _case(f"tiny_f32 layer bwd ln={use_ln}")
+    _case(f"tiny_f32 layer bwd ln={use_ln} saved={saved}")
     W, h, cu = synth.make_weights(wl), synth.make_hidden(wl), wl.cu_seqlens()
     g = synth.make_hidden(wl, hook=9)
     ref = G.layer_grads(h, cu, W, float(W["s"]), g, use_ln=use_ln)
-    dh, got = _layer_bwd_case(wl, W, h, cu, g, torch.float32, 0 if use_ln else B.R2L_FLAG_NO_LN)
+    dh, got = _layer_bwd_case(wl, W, h, cu, g, torch.float32, 0 if use_ln else B.R2L_FLAG_NO_LN, saved=saved)
     names = [n for n in GRAD_NAMES if use_ln or n not in ("ln_w", "ln_b")]
     got["h"], got["s"] = dh, got["s"].reshape(())
     ref["s"] = np.array(ref["s"])
@@ -160,15 +174,16 @@ def rel_fro(g, o):
     return float(np.linalg.norm(g - o)) / n if n else float(np.linalg.norm(g))
 
 
+@pytest.mark.parametrize("saved", [False, True])
 @pytest.mark.parametrize("lens", [[5, 0, 130, 1, 300], [700, 33]])
-def test_small_bf16_layer_bwd_matches_oracle(lens):
-    _case(f"small bf16 layer bwd lens={lens}")
+def test_small_bf16_layer_bwd_matches_oracle(lens, saved):
+    _case(f"small bf16 layer bwd lens={lens} saved={saved}")
     wl = synth.custom(lens, seed=19, h_kind="rms", d_model=256, d_inner=512, dt_rank=16)
     W = synth.make_weights(wl, affine_ln=True)
     h, cu = synth.make_hidden(wl), wl.cu_seqlens()
     g = synth.make_hidden(wl, hook=9)
     ref = G.layer_grads(h, cu, W, float(W["s"]), g)
-    dh, got = _layer_bwd_case(wl, W, h, cu, g, torch.bfloat16, 0)
+    dh, got = _layer_bwd_case(wl, W, h, cu, g, torch.bfloat16, 0, saved=saved)
     got["h"] = dh
     for k in list(GRAD_NAMES) + ["h"]:
         report(f"small bf16 d{k} (max / RMS, printed only)", err_rms(got[k], ref[k]), TOL_GRAD_BF16)
@@ -179,7 +194,8 @@ def test_small_bf16_layer_bwd_matches_oracle(lens):
     assert worst <= TOL_GRAD_BF16
 
 
-def test_serve_b8_backward_suffix_matches_oracle():
+@pytest.mark.parametrize("saved", [False, True])
+def test_serve_b8_backward_suffix_matches_oracle(saved):
     """The serving shape (B=8 x 4128 tokens, D=2048, E=4096: the launch
     configuration that bench.py --backward times).  The layer sees only the
     right context, so with g = dL/dh+ zero outside the last S tokens of each
@@ -188,7 +204,7 @@ def test_serve_b8_backward_suffix_matches_oracle():
     suffixes taken as sequences of their own, and dh is exactly zero on the
     other rows (no output there carries any gradient)."""
     wl = synth.workloads()["serve_b8"]
-    _case("serve_b8 backward, g on the last 192 tokens of each sequence")
+    _case(f"serve_b8 backward, g on the last 192 tokens of each sequence, saved={saved}")
     W = synth.make_weights(wl, affine_ln=True)
     h, cu = synth.make_hidden(wl), wl.cu_seqlens()
     S = 192
@@ -196,7 +212,7 @@ def test_serve_b8_backward_suffix_matches_oracle():
     for q in range(wl.nseq):
         mask[int(cu[q + 1]) - S:int(cu[q + 1])] = True
     g = np.where(mask[:, None], synth.make_hidden(wl, hook=9), 0.0).astype(np.float32)
-    dh, got = _layer_bwd_case(wl, W, h, cu, g, torch.bfloat16, 0)
+    dh, got = _layer_bwd_case(wl, W, h, cu, g, torch.bfloat16, 0, saved=saved)
     assert not np.any(dh[~mask]), "gradient outside the suffixes"
     idx = np.nonzero(mask)[0]
     t = time.time()
