@@ -36,7 +36,10 @@ def _case(name):
                                    # 264 tiles of 256 x 256: 8 past a round of 256, split along K with a workspace
                                    (8448, 2048, 1024),
                                    # few-row kernel (256-row tiles): the denoise-step projections, ragged M
-                                   (256, 8192, 2048), (256, 2048, 4096), (100, 1024, 512), (1024, 2048, 4096)])
+                                   (256, 8192, 2048), (256, 2048, 4096), (100, 1024, 512), (1024, 2048, 4096),
+                                   # 9 x 32 tiles of 256 x 256: a whole round, then the last (ragged) tile row
+                                   # on the 128 x 128 kernel
+                                   (2200, 8192, 512)])
 def test_gemm_bf16_matches_fp64_product(M, N, K):
     _case(f"gemm bf16 {M}x{N}x{K}")
     A = synth.make_aux(M * 7 + 1, (M, K))
