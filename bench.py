@@ -361,17 +361,21 @@ def bench_backward(args):
 
 
 KERNEL_SOURCES = {  # the source file that defines each timed kernel
-    "in_proj_gemm": "gemm.hip", "out_proj_gemm": "gemm.hip", "out_proj_tail": "gemm.hip",
-    "out_proj_reduce": "gemm.hip", "conv_xproj": "conv.hip", "conv_sum": "conv.hip",
+    "in_proj_gemm": "gemm.hip", "out_proj_gemm": "gemm.hip", "conv_xproj": "conv.hip", "conv_sum": "conv.hip",
     "scan_main": "scan.hip", "scan_summary": "scan.hip", "ln_gate": "ln.hip", "plan_chunks": "scan.hip",
 }
-ROCPROF_NAMES = {  # substring of the demangled kernel name in rocprofv3 output
-    "in_proj_gemm": "gemm_bf16_big_kernel<false, 4, false>", "out_proj_gemm": "gemm_bf16_big_kernel<true, 8, false>",
-    "out_proj_tail": "gemm_bf16_big_kernel<true, 8, true>", "out_proj_reduce": "gemm_tail_reduce_kernel<true, 8>",
-    "conv_xproj": "conv_xproj_sk_kernel<5, false>", "conv_sum": "sk_sum_kernel",
-    "scan_main": "E, false, 4, false, false>(r2l::ScanArgs)",
-    "scan_summary": "E, true, 4, false, false>(r2l::ScanArgs)",
-    "ln_gate": "ln_gate_kernel",
+# The launches behind each timed label of the serving-shape forward, as
+# substrings of the demangled names in rocprofv3 output; each launches once
+# per step, so a label's time and traffic per step are sums over its parts.
+ROCPROF_NAMES = {
+    "in_proj_gemm": ["gemm_bf16_big_kernel<false, 4, false>", "gemm_bf16_nt_kernel<128, 128, true>",
+                     "gemm_small_reduce_kernel<128, 128, false>"],
+    "out_proj_gemm": ["gemm_bf16_big_kernel<true, 8, false>", "gemm_bf16_big_kernel<true, 8, true>",
+                      "gemm_tail_reduce_kernel<true, 8>"],
+    "conv_xproj": ["conv_xproj_sk_kernel<5, false>"], "conv_sum": ["sk_sum_kernel"],
+    "scan_main": ["E, false, 4, false, false>(r2l::ScanArgs)"],
+    "scan_summary": ["E, true, 4, false, false>(r2l::ScanArgs)"],
+    "ln_gate": ["ln_gate_kernel"], "plan_chunks": ["plan_chunks_kernel"],
 }
 PROFILE_JSON = os.path.join(ROOT, "profiles", "traffic_serve_b8.json")
 
@@ -431,6 +435,16 @@ def summarize_profiles(argv, size_kib=0.0, bench_args=""):
             lines.append(f"| `{r['Name'][:90]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
                          f"{float(r['TotalDurationNs']) / 1e6:.3f} | {float(r['Percentage']):.1f} |")
         lines.append("")
+        if not extra:
+            # the timed labels of bench.py: sums of their launches' averages
+            lines += ["Per bench.py label (the sum of its launches' average durations; compare with the",
+                      "label's avg_ms in bench.py's `kernels`):", "", "| label | launches | avg us per step |",
+                      "|---|---|---|"]
+            for label, parts in ROCPROF_NAMES.items():
+                rows = [r for r in stats if any(p in r["Name"] for p in parts)]
+                if rows:
+                    lines.append(f"| {label} | {len(rows)} | {sum(float(r['AverageNs']) for r in rows) / 1e3:.1f} |")
+            lines.append("")
     if len(argv) >= 4:
         def per_kernel(d, counter):
             acc = {}
@@ -452,13 +466,13 @@ def summarize_profiles(argv, size_kib=0.0, bench_args=""):
             lines.append(f"Calibration: plain copy of {size_kib:.0f} KiB read as FETCH {calib['fetch_kib']:.0f} KiB, "
                          f"WRITE {calib['write_kib']:.0f} KiB -> scale read x{rs:.4f}, write x{ws:.4f}.")
             lines += ["", "| kernel | FETCH KiB | WRITE KiB | read MB (scaled) | write MB (scaled) |", "|---|---|---|---|---|"]
-            for ours, sub in ROCPROF_NAMES.items():
-                ks = [k for k in fetch if sub in k]
+            for ours, parts in ROCPROF_NAMES.items():
+                ks = [k for k in fetch if any(p in k for p in parts)]
                 if not ks:
                     continue
-                f = sum(sum(fetch[k]) / len(fetch[k]) for k in ks) / len(ks)
-                wv = [sum(write[k]) / len(write[k]) for k in ks if k in write]
-                wr = sum(wv) / len(wv) if wv else 0.0
+                # per step: the sum over the label's launches of each one's average per dispatch
+                f = sum(sum(fetch[k]) / len(fetch[k]) for k in ks)
+                wr = sum(sum(write[k]) / len(write[k]) for k in ks if k in write)
                 rb, wb = f * 1024 * rs, wr * 1024 * ws
                 rec["kernels"][ours] = {"fetch_kib": f, "write_kib": wr, "read_bytes": round(rb),
                                         "write_bytes": round(wb), "copy_scale": [round(rs, 5), round(ws, 5)],
