@@ -370,8 +370,8 @@ KERNEL_SOURCES = {  # the source file that defines each timed kernel
 ROCPROF_NAMES = {
     "in_proj_gemm": ["gemm_bf16_big_kernel<false, 4, false>", "gemm_bf16_nt_kernel<128, 128, true>",
                      "gemm_small_reduce_kernel<128, 128, false>"],
-    "out_proj_gemm": ["gemm_bf16_big_kernel<true, 8, false>", "gemm_bf16_big_kernel<true, 8, true>",
-                      "gemm_tail_reduce_kernel<true, 8>"],
+    "out_proj_gemm": ["gemm_bf16_big_kernel<true, 8, false>", "gemm_bf16_nt_kernel<128, 128, true>",
+                      "gemm_small_reduce_kernel<128, 128, true>"],
     "conv_xproj": ["conv_xproj_sk_kernel<5, false>"], "conv_sum": ["sk_sum_kernel"],
     "scan_main": ["E, false, 4, false, false>(r2l::ScanArgs)"],
     "scan_summary": ["E, true, 4, false, false>(r2l::ScanArgs)"],

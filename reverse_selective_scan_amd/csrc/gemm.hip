@@ -538,10 +538,11 @@ hipError_t gemm_bf16_nt(int M, int N, int K, const bf16* A, long lda, const bf16
     const int nTn = (N + kBigBN - 1) / kBigBN, nTm = (M + kBigBM - 1) / kBigBM;
     const int G = nTn <= 8 ? 8 : 4;
     // A leftover that is exactly the last row of tiles (the last group holds
-    // one tile row, and the leftover is that row) and too large to split
-    // along K: those rows go to the 128 x 128 kernel instead, after the
-    // whole rounds, where they fill the chip rather than a fraction of it.
-    if (!splits && ws != nullptr && big_tiles > ncu && rem == nTn && nTm % G == 1) {
+    // one tile row, and the leftover is that row): those rows go to the
+    // 128 x 128 kernel instead, after the whole rounds, where they fill the
+    // chip rather than a fraction of it (measured faster than the split
+    // tail for both projections of the serving shape).
+    if (ws != nullptr && big_tiles > ncu && rem == nTn && nTm % G == 1) {
       const int m_tail = (nTm - 1) * kBigBM;
       if (G == 8) launch_big<8>(m_tail, N, K, A, lda, B, ldb, C, ldc, out_f32, (int)big_tiles - rem, 0, 0, nk, ws, st);
       else launch_big<4>(m_tail, N, K, A, lda, B, ldb, C, ldc, out_f32, (int)big_tiles - rem, 0, 0, nk, ws, st);

@@ -33,8 +33,11 @@ def _case(name):
                                    (1031, 257, 2048), (640, 8192, 2048),
                                    # large-tile kernel: ragged M and N, and an N%4 != 0 fallback
                                    (8200, 2052, 512), (4099, 4096, 256), (8200, 2050, 512),
-                                   # 264 tiles of 256 x 256: 8 past a round of 256, split along K with a workspace
+                                   # 264 tiles of 256 x 256: a round of 256, then the last tile row (8 tiles) on
+                                   # the 128 x 128 kernel
                                    (8448, 2048, 1024),
+                                   # 272 tiles: 16 past a round, not a whole tile row: split along K
+                                   (8704, 2048, 1024),
                                    # few-row kernel (256-row tiles): the denoise-step projections, ragged M
                                    (256, 8192, 2048), (256, 2048, 4096), (100, 1024, 512), (1024, 2048, 4096),
                                    # 9 x 32 tiles of 256 x 256: a whole round, then the last (ragged) tile row
