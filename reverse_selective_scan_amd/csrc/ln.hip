@@ -54,16 +54,36 @@ __global__ __launch_bounds__(256) void ln_gate_kernel(int Tn, int D, const O* __
   if (row >= Tn) return;
   const int nch = D / 512;  // D % 512 == 0 here (other widths use the generic kernel)
   const O* orow = o + (long)row * D;
+  const long rb = (long)row * D;
   float v[NCH][8];
-  float sum = 0.0f;
+  // every load of the row is issued first (o, h, gamma, beta), so that h's,
+  // gamma's and beta's latencies hide behind the two reductions; h is read
+  // before any store, so h_out may alias h_in
+  Raw8h<T> hraw[NCH];
+  float gm[NCH][8], bt[NCH][8];
 #pragma unroll
   for (int c = 0; c < NCH; ++c) {
     if (c < nch) {
       ld8(orow + 512 * c + 8 * lane, v[c]);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) sum += v[c][i];
+      const long off = rb + 512 * c + 8 * lane;
+      if constexpr (sizeof(T) == 2) {
+        hraw[c].v = *(const bf16x8*)(h_in + off);
+      } else {
+        hraw[c].a = *(const f32x4*)(h_in + off);
+        hraw[c].b = *(const f32x4*)(h_in + off + 4);
+      }
+      if (!no_ln) {
+        ld8(gamma + 512 * c + 8 * lane, gm[c]);
+        ld8(beta + 512 * c + 8 * lane, bt[c]);
+      }
     }
   }
+  float sum = 0.0f;
+#pragma unroll
+  for (int c = 0; c < NCH; ++c)
+    if (c < nch)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) sum += v[c][i];
   const float invD = 1.0f / (float)D;
   if (!no_ln) {
     const float mu = wave_sum(sum) * invD;
@@ -79,16 +99,11 @@ __global__ __launch_bounds__(256) void ln_gate_kernel(int Tn, int D, const O* __
     const float rstd = 1.0f / sqrtf(wave_sum(sq) * invD + eps);
 #pragma unroll
     for (int c = 0; c < NCH; ++c)
-      if (c < nch) {
-        float gm[8], bt[8];
-        ld8(gamma + 512 * c + 8 * lane, gm);
-        ld8(beta + 512 * c + 8 * lane, bt);
+      if (c < nch)
 #pragma unroll
-        for (int i = 0; i < 8; ++i) v[c][i] = fmaf(gm[i], v[c][i] * rstd, bt[i]);
-      }
+        for (int i = 0; i < 8; ++i) v[c][i] = fmaf(gm[c][i], v[c][i] * rstd, bt[c][i]);
   }
   const float g = tanhf(s[0]);
-  const long rb = (long)row * D;
 #pragma unroll
   for (int c = 0; c < NCH; ++c)
     if (c < nch) {
@@ -97,14 +112,20 @@ __global__ __launch_bounds__(256) void ln_gate_kernel(int Tn, int D, const O* __
       if (g == 0.0f) {
         // a zero gate copies h bit for bit (no arithmetic on it at all)
         if constexpr (sizeof(T) == 2) {
-          *(bf16x8*)(h_out + off) = *(const bf16x8*)(h_in + off);
+          *(bf16x8*)(h_out + off) = hraw[c].v;
         } else {
-          *(f32x4*)(h_out + off) = *(const f32x4*)(h_in + off);
-          *(f32x4*)(h_out + off + 4) = *(const f32x4*)(h_in + off + 4);
+          *(f32x4*)(h_out + off) = hraw[c].a;
+          *(f32x4*)(h_out + off + 4) = hraw[c].b;
         }
       } else {
         float hv[8];
-        ld8(h_in + off, hv);
+        if constexpr (sizeof(T) == 2) {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) hv[i] = (float)hraw[c].v[i];
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) { hv[i] = hraw[c].a[i]; hv[4 + i] = hraw[c].b[i]; }
+        }
 #pragma unroll
         for (int i = 0; i < 8; ++i) hv[i] = fmaf(g, v[c][i], hv[i]);
         st8(h_out + off, hv);
