@@ -57,7 +57,7 @@ def _scan_case(T, E, act, seed):
 
 @pytest.mark.parametrize("act", ["f32", "bf16"])
 @pytest.mark.parametrize("lens,E", [([1], 64), ([17], 64), ([5, 0, 130, 1, 300], 128), ([700, 2, 129], 192),
-                                    ([2048], 64)])
+                                    ([2048], 64), ([8192, 3], 64)])
 @pytest.mark.parametrize("gated", [True, False])
 def test_scan_bwd_matches_oracle(act, lens, E, gated):
     _case(f"scan bwd {act} lens={lens} E={E} gated={gated}")
@@ -224,4 +224,25 @@ def test_serve_b8_backward_suffix_matches_oracle(saved):
     _, r = O.reverse_mamba_layer(h[idx], cu_s, W, float(W["s"]), return_branch=True)
     e = ds_err(got["s"].reshape(()), ref["s"], g[idx], r, float(W["s"]))
     assert report("serve_b8 suffix ds (against |g| |r|)", e, TOL_GRAD_BF16) <= TOL_GRAD_BF16
+    assert worst <= TOL_GRAD_BF16
+
+
+def test_long_sequence_bf16_layer_bwd_matches_oracle():
+    """One 4096-token sequence and a short one: the adjoint carried left to
+    right across 256 sub-blocks of the first, and reset at the boundary."""
+    lens = [4096, 37]
+    _case(f"long bf16 layer bwd lens={lens}")
+    wl = synth.custom(lens, seed=23, h_kind="rms", d_model=256, d_inner=512, dt_rank=16)
+    W = synth.make_weights(wl, affine_ln=True)
+    h, cu = synth.make_hidden(wl), wl.cu_seqlens()
+    g = synth.make_hidden(wl, hook=9)
+    t = time.time()
+    ref = G.layer_grads(h, cu, W, float(W["s"]), g)
+    print(f"oracle {time.time() - t:.1f}s", flush=True)
+    dh, got = _layer_bwd_case(wl, W, h, cu, g, torch.bfloat16, 0)
+    got["h"] = dh
+    worst = _layer_err(rel_fro, got, ref, list(GRAD_NAMES) + ["h"], TOL_GRAD_BF16, "long bf16 (Frobenius)")
+    _, r = O.reverse_mamba_layer(h, cu, W, float(W["s"]), return_branch=True)
+    e = ds_err(got["s"].reshape(()), ref["s"], g, r, float(W["s"]))
+    assert report("long bf16 ds (against |g| |r|)", e, TOL_GRAD_BF16) <= TOL_GRAD_BF16
     assert worst <= TOL_GRAD_BF16
