@@ -170,7 +170,9 @@ int r2l_layer_fwd(const r2l_dims* dims, r2l_dtype act, uint32_t flags, const r2l
  * and fp32 results for bf16 activations; the fp32 kernel for fp32), with
  * the transposed operands materialised.  Sums over tokens run in a fixed
  * order: results are deterministic.
- * flags: 0 or R2L_FLAG_NO_LN (R2L_FLAG_L2R returns R2L_ERR_UNSUPPORTED).
+ * flags: 0, R2L_FLAG_NO_LN and/or R2L_FLAG_L2R (the left-to-right layer:
+ * computed as the default layer's gradient of every sequence reversed, with
+ * dh reversed back; with saved != NULL it returns R2L_ERR_UNSUPPORTED).
  * bf16 activations need dt_rank a multiple of 8.  Other arguments as in
  * r2l_layer_fwd.  workspace: r2l_layer_bwd_workspace_bytes(...) bytes,
  * 256-byte aligned (several times the forward's: every recomputed

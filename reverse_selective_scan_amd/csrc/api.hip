@@ -300,7 +300,7 @@ int run_scan_bwd(r2l_dtype act, int E, int R, int T, int nseq, const void* u, in
 struct LayerBwdPlan {
   size_t xz, u, xdbl, xdbl2, xdbl3, delta, dt, yg, o, scanf, dout, gx, gr, do_a, doT, ygT, wT, dyg, du, ddt, dz, dB,
       dC, scanb, ddt_a, ddtT, deltaT, ddelta, dxdbl_a, dxdblT, uT, dux, convp, dxz_a, dxzT, hT, dhb, colp, dtpart,
-      scratch;
+      hflip, gflip, scratch;
   ScanPlan sp;
   int Tp;
   size_t total;
@@ -356,16 +356,30 @@ LayerBwdPlan plan_layer_bwd(const r2l_dims* d, r2l_dtype act, int64_t T, int32_t
   p.dhb = take(Tz * D * f);
   p.colp = take((size_t)colsum_parts((int)T) * (E > D ? E : D) * f);
   p.dtpart = take((size_t)((T + 63) / 64) * E * f);
+  // h and g reversed per sequence (the left-to-right direction)
+  p.hflip = take(Tz * D * sa);
+  p.gflip = take(Tz * D * sa);
   p.scratch = take(act == R2L_BF16 ? kSplitScratch : 0);
   p.total = off;
   return p;
 }
 
+// l2r: the left-to-right layer's gradient is the default layer's gradient
+// of every sequence reversed (h and g), with dh reversed back; the
+// parameter gradients are the same.
 template <typename A>
-int run_layer_bwd(const r2l_dims* d, r2l_dtype act, bool no_ln, const r2l_weights* w, const A* h, const A* g,
-                  A* dh, const r2l_grads* gr, const int32_t* cu_seqlens, int nseq, int T, int32_t max_seqlen,
-                  const void* saved, void* ws, hipStream_t st) {
+int run_layer_bwd(const r2l_dims* d, r2l_dtype act, bool no_ln, bool l2r, const r2l_weights* w, const A* h,
+                  const A* g, A* dh, const r2l_grads* gr, const int32_t* cu_seqlens, int nseq, int T,
+                  int32_t max_seqlen, const void* saved, void* ws, hipStream_t st) {
   const LayerBwdPlan p = plan_layer_bwd(d, act, T, nseq, max_seqlen);
+  if (l2r) {
+    A* hf = at<A>(ws, p.hflip);
+    A* gf = at<A>(ws, p.gflip);
+    R2L_RUN("bwd_flip", st, flip_rows<A>(T, d->d_model, h, d->d_model, hf, d->d_model, cu_seqlens, nseq, st));
+    R2L_RUN("bwd_flip", st, flip_rows<A>(T, d->d_model, g, d->d_model, gf, d->d_model, cu_seqlens, nseq, st));
+    h = hf;
+    g = gf;
+  }
   const int D = d->d_model, E = d->d_inner, N = d->d_state, R = d->dt_rank, P = R + 2 * N, Tp = p.Tp;
   const bool bf = act == R2L_BF16;
   const int ncu = bf ? num_cus() : 0;
@@ -525,6 +539,7 @@ int run_layer_bwd(const r2l_dims* d, r2l_dtype act, bool no_ln, const r2l_weight
   R2L_RUN("bwd_hT", st, (transpose<A, A>(T, D, Tp, h, D, hT, st)));
   R2L_RUN("bwd_dWin", st, gemm(2 * E, D, Tp, dxzT, Tp, hT, Tp, gr->in_proj_w, D, true));
   R2L_RUN("bwd_dh", st, (elementwise<kAddTo, A, A>(T, D, g, D, dhb, D, nullptr, dh, D, st)));
+  if (l2r) R2L_RUN("bwd_flip", st, flip_rows<A>(T, D, dh, D, dh, D, cu_seqlens, nseq, st));
   return R2L_OK;
 }
 
@@ -810,9 +825,9 @@ int r2l_layer_bwd(const r2l_dims* d, r2l_dtype act, uint32_t flags, const r2l_we
   int rc = check_dims(d);
   if (rc != R2L_OK) return rc;
   if ((rc = check_tokens(act, n_tokens, nseq, max_seqlen)) != R2L_OK) return rc;
-  if (flags & R2L_FLAG_L2R) return R2L_ERR_UNSUPPORTED;   // the backward runs the default direction only
-  if (flags & ~R2L_FLAG_NO_LN) return R2L_ERR_INVALID_ARG;
-  const bool no_ln = flags & R2L_FLAG_NO_LN;
+  if (flags & ~(R2L_FLAG_NO_LN | R2L_FLAG_L2R)) return R2L_ERR_INVALID_ARG;
+  const bool no_ln = flags & R2L_FLAG_NO_LN, l2r = flags & R2L_FLAG_L2R;
+  if (l2r && saved) return R2L_ERR_UNSUPPORTED;   // saved activations: the default direction only
   if (!w || !gr || !h_in || !g_out || !dh || !cu_seqlens) return R2L_ERR_INVALID_ARG;
   if (!w->in_proj_w || !w->conv_w || !w->conv_b || !w->x_proj_w || !w->dt_proj_w || !w->out_proj_w ||
       !w->dt_proj_b || !w->A_log || !w->Dskip || !w->s || (!no_ln && (!w->ln_w || !w->ln_b)))
@@ -834,10 +849,10 @@ int r2l_layer_bwd(const r2l_dims* d, r2l_dtype act, uint32_t flags, const r2l_we
   if (n_tokens == 0) return R2L_OK;
   hipStream_t st = (hipStream_t)stream;
   if (act == R2L_BF16)
-    return run_layer_bwd<bf16>(d, act, no_ln, w, (const bf16*)h_in, (const bf16*)g_out, (bf16*)dh, gr, cu_seqlens,
-                               nseq, (int)n_tokens, max_seqlen, saved, workspace, st);
-  return run_layer_bwd<float>(d, act, no_ln, w, (const float*)h_in, (const float*)g_out, (float*)dh, gr, cu_seqlens,
-                              nseq, (int)n_tokens, max_seqlen, saved, workspace, st);
+    return run_layer_bwd<bf16>(d, act, no_ln, l2r, w, (const bf16*)h_in, (const bf16*)g_out, (bf16*)dh, gr,
+                               cu_seqlens, nseq, (int)n_tokens, max_seqlen, saved, workspace, st);
+  return run_layer_bwd<float>(d, act, no_ln, l2r, w, (const float*)h_in, (const float*)g_out, (float*)dh, gr,
+                              cu_seqlens, nseq, (int)n_tokens, max_seqlen, saved, workspace, st);
 }
 
 int r2l_gemm_nt(r2l_dtype act, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,

@@ -119,6 +119,11 @@ enum EwOp { kConvert = 0, kSoftplusBias = 1, kDtPre = 2, kAddTo = 3 };
 template <int OP, typename Tin, typename Tout>
 hipError_t elementwise(int rows, int cols, const Tin* in, long ld_in, const float* aux, long ld_aux,
                        const float* vec, Tout* out, long ld_out, hipStream_t st);
+// out[t] = in[s + e - 1 - t] for t in sequence [s, e) (per-sequence row
+// reversal); out == in reverses in place.
+template <typename T>
+hipError_t flip_rows(int T_, int cols, const T* in, long ld_in, T* out, long ld_out, const int32_t* cu, int nseq,
+                     hipStream_t st);
 // One pass of v = op(in, aux) over [rows, cols] (kConvert or kDtPre): the
 // row-major copy out_rm, the transposed copy out_t [cols, rows_pad] (zeros
 // past rows) and column sums of each 64-row band colpart

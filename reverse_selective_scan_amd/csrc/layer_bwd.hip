@@ -501,3 +501,48 @@ template hipError_t concat3<float>(int, int, int, int, const float*, const float
                                    hipStream_t);
 
 }  // namespace r2l
+
+namespace r2l {
+
+// ---------------------------------------------------------------------------
+// Per-sequence row reversal: row t of sequence [s, e) <-> row s + e - 1 - t.
+// The backward of the left-to-right layer is the default layer's backward
+// on every sequence reversed, reversed back (the layer seen in the other
+// direction).  Sequence lookups are clamped (seq_start_of / seq_end_of), so
+// malformed offsets stay in bounds.  in_place: out == in, each pair swapped
+// once by the row of the pair that comes first.
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(256) void flip_rows_kernel(int Tn, int cols, const T* in, long ld_in, T* out,
+                                                        long ld_out, const int32_t* __restrict__ cu, int nseq,
+                                                        int in_place) {
+  for (int t = blockIdx.x; t < Tn; t += gridDim.x) {
+    const int s = seq_start_of(cu, nseq, t), e = seq_end_of(cu, nseq, t, Tn);
+    const int m = s + e - 1 - t;
+    if (m < 0 || m >= Tn) continue;
+    if (in_place) {
+      if (t >= m) continue;
+      for (int c = threadIdx.x; c < cols; c += 256) {
+        const T a = out[(long)t * ld_out + c], b = out[(long)m * ld_out + c];
+        out[(long)t * ld_out + c] = b;
+        out[(long)m * ld_out + c] = a;
+      }
+    } else {
+      for (int c = threadIdx.x; c < cols; c += 256) out[(long)t * ld_out + c] = in[(long)m * ld_in + c];
+    }
+  }
+}
+
+template <typename T>
+hipError_t flip_rows(int Tn, int cols, const T* in, long ld_in, T* out, long ld_out, const int32_t* cu, int nseq,
+                     hipStream_t st) {
+  if (Tn <= 0 || cols <= 0) return hipSuccess;
+  const int blocks = Tn < 16384 ? Tn : 16384;
+  hipLaunchKernelGGL((flip_rows_kernel<T>), dim3(blocks), dim3(256), 0, st, Tn, cols, in, ld_in, out, ld_out, cu,
+                     nseq, in == out ? 1 : 0);
+  return hipGetLastError();
+}
+template hipError_t flip_rows<float>(int, int, const float*, long, float*, long, const int32_t*, int, hipStream_t);
+template hipError_t flip_rows<bf16>(int, int, const bf16*, long, bf16*, long, const int32_t*, int, hipStream_t);
+
+}  // namespace r2l

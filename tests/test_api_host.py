@@ -144,7 +144,9 @@ def _layer_bwd(flags=0, saved=None, T=100, wsb=None, ws=FAKE * 256):
 
 
 def test_layer_bwd_rejects_bad_arguments():
-    assert _layer_bwd(flags=B.R2L_FLAG_L2R) == B.R2L_ERR_UNSUPPORTED
+    # the left-to-right direction is supported when the forward is recomputed, not with saved activations
+    assert _layer_bwd(flags=B.R2L_FLAG_L2R, saved=FAKE * 256) == B.R2L_ERR_UNSUPPORTED
+    assert _layer_bwd(flags=0x8) == B.R2L_ERR_INVALID_ARG
     assert _layer_bwd(flags=B.R2L_FLAG_TRAIN) == B.R2L_ERR_INVALID_ARG    # a forward-only flag
     assert _layer_bwd(wsb=1024) == B.R2L_ERR_WORKSPACE
     assert _layer_bwd(saved=FAKE * 256 + 16) == B.R2L_ERR_INVALID_ARG     # saved must be 256-byte aligned

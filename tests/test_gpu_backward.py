@@ -246,3 +246,49 @@ def test_long_sequence_bf16_layer_bwd_matches_oracle():
     e = ds_err(got["s"].reshape(()), ref["s"], g, r, float(W["s"]))
     assert report("long bf16 ds (against |g| |r|)", e, TOL_GRAD_BF16) <= TOL_GRAD_BF16
     assert worst <= TOL_GRAD_BF16
+
+
+# ---------------------------------------------------------------------------
+# the left-to-right direction (the ablation control)
+# ---------------------------------------------------------------------------
+def _flip_seqs(a, cu):
+    out = np.array(a, copy=True)
+    for q in range(len(cu) - 1):
+        t0, t1 = int(cu[q]), int(cu[q + 1])
+        out[t0:t1] = a[t0:t1][::-1]
+    return out
+
+
+@pytest.mark.parametrize("use_ln", [True, False])
+def test_tiny_f32_l2r_layer_bwd_matches_oracle(use_ln):
+    wl = synth.workloads()["tiny_f32"]
+    _case(f"tiny_f32 l2r layer bwd ln={use_ln}")
+    W, h, cu = synth.make_weights(wl), synth.make_hidden(wl), wl.cu_seqlens()
+    g = synth.make_hidden(wl, hook=9)
+    ref = G.layer_grads(h, cu, W, float(W["s"]), g, use_ln=use_ln, direction="l2r")
+    flags = B.R2L_FLAG_L2R | (0 if use_ln else B.R2L_FLAG_NO_LN)
+    dh, got = _layer_bwd_case(wl, W, h, cu, g, torch.float32, flags)
+    names = [n for n in GRAD_NAMES if use_ln or n not in ("ln_w", "ln_b")]
+    got["h"], got["s"] = dh, got["s"].reshape(())
+    ref["s"] = np.array(ref["s"])
+    assert _layer_err(_err, got, ref, names + ["h", "s"], TOL_GRAD, "tiny l2r") <= TOL_GRAD
+
+
+def test_small_bf16_l2r_layer_bwd_matches_oracle_and_mirror():
+    """Against the oracle's l2r gradients, and bit for bit against the
+    default direction's gradients of the reversed sequences (dh reversed)."""
+    lens = [5, 0, 130, 1, 300]
+    _case(f"small bf16 l2r layer bwd lens={lens}")
+    wl = synth.custom(lens, seed=29, h_kind="rms", d_model=256, d_inner=512, dt_rank=16)
+    W = synth.make_weights(wl, affine_ln=True)
+    h, cu = synth.make_hidden(wl), wl.cu_seqlens()
+    g = synth.make_hidden(wl, hook=9)
+    ref = G.layer_grads(h, cu, W, float(W["s"]), g, direction="l2r")
+    dh, got = _layer_bwd_case(wl, W, h, cu, g, torch.bfloat16, B.R2L_FLAG_L2R)
+    got["h"] = dh
+    worst = _layer_err(rel_fro, got, ref, list(GRAD_NAMES) + ["h"], TOL_GRAD_BF16, "small bf16 l2r (Frobenius)")
+    assert worst <= TOL_GRAD_BF16
+    dh_m, got_m = _layer_bwd_case(wl, W, _flip_seqs(h, cu), cu, _flip_seqs(g, cu), torch.bfloat16, 0)
+    assert np.array_equal(dh, _flip_seqs(dh_m, cu))
+    for k in list(GRAD_NAMES) + ["s"]:
+        assert np.array_equal(got[k], got_m[k]), k
