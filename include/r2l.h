@@ -250,8 +250,10 @@ int r2l_scan_fwd(const r2l_dims* dims, r2l_dtype act, uint32_t flags, const void
  * Method: a first sweep recomputes the states right to left and keeps the
  * state entering every 16-token sub-block; a second sweep runs the adjoint
  * recurrence left to right, recomputing each sub-block's states; sums over
- * channels and sequences are taken in a fixed order (deterministic).  Each
- * sequence is walked by one block per 64 channels (no time chunks).
+ * channels, chunks and sequences are taken in a fixed order
+ * (deterministic).  When the sequences give fewer than 512 blocks of 64
+ * channels, both sweeps also cut the sequences into time chunks, carried
+ * across through chunk summaries.
  * workspace: r2l_scan_bwd_workspace_bytes(...) bytes, 256-byte aligned.
  * ---------------------------------------------------------------------- */
 size_t r2l_scan_bwd_workspace_bytes(const r2l_dims* dims, int64_t n_tokens, int32_t nseq);

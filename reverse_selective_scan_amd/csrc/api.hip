@@ -175,23 +175,46 @@ ScanPlan plan_scan(int E, int64_t T, int32_t nseq, int32_t max_seqlen, size_t ba
 // Workspace of the scan backward: one chunk per sequence (no carries), the
 // state entering every 16-token sub-block, the per-channel-block dB | dC
 // partials and the per-sequence dA_log / dDskip partials.
+// Time chunks as the forward scan cuts them when the sequences alone would
+// leave the GPU idle (fewer than 512 blocks of 64 channels): chunks of Lc
+// tokens (a multiple of 32) cut from each sequence's end.  Both sweeps then
+// carry across chunks through chunk summaries: the state sweep the forward's
+// (S, P), the adjoint its own (M, Q).
 struct ScanBwdPlan {
-  int max_chunks;
-  size_t off_cu, off_chunks, off_n, off_hc, off_dbc, off_dA, off_dD, total;
+  int max_chunks, Lc;
+  bool chunked;
+  size_t off_cu, off_chunks, off_n, off_hc, off_dbc, off_dA, off_dD, off_sumS, off_sumP, off_adjM, off_adjQ, total;
 };
 
 ScanBwdPlan plan_scan_bwd(int E, int64_t T, int32_t nseq) {
   ScanBwdPlan p{};
-  p.max_chunks = nseq;
-  const size_t slots = (size_t)(T / 16) + (size_t)nseq + 1;   // sum over sequences of ceil(L / 16)
+  const int64_t NB = E / 64, target = 512;
+  int64_t Lc = T > 0 ? T : 1;
+  if ((int64_t)nseq * NB < target && T > 0) {
+    int64_t want = (T * NB + target - 1) / target;
+    want = ((want + kTB - 1) / kTB) * kTB;
+    if (want < 4 * kTB) want = 4 * kTB;
+    if (want < Lc) Lc = want;
+  }
+  p.chunked = Lc < T;
+  p.Lc = (int)Lc;
+  p.max_chunks = (int)(nseq + (p.chunked ? (T + Lc - 1) / Lc : 0));
+  if (p.max_chunks < 1) p.max_chunks = 1;
+  // 16-token state slots: every chunk but a sequence's leftmost is a multiple of 32 long
+  const size_t slots = (size_t)(T / 16) + (size_t)p.max_chunks + 1;
+  const size_t sumsz = p.chunked ? sizeof(float) * 16 * (size_t)E * (size_t)p.max_chunks : 0;
   size_t off = 0;
   p.off_cu = off;     off = align_up(off + sizeof(int32_t) * ((size_t)nseq + 1));
-  p.off_chunks = off; off = align_up(off + sizeof(ChunkDesc) * (size_t)nseq);
+  p.off_chunks = off; off = align_up(off + sizeof(ChunkDesc) * (size_t)p.max_chunks);
   p.off_n = off;      off = align_up(off + sizeof(int32_t));
   p.off_hc = off;     off = align_up(off + sizeof(float) * 16 * (size_t)E * slots);
   p.off_dbc = off;    off = align_up(off + sizeof(float) * 32 * (size_t)(E / 64) * (size_t)T);
-  p.off_dA = off;     off = align_up(off + sizeof(float) * 16 * (size_t)E * (size_t)nseq);
-  p.off_dD = off;     off = align_up(off + sizeof(float) * (size_t)E * (size_t)nseq);
+  p.off_dA = off;     off = align_up(off + sizeof(float) * 16 * (size_t)E * (size_t)p.max_chunks);
+  p.off_dD = off;     off = align_up(off + sizeof(float) * (size_t)E * (size_t)p.max_chunks);
+  p.off_sumS = off;   off = align_up(off + sumsz);
+  p.off_sumP = off;   off = align_up(off + sumsz);
+  p.off_adjM = off;   off = align_up(off + sumsz);
+  p.off_adjQ = off;   off = align_up(off + sumsz);
   p.total = off;
   return p;
 }
@@ -259,8 +282,8 @@ int run_scan_bwd(r2l_dtype act, int E, int R, int T, int nseq, const void* u, in
   ChunkDesc* chunks = at<ChunkDesc>(workspace, bp.off_chunks);
   int32_t* nch = at<int32_t>(workspace, bp.off_n);
   float* hc = at<float>(workspace, bp.off_hc);
-  // one chunk per sequence: the adjoint sweep carries lambda along a whole sequence
-  R2L_RUN("plan_chunks", st, plan_chunks(cu_seqlens, nseq, T, T, bp.max_chunks, false, cu_clean, chunks, nch, st));
+  // time chunks when the sequences alone would leave the GPU idle
+  R2L_RUN("plan_chunks", st, plan_chunks(cu_seqlens, nseq, T, bp.Lc, bp.max_chunks, false, cu_clean, chunks, nch, st));
   // sweep 1: states every 16 tokens, and dz
   ScanArgs a{};
   a.T = T; a.E = E; a.R = R; a.ldp = 0;
@@ -271,6 +294,10 @@ int run_scan_bwd(r2l_dtype act, int E, int R, int T, int nseq, const void* u, in
   a.chunks = chunks; a.n_chunks = nch; a.max_chunks = bp.max_chunks;
   a.l2r = false;
   a.dy = dy; a.ld_dy = ld_dy; a.dz = dz; a.hc = hc;
+  if (bp.chunked) {
+    a.sumS = at<float>(workspace, bp.off_sumS);
+    a.sumP = at<float>(workspace, bp.off_sumP);
+  }
   // sweep 2: the adjoint, then the sums over channel blocks and sequences
   ScanBwdArgs b{};
   b.T = T; b.E = E;
@@ -283,10 +310,16 @@ int run_scan_bwd(r2l_dtype act, int E, int R, int T, int nseq, const void* u, in
   b.dbc = at<float>(workspace, bp.off_dbc);
   b.dA = at<float>(workspace, bp.off_dA);
   b.dD = at<float>(workspace, bp.off_dD);
+  if (bp.chunked) {
+    b.adjM = at<float>(workspace, bp.off_adjM);
+    b.adjQ = at<float>(workspace, bp.off_adjQ);
+  }
   if (act == R2L_BF16) {
+    if (bp.chunked) R2L_RUN("scan_bwd_summary", st, scan_summary<bf16>(a, false, st));
     R2L_RUN("scan_bwd_states", st, scan_bwd_states<bf16>(a, st));
     R2L_RUN("scan_bwd_adjoint", st, scan_bwd_adjoint<bf16>(b, bp.max_chunks, dA_log, dB, dC, dDskip, st));
   } else {
+    if (bp.chunked) R2L_RUN("scan_bwd_summary", st, scan_summary<float>(a, false, st));
     R2L_RUN("scan_bwd_states", st, scan_bwd_states<float>(a, st));
     R2L_RUN("scan_bwd_adjoint", st, scan_bwd_adjoint<float>(b, bp.max_chunks, dA_log, dB, dC, dDskip, st));
   }

@@ -104,9 +104,12 @@ struct ScanBwdArgs {
   float* dbc;               // [E/64][T][32]: dB | dC partial sums of each channel block
   float* dA;                // [max_chunks][E][16] (d/dA_log)
   float* dD;                // [max_chunks][E]
+  // time chunks: the adjoint's zero-carry chunk summaries [max_chunks][16][E]
+  // (carry out M, decay Q), or null when every sequence is one chunk
+  float* adjM; float* adjQ;
 };
 // The adjoint sweep and the reductions into dA_log [E,16], dB, dC [T,16]
-// and dDskip [E] (may be null).
+// and dDskip [E] (may be null); with a.adjM set, the chunk summaries first.
 template <typename T>
 hipError_t scan_bwd_adjoint(const ScanBwdArgs& a, int max_chunks, float* dA_log, float* dB, float* dC,
                             float* dDskip, hipStream_t st);

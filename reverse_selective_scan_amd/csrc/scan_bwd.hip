@@ -18,7 +18,10 @@
 // recomputes the sub-block's 16 states right to left into registers (rows
 // past a sequence read as zeros, so they are identity steps: dt = 0 gives
 // a = 1 and no input), then runs the adjoint over them left to right.  A
-// block owns 64 channels of one sequence; its 4 waves split the 16 states as
+// block owns 64 channels of one time chunk (a whole sequence, or a piece of
+// one when the sequences alone would leave the GPU idle: the adjoint then
+// enters a chunk with the carry of the chunks to its left, from the chunk
+// summaries below); its 4 waves split the 16 states as
 // in the forward (lane = channel, 4 states per lane, the input term on a
 // 4x4x1 fp32 MFMA).  The sums over channels (dB, dC) are reduced across the
 // 64 lanes with lane swaps and row rotations, then across channel blocks by
@@ -150,6 +153,18 @@ __global__ __launch_bounds__(256, 2) void scan_bwd_adj_kernel(ScanBwdArgs a) {
   };
 
   f32x4 mu = {0.0f, 0.0f, 0.0f, 0.0f};     // a_{t-1} lambda_{t-1}, carried left to right
+  if (a.adjM != nullptr) {
+    // carry into this chunk from the chunks to its left (scan order: j grows
+    // leftward), folded from the leftmost: m = M_j + Q_j m
+    for (int jj = d.n_in_seq - 1; jj > d.j; --jj) {
+      const long base = (long)(d.first + jj) * NS * E;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const long off = base + (long)(4 * w + i) * E + e;
+        mu[i] = fmaf(a.adjQ[off], mu[i], a.adjM[off]);
+      }
+    }
+  }
   float dAacc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
   float dDacc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
   const int nq = (d.hi - d.lo + SB - 1) / SB;   // sub-blocks, q = 0 at the chunk's right end
@@ -277,6 +292,84 @@ __global__ __launch_bounds__(256, 2) void scan_bwd_adj_kernel(ScanBwdArgs a) {
   }
 }
 
+// Adjoint chunk summaries.  For a chunk [lo, hi) with nothing coming in from
+// its left, walk it left to right: lambda_t = g_t C_t + m, m <- a_t lambda_t,
+// Q <- Q a_t; then M = m (the carry leaving the chunk) and Q = the product of
+// its a_t, so that a carry m_in entering the chunk leaves as M + Q m_in.
+// Layout as the main sweep: a block owns 64 channels of one chunk, the four
+// waves split the 16 states; 16-token sub-blocks go through LDS, the next
+// one's loads in flight.
+template <typename T>
+__global__ __launch_bounds__(256) void scan_bwd_adj_summary_kernel(ScanBwdArgs a) {
+  constexpr unsigned SZ = sizeof(T);
+  __shared__ __attribute__((aligned(16))) float dt_s[SB][64];
+  __shared__ __attribute__((aligned(16))) float g_s[SB][64];
+  __shared__ __attribute__((aligned(16))) f32x4 c_s[SB][4];     // C[0..16)
+  const int E = a.E;
+  const int NB = E / 64;
+  const int ci = blockIdx.x / NB, cblk = blockIdx.x % NB;
+  if (ci >= *a.n_chunks) return;
+  const ChunkDesc d = a.chunks[ci];
+  if (d.j == 0) return;   // the rightmost chunk of a sequence: no chunk to its right reads it
+  const int tid = threadIdx.x, lane = lane_id(), w = wave_id();
+  const int e0 = cblk * 64, e = e0 + lane;
+  const int r16 = tid >> 4, c16 = tid & 15;
+  const int ea = e0 + 4 * c16;
+  float A2[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) A2[i] = -expf(a.A_log[(long)e * NS + 4 * w + i]) * kLog2e;
+  const bool has_z = a.z != nullptr;
+  const long lddt_b = a.ld_dt * 4, ldbc_b = a.ld_bc * 4;
+  const long ldz_b = a.ld_z * (long)SZ, lddy_b = a.ld_dy * (long)SZ;
+  const unsigned offDT = (unsigned)(r16 * lddt_b) + (unsigned)ea * 4;
+  const unsigned offZ = (unsigned)(r16 * ldz_b) + (unsigned)ea * SZ;
+  const unsigned offDY = (unsigned)(r16 * lddy_b) + (unsigned)ea * SZ;
+  const unsigned offC = c16 < 4 ? (unsigned)(r16 * ldbc_b) + 16u * c16 : kPast;
+  float pdt[4], pz[4], pdy[4], pc[4];
+  auto issue = [&](int blo, int bhi) __attribute__((always_inline)) {
+    const int rows = bhi - blo;
+    load4(pdt, rows_of(a.dt, blo, lddt_b, rows), offDT, (float*)nullptr);
+    load4(pdy, rows_of(a.dy, blo, lddy_b, rows), offDY, (T*)nullptr);
+    if (has_z) load4(pz, rows_of(a.z, blo, ldz_b, rows), offZ, (T*)nullptr);
+    const Rsrc rC = rows_of(a.Cm, blo, ldbc_b, rows);
+#pragma unroll
+    for (int p = 0; p < 4; ++p) pc[p] = ld1(rC, offC + 4u * p);
+  };
+  float m[4] = {0.0f, 0.0f, 0.0f, 0.0f}, q[4] = {1.0f, 1.0f, 1.0f, 1.0f};
+  const int nsb = (d.hi - d.lo + SB - 1) / SB;   // sub-blocks, left to right
+  if (nsb > 0) issue(d.lo, min(d.hi, d.lo + SB));
+  for (int k = 0; k < nsb; ++k) {
+    const int blo = d.lo + SB * k, bhi = min(d.hi, blo + SB), nt = bhi - blo;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      dt_s[r16][4 * c16 + j] = pdt[j];      // rows past the sub-block: dt = 0, so a = 1 (identity)
+      g_s[r16][4 * c16 + j] = has_z ? pdy[j] * silu_fast(pz[j]) : pdy[j];
+    }
+    if (c16 < 4) c_s[r16][c16] = f32x4{pc[0], pc[1], pc[2], pc[3]};
+    if (k + 1 < nsb) issue(blo + SB, min(d.hi, blo + 2 * SB));
+    __syncthreads();
+    for (int r = 0; r < nt; ++r) {
+      const float dtv = dt_s[r][lane], g = g_s[r][lane];
+      const f32x4 Cv = c_s[r][w];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float at = exp2_fast(dtv * A2[i]);
+        const float lam = fmaf(g, Cv[i], m[i]);
+        m[i] = at * lam;
+        q[i] *= at;
+      }
+    }
+    __syncthreads();
+  }
+  const long base = (long)ci * NS * E;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const long off = base + (long)(4 * w + i) * E + e;
+    a.adjM[off] = m[i];
+    a.adjQ[off] = q[i];
+  }
+}
+
 // dB, dC [T, 16] = sums over channel blocks of the partials, in order.
 __global__ __launch_bounds__(256) void scan_bwd_bc_kernel(int T, int NB, const float* __restrict__ part,
                                                           float* __restrict__ dB, float* __restrict__ dC) {
@@ -314,6 +407,8 @@ template <typename T>
 hipError_t scan_bwd_adjoint(const ScanBwdArgs& a, int max_chunks, float* dA_log, float* dB, float* dC,
                             float* dDskip, hipStream_t st) {
   const int NB = a.E / 64;
+  if (max_chunks * NB > 0 && a.adjM != nullptr)
+    hipLaunchKernelGGL((scan_bwd_adj_summary_kernel<T>), dim3(max_chunks * NB), dim3(256), 0, st, a);
   if (max_chunks * NB > 0)
     hipLaunchKernelGGL((scan_bwd_adj_kernel<T>), dim3(max_chunks * NB), dim3(256), 0, st, a);
   const long n = (long)a.T * 32;
