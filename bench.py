@@ -165,6 +165,39 @@ def main():
     tok_s = T * wl.n_hooks / (ms_step * 1e-3)
     print(f"[bench] timed {args.steps} steps: {ms_step:.3f} ms/step (wall {t_wall:.2f}s)", flush=True)
 
+    # the layer time as a median of single calls with the caches flushed in
+    # between (a 512 MiB write, past the 256 MB last-level cache), one event
+    # pair per call; reported beside the back-to-back throughput
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    per_call = []
+    for _ in range(args.steps):
+        flush.fill_(1)
+        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        c0.record(stream)
+        step()
+        c1.record(stream)
+        torch.cuda.synchronize()
+        per_call.append(c0.elapsed_time(c1))
+    del flush
+    flushed_ms = float(np.median(per_call))
+    l4096 = None
+    if wl.name == "serve_b8":
+        # the same batch at L = 4096 (the prompt alone: B = 8 x 4096 tokens)
+        cu4 = np.arange(0, 8 * 4096 + 1, 4096)
+        h4 = h[:8 * 4096].clone()
+        o4 = torch.empty_like(h4)
+        cu4_d, n4, m4 = B.cu_seqlens_device(cu4, 8 * 4096, dev)
+        for _ in range(args.warmup):
+            B.r2l_layer_fwd(h4, wd[0], cu4_d, out=o4, workspace=ws, nseq=n4, max_seqlen=m4)
+        torch.cuda.synchronize()
+        q0, q1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        q0.record(stream)
+        for _ in range(args.steps):
+            B.r2l_layer_fwd(h4, wd[0], cu4_d, out=o4, workspace=ws, nseq=n4, max_seqlen=m4)
+        q1.record(stream)
+        torch.cuda.synchronize()
+        l4096 = 8 * 4096 / (q0.elapsed_time(q1) / args.steps * 1e-3)
+
     # per-kernel durations (second timed region, events inside the library)
     B.timing_reset()
     B.timing_enable(True)
@@ -235,6 +268,8 @@ def main():
                    "d_inner": E, "d_state": N, "dt_rank": R, "d_conv": wl.d_conv, "hooks": wl.n_hooks,
                    "graph": use_graph, "state_dtype": "f32", "note": wl.note},
         "us_per_step": round(ms_step * 1e3, 2),
+        "flushed_median_ms": round(flushed_ms, 4),
+        "tokens_per_s_L4096": None if l4096 is None else round(l4096, 1),
         "scan_hbm_gbs": scan.get("achieved_gbs"),
         "scan_hbm_frac": scan.get("frac"),
         "roofline": roofline,
