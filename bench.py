@@ -403,7 +403,7 @@ KERNEL_SOURCES = {  # the source file that defines each timed kernel
 # substrings of the demangled names in rocprofv3 output; each launches once
 # per step, so a label's time and traffic per step are sums over its parts.
 ROCPROF_NAMES = {
-    "in_proj_gemm": ["gemm_bf16_big_kernel<false, 4, false>", "gemm_bf16_nt_kernel<128, 128, true>",
+    "in_proj_gemm": ["gemm_bf16_pers_kernel<4>", "gemm_bf16_nt_kernel<128, 128, true>",
                      "gemm_small_reduce_kernel<128, 128, false>"],
     "out_proj_gemm": ["gemm_bf16_big_kernel<true, 8, false>", "gemm_bf16_nt_kernel<128, 128, true>",
                       "gemm_small_reduce_kernel<128, 128, true>"],
@@ -491,9 +491,10 @@ def summarize_profiles(argv, size_kib=0.0, bench_args=""):
         fetch, write = per_kernel(argv[2], "FETCH_SIZE"), per_kernel(argv[3], "WRITE_SIZE")
         copy_k = [k for k in fetch if "copy" in k.lower() or "elementwise" in k.lower()]
         calib = {}
-        for k in copy_k:   # the largest copy dispatch is the calibration copy
+        for k in copy_k:   # the copy dispatch that reads the most is the calibration copy
             f, wr = max(fetch[k]), max(write.get(k, [0]))
-            calib = {"kernel": k, "fetch_kib": f, "write_kib": wr}
+            if not calib or f > calib["fetch_kib"]:
+                calib = {"kernel": k, "fetch_kib": f, "write_kib": wr}
         rec = {"copy": calib, "kernels": {}}
         lines += ["## HBM traffic (rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE, KiB per dispatch)", ""]
         if calib and size_kib:

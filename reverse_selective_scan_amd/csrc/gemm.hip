@@ -1,7 +1,7 @@
 // Dense projections C = A . B^T (in_proj and out_proj of the Mamba-1 block,
 // "Bifocal Diffusion Language Models", §3.4 step 2).
 //
-// Two bf16 kernels on the MFMA matrix cores (v_mfma_f32_32x32x16_bf16):
+// bf16 kernels on the MFMA matrix cores (v_mfma_f32_32x32x16_bf16):
 //
 //  * gemm_bf16_big_kernel -- the large-problem kernel.  One block of 256
 //    threads (one wave per SIMD) owns a 256 x 256 tile; each wave owns a
@@ -16,6 +16,10 @@
 //    so that fragment reads are bank-conflict free.  The MFMA operands are
 //    swapped (B-tile rows as the "A" operand) so that each lane ends up with
 //    4 consecutive output columns of one row: 8- or 16-byte stores.
+//  * gemm_bf16_pers_kernel -- the big kernel made persistent for bf16
+//    outputs (in_proj): one block per CU walks its tiles with the K-step
+//    pipeline running on across tile boundaries, and writes each finished
+//    tile from registers while it computes the next one.
 //  * gemm_bf16_nt_kernel -- the general kernel (any shape with K a multiple
 //    of 8): 128 x 128 tiles, 2 x 2 waves of 64 x 64, register-staged
 //    double-buffered LDS tiles.
@@ -175,6 +179,8 @@ constexpr int kBigSROW = kBigBK * 2;           // stage row bytes
 constexpr int kBigSBYTES = (kBigBM + kBigBN) * kBigSROW;
 constexpr int kBigSH = 2;                      // swizzle: chunk ^= (row >> 2) & 3
 
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+
 // s_waitcnt immediate that waits for vmcnt <= n and leaves the other counters alone
 constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 
@@ -198,6 +204,60 @@ R2L_DEV void big_tile(int lid, int nTm, int nTn, int& tm, int& tn) {
 }
 
 }  // namespace
+
+// Direct epilogue of a 256 x 256 tile through LDS: the four stages (free
+// now) hold the tile in row-major order, each 16-byte chunk of a row at
+// chunk ^ (row & 31) against bank conflicts; then every store instruction
+// writes whole rows (64 lanes x 16 bytes).  bf16: 64 rows of 512 bytes per
+// stage, one pass; f32: 32 rows of 1 KB per stage, two passes.  (Scattered
+// 8-byte stores straight from the MFMA layout took several times longer
+// when every CU stores its tile at once.)  acc[i][j] register 4q+e holds
+// C[m][n] with m = m0+wm+32i+(lane&31), n = n0+wn+32j+8q+4*(lane>>5)+e.
+template <bool OUT_F32>
+R2L_DEV void big_epilogue(const f32x16 (&acc)[4][4], char* s0, char* s1, char* s2, char* s3, int m0,
+                          int n0, int M, int N, void* __restrict__ Cv, long ldc) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
+  const int wm = (wave >> 1) * 128, wn = (wave & 1) * 128, fr = lane & 31, fh = lane >> 5;
+  auto stage = [&](int s) -> char* { return s == 0 ? s0 : s == 1 ? s1 : s == 2 ? s2 : s3; };
+  constexpr int ES = OUT_F32 ? 4 : 2;
+  constexpr int RB = kBigBN * ES;              // row bytes
+  constexpr int RPS = kBigSBYTES / RB;         // rows per stage
+  constexpr int RPP = 4 * RPS;                 // rows per pass
+  constexpr int LPR = RB / 16;                 // lanes per row in the store phase
+  asm volatile("s_barrier" ::: "memory");      // every wave is done reading the stages
+#pragma unroll
+  for (int pass = 0; pass < kBigBM / RPP; ++pass) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = wm + 32 * i + fr;
+      if (r / RPP != pass) continue;           // uniform per (wave, i)
+      const int rl = r - pass * RPP, rr = rl % RPS;
+      char* sb = stage(rl / RPS) + rr * RB;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int cb = (wn + 32 * j + 8 * q + 4 * fh) * ES;
+          char* dst = sb + (((cb >> 4) ^ (rr & 31)) << 4) + (cb & 15);
+          const f32x4 v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+          if (OUT_F32) *(f32x4*)dst = v;
+          else *(bf16x4*)dst = bf16x4{(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]};
+        }
+    }
+    __syncthreads();
+    for (int rl = wave * (64 / LPR) + lane / LPR; rl < RPP; rl += 4 * (64 / LPR)) {
+      const int rr = rl % RPS, ch = lane % LPR;
+      const int m = m0 + pass * RPP + rl, n = n0 + ch * (16 / ES);
+      const i32x4 v = *(const i32x4*)(stage(rl / RPS) + rr * RB + ((ch ^ (rr & 31)) << 4));
+      if (m < M) {
+        char* g = (char*)Cv + ((long)m * ldc + n) * ES;
+        if (n + 16 / ES <= N) *(i32x4*)g = v;
+        else if (!OUT_F32 && n + 4 <= N) *(int2*)g = int2{v[0], v[1]};   // N % 4 == 0 (bf16: 8-column chunks)
+      }
+    }
+    if (pass + 1 < kBigBM / RPP) __syncthreads();
+  }
+}
 
 // n_dp = number of whole tiles of the main launch.  !TAIL: block b
 // computes tile xcd_remap(b) of those, over all of K, into C.  TAIL (the
@@ -360,50 +420,246 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(int M, int N, int
         }
     return;
   }
-  // Direct epilogue through LDS: the four stages (free now) hold the tile in
-  // row-major order, each 16-byte chunk of a row at chunk ^ (row & 31)
-  // against bank conflicts; then every store instruction writes whole rows
-  // (64 lanes x 16 bytes).  bf16: 64 rows of 512 bytes per stage, one pass;
-  // f32: 32 rows of 1 KB per stage, two passes.  (Scattered 8-byte stores
-  // straight from the MFMA layout took several times longer.)
-  constexpr int ES = OUT_F32 ? 4 : 2;
-  constexpr int RB = BN * ES;                  // row bytes
-  constexpr int RPS = kBigSBYTES / RB;         // rows per stage
-  constexpr int RPP = 4 * RPS;                 // rows per pass
-  constexpr int LPR = RB / 16;                 // lanes per row in the store phase
-  asm volatile("s_barrier" ::: "memory");      // every wave is done reading the stages
+  big_epilogue<OUT_F32>(acc, s0, s1, s2, s3, m0, n0, M, N, Cv, ldc);
+}
+
+// Persistent form of the big kernel for bf16 outputs whose width is a
+// multiple of 256 (in_proj).  The grid is a multiple of 8 blocks, at most one
+// per CU; block b computes tiles xcd_remap(b + w * grid, n_dp), w = 0, 1, ...,
+// which is the order in which a one-tile-per-block launch would hand tiles
+// to that CU's XCD.  Two things differ from one launch per tile:
+//  * the K-step pipeline runs on across tile boundaries: the next tile's
+//    first three steps are loaded while this one finishes, so no tile but
+//    the first waits for a prologue;
+//  * a finished tile is rounded to bf16 in registers (128 VGPRs) and written
+//    by four 8-byte stores per lane and step during the next tile's first 16
+//    steps.  With one launch per tile every CU writes its 128 KB tile at the
+//    same moment at the end of each round and waits for the whole chip's
+//    writes to drain; spread over the next tile, the writes overlap the MFMAs.
+// Only the last tile of each block goes out through the LDS epilogue.
+template <int G>
+__global__ __launch_bounds__(256, 1) void gemm_bf16_pers_kernel(int M, int N, int K,
+                                                                const bf16* __restrict__ A, long lda,
+                                                                const bf16* __restrict__ B, long ldb,
+                                                                bf16* __restrict__ C, long ldc, int n_dp) {
+  constexpr int BM = kBigBM, BN = kBigBN, BK = kBigBK, ST = kBigST, LPT = kBigLPT, SROW = kBigSROW;
+  __shared__ __attribute__((aligned(1024))) char s0[kBigSBYTES];
+  __shared__ __attribute__((aligned(1024))) char s1[kBigSBYTES];
+  __shared__ __attribute__((aligned(1024))) char s2[kBigSBYTES];
+  __shared__ __attribute__((aligned(1024))) char s3[kBigSBYTES];
+  auto stage = [&](int s) -> char* { return s == 0 ? s0 : s == 1 ? s1 : s == 2 ? s2 : s3; };
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
+  const int wm = (wave >> 1) * 128, wn = (wave & 1) * 128;
+  const int nTm = (M + BM - 1) / BM, nTn = (N + BN - 1) / BN;
+  const int grid = gridDim.x, b = blockIdx.x;
+  const int ntile = (n_dp - b + grid - 1) / grid;  // >= 1: the grid is at most n_dp
+  auto tile_of = [&](int w, int& m0, int& n0) {
+    int tm, tn;
+    big_tile<G>(xcd_remap(b + w * grid, n_dp), nTm, nTn, tm, tn);
+    m0 = tm * BM;
+    n0 = tn * BN;
+  };
+  // buffer descriptors over a tile's operand rows (reads past row M or N return 0)
+  auto rsrc_a = [&](int m0) {
+    return __builtin_amdgcn_make_buffer_rsrc((void*)(A + (long)m0 * lda), 0, (int)((long)min(BM, M - m0) * lda * 2), 0x00020000);
+  };
+  auto rsrc_b = [&](int n0) {
+    return __builtin_amdgcn_make_buffer_rsrc((void*)(B + (long)n0 * ldb), 0, (int)((long)min(BN, N - n0) * ldb * 2), 0x00020000);
+  };
+  int m0, n0, m1, n1;
+  tile_of(0, m0, n0);
+  m1 = m0;
+  n1 = n0;
+  if (ntile > 1) tile_of(1, m1, n1);
+  __amdgpu_buffer_rsrc_t rA = rsrc_a(m0), rB = rsrc_b(n0), rAn = rsrc_a(m1), rBn = rsrc_b(n1);
+
+  unsigned voff[LPT];
 #pragma unroll
-  for (int pass = 0; pass < BM / RPP; ++pass) {
+  for (int i = 0; i < LPT; ++i) {
+    const int p = i * 256 + tid, row = p / kBigCPR;
+    const int kc = big_swz(row, p % kBigCPR);
+    voff[i] = i < LPT / 2 ? (unsigned)(((long)row * lda + kc * 8) * 2)
+                          : (unsigned)(((long)(row - BM) * ldb + kc * 8) * 2);
+  }
+  const int nk = K / BK;
+  // k-step kt of the current tile (nx: of the next tile; past the block's
+  // last tile that is the current tile again, loaded but never read) -> stage s
+  auto issue = [&](int s, int kt, bool nx) {
+    char* base = stage(s);
+    const __amdgpu_buffer_rsrc_t ra = nx ? rAn : rA, rb = nx ? rBn : rB;
+    const unsigned kb = (unsigned)(kt * BK * 2);
+#pragma unroll
+    for (int i = 0; i < LPT; ++i)
+      lds_dma16(i < LPT / 2 ? ra : rb, base + (i * 256 + wave * 64) * 16, voff[i], kb);
+  };
+
+  const int fr = lane & 31, fh = lane >> 5;
+  // fragment rows wm + 32 i + fr (A) and BM + wn + 32 i + fr (B): the
+  // swizzle depends on them only through (fr >> 2) & 3, so fragment i sits
+  // 32 rows (2 KB) after fragment 0
+  const int offA0 = (wm + fr) * SROW + big_swz(fr, fh) * 16, offA1 = (wm + fr) * SROW + big_swz(fr, 2 + fh) * 16;
+  const int offB0 = (BM + wn + fr) * SROW + big_swz(fr, fh) * 16, offB1 = (BM + wn + fr) * SROW + big_swz(fr, 2 + fh) * 16;
+  bf16x8 fa0[4], fb0[4], fa1[4], fb1[4];
+  auto rd0 = [&](const char* base) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int r = wm + 32 * i + fr;
-      if (r / RPP != pass) continue;           // uniform per (wave, i)
-      const int rl = r - pass * RPP, rr = rl % RPS;
-      char* sb = stage(rl / RPS) + rr * RB;
+      fa0[i] = *(const bf16x8*)(base + offA0 + 32 * SROW * i);
+      fb0[i] = *(const bf16x8*)(base + offB0 + 32 * SROW * i);
+    }
+  };
+  auto rd1 = [&](const char* base) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      fa1[i] = *(const bf16x8*)(base + offA1 + 32 * SROW * i);
+      fb1[i] = *(const bf16x8*)(base + offB1 + 32 * SROW * i);
+    }
+  };
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+  auto mm0 = [&]() {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb0[j], fa0[i], acc[i][j], 0, 0, 0);
+  };
+  auto mm0_first = [&]() {  // a tile's first MFMAs start from zero
+    const f32x16 z = {};
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb0[j], fa0[i], z, 0, 0, 0);
+  };
+  auto mm1 = [&]() {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb1[j], fa1[i], acc[i][j], 0, 0, 0);
+  };
+  auto sched_main = [&]() {
+#pragma unroll
+    for (int q = 0; q < LPT; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // one global->LDS load
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+    }
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    }
+  };
+  auto sched_tail = [&]() {
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    }
+  };
+
+  // At a tile boundary, accumulator row blocks i < 4 - PI are rounded to bf16
+  // and stored at once; row blocks i >= 4 - PI wait in pend (bf16, MFMA
+  // layout: pend[16 (i - 4 + PI) + 4 j + q] holds columns
+  // n0+wn+32j+8q+4*(lane>>5) .. +3 of row m0+wm+32i+(lane&31)) and are
+  // written by PI stores per step during the next tile's first 16 steps.
+  constexpr int PI = 3, NP = 16 * PI;
+  bf16x4 pend[NP];
+#pragma unroll
+  for (int p = 0; p < NP; ++p) pend[p] = bf16x4{};  // (written out, into an empty range, by the first tile)
+  __amdgpu_buffer_rsrc_t rC = __builtin_amdgcn_make_buffer_rsrc((void*)C, 0, 0, 0x00020000);
+  const unsigned voffC = (unsigned)((((long)(wm + fr) * ldc) + wn + 4 * fh) * 2);
+  auto store_acc = [&](int i, int j, int q, bf16x4 v) {
+    // an opaque copy of the lane offset: the constant column offset then
+    // stays in the instruction's offset field instead of being hoisted out
+    // of the tile loop as one more VGPR per store
+    unsigned vo = voffC;
+    asm volatile("" : "+v"(vo));
+    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v), rC, vo + (unsigned)((32 * j + 8 * q) * 2),
+                                          (int)(32 * i * ldc * 2), 0);
+  };
+  auto store_batch = [&](int t) {  // pend entries PI t .. PI t + PI - 1
+#pragma unroll
+    for (int u = 0; u < PI; ++u) {
+      const int p = PI * t + u;
+      store_acc(4 - PI + p / 16, (p / 4) % 4, p % 4, pend[p]);
+    }
+  };
+
+  // one K step: barrier, refill the stage of step kt-1 with step kt+3 (of the
+  // next tile when nx), the second half of step kt and the first half of
+  // step kt+1 from LDS; batch >= 0: also write pend batch `batch`
+  auto step = [&](int s, int kt, bool nx, bool first, int batch) {
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(LPT));
+    asm volatile("s_barrier" ::: "memory");
+    issue((s + ST - 1) % ST, nx ? kt + ST - 1 - nk : kt + ST - 1, nx);
+    rd1(stage(s));
+    if (first) mm0_first();
+    else mm0();
+    sched_main();
+    rd0(stage((s + 1) % ST));
+    if (batch >= 0) store_batch(batch);
+    mm1();
+    sched_tail();
+    if (batch >= 0) {
+#pragma unroll
+      for (int u = 0; u < PI; ++u) {
+        __builtin_amdgcn_sched_group_barrier(0x040, 1, 0);  // one global store
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      }
+    }
+  };
+
+  issue(0, 0, false);
+  issue(1, 1, false);
+  issue(2, 2, false);
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * LPT));
+  asm volatile("s_barrier" ::: "memory");
+  rd0(s0);
+  for (int w = 0; w < ntile; ++w) {
+    // the first 16 steps also write out the rest of the previous tile (for
+    // the first tile rC has an empty range and the stores are dropped)
+#pragma unroll
+    for (int t = 0; t < 16; ++t) step(t % ST, t, false, t == 0, t);
+    for (int kt0 = 16; kt0 < nk - ST; kt0 += ST) {
+#pragma unroll
+      for (int s = 0; s < ST; ++s) step(s, kt0 + s, false, false, -1);
+    }
+    // last group: steps 1..3 load the next tile's first steps
+#pragma unroll
+    for (int s = 0; s < ST; ++s) step(s, nk - ST + s, s > 0, false, -1);
+    __builtin_amdgcn_sched_barrier(0);  // keep the rounding out of the last step's MFMA schedule
+    // rows past M are dropped by the descriptor's range; N % 256 == 0
+    rC = __builtin_amdgcn_make_buffer_rsrc((void*)(C + (long)m0 * ldc + n0), 0,
+                                           (int)((long)min(BM, M - m0) * ldc * 2), 0x00020000);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const int cb = (wn + 32 * j + 8 * q + 4 * fh) * ES;
-          char* dst = sb + (((cb >> 4) ^ (rr & 31)) << 4) + (cb & 15);
-          const f32x4 v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
-          if (OUT_F32) *(f32x4*)dst = v;
-          else *(bf16x4*)dst = bf16x4{(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]};
+          const bf16x4 v = {(bf16)acc[i][j][4 * q], (bf16)acc[i][j][4 * q + 1], (bf16)acc[i][j][4 * q + 2],
+                            (bf16)acc[i][j][4 * q + 3]};
+          if (i < 4 - PI) store_acc(i, j, q, v);
+          else pend[16 * (i - 4 + PI) + 4 * j + q] = v;
         }
+    __builtin_amdgcn_sched_barrier(0);
+    m0 = m1;
+    n0 = n1;
+    rA = rAn;
+    rB = rBn;
+    if (w + 2 < ntile) {
+      tile_of(w + 2, m1, n1);
+      rAn = rsrc_a(m1);
+      rBn = rsrc_b(n1);
     }
-    __syncthreads();
-    for (int rl = wave * (64 / LPR) + lane / LPR; rl < RPP; rl += 4 * (64 / LPR)) {
-      const int rr = rl % RPS, ch = lane % LPR;
-      const int m = m0 + pass * RPP + rl, n = n0 + ch * (16 / ES);
-      const i32x4 v = *(const i32x4*)(stage(rl / RPS) + rr * RB + ((ch ^ (rr & 31)) << 4));
-      if (m < M) {
-        char* g = (char*)Cv + ((long)m * ldc + n) * ES;
-        if (n + 16 / ES <= N) *(i32x4*)g = v;
-        else if (!OUT_F32 && n + 4 <= N) *(int2*)g = int2{v[0], v[1]};   // N % 4 == 0 (bf16: 8-column chunks)
-      }
-    }
-    if (pass + 1 < BM / RPP) __syncthreads();
   }
+  // the last tile's pending rows
+#pragma unroll
+  for (int t = 0; t < 16; ++t) store_batch(t);
 }
 
 // C tile n_dp + t = sum over s of part[t * splits + s], in order of s.
@@ -479,8 +735,17 @@ static void launch_gemm(int M, int N, int K, const bf16* A, long lda, const bf16
 template <int G>
 static void launch_big(int M, int N, int K, const bf16* A, long lda, const bf16* B, long ldb, void* C,
                        long ldc, bool out_f32, int n_dp, int rem, int splits, int nk, float* ws,
-                       hipStream_t st) {
-  if (n_dp > 0 && out_f32)
+                       hipStream_t st, int ncu) {
+  // the persistent form: bf16 output a whole number of tiles wide, at least
+  // 20 K steps per tile (16 write out the previous tile, the last 3 load the
+  // next one), and at least two tiles per CU
+  const int pgrid = ncu & ~7;
+  const bool pers = !out_f32 && N % kBigBN == 0 && nk >= 20 && pgrid > 0 && n_dp >= 2 * pgrid &&
+                    (long)kBigBM * ldc * 2 < (1L << 31);
+  if (pers)
+    hipLaunchKernelGGL((gemm_bf16_pers_kernel<G>), dim3(pgrid), dim3(256), 0, st, M, N, K, A, lda, B, ldb,
+                       (bf16*)C, ldc, n_dp);
+  else if (n_dp > 0 && out_f32)
     hipLaunchKernelGGL((gemm_bf16_big_kernel<true, G, false>), dim3(n_dp), dim3(256), 0, st, M, N, K, A, lda,
                        B, ldb, C, ldc, n_dp, 0, 0, (float*)nullptr);
   else if (n_dp > 0)
@@ -544,16 +809,16 @@ hipError_t gemm_bf16_nt(int M, int N, int K, const bf16* A, long lda, const bf16
     // tail for both projections of the serving shape).
     if (ws != nullptr && big_tiles > ncu && rem == nTn && nTm % G == 1) {
       const int m_tail = (nTm - 1) * kBigBM;
-      if (G == 8) launch_big<8>(m_tail, N, K, A, lda, B, ldb, C, ldc, out_f32, (int)big_tiles - rem, 0, 0, nk, ws, st);
-      else launch_big<4>(m_tail, N, K, A, lda, B, ldb, C, ldc, out_f32, (int)big_tiles - rem, 0, 0, nk, ws, st);
+      if (G == 8) launch_big<8>(m_tail, N, K, A, lda, B, ldb, C, ldc, out_f32, (int)big_tiles - rem, 0, 0, nk, ws, st, ncu);
+      else launch_big<4>(m_tail, N, K, A, lda, B, ldb, C, ldc, out_f32, (int)big_tiles - rem, 0, 0, nk, ws, st, ncu);
       const long ce = out_f32 ? 4 : 2;
       launch_gemm<128, 128>(M - m_tail, N, K, A + (long)m_tail * lda, lda, B, ldb,
                             (char*)C + (long)m_tail * ldc * ce, ldc, out_f32, st, ws, ws_bytes, ncu);
       return hipGetLastError();
     }
     const int n_dp = (int)big_tiles - (splits ? rem : 0);
-    if (G == 8) launch_big<8>(M, N, K, A, lda, B, ldb, C, ldc, out_f32, n_dp, rem, splits, nk, ws, st);
-    else launch_big<4>(M, N, K, A, lda, B, ldb, C, ldc, out_f32, n_dp, rem, splits, nk, ws, st);
+    if (G == 8) launch_big<8>(M, N, K, A, lda, B, ldb, C, ldc, out_f32, n_dp, rem, splits, nk, ws, st, ncu);
+    else launch_big<4>(M, N, K, A, lda, B, ldb, C, ldc, out_f32, n_dp, rem, splits, nk, ws, st, ncu);
     return hipGetLastError();
   }
   // 128 x 128 tiles (4 waves of 64 x 64, two blocks per CU).

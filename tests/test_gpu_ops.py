@@ -42,7 +42,11 @@ def _case(name):
                                    (256, 8192, 2048), (256, 2048, 4096), (100, 1024, 512), (1024, 2048, 4096),
                                    # 9 x 32 tiles of 256 x 256: a whole round, then the last (ragged) tile row
                                    # on the 128 x 128 kernel
-                                   (2200, 8192, 512)])
+                                   (2200, 8192, 512),
+                                   # persistent bf16-output kernel: 576 tiles (2 or 3 per block, ragged last
+                                   # tile row); 544 tiles (2 or 3 per block; with a workspace 512 tiles plus
+                                   # the last tile row on the 128 x 128 kernel)
+                                   (9000, 4096, 768), (4352, 8192, 2048)])
 def test_gemm_bf16_matches_fp64_product(M, N, K):
     _case(f"gemm bf16 {M}x{N}x{K}")
     A = synth.make_aux(M * 7 + 1, (M, K))
