@@ -447,6 +447,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_pers_kernel(int M, int N, in
   __shared__ __attribute__((aligned(1024))) char s1[kBigSBYTES];
   __shared__ __attribute__((aligned(1024))) char s2[kBigSBYTES];
   __shared__ __attribute__((aligned(1024))) char s3[kBigSBYTES];
+  __shared__ __attribute__((aligned(1024))) char sE[64 * 512];   // a quarter of a finished tile
   auto stage = [&](int s) -> char* { return s == 0 ? s0 : s == 1 ? s1 : s == 2 ? s2 : s3; };
 
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
@@ -561,38 +562,61 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_pers_kernel(int M, int N, in
     }
   };
 
-  // At a tile boundary, accumulator row blocks i < 4 - PI are rounded to bf16
-  // and stored at once; row blocks i >= 4 - PI wait in pend (bf16, MFMA
-  // layout: pend[16 (i - 4 + PI) + 4 j + q] holds columns
-  // n0+wn+32j+8q+4*(lane>>5) .. +3 of row m0+wm+32i+(lane&31)) and are
-  // written by PI stores per step during the next tile's first 16 steps.
-  constexpr int PI = 3, NP = 16 * PI;
-  bf16x4 pend[NP];
+  // Write-out of a finished tile, a quarter at a time: quarter k is row
+  // block i = k of every wave (tile rows 32k + [0, 32) and 128 + 32k +
+  // [0, 32), all 256 columns, 32 KB in bf16).  At the tile boundary quarter
+  // 0 goes to sE and quarters 1..3 wait in pend (bf16, MFMA layout:
+  // pend[16 (k - 1) + 4 j + q] holds columns n0+wn+32j+8q+4*(lane>>5) .. +3
+  // of row m0+wm+32k+(lane&31)).  During the next tile's first 16 steps,
+  // quarter k is read back from sE a row per instruction at steps
+  // 4k+1..4k+3 and written with whole-row stores (64 lanes x 8 bytes);
+  // quarter k+1 is copied from pend to sE at step 4k+4.  sE holds 64 rows of
+  // 512 bytes; 8-byte slot c of local row r sits at slot c ^ (r & 31), so
+  // that neither the column writes (32 rows, one slot) nor the row reads
+  // meet a bank twice.
+  bf16x4 pend[48];
 #pragma unroll
-  for (int p = 0; p < NP; ++p) pend[p] = bf16x4{};  // (written out, into an empty range, by the first tile)
+  for (int p = 0; p < 48; ++p) pend[p] = bf16x4{};  // (written out, into an empty range, by the first tile)
   __amdgpu_buffer_rsrc_t rC = __builtin_amdgcn_make_buffer_rsrc((void*)C, 0, 0, 0x00020000);
-  const unsigned voffC = (unsigned)((((long)(wm + fr) * ldc) + wn + 4 * fh) * 2);
-  auto store_acc = [&](int i, int j, int q, bf16x4 v) {
-    // an opaque copy of the lane offset: the constant column offset then
-    // stays in the instruction's offset field instead of being hoisted out
-    // of the tile loop as one more VGPR per store
-    unsigned vo = voffC;
-    asm volatile("" : "+v"(vo));
-    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v), rC, vo + (unsigned)((32 * j + 8 * q) * 2),
-                                          (int)(32 * i * ldc * 2), 0);
-  };
-  auto store_batch = [&](int t) {  // pend entries PI t .. PI t + PI - 1
+  // quarter -> sE: this lane's local row is (wm ? 32 : 0) + (lane & 31); its
+  // slot for (j, q) is wn / 4 + 8 j + 2 q + (lane >> 5)
+  const int lrw = (wm ? 32 : 0) + fr;
+  auto quarter_to_lds = [&](const bf16x4* v) {  // v[4 j + q]
+    // opaque copies: the 16 addresses are formed here, not hoisted out of
+    // the tile loop as 16 more VGPRs
+    int row = lrw * 512, sl = fh ^ fr;
+    asm volatile("" : "+v"(row), "+v"(sl));
 #pragma unroll
-    for (int u = 0; u < PI; ++u) {
-      const int p = PI * t + u;
-      store_acc(4 - PI + p / 16, (p / 4) % 4, p % 4, pend[p]);
-    }
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        *(bf16x4*)(sE + row + ((wn / 4 + ((8 * j + 2 * q) ^ sl)) << 3)) = v[4 * j + q];
   };
+  // sE -> C: wave w writes local rows 16 w + rr, rr = 0..15; local rows
+  // 0..31 are tile rows 32k + r, 32..63 are 128 + 32k + r - 32
+  const unsigned voffE = (unsigned)(lane * 8);
+  auto drain_row = [&](int k, int rr) {
+    // opaque copies of the wave's first row and the row stride: the row
+    // addresses are formed here, not hoisted out of the tile loop as 64 more
+    // scalar registers
+    int w16 = 16 * wave, rb = (int)(ldc * 2);
+    asm volatile("" : "+v"(w16), "+v"(rb));
+    const int lr = __builtin_amdgcn_readfirstlane(w16) + rr;
+    const u32x2 v = *(const u32x2*)(sE + lr * 512 + ((lane ^ (lr & 31)) << 3));
+    const int row = (wave < 2 ? 0 : 96) + 32 * k + lr;   // tile row
+    __builtin_amdgcn_raw_buffer_store_b64(v, rC, voffE, row * __builtin_amdgcn_readfirstlane(rb), 0);
+  };
+
 
   // one K step: barrier, refill the stage of step kt-1 with step kt+3 (of the
   // next tile when nx), the second half of step kt and the first half of
-  // step kt+1 from LDS; batch >= 0: also write pend batch `batch`
-  auto step = [&](int s, int kt, bool nx, bool first, int batch) {
+  // step kt+1 from LDS.  t in [0, 16): also this step's part of the
+  // previous tile's write-out.
+  auto step = [&](int s, int kt, bool nx, bool first, int t) {
+    const bool wr = t >= 4 && t % 4 == 0;      // pend quarter t / 4 -> sE
+    const bool rd = t >= 0 && t % 4 != 0;      // sE quarter t / 4 -> C: rows 6 (t % 4 - 1) ..
+    const int k = t / 4, c0 = rd ? 6 * (t % 4 - 1) : 0, c1 = rd ? min(c0 + 6, 16) : 0;
+    if (t >= 0 && t % 4 == 1) __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): this wave's sE writes landed
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(LPT));
     asm volatile("s_barrier" ::: "memory");
     issue((s + ST - 1) % ST, nx ? kt + ST - 1 - nk : kt + ST - 1, nx);
@@ -601,16 +625,11 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_pers_kernel(int M, int N, in
     else mm0();
     sched_main();
     rd0(stage((s + 1) % ST));
-    if (batch >= 0) store_batch(batch);
+    if (wr) quarter_to_lds(pend + 16 * (k - 1));
+#pragma unroll
+    for (int rr = c0; rr < c1; ++rr) drain_row(k, rr);
     mm1();
     sched_tail();
-    if (batch >= 0) {
-#pragma unroll
-      for (int u = 0; u < PI; ++u) {
-        __builtin_amdgcn_sched_group_barrier(0x040, 1, 0);  // one global store
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      }
-    }
   };
 
   issue(0, 0, false);
@@ -620,8 +639,8 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_pers_kernel(int M, int N, in
   asm volatile("s_barrier" ::: "memory");
   rd0(s0);
   for (int w = 0; w < ntile; ++w) {
-    // the first 16 steps also write out the rest of the previous tile (for
-    // the first tile rC has an empty range and the stores are dropped)
+    // the first 16 steps also write out the previous tile (for the first
+    // tile rC has an empty range and the stores are dropped)
 #pragma unroll
     for (int t = 0; t < 16; ++t) step(t % ST, t, false, t == 0, t);
     for (int kt0 = 16; kt0 < nk - ST; kt0 += ST) {
@@ -635,6 +654,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_pers_kernel(int M, int N, in
     // rows past M are dropped by the descriptor's range; N % 256 == 0
     rC = __builtin_amdgcn_make_buffer_rsrc((void*)(C + (long)m0 * ldc + n0), 0,
                                            (int)((long)min(BM, M - m0) * ldc * 2), 0x00020000);
+    bf16x4 q0[16];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -643,9 +663,10 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_pers_kernel(int M, int N, in
         for (int q = 0; q < 4; ++q) {
           const bf16x4 v = {(bf16)acc[i][j][4 * q], (bf16)acc[i][j][4 * q + 1], (bf16)acc[i][j][4 * q + 2],
                             (bf16)acc[i][j][4 * q + 3]};
-          if (i < 4 - PI) store_acc(i, j, q, v);
-          else pend[16 * (i - 4 + PI) + 4 * j + q] = v;
+          if (i == 0) q0[4 * j + q] = v;
+          else pend[16 * (i - 1) + 4 * j + q] = v;
         }
+    quarter_to_lds(q0);
     __builtin_amdgcn_sched_barrier(0);
     m0 = m1;
     n0 = n1;
@@ -657,9 +678,17 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_pers_kernel(int M, int N, in
       rBn = rsrc_b(n1);
     }
   }
-  // the last tile's pending rows
+  // the last tile: quarter 0 is in sE, quarters 1..3 in pend
 #pragma unroll
-  for (int t = 0; t < 16; ++t) store_batch(t);
+  for (int k = 0; k < 4; ++k) {
+    if (k > 0) {
+      __syncthreads();  // every wave has read quarter k - 1
+      quarter_to_lds(pend + 16 * (k - 1));
+    }
+    __syncthreads();
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr) drain_row(k, rr);
+  }
 }
 
 // C tile n_dp + t = sum over s of part[t * splits + s], in order of s.
