@@ -205,60 +205,6 @@ R2L_DEV void big_tile(int lid, int nTm, int nTn, int& tm, int& tn) {
 
 }  // namespace
 
-// Direct epilogue of a 256 x 256 tile through LDS: the four stages (free
-// now) hold the tile in row-major order, each 16-byte chunk of a row at
-// chunk ^ (row & 31) against bank conflicts; then every store instruction
-// writes whole rows (64 lanes x 16 bytes).  bf16: 64 rows of 512 bytes per
-// stage, one pass; f32: 32 rows of 1 KB per stage, two passes.  (Scattered
-// 8-byte stores straight from the MFMA layout took several times longer
-// when every CU stores its tile at once.)  acc[i][j] register 4q+e holds
-// C[m][n] with m = m0+wm+32i+(lane&31), n = n0+wn+32j+8q+4*(lane>>5)+e.
-template <bool OUT_F32>
-R2L_DEV void big_epilogue(const f32x16 (&acc)[4][4], char* s0, char* s1, char* s2, char* s3, int m0,
-                          int n0, int M, int N, void* __restrict__ Cv, long ldc) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
-  const int wm = (wave >> 1) * 128, wn = (wave & 1) * 128, fr = lane & 31, fh = lane >> 5;
-  auto stage = [&](int s) -> char* { return s == 0 ? s0 : s == 1 ? s1 : s == 2 ? s2 : s3; };
-  constexpr int ES = OUT_F32 ? 4 : 2;
-  constexpr int RB = kBigBN * ES;              // row bytes
-  constexpr int RPS = kBigSBYTES / RB;         // rows per stage
-  constexpr int RPP = 4 * RPS;                 // rows per pass
-  constexpr int LPR = RB / 16;                 // lanes per row in the store phase
-  asm volatile("s_barrier" ::: "memory");      // every wave is done reading the stages
-#pragma unroll
-  for (int pass = 0; pass < kBigBM / RPP; ++pass) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = wm + 32 * i + fr;
-      if (r / RPP != pass) continue;           // uniform per (wave, i)
-      const int rl = r - pass * RPP, rr = rl % RPS;
-      char* sb = stage(rl / RPS) + rr * RB;
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int cb = (wn + 32 * j + 8 * q + 4 * fh) * ES;
-          char* dst = sb + (((cb >> 4) ^ (rr & 31)) << 4) + (cb & 15);
-          const f32x4 v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
-          if (OUT_F32) *(f32x4*)dst = v;
-          else *(bf16x4*)dst = bf16x4{(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]};
-        }
-    }
-    __syncthreads();
-    for (int rl = wave * (64 / LPR) + lane / LPR; rl < RPP; rl += 4 * (64 / LPR)) {
-      const int rr = rl % RPS, ch = lane % LPR;
-      const int m = m0 + pass * RPP + rl, n = n0 + ch * (16 / ES);
-      const i32x4 v = *(const i32x4*)(stage(rl / RPS) + rr * RB + ((ch ^ (rr & 31)) << 4));
-      if (m < M) {
-        char* g = (char*)Cv + ((long)m * ldc + n) * ES;
-        if (n + 16 / ES <= N) *(i32x4*)g = v;
-        else if (!OUT_F32 && n + 4 <= N) *(int2*)g = int2{v[0], v[1]};   // N % 4 == 0 (bf16: 8-column chunks)
-      }
-    }
-    if (pass + 1 < kBigBM / RPP) __syncthreads();
-  }
-}
-
 // n_dp = number of whole tiles of the main launch.  !TAIL: block b
 // computes tile xcd_remap(b) of those, over all of K, into C.  TAIL (the
 // tail launch, splits > 0): block u computes K-steps [s ksteps, (s+1) ksteps) with
@@ -420,7 +366,50 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(int M, int N, int
         }
     return;
   }
-  big_epilogue<OUT_F32>(acc, s0, s1, s2, s3, m0, n0, M, N, Cv, ldc);
+  // Direct epilogue through LDS: the four stages (free now) hold the tile in
+  // row-major order, each 16-byte chunk of a row at chunk ^ (row & 31)
+  // against bank conflicts; then every store instruction writes whole rows
+  // (64 lanes x 16 bytes).  bf16: 64 rows of 512 bytes per stage, one pass;
+  // f32: 32 rows of 1 KB per stage, two passes.  (Scattered 8-byte stores
+  // straight from the MFMA layout took several times longer.)
+  constexpr int ES = OUT_F32 ? 4 : 2;
+  constexpr int RB = BN * ES;                  // row bytes
+  constexpr int RPS = kBigSBYTES / RB;         // rows per stage
+  constexpr int RPP = 4 * RPS;                 // rows per pass
+  constexpr int LPR = RB / 16;                 // lanes per row in the store phase
+  asm volatile("s_barrier" ::: "memory");      // every wave is done reading the stages
+#pragma unroll
+  for (int pass = 0; pass < BM / RPP; ++pass) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = wm + 32 * i + fr;
+      if (r / RPP != pass) continue;           // uniform per (wave, i)
+      const int rl = r - pass * RPP, rr = rl % RPS;
+      char* sb = stage(rl / RPS) + rr * RB;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int cb = (wn + 32 * j + 8 * q + 4 * fh) * ES;
+          char* dst = sb + (((cb >> 4) ^ (rr & 31)) << 4) + (cb & 15);
+          const f32x4 v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+          if (OUT_F32) *(f32x4*)dst = v;
+          else *(bf16x4*)dst = bf16x4{(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]};
+        }
+    }
+    __syncthreads();
+    for (int rl = wave * (64 / LPR) + lane / LPR; rl < RPP; rl += 4 * (64 / LPR)) {
+      const int rr = rl % RPS, ch = lane % LPR;
+      const int m = m0 + pass * RPP + rl, n = n0 + ch * (16 / ES);
+      const i32x4 v = *(const i32x4*)(stage(rl / RPS) + rr * RB + ((ch ^ (rr & 31)) << 4));
+      if (m < M) {
+        char* g = (char*)Cv + ((long)m * ldc + n) * ES;
+        if (n + 16 / ES <= N) *(i32x4*)g = v;
+        else if (!OUT_F32 && n + 4 <= N) *(int2*)g = int2{v[0], v[1]};   // N % 4 == 0 (bf16: 8-column chunks)
+      }
+    }
+    if (pass + 1 < BM / RPP) __syncthreads();
+  }
 }
 
 // Persistent form of the big kernel for bf16 outputs whose width is a
@@ -595,17 +584,22 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_pers_kernel(int M, int N, in
   // sE -> C: wave w writes local rows 16 w + rr, rr = 0..15; local rows
   // 0..31 are tile rows 32k + r, 32..63 are 128 + 32k + r - 32
   const unsigned voffE = (unsigned)(lane * 8);
-  auto drain_row = [&](int k, int rr) {
+  auto drain_rows = [&](int k, int r0, int r1) {
     // opaque copies of the wave's first row and the row stride: the row
-    // addresses are formed here, not hoisted out of the tile loop as 64 more
-    // scalar registers
+    // addresses are formed here, not hoisted out of the tile loop as more
+    // registers
     int w16 = 16 * wave, rb = (int)(ldc * 2);
     asm volatile("" : "+v"(w16), "+v"(rb));
-    const int lr = __builtin_amdgcn_readfirstlane(w16) + rr;
-    const u32x2 v = *(const u32x2*)(sE + lr * 512 + ((lane ^ (lr & 31)) << 3));
-    const int row = (wave < 2 ? 0 : 96) + 32 * k + lr;   // tile row
-    __builtin_amdgcn_raw_buffer_store_b64(v, rC, voffE, row * __builtin_amdgcn_readfirstlane(rb), 0);
+    const int lr0 = __builtin_amdgcn_readfirstlane(w16), rbs = __builtin_amdgcn_readfirstlane(rb);
+    const int x8 = (lane ^ (lr0 & 31)) << 3;   // (lr0 & 31) is 0 or 16, rr < 16: the XOR of rr goes in separately
+    const int row0 = (wave < 2 ? 0 : 96) + 32 * k + lr0;   // tile row of rr = 0
+#pragma unroll
+    for (int rr = r0; rr < r1; ++rr) {
+      const u32x2 v = *(const u32x2*)(sE + (lr0 + rr) * 512 + (x8 ^ (rr << 3)));
+      __builtin_amdgcn_raw_buffer_store_b64(v, rC, voffE, (row0 + rr) * rbs, 0);
+    }
   };
+
 
 
   // one K step: barrier, refill the stage of step kt-1 with step kt+3 (of the
@@ -626,8 +620,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_pers_kernel(int M, int N, in
     sched_main();
     rd0(stage((s + 1) % ST));
     if (wr) quarter_to_lds(pend + 16 * (k - 1));
-#pragma unroll
-    for (int rr = c0; rr < c1; ++rr) drain_row(k, rr);
+    if (rd) drain_rows(k, c0, c1);
     mm1();
     sched_tail();
   };
@@ -686,8 +679,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_pers_kernel(int M, int N, in
       quarter_to_lds(pend + 16 * (k - 1));
     }
     __syncthreads();
-#pragma unroll
-    for (int rr = 0; rr < 16; ++rr) drain_row(k, rr);
+    drain_rows(k, 0, 16);
   }
 }
 
