@@ -67,6 +67,33 @@ def test_gemm_bf16_matches_fp64_product(M, N, K):
     assert report("gemm bf16-out (ws)", err_f32(w16, ref), 5e-3) <= 5e-3
 
 
+@pytest.mark.parametrize("M,N,K,pad", [(9000, 4096, 768, 64), (4352, 8192, 2048, 256)])
+def test_gemm_bf16_strided_operands_and_output(M, N, K, pad):
+    """Row strides past the logical widths (lda = K + pad, ldb = K + pad,
+    ldc = N + pad) through the C ABI: the product matches the fp64 one and the
+    padding columns of C are left untouched (persistent kernel's row range
+    and whole-row stores; one-tile-per-block kernel for the fp32 output)."""
+    _case(f"gemm bf16 strided {M}x{N}x{K} pad {pad}")
+    A = synth.bf16_round(synth.make_aux(M * 5 + 3, (M, K)))
+    Bm = synth.bf16_round(synth.make_aux(N * 5 + 4, (N, K)))
+    ref = A.astype(np.float64) @ Bm.astype(np.float64).T
+    Ap = torch.zeros(M, K + pad, dtype=torch.bfloat16, device=DEV)
+    Bp = torch.zeros(N, K + pad, dtype=torch.bfloat16, device=DEV)
+    Ap[:, :K] = _dev(A, "bf16")
+    Bp[:, :K] = _dev(Bm, "bf16")
+    ws = torch.empty(256 * 256 * 1024, dtype=torch.uint8, device=DEV)
+    for out_f32, tol in ((False, 5e-3), (True, 1e-4)):
+        C = torch.full((M, N + pad), 7.0, dtype=torch.float32 if out_f32 else torch.bfloat16, device=DEV)
+        rc = B.lib().r2l_gemm_nt(B.R2L_BF16, M, N, K, Ap.data_ptr(), K + pad, Bp.data_ptr(), K + pad,
+                                 C.data_ptr(), N + pad, 1 if out_f32 else 0, ws.data_ptr(), ws.numel(),
+                                 torch.cuda.current_stream().cuda_stream)
+        assert rc == 0, B.lib().r2l_status_string(rc)
+        torch.cuda.synchronize()
+        got = to_np(C)
+        assert report(f"gemm strided out_f32={out_f32}", err_f32(got[:, :N], ref), tol) <= tol
+        assert np.all(got[:, N:] == 7.0), "padding columns of C were written"
+
+
 @pytest.mark.parametrize("M,N,K", [(1, 1, 1), (65, 130, 33), (256, 96, 128)])
 def test_gemm_f32_matches_fp64_product(M, N, K):
     _case(f"gemm f32 {M}x{N}x{K}")
