@@ -416,9 +416,17 @@ PROFILE_JSON = os.path.join(ROOT, "profiles", "traffic_serve_b8.json")
 
 
 def _source_hash(kernel):
+    """Hash of the code of the file that defines `kernel`, comments and
+    whitespace removed: an edited comment keeps the stored counters valid,
+    any change to the code makes them stale."""
     import hashlib
+    import re
     f = os.path.join(ROOT, "reverse_selective_scan_amd", "csrc", KERNEL_SOURCES[kernel])
-    return hashlib.sha256(open(f, "rb").read()).hexdigest()[:16]
+    code = open(f, encoding="utf-8").read()
+    code = re.sub(r"/\*.*?\*/", " ", code, flags=re.S)
+    code = re.sub(r"//[^\n]*", " ", code)
+    code = " ".join(code.split())
+    return hashlib.sha256(code.encode()).hexdigest()[:16]
 
 
 def measured_traffic(kernel):

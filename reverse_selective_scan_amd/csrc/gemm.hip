@@ -19,7 +19,7 @@
 //  * gemm_bf16_pers_kernel -- the big kernel made persistent for bf16
 //    outputs (in_proj): one block per CU walks its tiles with the K-step
 //    pipeline running on across tile boundaries, and writes each finished
-//    tile from registers while it computes the next one.
+//    tile (through LDS, a quarter at a time) while it computes the next one.
 //  * gemm_bf16_nt_kernel -- the general kernel (any shape with K a multiple
 //    of 8): 128 x 128 tiles, 2 x 2 waves of 64 x 64, register-staged
 //    double-buffered LDS tiles.
@@ -420,12 +420,13 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(int M, int N, int
 //  * the K-step pipeline runs on across tile boundaries: the next tile's
 //    first three steps are loaded while this one finishes, so no tile but
 //    the first waits for a prologue;
-//  * a finished tile is rounded to bf16 in registers (128 VGPRs) and written
-//    by four 8-byte stores per lane and step during the next tile's first 16
-//    steps.  With one launch per tile every CU writes its 128 KB tile at the
-//    same moment at the end of each round and waits for the whole chip's
-//    writes to drain; spread over the next tile, the writes overlap the MFMAs.
-// Only the last tile of each block goes out through the LDS epilogue.
+//  * a finished tile is written during the next tile's first 16 steps, a
+//    quarter at a time through a fifth LDS buffer, with whole-row stores
+//    (details at the write-out below).  With one launch per tile every CU
+//    writes its 128 KB tile at the same moment at the end of each round and
+//    its next loads wait behind those writes (one in-order vmcnt counter
+//    covers both); spread over the next tile, the writes overlap the MFMAs.
+// The last tile of each block is written out after the loop.
 template <int G>
 __global__ __launch_bounds__(256, 1) void gemm_bf16_pers_kernel(int M, int N, int K,
                                                                 const bf16* __restrict__ A, long lda,
