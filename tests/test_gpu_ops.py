@@ -46,7 +46,10 @@ def _case(name):
                                    # persistent bf16-output kernel: 576 tiles (2 or 3 per block, ragged last
                                    # tile row); 544 tiles (2 or 3 per block; with a workspace 512 tiles plus
                                    # the last tile row on the 128 x 128 kernel)
-                                   (9000, 4096, 768), (4352, 8192, 2048)])
+                                   (9000, 4096, 768), (4352, 8192, 2048),
+                                   # few rows (the 128 x 128 kernel split along K): 7 rows; 256 rows with
+                                   # K = 768
+                                   (7, 2048, 2048), (256, 4096, 768)])
 def test_gemm_bf16_matches_fp64_product(M, N, K):
     _case(f"gemm bf16 {M}x{N}x{K}")
     A = synth.make_aux(M * 7 + 1, (M, K))
