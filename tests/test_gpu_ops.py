@@ -97,6 +97,25 @@ def test_gemm_bf16_strided_operands_and_output(M, N, K, pad):
         assert np.all(got[:, N:] == 7.0), "padding columns of C were written"
 
 
+def test_gemm_bf16_repeats_bit_for_bit():
+    """Twenty launches of the persistent kernel (its write-out staged through
+    LDS while the next tile's loads and MFMAs run) and of the
+    one-tile-per-block kernel give bit-identical outputs: no launch-to-launch
+    race in either pipeline."""
+    _case("gemm bf16 repeat 4352x8192x2048")
+    M, N, K = 4352, 8192, 2048
+    A = _dev(synth.bf16_round(synth.make_aux(11, (M, K))), "bf16")
+    Bm = _dev(synth.bf16_round(synth.make_aux(12, (N, K))), "bf16")
+    ws = torch.empty(256 * 256 * 1024, dtype=torch.uint8, device=DEV)
+    for out_f32 in (False, True):
+        first = B.r2l_gemm_nt(A, Bm, out_f32=out_f32, workspace=ws)
+        for _ in range(20):
+            again = B.r2l_gemm_nt(A, Bm, out_f32=out_f32, workspace=ws)
+            assert torch.equal(again.view(torch.int16 if not out_f32 else torch.int32),
+                               first.view(torch.int16 if not out_f32 else torch.int32))
+    torch.cuda.synchronize()
+
+
 @pytest.mark.parametrize("M,N,K", [(1, 1, 1), (65, 130, 33), (256, 96, 128)])
 def test_gemm_f32_matches_fp64_product(M, N, K):
     _case(f"gemm f32 {M}x{N}x{K}")
