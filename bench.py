@@ -180,6 +180,20 @@ def main():
         per_call.append(c0.elapsed_time(c1))
     del flush
     flushed_ms = float(np.median(per_call))
+    # a measured copy peak (device-to-device copy of 1 GiB, read + write
+    # bytes over the best of five), beside the published 8 TB/s
+    src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    copy_ms = []
+    for _ in range(5):
+        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        c0.record(stream)
+        dst.copy_(src)
+        c1.record(stream)
+        torch.cuda.synchronize()
+        copy_ms.append(c0.elapsed_time(c1))
+    del src, dst
+    copy_gbs = 2.0 * (1 << 30) / (min(copy_ms) * 1e-3) / 1e9
     l4096 = None
     if wl.name == "serve_b8":
         # the same batch at L = 4096 (the prompt alone: B = 8 x 4096 tokens)
@@ -272,6 +286,11 @@ def main():
         "tokens_per_s_L4096": None if l4096 is None else round(l4096, 1),
         "scan_hbm_gbs": scan.get("achieved_gbs"),
         "scan_hbm_frac": scan.get("frac"),
+        "copy_peak_gbs": round(copy_gbs, 1),
+        "scan_frac_of_copy": (None if scan.get("achieved_gbs") is None
+                              else round(scan["achieved_gbs"] / copy_gbs, 4)),
+        "ln_frac_of_copy": (None if kernels.get("ln_gate", {}).get("achieved_gbs") is None
+                            else round(kernels["ln_gate"]["achieved_gbs"] / copy_gbs, 4)),
         "roofline": roofline,
         "kernels": kernels,
         "cpu_baseline": cpu,
