@@ -684,6 +684,139 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_pers_kernel(int M, int N, in
   }
 }
 
+// Mid-size kernel (the 128 x 128 tiles of small problems and of the last
+// tile row of large ones): the big kernel's pipeline on 128 x 128 tiles.
+// Four LDS stages of 32-wide K steps (16 KB each, so two blocks fit a CU)
+// filled by buffer_load ... lds three steps ahead, the same swizzle and the
+// same barrier / vmcnt discipline; each wave owns a 64 x 64 quarter (2 x 2
+// MFMA tiles).  splits == 0: block b computes tile b (row-major) into C.
+// splits > 0: block u computes K steps [s ksteps, (s+1) ksteps), s = u %
+// splits, of tile u / splits as an fp32 partial sum into part[u][128][128],
+// added by gemm_small_reduce_kernel.
+constexpr int kMidB = 128, kMidSBYTES = 2 * kMidB * kBigSROW;
+
+template <bool OUT_F32>
+__global__ __launch_bounds__(256, 2) void gemm_bf16_mid_kernel(int M, int N, int K,
+                                                               const bf16* __restrict__ A, long lda,
+                                                               const bf16* __restrict__ B, long ldb,
+                                                               void* __restrict__ Cv, long ldc,
+                                                               int splits, int ksteps,
+                                                               float* __restrict__ part) {
+  constexpr int BK = kBigBK, ST = kBigST, SROW = kBigSROW, LPT = 4;
+  __shared__ __attribute__((aligned(1024))) char s0[kMidSBYTES];
+  __shared__ __attribute__((aligned(1024))) char s1[kMidSBYTES];
+  __shared__ __attribute__((aligned(1024))) char s2[kMidSBYTES];
+  __shared__ __attribute__((aligned(1024))) char s3[kMidSBYTES];
+  auto stage = [&](int s) -> char* { return s == 0 ? s0 : s == 1 ? s1 : s == 2 ? s2 : s3; };
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
+  const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64, fr = lane & 31, fh = lane >> 5;
+  const int nTn = (N + kMidB - 1) / kMidB;
+  const int u = blockIdx.x;
+  const int tile = splits ? u / splits : u;
+  const int kbeg = splits ? (u % splits) * ksteps : 0;
+  const int nk = splits ? ksteps : K / BK;
+  const int m0 = (tile / nTn) * kMidB, n0 = (tile % nTn) * kMidB;
+  // rows past M or N read as 0 through the descriptors' ranges
+  const __amdgpu_buffer_rsrc_t rA = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(A + (long)m0 * lda), 0, (int)((long)min(kMidB, M - m0) * lda * 2), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rB = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(B + (long)n0 * ldb), 0, (int)((long)min(kMidB, N - n0) * ldb * 2), 0x00020000);
+  // load i fills stage slot 256 i + tid: stage row 64 i + tid / 4 (A rows for
+  // i < 2, then B rows), physical chunk tid % 4
+  unsigned voff[LPT];
+#pragma unroll
+  for (int i = 0; i < LPT; ++i) {
+    const int row = 64 * i + tid / 4;
+    const int kc = big_swz(row, tid % 4);
+    voff[i] = i < 2 ? (unsigned)(((long)row * lda + kc * 8) * 2)
+                    : (unsigned)(((long)(row - kMidB) * ldb + kc * 8) * 2);
+  }
+  auto issue = [&](int s, int kt) {  // past the end: reload the last step (never read)
+    char* base = stage(s);
+    const unsigned kb = (unsigned)((kbeg + min(kt, nk - 1)) * BK * 2);
+#pragma unroll
+    for (int i = 0; i < LPT; ++i) lds_dma16(i < 2 ? rA : rB, base + (i * 256 + wave * 64) * 16, voff[i], kb);
+  };
+  int offA0[2], offB0[2], offA1[2], offB1[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int ra = wm + 32 * i + fr, rb = kMidB + wn + 32 * i + fr;
+    offA0[i] = ra * SROW + big_swz(ra, fh) * 16;
+    offB0[i] = rb * SROW + big_swz(rb, fh) * 16;
+    offA1[i] = ra * SROW + big_swz(ra, 2 + fh) * 16;
+    offB1[i] = rb * SROW + big_swz(rb, 2 + fh) * 16;
+  }
+  bf16x8 fa0[2], fb0[2], fa1[2], fb1[2];
+  auto rd0 = [&](const char* base) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      fa0[i] = *(const bf16x8*)(base + offA0[i]);
+      fb0[i] = *(const bf16x8*)(base + offB0[i]);
+    }
+  };
+  auto rd1 = [&](const char* base) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      fa1[i] = *(const bf16x8*)(base + offA1[i]);
+      fb1[i] = *(const bf16x8*)(base + offB1[i]);
+    }
+  };
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  issue(0, 0);
+  issue(1, 1);
+  issue(2, 2);
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * LPT));
+  asm volatile("s_barrier" ::: "memory");
+  rd0(s0);
+  for (int kt0 = 0; kt0 < nk; kt0 += ST) {
+#pragma unroll
+    for (int s = 0; s < ST; ++s) {
+      const int kt = kt0 + s;
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(LPT));
+      asm volatile("s_barrier" ::: "memory");
+      issue((s + ST - 1) % ST, kt + ST - 1);
+      rd1(stage(s));
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb0[j], fa0[i], acc[i][j], 0, 0, 0);
+      rd0(stage((s + 1) % ST));
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb1[j], fa1[i], acc[i][j], 0, 0, 0);
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+
+  // acc[i][j] register 4q+e holds row wm+32i+(lane&31), column
+  // wn+32j+8q+4*(lane>>5)+e of the tile
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int r = wm + 32 * i + fr, c = wn + 32 * j + 8 * q + 4 * fh;
+        const f32x4 v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+        if (splits) {
+          *(f32x4*)(part + (long)u * (kMidB * kMidB) + r * kMidB + c) = v;
+        } else if (m0 + r < M && n0 + c < N) {   // N % 4 == 0: all four columns or none
+          const long off = (long)(m0 + r) * ldc + n0 + c;
+          if (OUT_F32) *(f32x4*)((float*)Cv + off) = v;
+          else *(bf16x4*)((bf16*)Cv + off) = bf16x4{(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]};
+        }
+      }
+}
+
 // C tile n_dp + t = sum over s of part[t * splits + s], in order of s.
 // Block: 4 rows of 256 columns of one tail tile; thread: 4 consecutive columns.
 template <bool OUT_F32, int G>
@@ -725,6 +858,39 @@ static void launch_gemm(int M, int N, int K, const bf16* A, long lda, const bf16
                         void* C, long ldc, bool out_f32, hipStream_t st, float* ws, size_t ws_bytes,
                         int ncu) {
   const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+  // The mid-size kernel (direct-to-LDS, four stages) for whole 128-wide K
+  // chunks, 4-column output groups and 16-byte operand rows; the K split,
+  // when the tiles do not fill the GPU, keeps whole 128-wide chunks per split.
+  static_assert(BM == kMidB && BN == kMidB, "the mid-size kernel has 128 x 128 tiles");
+  if (K % (kBigBK * kBigST) == 0 && N % 4 == 0 && ldc % 4 == 0 && lda % 8 == 0 && ldb % 8 == 0 &&
+      ((uintptr_t)A & 15) == 0 && ((uintptr_t)B & 15) == 0 && ((uintptr_t)C & (out_f32 ? 15 : 7)) == 0 &&
+      (long)kMidB * lda * 2 < (1L << 31) && (long)kMidB * ldb * 2 < (1L << 31)) {
+    const int nk = K / kBigBK;
+    int splits = 1;
+    if (ws != nullptr && ((uintptr_t)ws & 15) == 0 && ncu > 0 && tiles * 2 <= ncu) {
+      while (tiles * splits * 2 <= ncu && nk % (splits * 2 * kBigST) == 0 && nk / (splits * 2) >= 8 &&
+             (size_t)tiles * splits * 2 * BM * BN * sizeof(float) <= ws_bytes)
+        splits *= 2;
+    }
+    if (splits > 1) {
+      hipLaunchKernelGGL((gemm_bf16_mid_kernel<true>), dim3(tiles * splits), dim3(256), 0, st, M, N, K, A, lda,
+                         B, ldb, C, ldc, splits, nk / splits, ws);
+      const long n = (long)M * N;
+      if (out_f32)
+        hipLaunchKernelGGL((gemm_small_reduce_kernel<BM, BN, true>), dim3((n + 255) / 256), dim3(256), 0, st,
+                           M, N, splits, (const float*)ws, C, ldc);
+      else
+        hipLaunchKernelGGL((gemm_small_reduce_kernel<BM, BN, false>), dim3((n + 255) / 256), dim3(256), 0,
+                           st, M, N, splits, (const float*)ws, C, ldc);
+    } else if (out_f32) {
+      hipLaunchKernelGGL((gemm_bf16_mid_kernel<true>), dim3(tiles), dim3(256), 0, st, M, N, K, A, lda, B, ldb,
+                         C, ldc, 0, 0, (float*)nullptr);
+    } else {
+      hipLaunchKernelGGL((gemm_bf16_mid_kernel<false>), dim3(tiles), dim3(256), 0, st, M, N, K, A, lda, B, ldb,
+                         C, ldc, 0, 0, (float*)nullptr);
+    }
+    return;
+  }
   // Few tiles for the GPU: split K over several blocks per tile (each split
   // at least 4 of the kernel's 64-wide K steps), fp32 partials in ws.
   int splits = 1;
