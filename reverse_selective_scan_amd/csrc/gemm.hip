@@ -20,6 +20,8 @@
 //    outputs (in_proj): one block per CU walks its tiles with the K-step
 //    pipeline running on across tile boundaries, and writes each finished
 //    tile (through LDS, a quarter at a time) while it computes the next one.
+//  * gemm_bf16_mid_kernel -- the big kernel's pipeline on 128 x 128 tiles
+//    (16 KB stages, two blocks per CU) for small problems and last tile rows.
 //  * gemm_bf16_nt_kernel -- the general kernel (any shape with K a multiple
 //    of 8): 128 x 128 tiles, 2 x 2 waves of 64 x 64, register-staged
 //    double-buffered LDS tiles.
