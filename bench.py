@@ -423,9 +423,9 @@ KERNEL_SOURCES = {  # the source file that defines each timed kernel
 # per step, so a label's time and traffic per step are sums over its parts.
 ROCPROF_NAMES = {
     "in_proj_gemm": ["gemm_bf16_pers_kernel<4>", "gemm_bf16_mid_kernel<true>",
-                     "gemm_small_reduce_kernel<128, 128, false>"],
+                     "gemm_small_reduce4_kernel<128, 128, false>"],
     "out_proj_gemm": ["gemm_bf16_big_kernel<true, 8, false>", "gemm_bf16_mid_kernel<true>",
-                      "gemm_small_reduce_kernel<128, 128, true>"],
+                      "gemm_small_reduce4_kernel<128, 128, true>"],
     "conv_xproj": ["conv_xproj_sk_kernel<5, false>"], "conv_sum": ["sk_sum_kernel"],
     "scan_main": ["E, false, 4, false, false>(r2l::ScanArgs)"],
     "scan_summary": ["E, true, 4, false, false>(r2l::ScanArgs)"],
