@@ -34,22 +34,26 @@ constexpr int NS = 16;    // d_state (§4.1)
 // made non-decreasing) and the chunk table, each sequence's chunks in scan
 // order (the chunk the scan starts in first).
 // ---------------------------------------------------------------------------
-// Exclusive block-wide scan of one value per thread (256 threads), max or sum,
-// Hillis-Steele in LDS: 8 steps.
+// Exclusive block-wide scan of one value per thread (256 threads), max or
+// sum: a shuffle scan inside each wave, then the earlier waves' totals from
+// LDS (two barriers instead of a barrier per step).
 template <bool MAX>
 R2L_DEV int block_exclusive_scan(int v, int* buf) {
-  const int tid = threadIdx.x;
-  buf[tid] = v;
-  __syncthreads();
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  auto op = [](int a, int b) { return MAX ? max(a, b) : a + b; };   // values are >= 0: 0 is neutral for both
+  int x = v;   // inclusive scan within the wave
 #pragma unroll
-  for (int off = 1; off < 256; off <<= 1) {
-    const int o = tid >= off ? buf[tid - off] : 0;   // values are >= 0: 0 is neutral for both
-    __syncthreads();
-    if (tid >= off) buf[tid] = MAX ? max(buf[tid], o) : buf[tid] + o;
-    __syncthreads();
+  for (int off = 1; off < 64; off <<= 1) {
+    const int o = __shfl_up(x, off, 64);
+    if (lane >= off) x = op(x, o);
   }
-  const int excl = tid > 0 ? buf[tid - 1] : 0;
+  if (lane == 63) buf[w] = x;
   __syncthreads();
+  int pre = 0;
+  for (int k = 0; k < w; ++k) pre = op(pre, buf[k]);
+  const int below = __shfl_up(x, 1, 64);
+  const int excl = lane > 0 ? op(pre, below) : pre;
+  __syncthreads();   // buf is reused by the next scan
   return excl;
 }
 
