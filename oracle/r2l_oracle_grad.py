@@ -60,19 +60,35 @@ def _scan_causal(u, dt, A, Bm, Cm):
     return torch.stack(ys) if ys else torch.zeros(0, E, dtype=u.dtype)
 
 
-def _mamba_block(F, P):
+def _keep(keep, **tensors):
+    """Record intermediate tensors (and keep their gradients) for the
+    Cauchy-Schwarz scales of layer_grads(factors=True); arithmetic-free."""
+    if keep is None:
+        return
+    for name, t in tensors.items():
+        if t.requires_grad:
+            t.retain_grad()
+        keep.setdefault(name, []).append(t)
+
+
+def _mamba_block(F, P, keep=None):
     E = P["conv_w"].shape[0]
     N = P["A_log"].shape[1]
     R = P["dt_proj_w"].shape[1]
     xz = F @ P["in_proj_w"].T
     x, z = xz[:, :E], xz[:, E:]
-    u = _silu(_causal_conv(x, P["conv_w"], P["conv_b"]))
+    c = _causal_conv(x, P["conv_w"], P["conv_b"])
+    u = _silu(c)
     xdbl = u @ P["x_proj_w"].T
     delta, Bm, Cm = xdbl[:, :R], xdbl[:, R:R + N], xdbl[:, R + N:R + 2 * N]
-    dt = torch.nn.functional.softplus(delta @ P["dt_proj_w"].T + P["dt_proj_b"])
+    dtpre = delta @ P["dt_proj_w"].T + P["dt_proj_b"]
+    dt = torch.nn.functional.softplus(dtpre)
     A = -torch.exp(P["A_log"])
     y = _scan_causal(u, dt, A, Bm, Cm) + P["Dskip"] * u
-    return (y * _silu(z)) @ P["out_proj_w"].T
+    yg = y * _silu(z)
+    m = yg @ P["out_proj_w"].T
+    _keep(keep, F=F, xz=xz, x=x, c=c, u=u, xdbl=xdbl, delta=delta, dtpre=dtpre, y=y, yg=yg, m=m)
+    return m
 
 
 def _bounds(cu, T):
@@ -81,9 +97,10 @@ def _bounds(cu, T):
     return list(zip(cu[:-1], cu[1:]))
 
 
-def layer_forward_t(h, cu, P, s, use_ln=True, eps=1e-5, direction="r2l"):
+def layer_forward_t(h, cu, P, s, use_ln=True, eps=1e-5, direction="r2l", keep=None):
     """h+ = h + tanh(s) LN(unflip(Mamba1(flip(h)))) per sequence (§3.4 ❶-❹);
-    direction="l2r" drops the flips.  h, P[*], s: float64 tensors."""
+    direction="l2r" drops the flips.  h, P[*], s: float64 tensors.  keep
+    (optional dict): collects the intermediate tensors of every sequence."""
     assert direction in ("r2l", "l2r")
     T, D = h.shape
     rows = []
@@ -93,31 +110,81 @@ def layer_forward_t(h, cu, P, s, use_ln=True, eps=1e-5, direction="r2l"):
         F = h[t0:t1]
         if direction == "r2l":
             F = torch.flip(F, [0])
-        m = _mamba_block(F, P)
+        m = _mamba_block(F, P, keep)
         if direction == "r2l":
             m = torch.flip(m, [0])
         if use_ln:
             mu = m.mean(dim=1, keepdim=True)
             var = ((m - mu) ** 2).mean(dim=1, keepdim=True)
-            m = P["ln_w"] * (m - mu) / torch.sqrt(var + eps) + P["ln_b"]
+            xhat = (m - mu) / torch.sqrt(var + eps)
+            m = P["ln_w"] * xhat + P["ln_b"]
+            _keep(keep, xhat=xhat, r=m)
         rows.append(m)
     r = torch.cat(rows) if rows else torch.zeros(0, D, dtype=h.dtype)
     return h + torch.tanh(s) * r
 
 
-def layer_grads(h, cu, W, s, g_out, use_ln=True, eps=1e-5, direction="r2l"):
+def layer_grads(h, cu, W, s, g_out, use_ln=True, eps=1e-5, direction="r2l", factors=False):
     """Gradients of sum(g_out * h+) with respect to h, every parameter in
-    PARAMS and s.  Returns a dict of float64 numpy arrays ("h", names, "s")."""
+    PARAMS and s.  Returns a dict of float64 numpy arrays ("h", names, "s").
+
+    factors=True adds "cs": for each parameter whose gradient is a sum over
+    tokens of products, dW[i, j] = sum_t a_t[i] b_t[j], an array of dW's
+    shape holding ||a[:, i]|| ||b[:, j]|| (norms over all tokens; a constant
+    factor contributes sqrt(T)).  By the Cauchy-Schwarz inequality |dW| is
+    at most that scale elementwise, and so is the error of dW caused by
+    relative 2-norm errors of the factors, times the sum of those errors.
+    (A_log's gradient has no such two-factor form and gets none.)"""
     ht = _t(h, True)
     P = {k: _t(W[k], True) for k in PARAMS}
     st = _t(s, True)
-    out = layer_forward_t(ht, cu, P, st, use_ln=use_ln, eps=eps, direction=direction)
+    keep = {} if factors else None
+    out = layer_forward_t(ht, cu, P, st, use_ln=use_ln, eps=eps, direction=direction, keep=keep)
     out.backward(_t(g_out))
     # (a parameter that does not enter the output, e.g. the LN's without LN, gets zeros)
     g = {k: (P[k].grad.numpy() if P[k].grad is not None else np.zeros(np.shape(W[k]))) for k in PARAMS}
     g["h"] = ht.grad.numpy()
     g["s"] = float(st.grad)
+    if factors:
+        g["cs"] = _cs_factors(keep, np.shape(W["conv_w"])[1])
     return g
+
+
+def _cs_factors(keep, K):
+    """Cauchy-Schwarz scales of the token-summed parameter gradients (see
+    layer_grads), from the intermediates of every sequence."""
+    if not keep:
+        return {}
+
+    def val(name):
+        return torch.cat([t.detach() for t in keep[name]])
+
+    def grad(name):
+        return torch.cat([(t.grad if t.grad is not None else torch.zeros_like(t)) for t in keep[name]])
+
+    def cn(a):
+        return a.norm(dim=0).numpy()
+
+    n = float(np.sqrt(val("u").shape[0]))   # a constant factor of 1 per token
+    dc = cn(grad("c"))
+    cs = {
+        "in_proj_w": np.outer(cn(grad("xz")), cn(val("F"))),
+        "x_proj_w": np.outer(cn(grad("xdbl")), cn(val("u"))),
+        "dt_proj_w": np.outer(cn(grad("dtpre")), cn(val("delta"))),
+        "out_proj_w": np.outer(cn(grad("m")), cn(val("yg"))),
+        # tap k of channel e multiplies a copy of x[:, e] shifted by K-1-k
+        # tokens within each sequence (zeros shifted in): its norm is at
+        # most ||x[:, e]||
+        "conv_w": np.outer(dc * cn(val("x")), np.ones(K)),
+        "conv_b": dc * n,
+        "dt_proj_b": cn(grad("dtpre")) * n,
+        "Dskip": cn(grad("y")) * cn(val("u")),
+    }
+    if "xhat" in keep:
+        dr = cn(grad("r"))
+        cs["ln_w"] = dr * cn(val("xhat"))
+        cs["ln_b"] = dr * n
+    return cs
 
 
 def scan_forward_t(u, dt, A_log, Bm, Cm, cu, Dskip=None, z=None, direction="r2l"):

@@ -155,3 +155,43 @@ def test_scan_torch_forward_equals_numpy_oracle():
                                direction=direction).numpy()
         ref = O.reverse_selective_scan(u, dt, A_log, Bm, Cm, cu, Dskip=Dk, z=z, direction=direction)
         np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# Cauchy-Schwarz scales of the token-summed gradients (layer_grads(factors=True))
+# ---------------------------------------------------------------------------
+CS_NAMES = ("in_proj_w", "x_proj_w", "dt_proj_w", "out_proj_w", "conv_w", "conv_b", "dt_proj_b", "Dskip",
+            "ln_w", "ln_b")
+
+
+@pytest.mark.parametrize("direction", ["r2l", "l2r"])
+def test_cs_scales_bound_the_exact_gradients(direction):
+    """|sum_t a_t b_t| <= ||a|| ||b||: the exact gradient lies within its
+    scale elementwise, and somewhere strictly inside (several tokens)."""
+    _, W, h, cu, g, s = _case()
+    grads = G.layer_grads(h, cu, W, s, g, direction=direction, factors=True)
+    assert set(grads["cs"]) == set(CS_NAMES)
+    for k in CS_NAMES:
+        sc = grads["cs"][k]
+        assert sc.shape == np.shape(W[k]), k
+        assert np.all(np.abs(grads[k]) <= sc * (1 + 1e-12) + 1e-300), k
+        assert np.any(np.abs(grads[k]) < 0.999 * sc), k
+
+
+def test_cs_scales_are_exact_for_one_token():
+    """With a single token every sum over tokens has one term, so the
+    Cauchy-Schwarz bound is attained: |dW| equals its scale (for the conv
+    only the tap that meets the token itself is non-zero, and it attains
+    it).  A factor taken from the wrong tensor fails here."""
+    rng = _rng(71)
+    W = _weights(rng)
+    h = rng.standard_normal((1, 6))
+    g = rng.standard_normal((1, 6))
+    grads = G.layer_grads(h, [0, 1], W, 0.8, g, factors=True)
+    for k in CS_NAMES:
+        got, sc = np.abs(grads[k]), grads["cs"][k]
+        if k == "conv_w":
+            np.testing.assert_allclose(got[:, -1], sc[:, -1], rtol=1e-12, err_msg=k)
+            assert not np.any(got[:, :-1]), k
+        else:
+            np.testing.assert_allclose(got, sc, rtol=1e-12, atol=1e-300, err_msg=k)
