@@ -41,7 +41,8 @@
  *    wrong numbers but never an out-of-bounds access.  Callers that hold a
  *    host copy can validate it with r2l_check_cu_seqlens first.
  *  - Threading: calls are reentrant; concurrent calls must use distinct
- *    workspaces and outputs.
+ *    workspaces and outputs.  (The opt-in per-kernel timing below is the
+ *    one process-wide state.)
  *  - Supported shapes: d_state == 16, d_conv == 4, d_model and d_inner
  *    multiples of 64 with d_model <= 8192, 1 <= dt_rank <= 1024,
  *    nseq >= 1, n_tokens >= 0 (all int32-indexable).
@@ -289,12 +290,21 @@ int r2l_check_cu_seqlens(const int32_t* cu_seqlens_host, int32_t nseq, int64_t n
                          int32_t max_seqlen);
 
 /* ------------------------------------------------------------------------
- * Per-kernel timing (process-wide, for benchmarking).  While enabled, each
- * kernel launched by the library is bracketed by a pair of HIP events on
- * its own stream.  r2l_timing_read synchronises on those events, adds each
- * kernel's elapsed time to a per-kernel-name total and clears the event
- * list; it returns the number of distinct kernel names (at most max_names
- * are written).  names[i] point to static strings.
+ * Per-kernel timing, for benchmarking.  Off by default; its state is
+ * process-wide (one registry shared by all threads and devices) and it is
+ * the one part of the library that holds state between calls.
+ * r2l_timing_enable(1) creates a pool of 4096 HIP events on the current
+ * device (R2L_ERR_HIP if that fails); no other call creates events.  While
+ * enabled, each kernel the library launches is bracketed by a pair of pool
+ * events recorded on its stream, except when that stream is being captured
+ * into a HIP graph (captured launches are never timed, so graphs hold no
+ * event records) or when the pool is exhausted (up to 2048 launches between
+ * reads are timed; later ones are not).  r2l_timing_read synchronises on
+ * the recorded events, adds each kernel's elapsed time to a per-kernel-name
+ * total, returns the events to the pool and clears the list; it returns the
+ * number of distinct kernel names (at most max_names are written).
+ * names[i] point to static strings.  r2l_timing_reset waits for and drops
+ * the recorded events and the totals.
  * ---------------------------------------------------------------------- */
 int r2l_timing_enable(int enable);
 int r2l_timing_read(const char** names, double* total_ms, int64_t* counts, int max_names);

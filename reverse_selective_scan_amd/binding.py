@@ -354,7 +354,7 @@ def r2l_gemm_nt(A: torch.Tensor, B: torch.Tensor, *, out_f32: bool = False,
 # per-kernel timing
 # ---------------------------------------------------------------------------
 def timing_enable(on: bool = True) -> None:
-    lib().r2l_timing_enable(1 if on else 0)
+    _check("r2l_timing_enable", lib().r2l_timing_enable(1 if on else 0))
 
 
 def timing_reset() -> None:

@@ -15,8 +15,12 @@ using namespace r2l;
 namespace {
 
 // ---------------------------------------------------------------------------
-// per-kernel timing
+// per-kernel timing (process-wide, opt-in): r2l_timing_enable creates a pool
+// of events once; a launch is timed only while the pool has two free events
+// and its stream is not being captured into a graph, so the launch path
+// itself never creates an event and a captured graph holds no event record.
 // ---------------------------------------------------------------------------
+constexpr size_t kEventPool = 4096;
 struct TimingRec {
   const char* name;
   hipEvent_t a, b;
@@ -34,16 +38,6 @@ TimingState& timing() {
   static TimingState* t = new TimingState();  // never destroyed: safe at process exit
   return *t;
 }
-hipEvent_t take_event(TimingState& t) {
-  if (!t.pool.empty()) {
-    hipEvent_t e = t.pool.back();
-    t.pool.pop_back();
-    return e;
-  }
-  hipEvent_t e = nullptr;
-  if (hipEventCreate(&e) != hipSuccess) return nullptr;
-  return e;
-}
 
 template <typename F>
 int run_kernel(const char* name, hipStream_t st, F&& launch) {
@@ -52,11 +46,16 @@ int run_kernel(const char* name, hipStream_t st, F&& launch) {
   bool en;
   {
     std::lock_guard<std::mutex> g(t.mu);
-    en = t.enabled;
+    en = t.enabled && t.pool.size() >= 2;
     if (en) {
-      ea = take_event(t);
-      eb = take_event(t);
-      if (!ea || !eb) en = false;
+      hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+      if (hipStreamIsCapturing(st, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) en = false;
+    }
+    if (en) {
+      ea = t.pool.back();
+      t.pool.pop_back();
+      eb = t.pool.back();
+      t.pool.pop_back();
     }
   }
   if (en && hipEventRecord(ea, st) != hipSuccess) en = false;
@@ -224,7 +223,7 @@ ScanBwdPlan plan_scan_bwd(int E, int64_t T, int32_t nseq) {
 constexpr size_t kSplitScratch = 256ull * 256 * 256 * sizeof(float);
 
 struct LayerPlan {
-  size_t off_xz, off_xdbl, off_xdbl2, off_xdbl3, off_u, off_y, off_scratch, off_o;
+  size_t off_xz, off_xdbl, off_xdbl2, off_xdbl3, off_dsplit, off_u, off_y, off_scratch, off_o;
   bool need_u;
   ScanPlan scan;
   size_t total;
@@ -247,6 +246,8 @@ LayerPlan plan_layer(const r2l_dims* d, r2l_dtype act, int64_t T, int32_t nseq, 
   // second and third partial x_proj sums of the split-K conv kernel (bf16, large T)
   p.off_xdbl2 = off; off = align_up(off + (act == R2L_BF16 ? Tz * P * 4 : 0));
   p.off_xdbl3 = off; off = align_up(off + (act == R2L_BF16 ? Tz * P * 4 : 0));
+  // delta split for the scan's dt_proj on MFMA (bf16): [T, 2 RP] bf16
+  p.off_dsplit = off; off = align_up(off + (act == R2L_BF16 ? Tz * 4 * (size_t)delta_split_width(d->dt_rank) : 0));
   p.need_u = act == R2L_F32 || P > 256;
   p.off_u = off;    off = align_up(off + (p.need_u ? Tz * E * sa : 0));
   p.off_y = off;    off = align_up(off + Tz * E * sa);
@@ -365,8 +366,13 @@ LayerBwdPlan plan_layer_bwd(const r2l_dims* d, r2l_dtype act, int64_t T, int32_t
   p.do_a = take(Tz * D * sa);
   p.doT = take(D * Tp * sa);
   p.ygT = take(E * Tp * sa);
-  // W_out^T [E, D], W_dt^T [R, E], W_x^T [E, P], W_in^T [D, 2E] share one region
-  p.wT = take((E * D > 2 * E * D ? E * D : 2 * E * D) * sa);
+  // W_out^T [E, D], W_dt^T [R, E], W_x^T [E, P], W_in^T [D, 2E] share one
+  // region, sized for the largest of the four (P = R + 2N exceeds 2D when
+  // the model is narrow and dt_rank large)
+  size_t wt = 2 * E * D;
+  if (R * E > wt) wt = R * E;
+  if (E * P > wt) wt = E * P;
+  p.wT = take(wt * sa);
   p.dyg = take(Tz * E * sa);
   p.du = take(Tz * E * f);
   p.ddt = take(Tz * E * f);
@@ -687,6 +693,7 @@ int r2l_layer_fwd(const r2l_dims* d, r2l_dtype act, uint32_t flags, const r2l_we
     bf16* y = at<bf16>(workspace, lp.off_y);
     const int ncu = num_cus();
     float* scratch = at<float>(workspace, lp.off_scratch);
+    bf16* dsplit = delta_split_width(R) > 0 ? at<bf16>(workspace, lp.off_dsplit) : nullptr;
     R2L_RUN("in_proj_gemm", st, gemm_bf16_nt(T, 2 * E, D, (const bf16*)h_in, D, (const bf16*)w->in_proj_w, D, xz, 2L * E, false, st,
                                              scratch, kSplitScratch, ncu));
     if (!lp.need_u) {
@@ -696,18 +703,19 @@ int r2l_layer_fwd(const r2l_dims* d, r2l_dtype act, uint32_t flags, const r2l_we
         float* xdbl2 = at<float>(workspace, lp.off_xdbl2);
         float* xdbl3 = at<float>(workspace, lp.off_xdbl3);
         R2L_RUN("conv_xproj", st, conv_xproj_bf16_sk(T, E, P, xz, 2L * E, (const bf16*)w->conv_w, (const bf16*)w->conv_b, (const bf16*)w->x_proj_w, xdbl, xdbl2, xdbl3, cu_clean, nseq, ncu, l2r, st));
-        R2L_RUN("conv_sum", st, conv_sk_sum(T, E, P, xdbl, xdbl2, xdbl3, ncu, st));
+        R2L_RUN("conv_sum", st, conv_sk_sum(T, E, P, xdbl, xdbl2, xdbl3, ncu, st, R, dsplit));
       } else {
         R2L_RUN("conv_xproj", st, conv_xproj_bf16(T, E, P, xz, 2L * E, (const bf16*)w->conv_w, (const bf16*)w->conv_b, (const bf16*)w->x_proj_w, nullptr, xdbl, cu_clean, nseq, l2r, st,
-                                                  scratch, kSplitScratch, ncu));
+                                                  scratch, kSplitScratch, ncu, R, dsplit));
       }
     } else {
       bf16* u = at<bf16>(workspace, lp.off_u);
       R2L_RUN("conv_silu", st, conv_silu<bf16>(T, E, xz, 2L * E, (const bf16*)w->conv_w, (const bf16*)w->conv_b, u, cu_clean, nseq, l2r, st));
       // x_proj with a bf16 output would lose precision; run it through the fp32-out MFMA GEMM
       R2L_RUN("x_proj_gemm", st, gemm_bf16_nt(T, P, E, u, E, (const bf16*)w->x_proj_w, E, xdbl, P, true, st));
+      if (dsplit) R2L_RUN("split_delta", st, split_delta(T, P, R, xdbl, dsplit, st));
     }
-    a.x = xz; a.z = xz + E; a.y = y;
+    a.x = xz; a.z = xz + E; a.y = y; a.dsplit = dsplit;
     if (sp.summary) R2L_RUN("scan_summary", st, scan_summary<bf16>(a, true, st));
     R2L_RUN("scan_main", st, scan_main<bf16>(a, true, st));
     // o stays fp32: rounding it to bf16 before the LayerNorm would add up to
@@ -911,6 +919,15 @@ int r2l_gemm_nt(r2l_dtype act, int64_t M, int64_t N, int64_t K, const void* A, i
 int r2l_timing_enable(int enable) {
   TimingState& t = timing();
   std::lock_guard<std::mutex> g(t.mu);
+  if (enable) {
+    // the whole pool is created here, once (events in flight count as taken)
+    const size_t have = t.pool.size() + 2 * t.recs.size();
+    for (size_t i = have; i < kEventPool; ++i) {
+      hipEvent_t e = nullptr;
+      if (hipEventCreate(&e) != hipSuccess) return R2L_ERR_HIP;
+      t.pool.push_back(e);
+    }
+  }
   t.enabled = enable != 0;
   return R2L_OK;
 }

@@ -10,6 +10,60 @@
 
 namespace r2l {
 
+// ---------------------------------------------------------------------------
+// delta split (see kernels.h): RP = the dt_rank padded to the scan's k-steps
+// of 32 (1, 2, 4 or 8 of them); beyond 8 the scan computes dt on the VALU.
+// ---------------------------------------------------------------------------
+int delta_split_width(int R) {
+  const int ks = (R + 31) / 32;
+  return ks > 8 ? 0 : 32 * (ks <= 1 ? 1 : ks <= 2 ? 2 : ks <= 4 ? 4 : 8);
+}
+
+// columns [col, col + V) of one x_proj output row (col % V == 0, RP % V == 0)
+template <int V>
+R2L_DEV void split_store(bf16* __restrict__ ds, long row, int col, int R, int RP, const float* v) {
+  if (col >= RP) return;
+  bf16 hi[V], lo[V];
+#pragma unroll
+  for (int i = 0; i < V; ++i) {
+    const bool in = col + i < R;
+    hi[i] = (bf16)(in ? v[i] : 0.0f);
+    lo[i] = (bf16)(in ? v[i] - (float)hi[i] : 0.0f);
+  }
+  bf16* p = ds + row * 2L * RP + col;
+  if constexpr (V == 4) {
+    *(bf16x4*)p = bf16x4{hi[0], hi[1], hi[2], hi[3]};
+    *(bf16x4*)(p + RP) = bf16x4{lo[0], lo[1], lo[2], lo[3]};
+  } else {
+#pragma unroll
+    for (int i = 0; i < V; ++i) {
+      p[i] = hi[i];
+      p[RP + i] = lo[i];
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void split_delta_kernel(long n, int P, int R, int RP, const float* __restrict__ xdbl,
+                                                          bf16* __restrict__ ds) {
+  // one thread per (row, column < RP)
+  for (long i = blockIdx.x * 256L + threadIdx.x; i < n; i += (long)gridDim.x * 256) {
+    const long row = i / RP;
+    const int col = (int)(i % RP);
+    const float v = col < R ? xdbl[row * P + col] : 0.0f;
+    split_store<1>(ds, row, col, R, RP, &v);
+  }
+}
+
+hipError_t split_delta(int Tn, int P, int R, const float* xdbl, bf16* dsplit, hipStream_t st) {
+  const int RP = delta_split_width(R);
+  if (Tn <= 0 || RP == 0) return hipSuccess;
+  const long n = (long)Tn * RP;
+  const long want = (n + 255) / 256;
+  hipLaunchKernelGGL(split_delta_kernel, dim3((unsigned)(want < 4096 ? want : 4096)), dim3(256), 0, st, n, P, R,
+                     RP, xdbl, dsplit);
+  return hipGetLastError();
+}
+
 constexpr int KC = 4;  // d_conv (§4.1)
 
 // ---------------------------------------------------------------------------
@@ -104,7 +158,8 @@ __global__ __launch_bounds__(256) void conv_xproj_kernel(int Tn, int E, int P,
                                                          const bf16* __restrict__ Wx,
                                                          bf16* __restrict__ u_out,
                                                          float* __restrict__ xdbl,
-                                                         const int32_t* __restrict__ cu, int nseq) {
+                                                         const int32_t* __restrict__ cu, int nseq,
+                                                         int R, int RP, bf16* __restrict__ dsplit) {
   constexpr int NC = NCS * 32;
   __shared__ float red[3][32 * NC];
   const int lane = lane_id(), w = wave_id();
@@ -206,7 +261,10 @@ __global__ __launch_bounds__(256) void conv_xproj_kernel(int Tn, int E, int P,
         const int row = 8 * (r >> 2) + 4 * kh + (r & 3);
         const int idx = row * NC + col;
         const float v = acc[c][r] + red[0][idx] + red[1][idx] + red[2][idx];
-        if (col < P && t0 + row < Tn) xdbl[(long)(t0 + row) * P + col] = v;
+        if (col < P && t0 + row < Tn) {
+          xdbl[(long)(t0 + row) * P + col] = v;
+          if (dsplit != nullptr) split_store<1>(dsplit, t0 + row, col, R, RP, &v);
+        }
       }
     }
   }
@@ -215,8 +273,10 @@ __global__ __launch_bounds__(256) void conv_xproj_kernel(int Tn, int E, int P,
 // out[i] = sum over k < ks of slab[k][i] (slab stride n), in order of k.
 // A thread owns 4 consecutive elements and loads all of its slabs (up to
 // 16) before adding, so the loads are in flight together.
+// dsplit (optional): also the delta split of the sum (out is [n / P, P]).
 __global__ __launch_bounds__(256) void sum_slabs_kernel(long n, int ks, const float* __restrict__ slab,
-                                                        float* __restrict__ out) {
+                                                        float* __restrict__ out, int P, int R, int RP,
+                                                        bf16* __restrict__ dsplit) {
   const long i = (blockIdx.x * 256L + threadIdx.x) * 4;
   if (i >= n) return;
   if (i + 4 <= n && (n & 3) == 0) {
@@ -229,11 +289,18 @@ __global__ __launch_bounds__(256) void sum_slabs_kernel(long n, int ks, const fl
     for (int k = 1; k < 16; ++k)
       if (k < ks) acc += v[k];
     *(f32x4*)(out + i) = acc;
+    if (dsplit != nullptr)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float a = acc[e];
+        split_store<1>(dsplit, (i + e) / P, (int)((i + e) % P), R, RP, &a);
+      }
   } else {
     for (long j = i; j < i + 4 && j < n; ++j) {
       float v = 0.0f;
       for (int k = 0; k < ks; ++k) v += slab[k * n + j];
       out[j] = v;
+      if (dsplit != nullptr) split_store<1>(dsplit, j / P, (int)(j % P), R, RP, &v);
     }
   }
 }
@@ -241,10 +308,12 @@ __global__ __launch_bounds__(256) void sum_slabs_kernel(long n, int ks, const fl
 hipError_t conv_xproj_bf16(int Tn, int E, int P, const bf16* x, long ld_x, const bf16* conv_w,
                            const bf16* conv_b, const bf16* x_proj_w, bf16* u_out, float* xdbl,
                            const int32_t* cu, int nseq, bool l2r, hipStream_t st, float* ws,
-                           size_t ws_bytes, int ncu) {
+                           size_t ws_bytes, int ncu, int R, bf16* dsplit) {
   if (Tn <= 0) return hipSuccess;
   const int ncs = (P + 31) / 32;
   const int ntiles = (Tn + 31) / 32;
+  const int RP = dsplit != nullptr ? delta_split_width(R) : 0;
+  if (RP == 0) dsplit = nullptr;
   // Few token tiles for the GPU: split the channels over KS blocks per tile
   // (each wave keeps at least one 16-channel step), partial sums in ws.
   int ks = 1;
@@ -259,10 +328,12 @@ hipError_t conv_xproj_bf16(int Tn, int E, int P, const bf16* x, long ld_x, const
   case n:                                                                                         \
     if (l2r)                                                                                      \
       hipLaunchKernelGGL((conv_xproj_kernel<n, true>), grid, block, 0, st, Tn, E, P, x, ld_x,     \
-                         conv_w, conv_b, x_proj_w, u_out, dst, cu, nseq);                         \
+                         conv_w, conv_b, x_proj_w, u_out, dst, cu, nseq, R, RP,                   \
+                         ks > 1 ? nullptr : dsplit);                                              \
     else                                                                                          \
       hipLaunchKernelGGL((conv_xproj_kernel<n, false>), grid, block, 0, st, Tn, E, P, x, ld_x,    \
-                         conv_w, conv_b, x_proj_w, u_out, dst, cu, nseq);                         \
+                         conv_w, conv_b, x_proj_w, u_out, dst, cu, nseq, R, RP,                   \
+                         ks > 1 ? nullptr : dsplit);                                              \
     break;
   switch (ncs) {
     R2L_CX(1) R2L_CX(2) R2L_CX(3) R2L_CX(4) R2L_CX(5) R2L_CX(6) R2L_CX(7) R2L_CX(8)
@@ -272,7 +343,7 @@ hipError_t conv_xproj_bf16(int Tn, int E, int P, const bf16* x, long ld_x, const
   if (ks > 1) {   // (ks <= 16, as sum_slabs_kernel needs)
     const long n = (long)Tn * P;
     hipLaunchKernelGGL(sum_slabs_kernel, dim3((unsigned)((n / 4 + 255) / 256 + 1)), dim3(256), 0, st, n, ks,
-                       (const float*)ws, xdbl);
+                       (const float*)ws, xdbl, P, R, RP, dsplit);
   }
   return hipGetLastError();
 }
@@ -571,7 +642,8 @@ R2L_DEV int sk_pieces(long tile, long S, long W, long G) {
 template <int V>
 __global__ __launch_bounds__(256) void sk_sum_kernel(long rows, int P, int S, long W, int G,
                                                      float* __restrict__ a, const float* __restrict__ b,
-                                                     const float* __restrict__ c) {
+                                                     const float* __restrict__ c, int R, int RP,
+                                                     bf16* __restrict__ dsplit) {
   const long per_row = P / V;
   const long n = rows * per_row;
   for (long i = blockIdx.x * 256L + threadIdx.x; i < n; i += (long)gridDim.x * 256) {
@@ -584,11 +656,16 @@ __global__ __launch_bounds__(256) void sk_sum_kernel(long rows, int P, int S, lo
       if (pieces > 1) v = v + *(const f32x4*)(b + off);
       if (pieces > 2) v = v + *(const f32x4*)(c + off);
       *(f32x4*)pa = v;
+      if (dsplit != nullptr) {
+        const float vv[4] = {v[0], v[1], v[2], v[3]};
+        split_store<4>(dsplit, row, (int)(i % per_row) * 4, R, RP, vv);
+      }
     } else {
       float v = *pa;
       if (pieces > 1) v = v + b[off];
       if (pieces > 2) v = v + c[off];
       *pa = v;
+      if (dsplit != nullptr) split_store<1>(dsplit, row, (int)(i % per_row), R, RP, &v);
     }
   }
 }
@@ -610,8 +687,10 @@ static int sk_grid(int P, int ncu) {
 }
 
 hipError_t conv_sk_sum(int Tn, int E, int P, float* part0, const float* part1, const float* part2, int ncu,
-                       hipStream_t st) {
+                       hipStream_t st, int R, bf16* dsplit) {
   if (Tn <= 0) return hipSuccess;
+  const int RP = dsplit != nullptr ? delta_split_width(R) : 0;
+  if (RP == 0) dsplit = nullptr;
   const int S = E / kSkK;
   const long W = (long)((Tn + kSkTok - 1) / kSkTok) * S;
   const int G = sk_grid(P, ncu);
@@ -619,9 +698,11 @@ hipError_t conv_sk_sum(int Tn, int E, int P, float* part0, const float* part1, c
   const long want = (n + 255) / 256;
   const dim3 grid((unsigned)(want < 1 ? 1 : (want < 4096 ? want : 4096)));
   if (P % 4 == 0)
-    hipLaunchKernelGGL(sk_sum_kernel<4>, grid, dim3(256), 0, st, (long)Tn, P, S, W, G, part0, part1, part2);
+    hipLaunchKernelGGL(sk_sum_kernel<4>, grid, dim3(256), 0, st, (long)Tn, P, S, W, G, part0, part1, part2, R, RP,
+                       dsplit);
   else
-    hipLaunchKernelGGL(sk_sum_kernel<1>, grid, dim3(256), 0, st, (long)Tn, P, S, W, G, part0, part1, part2);
+    hipLaunchKernelGGL(sk_sum_kernel<1>, grid, dim3(256), 0, st, (long)Tn, P, S, W, G, part0, part1, part2, R, RP,
+                       dsplit);
   return hipGetLastError();
 }
 

@@ -28,24 +28,36 @@ hipError_t gemm_f32_nt(int M, int N, int K, const float* A, long lda, const floa
 template <typename T>
 hipError_t conv_silu(int T_, int E, const T* x, long ld_x, const T* conv_w, const T* conv_b,
                      T* u, const int32_t* cu, int nseq, bool l2r, hipStream_t st);
+// delta split for the scan's dt_proj on MFMA: the first R columns of each
+// x_proj output row (delta), as a bf16 pair per value: row t of dsplit
+// [T, 2 RP] holds hi = bf16(delta) in columns [0, RP) and lo =
+// bf16(delta - hi) in [RP, 2 RP), zeros in columns R .. RP-1.  RP is the
+// dt_rank padded to the scan's MFMA k-steps (0: the scan computes dt on the
+// VALU from xdbl and needs no split).
+int delta_split_width(int R);
+
 // Fused conv + SiLU + x_proj (bf16, MFMA): xdbl f32 [T, P] with P = R+2N;
 // u_out optional.  Requires E % 64 == 0 and P <= 256.
 // ws (optional, ws_bytes): scratch for splitting the channels over several
 // blocks per 32-token tile when there are few tiles (not with u_out).
+// dsplit (optional): also written, see delta_split_width.
 hipError_t conv_xproj_bf16(int T_, int E, int P, const bf16* x, long ld_x, const bf16* conv_w,
                            const bf16* conv_b, const bf16* x_proj_w, bf16* u_out, float* xdbl,
                            const int32_t* cu, int nseq, bool l2r, hipStream_t st, float* ws = nullptr,
-                           size_t ws_bytes = 0, int ncu = 0);
+                           size_t ws_bytes = 0, int ncu = 0, int R = 0, bf16* dsplit = nullptr);
 
 // The same for large inputs, split along K over one or two blocks per CU
 // (`ncu` CUs) into up to three partial sums; conv_sk_sum (same T, E, P, ncu)
-// then leaves xdbl in part0.  Parts [T, P] fp32, 16-byte aligned.  Requires
+// then leaves xdbl in part0 (and, when dsplit is given, the delta split of
+// its first R columns).  Parts [T, P] fp32, 16-byte aligned.  Requires
 // E % 64 == 0, P <= 256 and ceil(T / 128) >= ncu.
 hipError_t conv_xproj_bf16_sk(int T_, int E, int P, const bf16* x, long ld_x, const bf16* conv_w,
                               const bf16* conv_b, const bf16* x_proj_w, float* part0, float* part1,
                               float* part2, const int32_t* cu, int nseq, int ncu, bool l2r, hipStream_t st);
 hipError_t conv_sk_sum(int T_, int E, int P, float* part0, const float* part1, const float* part2, int ncu,
-                       hipStream_t st);
+                       hipStream_t st, int R = 0, bf16* dsplit = nullptr);
+// The delta split of an x_proj output computed elsewhere (xdbl f32 [T, P]).
+hipError_t split_delta(int T_, int P, int R, const float* xdbl, bf16* dsplit, hipStream_t st);
 
 // Chunk planning for the scan: sanitised cu_seqlens and the chunk table
 // (chunks cut from the end the scan starts at).
@@ -58,6 +70,7 @@ struct ScanArgs {
   const void* x; long ld_x;
   const void* z; long ld_z;
   const float* xdbl;
+  const bf16* dsplit;          // delta split (fused bf16 with dt_proj on MFMA), [T, 2 RP]
   const void* conv_w; const void* conv_b;
   const void* dt_w; const float* dt_b;
   // standalone mode: u, dt, B, C

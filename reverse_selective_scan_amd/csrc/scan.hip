@@ -143,6 +143,10 @@ R2L_DEV Rsrc row_window(const void* base, long row0, long pitch_bytes, int rows)
                                            0x00020000);
 }
 R2L_DEV u32x4 bload16(Rsrc r, unsigned off) { return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0); }
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+R2L_DEV u32x2 bload8(Rsrc r, unsigned off) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+}
 R2L_DEV float bload4(Rsrc r, unsigned off) {
   return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
 }
@@ -220,19 +224,26 @@ template <> R2L_DEV float softplus_dt<bf16>(float v) {
 // backward pass.  The recurrence runs as above; before each 16-token
 // sub-block it stores the state entering it from the right into a.hc, and
 // phase C writes dz = dy SiLU'(z) (C.h + Dskip u) instead of y.
+// (Two blocks per CU; with dt_rank above 128 the delta rows alone take so
+// much LDS that one block per CU is all that fits.)
 template <typename T, bool FUSED, bool SUMMARY, int KS, bool L2R, bool BWD = false>
-__global__ __launch_bounds__(256, 2) void scan_kernel(ScanArgs a) {
+__global__ __launch_bounds__(256, KS > 4 ? 1 : 2) void scan_kernel(ScanArgs a) {
   static_assert(!BWD || (!FUSED && !SUMMARY && !L2R), "the backward sweep is standalone and right to left");
   constexpr int TB = 32;
   constexpr bool MFMA_DT = FUSED && KS > 0;
   constexpr int RP = MFMA_DT ? KS * 32 : 32;   // padded dt_rank for the MFMA k loop
-  constexpr int DLS = RP + 8;                   // delta row stride in LDS (bf16)
+  // delta in LDS as two bf16 parts per value, hi = bf16(delta) in columns
+  // [0, RP) and lo = bf16(delta - hi) in [RP, 2 RP): the two MFMAs of a
+  // k-step then carry delta to about 16 significant bits (the weights are
+  // bf16, so every product is exact in the fp32 accumulator)
+  constexpr int DLS = 2 * RP + 8;               // delta row stride in LDS (bf16)
   constexpr int DPT = RP / 8;                   // delta floats per thread per row (4..32)
   constexpr bool BF = std::is_same<T, bf16>::value;
   constexpr unsigned SZ = sizeof(T);
   // Rows of yp_s, pre_s and u_s are padded by 4 words: the accesses that
   // touch several rows at once (16 lanes over rows 4 apart in the dt phase,
   // 8 lanes per row over 2 rows in phases A and C) then fall in distinct banks.
+  // (At dt_rank 128 the five arrays take 80 KB: two blocks fill a CU's LDS.)
   constexpr int RW = 64 + 4;
   __shared__ __attribute__((aligned(16))) float yp_s[4][TB][RW];   // partial C.h of each wave
   __shared__ __attribute__((aligned(16))) float2 pre_s[TB][RW];    // (dt, dt*u)
@@ -332,7 +343,7 @@ __global__ __launch_bounds__(256, 2) void scan_kernel(ScanArgs a) {
   const unsigned offX = (unsigned)(r8 * ldx_b) + (unsigned)ea * SZ;
   const unsigned offZ = (unsigned)(r8 * ldz_b) + (unsigned)ea * SZ;
   const unsigned offY = (unsigned)(r8 * ldy_b) + (unsigned)ea * SZ;
-  const unsigned offD = (unsigned)(r8 * ldp_b) + (unsigned)(c8 * DPT) * 4;         // delta (fused)
+  const unsigned offS = (unsigned)(r8 * RP * 4) + (unsigned)(c8 * DPT) * 2;         // delta split (fused)
   const unsigned offBC = (unsigned)(r8 * ldp_b) + (unsigned)(a.R + 4 * c8) * 4;   // B then C (fused)
   const unsigned offDT = (unsigned)(r8 * lddt_b) + (unsigned)ea * 4;               // dt (standalone)
   const unsigned offB = c8 < 4 ? (unsigned)(r8 * ldbc_b) + 16u * c8 : kOutside;    // B (standalone)
@@ -345,7 +356,7 @@ __global__ __launch_bounds__(256, 2) void scan_kernel(ScanArgs a) {
   Raw8<T> px[FUSED ? 4 : 1];   // x rows r8 .. r8+3 (fused) or the u row r8
   Raw8<T> pz;                  // z row r8
   Raw8<T> pdy;                 // dy row r8 (backward)
-  u32x4 pd[FUSED ? (MFMA_DT ? DPT / 4 : 1) : 2];   // delta (fused) or dt (standalone) of row r8
+  u32x4 pd[FUSED ? (MFMA_DT ? DPT / 4 : 1) : 2];   // delta split (fused) or dt (standalone) of row r8
   float pbc[4];                // 4 of the row's 32 B/C floats
 
   auto issue = [&](int blo, int bhi) {
@@ -362,8 +373,18 @@ __global__ __launch_bounds__(256, 2) void scan_kernel(ScanArgs a) {
         raw_load(px[j], rX, offX + (unsigned)((L2R ? blo - wb - j : j) * ldx_b));
       const Rsrc rD = row_window(a.xdbl, blo, ldp_b, rows);
       if constexpr (MFMA_DT) {
+        // this thread's DPT columns of the delta split's hi and lo halves
+        const Rsrc rS = row_window(a.dsplit, blo, (long)RP * 4, rows);
+        if constexpr (DPT >= 8) {
 #pragma unroll
-        for (int q = 0; q < DPT / 4; ++q) pd[q] = bload16(rD, offD + 16u * q);
+          for (int q = 0; q < DPT / 8; ++q) {
+            pd[q] = bload16(rS, offS + 16u * q);
+            pd[DPT / 8 + q] = bload16(rS, offS + 2u * RP + 16u * q);
+          }
+        } else {
+          const u32x2 hi = bload8(rS, offS), lo = bload8(rS, offS + 2u * RP);
+          pd[0] = u32x4{hi[0], hi[1], lo[0], lo[1]};
+        }
       }
 #pragma unroll
       for (int p = 0; p < 4; ++p) pbc[p] = bload4(rD, offBC + 4u * p);
@@ -427,13 +448,17 @@ __global__ __launch_bounds__(256, 2) void scan_kernel(ScanArgs a) {
           }
         }
         if constexpr (MFMA_DT) {
-          // delta -> bf16; columns at or past dt_rank meet zero rows of W_dt
-          // (they hold finite B/C values of the same row)
+          // the delta split's hi and lo halves, as they are (zeros past dt_rank)
+          bf16* dst = dl_s + r8 * DLS + c8 * DPT;
+          if constexpr (DPT >= 8) {
 #pragma unroll
-          for (int q = 0; q < DPT / 4; ++q) {
-            const f32x4 v = __builtin_bit_cast(f32x4, pd[q]);
-            const bf16x4 pk = {(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]};
-            *(bf16x4*)(dl_s + r8 * DLS + c8 * DPT + 4 * q) = pk;
+            for (int q = 0; q < DPT / 8; ++q) {
+              *(u32x4*)(dst + 8 * q) = pd[q];
+              *(u32x4*)(dst + RP + 8 * q) = pd[DPT / 8 + q];
+            }
+          } else {
+            *(u32x2*)dst = u32x2{pd[0][0], pd[0][1]};
+            *(u32x2*)(dst + RP) = u32x2{pd[0][2], pd[0][3]};
           }
         }
         *(f32x4*)&u_s[r8][8 * c8] = f32x4{uu[0], uu[1], uu[2], uu[3]};
@@ -471,20 +496,30 @@ __global__ __launch_bounds__(256, 2) void scan_kernel(ScanArgs a) {
     // ---------------- M: dt = softplus(delta . W_dt^T + b) ----------------
     if constexpr (FUSED) {
       if constexpr (MFMA_DT) {
+        // four independent accumulator chains (two row tiles x the lo and
+        // hi parts of delta), interleaved so that no MFMA waits for the
+        // previous one's result
+        f32x4 acc[TB / 16][2];
+#pragma unroll
+        for (int rt = 0; rt < TB / 16; ++rt)
+#pragma unroll
+          for (int part = 0; part < 2; ++part) acc[rt][part] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        const bf16* drow = dl_s + (lane & 15) * DLS + (lane >> 4) * 8;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+          for (int rt = 0; rt < TB / 16; ++rt)
+#pragma unroll
+            for (int part = 0; part < 2; ++part)
+              acc[rt][part] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                  *(const bf16x8*)(drow + rt * 16 * DLS + part * RP + ks * 32), wdt[ks], acc[rt][part], 0, 0, 0);
 #pragma unroll
         for (int rt = 0; rt < TB / 16; ++rt) {
-          f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-          const int row = rt * 16 + (lane & 15);
-          bf16x8 af[KS];
-#pragma unroll
-          for (int ks = 0; ks < KS; ++ks) af[ks] = *(const bf16x8*)(dl_s + row * DLS + ks * 32 + (lane >> 4) * 8);
-#pragma unroll
-          for (int ks = 0; ks < KS; ++ks) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[ks], wdt[ks], acc, 0, 0, 0);
           // D layout: lane holds rows 4 (lane >> 4) + i, column (lane & 15)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int rr = rt * 16 + 4 * (lane >> 4) + i;
-            const float dtv = softplus_dt<T>(acc[i] + dtb_col);
+            const float dtv = softplus_dt<T>((acc[rt][1][i] + acc[rt][0][i]) + dtb_col);
             pre_s[rr][dcol] = make_float2(dtv, dtv * u_s[rr][dcol]);
           }
         }

@@ -9,7 +9,8 @@ import pytest
 import torch
 
 from oracle import r2l_oracle as O
-from parity import TOL_BF16, TOL_BF16_BRANCH, err_f32, err_rms, report, to_np
+import bf16_floor
+from parity import TOL_BF16, TOL_BF16_BRANCH, check_bf16, err_f32, err_rms, report, to_np
 from reverse_selective_scan_amd import binding as B
 from reverse_selective_scan_amd import synth
 
@@ -172,9 +173,10 @@ def test_small_bf16_layer_l2r_matches_oracle(lens):
     W = synth.make_weights(wl, affine_ln=True)
     h, cu = synth.make_hidden(wl), wl.cu_seqlens()
     ref, rref = O.reverse_mamba_layer(h, cu, W, float(W["s"]), return_branch=True, direction="l2r")
+    fo, fr = bf16_floor.layer_rounded(h, cu, W, float(W["s"]), direction="l2r")
     g, gr = _gpu_layer(W, h, cu, torch.bfloat16, L2R, branch=True)
-    assert report("out l2r", err_rms(g, ref), TOL_BF16) <= TOL_BF16
-    assert report("branch l2r", err_rms(gr, rref), TOL_BF16_BRANCH) <= TOL_BF16_BRANCH
+    check_bf16("out l2r", g, ref, fo, TOL_BF16)
+    check_bf16("branch l2r", gr, rref, fr, TOL_BF16_BRANCH)
 
 
 def test_bf16_layer_l2r_split_k_conv_path_matches_oracle():
@@ -187,9 +189,10 @@ def test_bf16_layer_l2r_split_k_conv_path_matches_oracle():
     W = synth.make_weights(wl, affine_ln=True)
     h, cu = synth.make_hidden(wl), wl.cu_seqlens()
     ref, rref = O.reverse_mamba_layer(h, cu, W, float(W["s"]), return_branch=True, direction="l2r")
+    fo, fr = bf16_floor.layer_rounded(h, cu, W, float(W["s"]), direction="l2r")
     g, gr = _gpu_layer(W, h, cu, torch.bfloat16, L2R, branch=True)
-    assert report("out l2r", err_rms(g, ref), TOL_BF16) <= TOL_BF16
-    assert report("branch l2r", err_rms(gr, rref), TOL_BF16_BRANCH) <= TOL_BF16_BRANCH
+    check_bf16("out l2r", g, ref, fo, TOL_BF16)
+    check_bf16("branch l2r", gr, rref, fr, TOL_BF16_BRANCH)
 
 
 @pytest.mark.parametrize("act", ["f32", "bf16"])

@@ -14,7 +14,8 @@ import pytest
 import torch
 
 from oracle import r2l_oracle as O
-from parity import TOL_BF16, TOL_BF16_BRANCH, TOL_F32, err_f32, err_rms, report, to_np
+import bf16_floor
+from parity import TOL_BF16, TOL_BF16_BRANCH, TOL_F32, check_bf16, err_f32, err_rms, report, to_np
 from reverse_selective_scan_amd import binding as B
 from reverse_selective_scan_amd import synth
 
@@ -82,9 +83,10 @@ def test_small_bf16_varlen_matches_oracle(lens, affine):
     W = synth.make_weights(wl, affine_ln=affine)
     h, cu = synth.make_hidden(wl), wl.cu_seqlens()
     ref, rref = O.reverse_mamba_layer(h, cu, W, float(W["s"]), return_branch=True)
+    fo, fr = bf16_floor.layer_rounded(h, cu, W, float(W["s"]))
     g, gr = _gpu_layer(wl, W, h, cu, branch=True)
-    assert report("out", err_rms(g, ref), TOL_BF16) <= TOL_BF16
-    assert report("branch", err_rms(gr, rref), TOL_BF16_BRANCH) <= TOL_BF16_BRANCH
+    check_bf16("out", g, ref, fo, TOL_BF16)
+    check_bf16("branch", gr, rref, fr, TOL_BF16_BRANCH)
 
 
 def test_bf16_split_k_conv_path_matches_oracle():
@@ -100,9 +102,28 @@ def test_bf16_split_k_conv_path_matches_oracle():
     W = synth.make_weights(wl, affine_ln=True)
     h, cu = synth.make_hidden(wl), wl.cu_seqlens()
     ref, rref = O.reverse_mamba_layer(h, cu, W, float(W["s"]), return_branch=True)
+    fo, fr = bf16_floor.layer_rounded(h, cu, W, float(W["s"]))
     g, gr = _gpu_layer(wl, W, h, cu, branch=True)
-    assert report("out", err_rms(g, ref), TOL_BF16) <= TOL_BF16
-    assert report("branch", err_rms(gr, rref), TOL_BF16_BRANCH) <= TOL_BF16_BRANCH
+    check_bf16("out", g, ref, fo, TOL_BF16)
+    check_bf16("branch", gr, rref, fr, TOL_BF16_BRANCH)
+
+
+@pytest.mark.parametrize("dt_rank", [40, 240, 300])
+def test_small_bf16_dt_rank_paths_match_oracle(dt_rank):
+    """dt_proj inside the scan on each of its paths: 40 (two MFMA k-steps,
+    24 zero columns of padding in the delta split), 240 (x_proj width 272:
+    u staged, x_proj on the GEMM, the split made by its own kernel, eight
+    k-steps) and 300 (past eight k-steps: dt on the VALU from xdbl)."""
+    lens = [300, 1, 77]
+    _case(f"small bf16 dt_rank={dt_rank} lens={lens}")
+    wl = synth.custom(lens, seed=27, h_kind="rms", d_model=256, d_inner=512, dt_rank=dt_rank)
+    W = synth.make_weights(wl, affine_ln=True)
+    h, cu = synth.make_hidden(wl), wl.cu_seqlens()
+    ref, rref = O.reverse_mamba_layer(h, cu, W, float(W["s"]), return_branch=True)
+    fo, fr = bf16_floor.layer_rounded(h, cu, W, float(W["s"]))
+    g, gr = _gpu_layer(wl, W, h, cu, branch=True)
+    check_bf16("out", g, ref, fo, TOL_BF16)
+    check_bf16("branch", gr, rref, fr, TOL_BF16_BRANCH)
 
 
 @pytest.mark.parametrize("hint", ["too_small", "too_large"])
@@ -115,12 +136,13 @@ def test_max_seqlen_hint_does_not_change_results(hint):
     wl = synth.custom(lens, seed=23, h_kind="rms", **SMALL)
     W, h, cu = synth.make_weights(wl), synth.make_hidden(wl), wl.cu_seqlens()
     ref = O.reverse_mamba_layer(h, cu, W, float(W["s"]))
+    fo, _ = bf16_floor.layer_rounded(h, cu, W, float(W["s"]))
     w = B.to_device_weights(W, torch.bfloat16, DEV)
     hd = torch.from_numpy(h).to(torch.bfloat16).to(DEV)
     cu_d = torch.from_numpy(np.asarray(cu, np.int32)).to(DEV)
     ms = 2 if hint == "too_small" else 100000
     g = to_np(B.r2l_layer_fwd(hd, w, cu_d, nseq=len(lens), max_seqlen=ms))
-    assert report(f"out (max_seqlen {ms})", err_rms(g, ref), TOL_BF16) <= TOL_BF16
+    check_bf16(f"out (max_seqlen {ms})", g, ref, fo, TOL_BF16)
 
 
 def test_small_bf16_no_ln_and_in_place():
@@ -128,8 +150,9 @@ def test_small_bf16_no_ln_and_in_place():
     wl = synth.custom([200, 57], seed=8, h_kind="rms", **SMALL)
     W, h, cu = synth.make_weights(wl), synth.make_hidden(wl), wl.cu_seqlens()
     ref = O.reverse_mamba_layer(h, cu, W, float(W["s"]), use_ln=False)
+    fo, _ = bf16_floor.layer_rounded(h, cu, W, float(W["s"]), use_ln=False)
     g, _ = _gpu_layer(wl, W, h, cu, flags=B.R2L_FLAG_NO_LN, inplace=True)
-    assert report("out no-ln", err_rms(g, ref), TOL_BF16) <= TOL_BF16
+    check_bf16("out no-ln", g, ref, fo, TOL_BF16)
 
 
 def test_small_bf16_right_context_only_bitwise():
@@ -179,8 +202,18 @@ def test_small_bf16_gate_linearity():
 # workload shapes at full size
 # ---------------------------------------------------------------------------
 def _suffix_ref(h, W, s, t0, t1, start):
-    """Exact oracle outputs for positions [start, t1) of sequence [t0, t1)."""
-    return O.reverse_mamba_layer(h[start:t1], [0, t1 - start], W, s)
+    """Exact oracle outputs (h+, branch r) for positions [start, t1) of
+    sequence [t0, t1), and the same outputs of the bf16 storage floor."""
+    ref = O.reverse_mamba_layer(h[start:t1], [0, t1 - start], W, s, return_branch=True)
+    return ref + bf16_floor.layer_rounded(h[start:t1], [0, t1 - start], W, s)
+
+
+def _check_rows(tag, g, gr, ref, rref, fo=None, fr=None):
+    """h+ (the graded output) and the LayerNorm branch r, each against the
+    oracle in the bf16 metric and against the storage floor's bound: h+ ~ h
+    hides branch errors when tanh(s) is small, so r is held on its own."""
+    check_bf16(f"{tag} out", g, ref, fo, TOL_BF16)
+    check_bf16(f"{tag} branch", gr, rref, fr, TOL_BF16_BRANCH)
 
 
 def test_single_2k_matches_oracle_and_zero_gate():
@@ -188,30 +221,51 @@ def test_single_2k_matches_oracle_and_zero_gate():
     _case("single_2k (B=1 L=2048 D=2048)")
     W, h, cu = synth.make_weights(wl), synth.make_hidden(wl), wl.cu_seqlens()
     t = time.time()
-    ref, rref = O.reverse_mamba_layer(h, cu, W, float(W["s"]), return_branch=True)
+    ref, rref, fo, fr = _suffix_ref(h, W, float(W["s"]), 0, 2048, 0)
     print(f"oracle {time.time() - t:.1f}s", flush=True)
     g, gr = _gpu_layer(wl, W, h, cu, branch=True)
-    assert report("single_2k out", err_rms(g, ref), TOL_BF16) <= TOL_BF16
-    assert report("single_2k branch", err_rms(gr, rref), TOL_BF16_BRANCH) <= TOL_BF16_BRANCH
+    _check_rows("single_2k", g, gr, ref, rref, fo, fr)
     g0, _ = _gpu_layer(wl, W, h, cu, s=0.0)
     assert np.array_equal(g0.astype(np.float32).view(np.uint32), h.view(np.uint32))
 
 
 def test_serve_b8_matches_oracle():
+    """The serving shape in the launch configuration the benchmark times:
+    sequence 0 in full, the last 384 tokens of the other seven."""
     wl = synth.workloads()["serve_b8"]
     _case("serve_b8 (B=8 L=4128 D=2048)")
     W, h, cu = synth.make_weights(wl), synth.make_hidden(wl), wl.cu_seqlens()
     s = float(W["s"])
-    g, _ = _gpu_layer(wl, W, h, cu)
+    g, gr = _gpu_layer(wl, W, h, cu, branch=True)
     t = time.time()
-    t0, t1 = int(cu[0]), int(cu[1])
-    ref = O.reverse_mamba_layer(h[t0:t1], [0, t1 - t0], W, s)
-    assert report("serve_b8 seq0 full", err_rms(g[t0:t1], ref), TOL_BF16) <= TOL_BF16
-    for q in range(1, wl.nseq):
+    for q in range(wl.nseq):
         t0, t1 = int(cu[q]), int(cu[q + 1])
-        ref = _suffix_ref(h, W, s, t0, t1, t1 - 384)
-        assert report(f"serve_b8 seq{q} suffix", err_rms(g[t1 - 384:t1], ref), TOL_BF16) <= TOL_BF16
+        a = t0 if q == 0 else t1 - 384
+        ref, rref, fo, fr = _suffix_ref(h, W, s, t0, t1, a)
+        _check_rows(f"serve_b8 seq{q} rows {a - t0}..", g[a:t1], gr[a:t1], ref, rref, fo, fr)
     print(f"oracle {time.time() - t:.1f}s", flush=True)
+
+
+def _chain_metrics(tag, g_chain, ref, n_hooks):
+    """End-to-end error of a chain of hooks whose hidden stream is bf16 on
+    both sides (the reference chain rounds each hook's output to bf16 before
+    the next hook, as the GPU chain does).  Two measures:
+      * RMS-normalised, ||g - o||_2 / ||o||_2.  The two chains round the
+        stream at slightly different values after every hook, so they drift
+        apart like a random walk over n_hooks + 1 roundings.  One rounding's
+        RMS is measured on the reference itself (||bf16(o) - o|| / ||o||),
+        and the chain is held to 2 sqrt(n_hooks + 1) times that (measured:
+        about 0.5 to 0.75 of the bound).
+      * max-norm (the per-hook metric).  One rounding flip of an element in
+        [4, 8) moves it by 2^-5, about 3e-2 of the stream's RMS, and along
+        the chain such flips compound (measured 4e-2 .. 6.6e-2); held to
+        0.1, about three flips."""
+    one = float(np.linalg.norm(synth.bf16_round(ref.astype(np.float32)) - ref) / np.linalg.norm(ref))
+    rel = float(np.linalg.norm(g_chain - ref) / np.linalg.norm(ref))
+    bound = 2.0 * np.sqrt(n_hooks + 1) * one
+    print(f"[parity] {tag} one bf16 rounding (RMS-normalised): {one:.3e}", flush=True)
+    assert report(f"{tag} end-to-end RMS-normalised", rel, bound) <= bound
+    assert report(f"{tag} end-to-end max-norm", err_rms(g_chain, ref), 0.1) <= 0.1
 
 
 def test_stack7_matches_oracle():
@@ -220,14 +274,10 @@ def test_stack7_matches_oracle():
     each hook's output to bf16 before feeding the next hook, as the stack's
     input itself is bf16.
 
-    Per hook (strict, 2e-2): GPU hook k run on the oracle's bf16 stream at
-    position k against the oracle's fp64 output of hook k.
-    End to end (GPU output feeding the next GPU hook): each hook's error
-    passes the residual path unchanged and the hooks' errors add, so the
-    chain is held to the sum of the per-hook bounds, 7 x 2e-2; the measured
-    value is printed.  (A single bf16 rounding flip of the stream at
-    |h| in [4, 8) already moves an element by 2^-5, about 3e-2 of the
-    stream's RMS, so 2e-2 end to end is out of reach for any bf16 stream.)"""
+    Per hook (strict, 2e-2, and the branch r): GPU hook k run on the
+    oracle's bf16 stream at position k against the oracle's fp64 output of
+    hook k.  End to end (GPU output feeding the next GPU hook): the two
+    measures of _chain_metrics."""
     wl = synth.workloads()["stack7"]
     _case("stack7 (7 hooks, B=8 L=4096 D=2048)")
     h0, cu = synth.make_hidden(wl), wl.cu_seqlens()
@@ -246,44 +296,55 @@ def test_stack7_matches_oracle():
         a = t0 if start is None else t1 - start
         cur = h0[a:t1].astype(np.float64)
         for k, W in enumerate(Ws):
-            ref = O.reverse_mamba_layer(cur, [0, t1 - a], W, float(W["s"]))
+            ref, rref, fo, fr = _suffix_ref(cur, W, float(W["s"]), 0, t1 - a, 0)
             hin = torch.from_numpy(cur.astype(np.float32)).to(torch.bfloat16).to(DEV)
-            g = to_np(B.r2l_layer_fwd(hin, wd[k], [0, t1 - a]))
-            assert report(f"stack7 seq{q} rows {a - t0}.. hook {k}", err_rms(g, ref), TOL_BF16) <= TOL_BF16
+            br = torch.empty(hin.shape, dtype=torch.float32, device=DEV)
+            g = to_np(B.r2l_layer_fwd(hin, wd[k], [0, t1 - a], branch_out=br))
+            _check_rows(f"stack7 seq{q} rows {a - t0}.. hook {k}", g, to_np(br), ref, rref, fo, fr)
             cur = synth.bf16_round(ref.astype(np.float32)).astype(np.float64)
-        e2e = err_rms(g_chain[a:t1], ref)
-        assert report(f"stack7 seq{q} end-to-end", e2e, 7 * TOL_BF16) <= 7 * TOL_BF16
+        _chain_metrics(f"stack7 seq{q}", g_chain[a:t1], ref, wl.n_hooks)
     print(f"oracle {time.time() - t:.1f}s", flush=True)
 
 
 def test_varlen16_matches_oracle():
+    """16 packed sequences of 512..16384 tokens: the shortest and the median
+    one in full, the last 300 tokens of every sequence."""
     wl = synth.workloads()["varlen16"]
     _case(f"varlen16 (T={wl.n_tokens}, lengths {min(wl.lengths)}..{max(wl.lengths)})")
     W, h, cu = synth.make_weights(wl), synth.make_hidden(wl), wl.cu_seqlens()
     s = float(W["s"])
-    g, _ = _gpu_layer(wl, W, h, cu)
+    g, gr = _gpu_layer(wl, W, h, cu, branch=True)
     t = time.time()
     order = np.argsort(wl.lengths)
-    for q in (int(order[0]), int(order[len(order) // 2])):      # shortest and median, in full
+    full = (int(order[0]), int(order[len(order) // 2]))
+    for q in full:
         t0, t1 = int(cu[q]), int(cu[q + 1])
-        ref = O.reverse_mamba_layer(h[t0:t1], [0, t1 - t0], W, s)
-        assert report(f"varlen16 seq{q} (L={t1 - t0}) full", err_rms(g[t0:t1], ref), TOL_BF16) <= TOL_BF16
+        ref, rref, fo, fr = _suffix_ref(h, W, s, t0, t1, t0)
+        _check_rows(f"varlen16 seq{q} (L={t1 - t0}) full", g[t0:t1], gr[t0:t1], ref, rref, fo, fr)
     for q in range(wl.nseq):
+        if q in full:
+            continue
         t0, t1 = int(cu[q]), int(cu[q + 1])
-        ref = _suffix_ref(h, W, s, t0, t1, t1 - 300)
-        assert report(f"varlen16 seq{q} suffix", err_rms(g[t1 - 300:t1], ref), TOL_BF16) <= TOL_BF16
+        ref, rref, fo, fr = _suffix_ref(h, W, s, t0, t1, t1 - 300)
+        _check_rows(f"varlen16 seq{q} suffix", g[t1 - 300:t1], gr[t1 - 300:t1], ref, rref, fo, fr)
     print(f"oracle {time.time() - t:.1f}s", flush=True)
 
 
 def test_long32k_matches_oracle():
+    """One 32,768-token sequence, compared in full: the scan cuts it into
+    eight time chunks of 4,096 tokens, so every carry (folding up to seven
+    chunk summaries) is compared with the oracle."""
     wl = synth.workloads()["long32k"]
     _case("long32k (B=1 L=32768)")
     W, h, cu = synth.make_weights(wl), synth.make_hidden(wl), wl.cu_seqlens()
-    g, _ = _gpu_layer(wl, W, h, cu)
+    g, gr = _gpu_layer(wl, W, h, cu, branch=True)
     t = time.time()
     L = wl.lengths[0]
-    ref = _suffix_ref(h, W, float(W["s"]), 0, L, L - 6144)   # spans several scan chunks
-    assert report("long32k suffix 6144", err_rms(g[L - 6144:], ref), TOL_BF16) <= TOL_BF16
+    ref, rref, fo, fr = _suffix_ref(h, W, float(W["s"]), 0, L, 0)
+    _check_rows("long32k full", g, gr, ref, rref, fo, fr)
+    for c in range(8):   # per time chunk, rightmost first
+        lo, hi = L - 4096 * (c + 1), L - 4096 * c
+        print(f"[parity] long32k chunk {c} branch: {err_rms(gr[lo:hi], rref[lo:hi]):.3e}", flush=True)
     print(f"oracle {time.time() - t:.1f}s", flush=True)
 
 
@@ -299,9 +360,9 @@ def _denoise_setup(wl):
 
 @pytest.mark.parametrize("name", ["denoise_g32", "denoise_g128"])
 def test_denoise_step_matches_oracle(name):
-    """Every hook of one denoise step on the oracle's bf16 stream (strict),
-    and the GPU chain end to end (sum of the per-hook bounds, as for the
-    seven-hook stack), over all eight blocks."""
+    """Every hook of one denoise step on the oracle's bf16 stream (strict,
+    h+ and the branch r), and the GPU chain end to end (the two measures of
+    _chain_metrics), over all eight blocks."""
     wl = synth.workloads()[name]
     _case(f"{name} (7 hooks, B=8 x G={wl.lengths[0]})")
     h0, cu, Ws, wd = _denoise_setup(wl)
@@ -312,12 +373,14 @@ def test_denoise_step_matches_oracle(name):
     g_chain = to_np(hd)
     cur = h0.astype(np.float64)
     for k, W in enumerate(Ws):
-        ref = O.reverse_mamba_layer(cur, cu, W, float(W["s"]))
+        ref, rref = O.reverse_mamba_layer(cur, cu, W, float(W["s"]), return_branch=True)
+        fo, fr = bf16_floor.layer_rounded(cur, cu, W, float(W["s"]))
         hin = torch.from_numpy(cur.astype(np.float32)).to(torch.bfloat16).to(DEV)
-        g = to_np(B.r2l_layer_fwd(hin, wd[k], cu))
-        assert report(f"{name} hook {k}", err_rms(g, ref), TOL_BF16) <= TOL_BF16
+        br = torch.empty(hin.shape, dtype=torch.float32, device=DEV)
+        g = to_np(B.r2l_layer_fwd(hin, wd[k], cu, branch_out=br))
+        _check_rows(f"{name} hook {k}", g, to_np(br), ref, rref, fo, fr)
         cur = synth.bf16_round(ref.astype(np.float32)).astype(np.float64)
-    assert report(f"{name} end-to-end", err_rms(g_chain, ref), 7 * TOL_BF16) <= 7 * TOL_BF16
+    _chain_metrics(name, g_chain, ref, wl.n_hooks)
 
 
 def test_denoise_step_graph_replays_match_eager():
