@@ -154,6 +154,31 @@ int r2l_layer_fwd(const r2l_dims* dims, r2l_dtype act, uint32_t flags, const r2l
                   float* branch_out, void* stream);
 
 /* ------------------------------------------------------------------------
+ * r2l_layer_fwd_noalloc -- r2l_layer_fwd for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  Same arguments and results as
+ * r2l_layer_fwd minus the workspace: the library's own static device array
+ * of R2L_NOALLOC_SCRATCH_BYTES (128 MiB) serves as the workspace.  Each GPU
+ * the library runs on holds one copy of it until the process ends; its
+ * address is resolved (hipGetSymbolAddress) on the first call on a device,
+ * with that device current.  The call allocates nothing.
+ *  - Returns R2L_ERR_WORKSPACE when r2l_layer_workspace_bytes(...) for the
+ *    call exceeds R2L_NOALLOC_SCRATCH_BYTES (at d_model 2048, d_inner 4096,
+ *    dt_rank 128: up to about 2,000 tokens, e.g. a denoise step of 8 blocks
+ *    of 128), R2L_ERR_UNSUPPORTED with R2L_FLAG_TRAIN (its saved activations
+ *    would be overwritten by the next call), R2L_ERR_INVALID_ARG for shapes
+ *    the query rejects, R2L_ERR_HIP if the array cannot be resolved.
+ *  - Every call on a GPU shares that GPU's array and leaves its contents
+ *    behind; calls do not depend on them.  Calls that overlap in time on one
+ *    GPU (concurrent streams or host threads) race on the array: the caller
+ *    must order them, e.g. on one stream.
+ * ---------------------------------------------------------------------- */
+#define R2L_NOALLOC_SCRATCH_BYTES (128ull << 20)
+int r2l_layer_fwd_noalloc(const r2l_dims* dims, r2l_dtype act, uint32_t flags, const r2l_weights* w,
+                          const void* h_in, void* h_out, const int32_t* cu_seqlens, int32_t nseq,
+                          int64_t n_tokens, int32_t max_seqlen, float* branch_out, void* stream);
+
+/* ------------------------------------------------------------------------
  * r2l_layer_bwd -- the gradient of r2l_layer_fwd for training the sidecar
  * (§3.5, plug-in mode: the backbone is frozen, the Mamba block, the stream
  * LayerNorm and the gate s are trained).  Given g_out = dL/dh+ for the

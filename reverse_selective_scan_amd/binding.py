@@ -55,6 +55,8 @@ _SIGS = {
     "r2l_layer_workspace_bytes": (_SZ, [C.POINTER(Dims), C.c_int, _I64, _I32, _I32]),
     "r2l_layer_fwd": (C.c_int, [C.POINTER(Dims), C.c_int, C.c_uint32, C.POINTER(Weights), _P, _P, _P,
                                 _I32, _I64, _I32, _P, _SZ, _P, _P]),
+    "r2l_layer_fwd_noalloc": (C.c_int, [C.POINTER(Dims), C.c_int, C.c_uint32, C.POINTER(Weights), _P, _P, _P,
+                                        _I32, _I64, _I32, _P, _P]),
     "r2l_conv_fwd": (C.c_int, [C.POINTER(Dims), C.c_int, C.c_uint32, _P, _I64, _P, _P, _P, _P, _P, _P, _I32,
                                _I64, _I32, _P]),
     "r2l_scan_workspace_bytes": (_SZ, [C.POINTER(Dims), _I64, _I32, _I32]),
@@ -197,6 +199,25 @@ def r2l_layer_fwd(h: torch.Tensor, w: Dict[str, torch.Tensor], cu_seqlens, *, ou
     _check("r2l_layer_fwd", lib().r2l_layer_fwd(
         C.byref(d), act, flags, C.byref(W), _ptr(h), _ptr(out), _ptr(cu_dev), nseq, T, max_seqlen,
         _ptr(workspace), workspace.numel(), _ptr(branch_out), _stream()))
+    return out
+
+
+def r2l_layer_fwd_noalloc(h: torch.Tensor, w: Dict[str, torch.Tensor], cu_seqlens: torch.Tensor, nseq: int,
+                          max_seqlen: int, *, out: torch.Tensor, flags: int = 0,
+                          branch_out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """r2l_layer_fwd on the library's static scratch array: no workspace and
+    no allocation here either (out, and branch_out if wanted, are given;
+    cu_seqlens is an int32 device tensor)."""
+    _need(h, "h")
+    _need(out, "out", h.dtype)
+    _need(cu_seqlens, "cu_seqlens", torch.int32)
+    if branch_out is not None:
+        _need(branch_out, "branch_out", torch.float32)
+    d = dims_of(w)
+    W = Weights(**{f[0]: _ptr(w[f[0]]) for f in Weights._fields_})
+    _check("r2l_layer_fwd_noalloc", lib().r2l_layer_fwd_noalloc(
+        C.byref(d), _act(h), flags, C.byref(W), _ptr(h), _ptr(out), _ptr(cu_seqlens), nseq, h.shape[0],
+        max_seqlen, _ptr(branch_out), _stream()))
     return out
 
 

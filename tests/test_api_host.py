@@ -234,3 +234,20 @@ def test_scan_bwd_rejects_bad_arguments():
     assert call(ld_u=4000) == B.R2L_ERR_INVALID_ARG
     assert call(ws=None, wsb=0) == B.R2L_ERR_WORKSPACE
     assert call(wsb=need - 1) == B.R2L_ERR_WORKSPACE
+
+
+def test_layer_fwd_noalloc_rejects_before_touching_a_device():
+    """The allocation-free forward checks its size against the static array
+    (and its flags) before resolving the array on a device."""
+    lib = B.lib()
+    d = _dims()
+    W = B.Weights(**{f[0]: FAKE for f in B.Weights._fields_})
+    args = (C.byref(W), FAKE, FAKE, FAKE)
+    big = 33024
+    assert lib.r2l_layer_workspace_bytes(C.byref(d), B.R2L_BF16, big, 8, 4128) > (128 << 20)
+    assert lib.r2l_layer_fwd_noalloc(C.byref(d), B.R2L_BF16, 0, *args, 8, big, 4128, None, None) == B.R2L_ERR_WORKSPACE
+    assert lib.r2l_layer_fwd_noalloc(C.byref(d), B.R2L_BF16, B.R2L_FLAG_TRAIN, *args, 8, 256, 32, None,
+                                     None) == B.R2L_ERR_UNSUPPORTED
+    bad = _dims(N=8)
+    assert lib.r2l_layer_fwd_noalloc(C.byref(bad), B.R2L_BF16, 0, *args, 8, 256, 32, None, None) == \
+        B.R2L_ERR_INVALID_ARG
