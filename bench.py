@@ -69,9 +69,14 @@ def main():
     ap.add_argument("--summarize", nargs="+", metavar=("OUT_MD", "DIR"),
                     help="write a profile summary from rocprofv3 outputs instead of benchmarking: "
                          "OUT_MD TRACE_DIR [FETCH_DIR WRITE_DIR]")
+    ap.add_argument("--summarize-pmc", nargs="+", metavar=("OUT_MD", "DIR"),
+                    help="write a markdown summary of rocprofv3 --pmc runs (one DIR per counter pass) and exit")
     ap.add_argument("--summarize-args", default="",
                     help="with --summarize: the bench.py arguments of the profiled runs (for the header)")
     args = ap.parse_args()
+    if args.summarize_pmc:
+        summarize_pmc(args.summarize_pmc, args.summarize_args)
+        return
     if args.summarize:
         summarize_profiles(args.summarize, args.calib_mib * 1024.0, args.summarize_args)
         return
@@ -221,10 +226,12 @@ def main():
     kt = B.timing_read()
     B.timing_enable(False)
 
-    flops = {"in_proj_gemm": 2.0 * T * D * 2 * E, "out_proj_gemm": 2.0 * T * E * D}
+    Tf = fused_ln_rows(T, D, E)   # rows of the fused out_proj + LayerNorm kernel; the rest run unfused
+    flops = {"in_proj_gemm": 2.0 * T * D * 2 * E, "out_proj_gemm": 2.0 * (T - Tf) * E * D,
+             "out_proj_ln": 2.0 * Tf * E * D}
     bytes_ = {"conv_xproj": T * (2.0 * E + 4.0 * P),
               "scan_main": T * (2.0 * E + 2.0 * E + 4.0 * P + 2.0 * E),
-              "ln_gate": T * D * 8.0}
+              "ln_gate": (T - Tf) * D * 8.0}
     kernels = {}
     for name, (tot_ms, cnt) in kt.items():
         avg = tot_ms / max(cnt, 1)
@@ -414,8 +421,25 @@ def bench_backward(args):
     print(json.dumps(rec), flush=True)
 
 
+def fused_ln_rows(T, D, E):
+    """Token rows the library gives to its fused out_proj + LayerNorm kernel:
+    whole rounds of 256-row blocks over a grid of 8 x NT x c blocks (NT =
+    D / 256 column tiles per row block, at most one block per CU)."""
+    import torch
+    if D % 256 or E % 32:
+        return 0
+    ncu = torch.cuda.get_device_properties(0).multi_processor_count
+    nt = D // 256
+    grid = 8 * nt * (ncu // (8 * nt))
+    if grid <= 0:
+        return 0
+    rb_round = grid // nt
+    return ((T // 256) // rb_round) * rb_round * 256
+
+
 KERNEL_SOURCES = {  # the source file that defines each timed kernel
-    "in_proj_gemm": "gemm.hip", "out_proj_gemm": "gemm.hip", "conv_xproj": "conv.hip", "conv_sum": "conv.hip",
+    "in_proj_gemm": "gemm.hip", "out_proj_gemm": "gemm.hip", "out_proj_ln": "gemm.hip", "conv_xproj": "conv.hip",
+    "conv_sum": "conv.hip",
     "scan_main": "scan.hip", "scan_summary": "scan.hip", "ln_gate": "ln.hip", "plan_chunks": "scan.hip",
 }
 # The launches behind each timed label of the serving-shape forward, as
@@ -426,6 +450,7 @@ ROCPROF_NAMES = {
                      "gemm_small_reduce4_kernel<128, 128, false>"],
     "out_proj_gemm": ["gemm_bf16_big_kernel<true, 8, false>", "gemm_bf16_mid_kernel<true>",
                       "gemm_small_reduce4_kernel<128, 128, true>"],
+    "out_proj_ln": ["gemm_out_ln_kernel"],
     "conv_xproj": ["conv_xproj_sk_kernel<5, false>"], "conv_sum": ["sk_sum_kernel"],
     "scan_main": ["E, false, 4, false, false>(r2l::ScanArgs)"],
     "scan_summary": ["E, true, 4, false, false>(r2l::ScanArgs)"],
@@ -544,6 +569,61 @@ def summarize_profiles(argv, size_kib=0.0, bench_args=""):
             if not extra:
                 json.dump(rec, open(PROFILE_JSON, "w"), indent=1)
         lines.append("")
+    open(out_md, "w").write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def summarize_pmc(argv, bench_args=""):
+    """OUT_MD DIR...: per bench.py label, each counter averaged over the
+    label's dispatches (summed over its launches per step) from rocprofv3
+    --pmc runs, with the derived fractions: MFMA busy and VALU active per
+    SIMD against the shader clock (GRBM_GUI_ACTIVE counts cycles on each of
+    the 8 XCDs; the SQ counters count per wave, and ACTIVE / BUSY ones in
+    units of 4 cycles)."""
+    out_md, dirs = argv[0], argv[1:]
+    extra = (" " + bench_args.strip()) if bench_args.strip() else ""
+    lines = ["# Counter profile: " + os.path.basename(out_md), "",
+             "Commands (from the repository root, TMPDIR=/tmp; one counter pass per run):", ""]
+    counters = {}
+    for d in dirs:
+        names = sorted({r["Counter_Name"] for r in _rocprof_rows(d, "*counter_collection.csv")})
+        lines.append(f"    rocprofv3 --pmc {' '.join(names)} --output-format csv -d {d} -o run -- "
+                     "python -u bench.py --steps 2 --warmup 1 --no-cpu-baseline" + extra)
+        for r in _rocprof_rows(d, "*counter_collection.csv"):
+            for label, parts in ROCPROF_NAMES.items():
+                if any(p in r["Kernel_Name"] for p in parts):
+                    counters.setdefault(label, {}).setdefault(r["Counter_Name"], {}).setdefault(
+                        r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    lines += ["    python bench.py --summarize-pmc " + " ".join(argv) +
+              (f' --summarize-args="{bench_args.strip()}"' if extra else ""), ""]
+    names = sorted({c for lab in counters.values() for c in lab})
+    lines += ["## Counters per step (averaged over dispatches, summed over a label's launches)", "",
+              "| label | " + " | ".join(names) + " |", "|---|" + "---|" * len(names)]
+    per = {}
+    for label, cs in counters.items():
+        per[label] = {c: sum(sum(v) / len(v) for v in ks.values()) for c, ks in cs.items()}
+        lines.append(f"| {label} | " + " | ".join(f"{per[label].get(c, float('nan')):.4g}" for c in names) + " |")
+    lines += ["", "## Derived (per SIMD; 256 CUs x 4 SIMDs, 8 XCDs)", "",
+              "| label | clock cycles per XCD | MFMA busy | VALU active | LDS active | VALU instr per wave | "
+              "transcendental share |", "|---|---|---|---|---|---|---|"]
+    for label, c in per.items():
+        gui = c.get("GRBM_GUI_ACTIVE")
+        if not gui:
+            continue
+        cyc = gui / 8.0
+        mfma = c.get("SQ_VALU_MFMA_BUSY_CYCLES")
+        valu = c.get("SQ_ACTIVE_INST_VALU")
+        lds = c.get("SQ_ACTIVE_INST_LDS")
+        waves = c.get("SQ_WAVES")
+        vi = c.get("SQ_INSTS_VALU")
+        tr = c.get("SQ_INSTS_VALU_TRANS_F32")
+
+        def frac(x, scale):
+            return f"{x * scale / 1024.0 / cyc:.3f}" if x is not None else "-"
+        lines.append(f"| {label} | {cyc:.4g} | {frac(mfma, 1.0)} | {frac(valu, 4.0)} | {frac(lds, 4.0)} | "
+                     f"{(vi / waves) if (vi and waves) else float('nan'):.0f} | "
+                     f"{(tr / vi) if (tr and vi) else float('nan'):.3f} |")
+    lines.append("")
     open(out_md, "w").write("\n".join(lines) + "\n")
     print("\n".join(lines))
 

@@ -223,8 +223,8 @@ ScanBwdPlan plan_scan_bwd(int E, int64_t T, int32_t nseq) {
 constexpr size_t kSplitScratch = 256ull * 256 * 256 * sizeof(float);
 
 struct LayerPlan {
-  size_t off_xz, off_xdbl, off_xdbl2, off_xdbl3, off_dsplit, off_u, off_y, off_scratch, off_o;
-  bool need_u;
+  size_t off_xz, off_xdbl, off_xdbl2, off_xdbl3, off_dsplit, off_u, off_y, off_scratch, off_o, off_lnst, off_lncnt;
+  bool need_u, fuse_ln;   // fuse_ln: out_proj may run fused with the LayerNorm and the gated residual
   ScanPlan scan;
   size_t total;
 };
@@ -252,6 +252,15 @@ LayerPlan plan_layer(const r2l_dims* d, r2l_dtype act, int64_t T, int32_t nseq, 
   p.off_u = off;    off = align_up(off + (p.need_u ? Tz * E * sa : 0));
   p.off_y = off;    off = align_up(off + Tz * E * sa);
   p.off_scratch = off; off = align_up(off + (act == R2L_BF16 ? kSplitScratch : 0));
+  // the fused out_proj + LayerNorm (bf16; in training mode it also stores
+  // out_proj's output for the backward): per-row partial statistics of
+  // every row block's column tiles, and one counter per row block (sized
+  // for every whole row block, whatever the device; the launch plan is made
+  // per call from the device's compute units)
+  p.fuse_ln = act == R2L_BF16 && D % 256 == 0;
+  const size_t rbmax = p.fuse_ln ? Tz / 256 : 0;
+  p.off_lnst = off;  off = align_up(off + rbmax * D * 8);
+  p.off_lncnt = off; off = align_up(off + rbmax * sizeof(int));
   p.scan = plan_scan((int)E, T, nseq, max_seqlen, off);
   p.total = p.scan.total;
   return p;
@@ -685,8 +694,12 @@ int r2l_layer_fwd(const r2l_dims* d, r2l_dtype act, uint32_t flags, const r2l_we
   a.sumP = at<float>(workspace, sp.off_sumP);
   a.l2r = l2r;
 
-  // chunk table first: the conv kernel also reads the sanitised offsets
-  R2L_RUN("plan_chunks", st, plan_chunks(cu_seqlens, nseq, T, sp.Lc, sp.max_chunks, l2r, cu_clean, chunks, nch, st));
+  // chunk table first: the conv kernel also reads the sanitised offsets (and
+  // the fused out_proj's counters start at zero)
+  const OutLnPlan oln = lp.fuse_ln ? plan_out_ln(T, D, E, num_cus()) : OutLnPlan{};
+  int* lncnt = at<int>(workspace, lp.off_lncnt);
+  R2L_RUN("plan_chunks", st, plan_chunks(cu_seqlens, nseq, T, sp.Lc, sp.max_chunks, l2r, cu_clean, chunks, nch, st,
+                                         lncnt, oln.row_blocks));
 
   if (act == R2L_BF16) {
     bf16* xz = at<bf16>(workspace, lp.off_xz);
@@ -718,11 +731,26 @@ int r2l_layer_fwd(const r2l_dims* d, r2l_dtype act, uint32_t flags, const r2l_we
     a.x = xz; a.z = xz + E; a.y = y; a.dsplit = dsplit;
     if (sp.summary) R2L_RUN("scan_summary", st, scan_summary<bf16>(a, true, st));
     R2L_RUN("scan_main", st, scan_main<bf16>(a, true, st));
-    // o stays fp32: rounding it to bf16 before the LayerNorm would add up to
-    // half a bf16 step of |o| / std(o) to r at the rows' extremes
-    R2L_RUN("out_proj_gemm", st, gemm_bf16_nt(T, D, E, y, E, (const bf16*)w->out_proj_w, E, o, D, true, st,
-                                              scratch, kSplitScratch, ncu));
-    R2L_RUN("ln_gate", st, (ln_gate<bf16, float>(T, D, o, (const bf16*)h_in, (bf16*)h_out, w->ln_w, w->ln_b, w->s, branch_out, no_ln, R2L_LN_EPS, st)));
+    // out_proj, the LayerNorm and the gated residual in one kernel over
+    // whole rounds of row blocks; o stays in registers (fp32: rounding it to
+    // bf16 before the LayerNorm would add up to half a bf16 step of
+    // |o| / std(o) to r at the rows' extremes)
+    const int Tf = oln.rows;
+    if (Tf > 0)
+      R2L_RUN("out_proj_ln", st, gemm_out_ln(oln, E, y, E, (const bf16*)w->out_proj_w, E, (const bf16*)h_in,
+                                             (bf16*)h_out, D, w->ln_w, w->ln_b, w->s, branch_out,
+                                             (flags & R2L_FLAG_TRAIN) ? o : nullptr, no_ln, R2L_LN_EPS,
+                                             at<unsigned long long>(workspace, lp.off_lnst), lncnt, st));
+    // the remaining rows: out_proj into o (fp32, at its rows: the backward
+    // reads all of o in training mode), then the LayerNorm kernel
+    if (Tf < T) {
+      const long r0 = Tf;
+      R2L_RUN("out_proj_gemm", st, gemm_bf16_nt(T - Tf, D, E, y + r0 * E, E, (const bf16*)w->out_proj_w, E,
+                                                o + r0 * D, D, true, st, scratch, kSplitScratch, ncu));
+      R2L_RUN("ln_gate", st, (ln_gate<bf16, float>(T - Tf, D, o + r0 * D, (const bf16*)h_in + r0 * D, (bf16*)h_out + r0 * D,
+                                                    w->ln_w, w->ln_b, w->s, branch_out ? branch_out + r0 * D : nullptr,
+                                                    no_ln, R2L_LN_EPS, st)));
+    }
   } else {
     float* xz = at<float>(workspace, lp.off_xz);
     float* u = at<float>(workspace, lp.off_u);

@@ -182,6 +182,7 @@ constexpr int kBigSBYTES = (kBigBM + kBigBN) * kBigSROW;
 constexpr int kBigSH = 2;                      // swizzle: chunk ^= (row >> 2) & 3
 
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 // s_waitcnt immediate that waits for vmcnt <= n and leaves the other counters alone
 constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
@@ -411,6 +412,364 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(int M, int N, int
       }
     }
     if (pass + 1 < BM / RPP) __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------------------
+// out_proj with the stream LayerNorm and the tanh(s)-gated residual in its
+// epilogue ("Bifocal Diffusion Language Models", §3.4 steps 3-4):
+//   o = y W_out^T,  r = gamma (.) (o - mean) / sqrt(var + eps) + beta,
+//   h_out = h_in + tanh(s) r   (h_in copied bit for bit when tanh(s) == 0),
+// mean and var over each token's d_model outputs.  o never leaves the
+// registers: a token row spans the NT = d_model / 256 column tiles of its
+// 256-row block, so the NT tiles of a row block run at the same time on NT
+// blocks of one XCD and exchange per-row partial statistics.
+//
+// Persistent grid of G = 8 x NT x c blocks (at most one per CU, all resident
+// together): block b on XCD b % 8 owns column tile (b / 8) % NT of row block
+// (round x G / NT) + (b % 8) (G / 8 / NT) + (b / 8) / NT in every round.
+// Each tile runs the big kernel's K loop (256 x 256 tile, four 32-deep LDS
+// stages filled by buffer_load ... lds), then:
+//  1. per row, the tile's mean and centred sum of squares (M2) over its 256
+//     columns, from the accumulators (lane pairs by a shuffle, wave pairs
+//     through LDS, always in the same order);
+//  2. publishes them with agent-scope atomic stores, waits for those stores,
+//     and adds 1 to the row block's counter (an agent-scope atomic, zeroed by
+//     the layer's first kernel); one thread polls the counter until all NT
+//     tiles have published, with a bounded number of sleeps (past it the
+//     tile writes NaN, so a scheduling failure can never hang the GPU or go
+//     unnoticed);
+//  3. combines the NT partials of its rows in tile order (Chan's pairwise
+//     mean/M2 update: the same result on every tile, whatever the timing);
+//  4. stages its h tile in LDS with whole-row loads, normalises the
+//     accumulators, adds the gated branch, and writes h_out with whole-row
+//     stores (and the branch r, when asked for, from the registers).
+// NO_LN: r = o, no statistics or exchange.
+// ---------------------------------------------------------------------------
+struct OutLnArgs {
+  int K;                         // d_inner (a multiple of 32)
+  const bf16* A; long lda;       // y [M, K]
+  const bf16* B; long ldb;       // W_out [N, K], N = NT x 256
+  const bf16* h; bf16* out; long ldh;   // h_in, h_out [M, N] (may alias)
+  const float* gamma; const float* beta; const float* s;
+  float* branch;                 // optional fp32 [M, ldh]
+  float* o_save;                 // optional fp32 [M, ldh]: the out_proj output itself (training)
+  float eps;
+  unsigned long long* stats;     // [row blocks][NT][256]: (mean, M2) per tile row as two fp32
+  int* cnt;                      // [row blocks], zero on entry
+  int nt, rounds;
+};
+constexpr int kOutLnSpins = 1 << 24;
+
+// EXTRA: also the optional fp32 outputs (branch, o_save); the plain forward
+// runs the instance without them, which keeps its registers for the K loop.
+template <bool NO_LN, bool EXTRA>
+__global__ __launch_bounds__(256, 1) void gemm_out_ln_kernel(OutLnArgs a) {
+  constexpr int BM = kBigBM, BN = kBigBN, BK = kBigBK, ST = kBigST, LPT = kBigLPT, SROW = kBigSROW;
+  __shared__ __attribute__((aligned(1024))) char s0[kBigSBYTES];
+  __shared__ __attribute__((aligned(1024))) char s1[kBigSBYTES];
+  __shared__ __attribute__((aligned(1024))) char s2[kBigSBYTES];
+  __shared__ __attribute__((aligned(1024))) char s3[kBigSBYTES];
+  __shared__ float red[4][4][32];      // [wave][i][row]: per-wave row sums
+  __shared__ float2 rstat[BM];         // (mean, 1 / std) of the tile's rows
+  __shared__ __attribute__((aligned(16))) float gb_s[2][BN];   // gamma, beta of this block's columns
+  __shared__ int okflag;
+  auto stage = [&](int s) -> char* { return s == 0 ? s0 : s == 1 ? s1 : s == 2 ? s2 : s3; };
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
+  const int wm0 = (wave >> 1) * 128, wn0 = (wave & 1) * 128;
+  const int fr0 = lane & 31, fh0 = lane >> 5;
+  const int NT = a.nt, G = gridDim.x, per_xcd = G >> 3;
+  const int xcd = blockIdx.x & 7, pos = blockIdx.x >> 3;
+  const int rb0 = xcd * (per_xcd / NT) + pos / NT, ct = pos % NT;
+  const int n0 = ct * BN;
+  const float tg = tanhf(a.s[0]);
+  if constexpr (!NO_LN) {   // the block's column tile is the same in every round
+    gb_s[0][tid] = a.gamma[n0 + tid];
+    gb_s[1][tid] = a.beta[n0 + tid];
+  }
+  // the row statistics of all blocks, read with the agent-coherent cache
+  // policy (as the atomic stores that wrote them) but as plain loads, so
+  // that a thread's NT loads are in flight together
+  const __amdgpu_buffer_rsrc_t rS = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)a.stats, 0, 0x7fffffff, 0x00020000);
+
+  unsigned voff[LPT];
+#pragma unroll
+  for (int i = 0; i < LPT; ++i) {
+    const int p = i * 256 + tid, row = p / kBigCPR;
+    const int kc = big_swz(row, p % kBigCPR);
+    voff[i] = i < LPT / 2 ? (unsigned)(((long)row * a.lda + kc * 8) * 2)
+                          : (unsigned)(((long)(row - BM) * a.ldb + kc * 8) * 2);
+  }
+  const int nk = a.K / BK;
+  const __amdgpu_buffer_rsrc_t rB = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(a.B + (long)n0 * a.ldb), 0, (int)((long)BN * a.ldb * 2), 0x00020000);
+  int offA0[4], offB0[4], offA1[4], offB1[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int ra = wm0 + 32 * i + fr0, rbr = BM + wn0 + 32 * i + fr0;
+    offA0[i] = ra * SROW + big_swz(ra, fh0) * 16;
+    offB0[i] = rbr * SROW + big_swz(rbr, fh0) * 16;
+    offA1[i] = ra * SROW + big_swz(ra, 2 + fh0) * 16;
+    offB1[i] = rbr * SROW + big_swz(rbr, 2 + fh0) * 16;
+  }
+
+  for (int rd = 0; rd < a.rounds; ++rd) {
+    const int rbk = rd * (G / NT) + rb0;
+    const long m0 = (long)rbk * BM;
+    const __amdgpu_buffer_rsrc_t rA = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(a.A + m0 * a.lda), 0, (int)((long)BM * a.lda * 2), 0x00020000);
+    auto issue = [&](int s, int kt) {  // k-step kt -> stage s (past the end: reload the last step)
+      char* base = stage(s);
+      const unsigned kb = (unsigned)(min(kt, nk - 1) * BK * 2);
+#pragma unroll
+      for (int i = 0; i < LPT; ++i)
+        lds_dma16(i < LPT / 2 ? rA : rB, base + (i * 256 + wave * 64) * 16, voff[i], kb);
+    };
+    bf16x8 fa0[4], fb0[4], fa1[4], fb1[4];
+    auto rd0 = [&](const char* base) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        fa0[i] = *(const bf16x8*)(base + offA0[i]);
+        fb0[i] = *(const bf16x8*)(base + offB0[i]);
+      }
+    };
+    auto rd1 = [&](const char* base) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        fa1[i] = *(const bf16x8*)(base + offA1[i]);
+        fb1[i] = *(const bf16x8*)(base + offB1[i]);
+      }
+    };
+    f32x16 acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+    // ---------------- the K loop (as gemm_bf16_big_kernel) ----------------
+    issue(0, 0);
+    issue(1, 1);
+    issue(2, 2);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * LPT));
+    asm volatile("s_barrier" ::: "memory");
+    rd0(s0);
+    for (int kt0 = 0; kt0 < nk; kt0 += ST) {
+#pragma unroll
+      for (int s = 0; s < ST; ++s) {
+        const int kt = kt0 + s;
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(LPT));
+        asm volatile("s_barrier" ::: "memory");
+        issue((s + ST - 1) % ST, kt + ST - 1);
+        rd1(stage(s));
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb0[j], fa0[i], acc[i][j], 0, 0, 0);
+#pragma unroll
+        for (int q = 0; q < LPT; ++q) {
+          __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        }
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        }
+        rd0(stage((s + 1) % ST));
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb1[j], fa1[i], acc[i][j], 0, 0, 0);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        }
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    asm volatile("s_barrier" ::: "memory");   // every wave is done with the stages
+    __builtin_amdgcn_sched_barrier(0);
+    // acc[i][j] register 4q+e: row wm+32i+fr, column wn+32j+8q+4fh+e of the tile.
+    // The epilogue forms its addresses from opaque copies of the lane
+    // coordinates, so that none of them is hoisted out of the round loop
+    // (they would stay live across the K loop and push it into spilling).
+    int fr = fr0, fh = fh0, wm = wm0, wn = wn0;
+    asm volatile("" : "+v"(fr), "+v"(fh), "+v"(wm), "+v"(wn));
+
+    // ---------------- 1-3: row statistics over all NT tiles ----------------
+    if constexpr (!NO_LN) {
+      float mean[4], part[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float sm = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) sm += acc[i][j][r];
+        part[i] = sm + __shfl_xor(sm, 32, 64);
+      }
+      if (lane < 32)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) red[wave][i][lane] = part[i];
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < 4; ++i) mean[i] = (red[wave & 2][i][fr] + red[(wave & 2) | 1][i][fr]) * (1.0f / BN);
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float sq = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const float d = acc[i][j][r] - mean[i];
+            sq = fmaf(d, d, sq);
+          }
+        part[i] = sq + __shfl_xor(sq, 32, 64);
+      }
+      if (lane < 32)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) red[wave][i][lane] = part[i];
+      __syncthreads();
+      unsigned long long* my = a.stats + ((size_t)rbk * NT + ct) * BM;
+      if ((wave & 1) == 0 && lane < 32)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float m2 = red[wave][i][lane] + red[wave | 1][i][lane];
+          const unsigned long long v = (unsigned long long)__builtin_bit_cast(unsigned, mean[i]) |
+                                       ((unsigned long long)__builtin_bit_cast(unsigned, m2) << 32);
+          __hip_atomic_store(my + wm + 32 * i + lane, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+      __builtin_amdgcn_s_waitcnt(0);   // this thread's statistics have reached memory
+      __syncthreads();
+      if (tid == 0) {
+        __hip_atomic_fetch_add(a.cnt + rbk, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        int spins = 0;
+        while (__hip_atomic_load(a.cnt + rbk, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < NT &&
+               ++spins < kOutLnSpins)
+          __builtin_amdgcn_s_sleep(2);
+        okflag = spins < kOutLnSpins;
+      }
+      __syncthreads();
+      {
+        // thread t combines the NT partials of tile row t in tile order
+        const unsigned base = (unsigned)((size_t)rbk * NT * BM + tid) * 8u;
+        float mu = 0.0f, m2 = 0.0f, n = 0.0f;
+        for (int k0 = 0; k0 < NT; k0 += 8) {
+          unsigned long long v[8];
+#pragma unroll
+          for (int k = 0; k < 8; ++k)
+            v[k] = k0 + k < NT ? __builtin_bit_cast(unsigned long long, __builtin_amdgcn_raw_buffer_load_b64(
+                                     rS, base + (unsigned)((k0 + k) * BM * 8), 0, 16))
+                               : 0ull;
+#pragma unroll
+          for (int k = 0; k < 8; ++k) {
+            if (k0 + k >= NT) break;
+            const float mk = __builtin_bit_cast(float, (unsigned)v[k]);
+            const float qk = __builtin_bit_cast(float, (unsigned)(v[k] >> 32));
+            if (k0 + k == 0) {
+              mu = mk;
+              m2 = qk;
+            } else {
+              // Chan's update for two sets of n and BN values
+              const float d = mk - mu, f = (float)BN / (n + BN);
+              mu = fmaf(d, f, mu);
+              m2 = m2 + qk + d * d * n * f;
+            }
+            n += BN;
+          }
+        }
+        const float rstd = 1.0f / sqrtf(m2 / n + a.eps);
+        rstat[tid] = okflag ? make_float2(mu, rstd) : make_float2(__builtin_nanf(""), __builtin_nanf(""));
+      }
+    }
+    // ---------------- 4: h tile in LDS (row rr at stage rr / 64, 16-byte chunk c at c ^ (rr & 31)) --------
+    const __amdgpu_buffer_rsrc_t rH = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(a.h + m0 * a.ldh + n0), 0, (int)((long)BM * a.ldh * 2), 0x00020000);
+#pragma unroll
+    for (int k = 0; k < 32; ++k) {
+      const int rr = 64 * wave + 2 * k + fh;
+      const unsigned c = (unsigned)(fr ^ (rr & 31));
+      lds_dma16(rH, stage(wave) + (2 * k) * 512, (unsigned)(rr * a.ldh * 2) + c * 16u, 0);
+    }
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    __syncthreads();
+    // r from the accumulators; h_out = h + tanh(s) r back into the h tile
+    // (a zero gate leaves the tile as loaded); the branch, when asked for,
+    // straight from the registers
+    auto branch_at = [&](int i, int j, int q) -> f32x4 {
+      const int cl = wn + 32 * j + 8 * q + 4 * fh, row = wm + 32 * i + fr;
+      f32x4 rv;
+      if constexpr (NO_LN) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) rv[e] = acc[i][j][4 * q + e];
+      } else {
+        const float2 st = rstat[row];
+        const f32x4 gm = *(const f32x4*)&gb_s[0][cl], bt = *(const f32x4*)&gb_s[1][cl];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) rv[e] = fmaf(gm[e], (acc[i][j][4 * q + e] - st.x) * st.y, bt[e]);
+      }
+      return rv;
+    };
+    auto h_at = [&](int i, int j, int q) -> char* {
+      const int cl = wn + 32 * j + 8 * q + 4 * fh, row = wm + 32 * i + fr;
+      return stage(row >> 6) + (row & 63) * 512 + (((cl >> 3) ^ (row & 31)) << 4) + (fh << 3);
+    };
+    if (tg != 0.0f) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const f32x4 rv = branch_at(i, j, q);
+            char* p = h_at(i, j, q);
+            const bf16x4 hv = *(const bf16x4*)p;
+            bf16x4 ov;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) ov[e] = (bf16)fmaf(tg, rv[e], (float)hv[e]);
+            *(bf16x4*)p = ov;
+          }
+    }
+    if (EXTRA && a.branch != nullptr) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int cl = wn + 32 * j + 8 * q + 4 * fh, row = wm + 32 * i + fr;
+            *(f32x4*)(a.branch + (m0 + row) * a.ldh + n0 + cl) = branch_at(i, j, q);
+          }
+    }
+    if (EXTRA && a.o_save != nullptr) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int cl = wn + 32 * j + 8 * q + 4 * fh, row = wm + 32 * i + fr;
+            *(f32x4*)(a.o_save + (m0 + row) * a.ldh + n0 + cl) =
+                f32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+          }
+    }
+    __syncthreads();
+    // h_out rows from LDS, whole rows per store
+    const __amdgpu_buffer_rsrc_t rO = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(a.out + m0 * a.ldh + n0), 0, (int)((long)BM * a.ldh * 2), 0x00020000);
+#pragma unroll
+    for (int k = 0; k < 32; ++k) {
+      const int rr = 64 * wave + 2 * k + fh;
+      const unsigned c = (unsigned)(fr ^ (rr & 31));
+      const u32x4 v = *(const u32x4*)(stage(wave) + (2 * k) * 512 + lane * 16);
+      __builtin_amdgcn_raw_buffer_store_b128(v, rO, (unsigned)(rr * a.ldh * 2) + c * 16u, 0, 0);
+    }
+    __syncthreads();   // the stages are refilled by the next tile
   }
 }
 
@@ -970,6 +1329,48 @@ static void launch_big(int M, int N, int K, const bf16* A, long lda, const bf16*
       hipLaunchKernelGGL((gemm_tail_reduce_kernel<false, G>), dim3(rem * (kBigBM / 4)), dim3(256), 0, st, M,
                          N, n_dp, splits, (const float*)ws, C, ldc);
   }
+}
+
+OutLnPlan plan_out_ln(int T, int D, int K, int ncu) {
+  OutLnPlan p{};
+  if (D % kBigBN || K % kBigBK || ncu <= 0) return p;
+  const int nt = D / kBigBN;
+  const int grid = 8 * nt * (ncu / (8 * nt));   // whole row blocks on every XCD, at most one block per CU
+  if (grid <= 0) return p;
+  const int rb_round = grid / nt;
+  const int rounds = (T / kBigBM) / rb_round;
+  if (rounds < 1 || (long)kBigBM * K * 2 >= (1L << 31) || (long)kBigBM * D * 2 >= (1L << 31)) return p;
+  p.nt = nt;
+  p.grid = grid;
+  p.rounds = rounds;
+  p.rows = rounds * rb_round * kBigBM;
+  p.row_blocks = rounds * rb_round;
+  return p;
+}
+
+hipError_t gemm_out_ln(const OutLnPlan& p, int K, const bf16* y, long ldy, const bf16* W, long ldw, const bf16* h,
+                       bf16* out, long ldh, const float* gamma, const float* beta, const float* s, float* branch,
+                       float* o_save, bool no_ln, float eps, unsigned long long* stats, int* cnt, hipStream_t st) {
+  if (p.rows <= 0) return hipSuccess;
+  OutLnArgs a{};
+  a.K = K;
+  a.A = y; a.lda = ldy;
+  a.B = W; a.ldb = ldw;
+  a.h = h; a.out = out; a.ldh = ldh;
+  a.gamma = gamma; a.beta = beta; a.s = s; a.branch = branch; a.o_save = o_save; a.eps = eps;
+  a.stats = stats; a.cnt = cnt;
+  a.nt = p.nt;
+  a.rounds = p.rounds;
+  const bool extra = branch != nullptr || o_save != nullptr;
+  if (no_ln && extra)
+    hipLaunchKernelGGL((gemm_out_ln_kernel<true, true>), dim3(p.grid), dim3(256), 0, st, a);
+  else if (no_ln)
+    hipLaunchKernelGGL((gemm_out_ln_kernel<true, false>), dim3(p.grid), dim3(256), 0, st, a);
+  else if (extra)
+    hipLaunchKernelGGL((gemm_out_ln_kernel<false, true>), dim3(p.grid), dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL((gemm_out_ln_kernel<false, false>), dim3(p.grid), dim3(256), 0, st, a);
+  return hipGetLastError();
 }
 
 hipError_t gemm_bf16_nt(int M, int N, int K, const bf16* A, long lda, const bf16* B, long ldb,

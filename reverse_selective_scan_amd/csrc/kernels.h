@@ -15,6 +15,19 @@ namespace r2l {
 hipError_t gemm_bf16_nt(int M, int N, int K, const bf16* A, long lda, const bf16* B, long ldb,
                         void* C, long ldc, bool out_f32, hipStream_t st, float* ws = nullptr,
                         size_t ws_bytes = 0, int ncu = 0);
+// out_proj fused with the stream LayerNorm and the gated residual (bf16):
+// h_out = h + tanh(s) LN(y W^T) for the first `rows` token rows, which the
+// plan makes whole rounds of 256-row blocks over a persistent grid (rows = 0:
+// the shape does not fit and the caller runs out_proj and ln_gate instead).
+// stats: row_blocks * nt * 256 * 8 bytes; cnt: row_blocks ints, zero on entry.
+// o_save (optional, fp32 [rows, ldh]): the out_proj output itself (training).
+struct OutLnPlan {
+  int nt, grid, rounds, rows, row_blocks;
+};
+OutLnPlan plan_out_ln(int T, int D, int K, int ncu);
+hipError_t gemm_out_ln(const OutLnPlan& p, int K, const bf16* y, long ldy, const bf16* W, long ldw, const bf16* h,
+                       bf16* out, long ldh, const float* gamma, const float* beta, const float* s, float* branch,
+                       float* o_save, bool no_ln, float eps, unsigned long long* stats, int* cnt, hipStream_t st);
 // fp32 inputs on the VALU; output f32.
 hipError_t gemm_f32_nt(int M, int N, int K, const float* A, long lda, const float* B, long ldb,
                        float* C, long ldc, hipStream_t st);
@@ -61,8 +74,10 @@ hipError_t split_delta(int T_, int P, int R, const float* xdbl, bf16* dsplit, hi
 
 // Chunk planning for the scan: sanitised cu_seqlens and the chunk table
 // (chunks cut from the end the scan starts at).
+// zero (optional): n_zero ints cleared on the way (counters of later kernels).
 hipError_t plan_chunks(const int32_t* cu, int nseq, int T_, int Lc, int max_chunks, bool l2r,
-                       int32_t* cu_clean, ChunkDesc* chunks, int32_t* n_chunks, hipStream_t st);
+                       int32_t* cu_clean, ChunkDesc* chunks, int32_t* n_chunks, hipStream_t st,
+                       int* zero = nullptr, int n_zero = 0);
 
 struct ScanArgs {
   int T, E, R, ldp;            // ldp: row stride of xdbl (fused) in floats

@@ -61,9 +61,11 @@ __global__ __launch_bounds__(256) void plan_chunks_kernel(const int32_t* __restr
                                                           int Tn, int Lc, int max_chunks, int l2r,
                                                           int32_t* __restrict__ cu_clean,
                                                           ChunkDesc* __restrict__ chunks,
-                                                          int32_t* __restrict__ n_chunks) {
+                                                          int32_t* __restrict__ n_chunks,
+                                                          int* __restrict__ zero, int n_zero) {
   __shared__ int s_v[256];
   const int tid = threadIdx.x;
+  for (int i = tid; i < n_zero; i += 256) zero[i] = 0;
   const int n1 = nseq + 1;
   const int per = (n1 + 255) / 256;
   const int qa = min(tid * per, n1), qb = min(qa + per, n1);
@@ -119,9 +121,10 @@ __global__ __launch_bounds__(256) void plan_chunks_kernel(const int32_t* __restr
 }
 
 hipError_t plan_chunks(const int32_t* cu, int nseq, int Tn, int Lc, int max_chunks, bool l2r,
-                       int32_t* cu_clean, ChunkDesc* chunks, int32_t* n_chunks, hipStream_t st) {
+                       int32_t* cu_clean, ChunkDesc* chunks, int32_t* n_chunks, hipStream_t st, int* zero,
+                       int n_zero) {
   hipLaunchKernelGGL(plan_chunks_kernel, dim3(1), dim3(256), 0, st, cu, nseq, Tn, Lc, max_chunks,
-                     l2r ? 1 : 0, cu_clean, chunks, n_chunks);
+                     l2r ? 1 : 0, cu_clean, chunks, n_chunks, zero, zero ? n_zero : 0);
   return hipGetLastError();
 }
 
@@ -339,7 +342,7 @@ __global__ __launch_bounds__(256, KS > 4 ? 1 : 2) void scan_kernel(ScanArgs a) {
   const long lddt_b = a.ld_dt * 4, ldbc_b = a.ld_bc * 4;
   const long ldy_b = (long)E * SZ;
   const void* zin = a.z;
-  const bool has_z = zin != nullptr;
+  const bool has_z = FUSED || zin != nullptr;   // the layer always gates
   const unsigned offX = (unsigned)(r8 * ldx_b) + (unsigned)ea * SZ;
   const unsigned offZ = (unsigned)(r8 * ldz_b) + (unsigned)ea * SZ;
   const unsigned offY = (unsigned)(r8 * ldy_b) + (unsigned)ea * SZ;

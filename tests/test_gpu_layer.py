@@ -126,6 +126,39 @@ def test_small_bf16_dt_rank_paths_match_oracle(dt_rank):
     check_bf16("branch", gr, rref, fr, TOL_BF16_BRANCH)
 
 
+def test_fused_out_proj_layernorm_path_matches_oracle():
+    """d_model 512: the fused out_proj + LayerNorm + gated residual kernel
+    runs with two column tiles per 256-row block (on 256 compute units:
+    128 row blocks per round).  33,308 tokens = one fused round of 32,768
+    rows plus 540 rows on the unfused path (out_proj, then the LayerNorm
+    kernel), across which sequences run.  Affine LayerNorm and the branch r,
+    without the LayerNorm, and s = 0 (an exact copy)."""
+    lens = [20000, 7, 13000, 1, 300]
+    _case(f"fused out_proj + LN path lens={lens}")
+    wl = synth.custom(lens, seed=33, h_kind="rms", d_model=512, d_inner=1024, dt_rank=32)
+    W = synth.make_weights(wl, affine_ln=True)
+    h, cu = synth.make_hidden(wl), wl.cu_seqlens()
+    s = float(W["s"])
+    B.timing_reset()
+    B.timing_enable(True)
+    g, gr = _gpu_layer(wl, W, h, cu, branch=True)
+    names = B.timing_read()
+    B.timing_enable(False)
+    print(f"kernels: {sorted(names)}", flush=True)
+    ref, rref = O.reverse_mamba_layer(h, cu, W, s, return_branch=True)
+    fo, fr = bf16_floor.layer_rounded(h, cu, W, s)
+    check_bf16("fused out", g, ref, fo, TOL_BF16)
+    check_bf16("fused branch", gr, rref, fr, TOL_BF16_BRANCH)
+    ref, _ = O.reverse_mamba_layer(h, cu, W, s, use_ln=False, return_branch=True)
+    fo, _ = bf16_floor.layer_rounded(h, cu, W, s, use_ln=False)
+    g2, _ = _gpu_layer(wl, W, h, cu, flags=B.R2L_FLAG_NO_LN)
+    check_bf16("fused out no-ln", g2, ref, fo, TOL_BF16)
+    g0, _ = _gpu_layer(wl, W, h, cu, s=0.0)
+    assert np.array_equal(g0.astype(np.float32).view(np.uint32), h.view(np.uint32))
+    if torch.cuda.get_device_properties(0).multi_processor_count == 256:
+        assert "out_proj_ln" in names and "ln_gate" in names, names
+
+
 @pytest.mark.parametrize("hint", ["too_small", "too_large"])
 def test_max_seqlen_hint_does_not_change_results(hint):
     """max_seqlen only plans the scan's time chunks: a value below the true
