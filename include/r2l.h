@@ -86,7 +86,11 @@ enum {
 /* LayerNorm epsilon used by r2l_layer_fwd (biased variance over d_model). */
 #define R2L_LN_EPS 1e-5f
 
-typedef enum { R2L_F32 = 0, R2L_BF16 = 1 } r2l_dtype;
+/* Activation dtypes, the values of an r2l_dtype argument.  r2l_dtype is a
+ * plain 32-bit integer (the size of an enum in this ABI) so that every
+ * value a caller passes can be checked: any other value is rejected. */
+enum { R2L_F32 = 0, R2L_BF16 = 1 };
+typedef int32_t r2l_dtype;
 
 /* Layer dimensions: D = d_model, E = d_inner (expand * D), N = d_state,
  * R = dt_rank, K = d_conv. */

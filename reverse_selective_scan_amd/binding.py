@@ -15,7 +15,9 @@ import numpy as np
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libr2l.so")
+# R2L_LIB overrides the library file (the host-sanitizer test loads its
+# instrumented build this way); the default is the in-tree libr2l.so
+LIB_PATH = os.environ.get("R2L_LIB") or os.path.join(_PKG, "libr2l.so")
 
 R2L_OK, R2L_ERR_INVALID_ARG, R2L_ERR_UNSUPPORTED, R2L_ERR_WORKSPACE, R2L_ERR_HIP = 0, -1, -2, -3, -4
 R2L_F32, R2L_BF16 = 0, 1
