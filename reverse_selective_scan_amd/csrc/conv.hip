@@ -368,8 +368,9 @@ hipError_t conv_xproj_bf16(int Tn, int E, int P, const bf16* x, long ld_x, const
 // copy of each W_x slice (and the conv taps) per block serves 128 tokens.
 // Every operand of a step is copied global -> LDS by buffer_load ... lds
 // into a ring of RS stages (rows past the token count read as zero through
-// the buffer descriptor's range); the barrier of step q waits for step q+1,
-// and loads run RS - 2 steps ahead.  x and W_x stage rows are 64 bytes with the
+// the buffer descriptor's range).  A step reads its own stage only, so the
+// barrier of step q waits for step q's copies alone: each copy has RS - 1
+// steps to land.  x and W_x stage rows are 64 bytes with the
 // 16-byte chunk index XOR-ed by (row >> 2) & 3 against bank conflicts.
 // Lanes compute their own MFMA A-fragments (token lane & 31, 8 channels) as
 // in conv_xproj_kernel.
@@ -616,10 +617,12 @@ __global__ __launch_bounds__(256, SkGeo<NCS>::BPC) void conv_xproj_sk_kernel(int
   for (int i0 = 0; i0 < n; i0 += RS) {
 #pragma unroll
     for (int s = 0; s < RS; ++s) {
-      // own copies of step q+1 done (later steps may fly); after the barrier
-      // everyone's are, and every wave is done with the stage of step q-1,
-      // which receives the copies of step q+RS-1
-      __builtin_amdgcn_s_waitcnt(sk_vmcnt((RS - 3) * PW));
+      // own copies of step q done (those of steps q+1 .. q+RS-2 may fly: the
+      // copies complete in order, and partial-sum stores issued between them
+      // can only make this wait longer); after the barrier everyone's are,
+      // and every wave is done with the stage of step q-1, which receives
+      // the copies of step q+RS-1
+      __builtin_amdgcn_s_waitcnt(sk_vmcnt((RS - 2) * PW));
       asm volatile("s_barrier" ::: "memory");
       issue((s + RS - 1) % RS);
       if (i0 + s < n) compute(stage(s));
