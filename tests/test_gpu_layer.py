@@ -89,16 +89,18 @@ def test_small_bf16_varlen_matches_oracle(lens, affine):
     check_bf16("branch", gr, rref, fr, TOL_BF16_BRANCH)
 
 
-def test_bf16_split_k_conv_path_matches_oracle():
+@pytest.mark.parametrize("dt_rank", [5, 192])
+def test_bf16_split_k_conv_path_matches_oracle(dt_rank):
     """More than 256 tiles of 128 tokens: the conv + x_proj step runs split
-    along K over one block per CU (tiles cut between two blocks, partial sums
-    added afterwards); odd x_proj width (R = 5, P = 37) and sequences of 1
-    and 7 tokens inside split tiles.  (At d_model 64 the bf16 roundings alone
-    exceed the tolerance on the LayerNorm branch, so the small-model widths
-    are used.)"""
+    along K over the CUs (tiles cut between blocks, partial sums added
+    afterwards); sequences of 1 and 7 tokens inside split tiles.  R = 5: odd
+    x_proj width (P = 37), two blocks per CU with a 3-stage copy ring;
+    R = 192 (P = 224, seven 32-column slices): one block per CU with a
+    5-stage ring.  (At d_model 64 the bf16 roundings alone exceed the
+    tolerance on the LayerNorm branch, so the small-model widths are used.)"""
     lens = [20000, 7, 13000, 1, 300]
-    _case(f"split-K conv path lens={lens}")
-    wl = synth.custom(lens, seed=21, h_kind="rms", d_model=256, d_inner=512, dt_rank=5)
+    _case(f"split-K conv path dt_rank={dt_rank} lens={lens}")
+    wl = synth.custom(lens, seed=21, h_kind="rms", d_model=256, d_inner=512, dt_rank=dt_rank)
     W = synth.make_weights(wl, affine_ln=True)
     h, cu = synth.make_hidden(wl), wl.cu_seqlens()
     ref, rref = O.reverse_mamba_layer(h, cu, W, float(W["s"]), return_branch=True)
