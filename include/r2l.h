@@ -43,6 +43,13 @@
  *  - Threading: calls are reentrant; concurrent calls must use distinct
  *    workspaces and outputs.  (The opt-in per-kernel timing below is the
  *    one process-wide state.)
+ *  - Co-residency: with bf16 activations and d_model a multiple of 256,
+ *    r2l_layer_fwd's out_proj kernel (with the LayerNorm and the residual
+ *    in its epilogue) runs at most one block per compute unit, and the
+ *    blocks sharing a 256-row block exchange row statistics while they run.
+ *    Work on other streams of the same GPU can delay some of them; a block
+ *    waits a bounded number of polls (many seconds) and past that writes
+ *    NaN for its rows rather than wait longer, so it never hangs the GPU.
  *  - Supported shapes: d_state == 16, d_conv == 4, d_model and d_inner
  *    multiples of 64 with d_model <= 8192, 1 <= dt_rank <= 1024,
  *    nseq >= 1, n_tokens >= 0 (all int32-indexable).
