@@ -28,6 +28,8 @@
 //
 // Block indices are remapped so that each XCD works on a contiguous,
 // group-M-ordered range of tiles (tiles that share operands share an L2).
+#include <type_traits>
+
 #include "kernels.h"
 
 namespace r2l {
@@ -1047,28 +1049,63 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_pers_kernel(int M, int N, in
 
 // Mid-size kernel (the 128 x 128 tiles of small problems and of the last
 // tile row of large ones): the big kernel's pipeline on 128 x 128 tiles.
-// Four LDS stages of 32-wide K steps (16 KB each, so two blocks fit a CU)
-// filled by buffer_load ... lds three steps ahead, the same swizzle and the
-// same barrier / vmcnt discipline; each wave owns a 64 x 64 quarter (2 x 2
-// MFMA tiles).  splits == 0: block b computes tile b (row-major) into C.
-// splits > 0: block u computes K steps [s ksteps, (s+1) ksteps), s = u %
-// splits, of tile u / splits as an fp32 partial sum into part[u][128][128],
-// added by gemm_small_reduce_kernel.
+// ST LDS stages of 32-wide K steps (16 KB each) filled by buffer_load ... lds
+// ST - 1 steps ahead, the same swizzle and the same barrier / vmcnt
+// discipline; each wave owns a 64 x 64 quarter (2 x 2 MFMA tiles).  ST = 4
+// fits two blocks in a CU; ST = 8 (128 KB) is for launches of at most one
+// block per CU, where a block's own copies in flight set the pace.  The last
+// ST steps issue nothing new and wait for exactly the copies they read.
+// splits == 0: block b computes tile b (row-major) into C.  splits > 0:
+// block u computes K steps [s ksteps, (s+1) ksteps), s = u % splits, of tile
+// u / splits as an fp32 partial sum into part[u][128][128], added by
+// gemm_small_reduce4_kernel.  The K steps per block are a multiple of ST.
 constexpr int kMidB = 128, kMidSBYTES = 2 * kMidB * kBigSROW;
 
-template <bool OUT_F32>
-__global__ __launch_bounds__(256, 2) void gemm_bf16_mid_kernel(int M, int N, int K,
-                                                               const bf16* __restrict__ A, long lda,
-                                                               const bf16* __restrict__ B, long ldb,
-                                                               void* __restrict__ Cv, long ldc,
-                                                               int splits, int ksteps,
-                                                               float* __restrict__ part) {
-  constexpr int BK = kBigBK, ST = kBigST, SROW = kBigSROW, LPT = 4;
+// s_waitcnt until at most n stages of LPT copies each are outstanding (n is
+// a constant once the calling loop is unrolled)
+template <int LPT>
+R2L_DEV void wait_stages(int n) {
+  switch (n) {
+    case 0: __builtin_amdgcn_s_waitcnt(vmcnt_imm(0)); break;
+    case 1: __builtin_amdgcn_s_waitcnt(vmcnt_imm(LPT)); break;
+    case 2: __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * LPT)); break;
+    case 3: __builtin_amdgcn_s_waitcnt(vmcnt_imm(3 * LPT)); break;
+    case 4: __builtin_amdgcn_s_waitcnt(vmcnt_imm(4 * LPT)); break;
+    case 5: __builtin_amdgcn_s_waitcnt(vmcnt_imm(5 * LPT)); break;
+    default: __builtin_amdgcn_s_waitcnt(vmcnt_imm(6 * LPT)); break;
+  }
+}
+
+template <bool OUT_F32, int ST>
+__global__ __launch_bounds__(256, ST == 4 ? 2 : 1) void gemm_bf16_mid_kernel(int M, int N, int K,
+                                                                             const bf16* __restrict__ A, long lda,
+                                                                             const bf16* __restrict__ B, long ldb,
+                                                                             void* __restrict__ Cv, long ldc,
+                                                                             int splits, int ksteps,
+                                                                             float* __restrict__ part) {
+  static_assert(ST == 4 || ST == 8, "four or eight stages");
+  constexpr int BK = kBigBK, SROW = kBigSROW, LPT = 4, XB = ST == 8 ? kMidSBYTES : 16;
+  // one object per stage: the compiler orders LDS copies against reads per object
   __shared__ __attribute__((aligned(1024))) char s0[kMidSBYTES];
   __shared__ __attribute__((aligned(1024))) char s1[kMidSBYTES];
   __shared__ __attribute__((aligned(1024))) char s2[kMidSBYTES];
   __shared__ __attribute__((aligned(1024))) char s3[kMidSBYTES];
-  auto stage = [&](int s) -> char* { return s == 0 ? s0 : s == 1 ? s1 : s == 2 ? s2 : s3; };
+  __shared__ __attribute__((aligned(1024))) char s4[XB];
+  __shared__ __attribute__((aligned(1024))) char s5[XB];
+  __shared__ __attribute__((aligned(1024))) char s6[XB];
+  __shared__ __attribute__((aligned(1024))) char s7[XB];
+  auto stage = [&](int s) -> char* {
+    switch (s) {
+      case 0: return s0;
+      case 1: return s1;
+      case 2: return s2;
+      case 3: return s3;
+      case 4: return s4;
+      case 5: return s5;
+      case 6: return s6;
+      default: return s7;
+    }
+  };
 
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64, fr = lane & 31, fh = lane >> 5;
@@ -1093,9 +1130,9 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_mid_kernel(int M, int N, int
     voff[i] = i < 2 ? (unsigned)(((long)row * lda + kc * 8) * 2)
                     : (unsigned)(((long)(row - kMidB) * ldb + kc * 8) * 2);
   }
-  auto issue = [&](int s, int kt) {  // past the end: reload the last step (never read)
+  auto issue = [&](int s, int kt) {
     char* base = stage(s);
-    const unsigned kb = (unsigned)((kbeg + min(kt, nk - 1)) * BK * 2);
+    const unsigned kb = (unsigned)((kbeg + kt) * BK * 2);
 #pragma unroll
     for (int i = 0; i < LPT; ++i) lds_dma16(i < 2 ? rA : rB, base + (i * 256 + wave * 64) * 16, voff[i], kb);
   };
@@ -1131,31 +1168,41 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_mid_kernel(int M, int N, int
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  issue(0, 0);
-  issue(1, 1);
-  issue(2, 2);
-  __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * LPT));
+  // nk is a positive multiple of ST.  Step kt reads the second half of stage
+  // kt and the first half of stage kt + 1, so its wait leaves outstanding only
+  // the stages issued after kt + 1; stage kt + ST - 1 goes into the slot that
+  // step kt - 1 finished reading (the barrier orders it after those reads).
+#pragma unroll
+  for (int s = 0; s < ST - 1; ++s) issue(s, s);
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm((ST - 2) * LPT));
   asm volatile("s_barrier" ::: "memory");
   rd0(s0);
-  for (int kt0 = 0; kt0 < nk; kt0 += ST) {
+  // the waits are constants once the loops are unrolled: a branch on "last
+  // group" inside the loop would make the compiler assume the fewer copies of
+  // either path and add waits of its own
+  auto step = [&](int s, int wait, bool iss, int kt, bool next) {
+    wait_stages<LPT>(wait);
+    asm volatile("s_barrier" ::: "memory");
+    if (iss) issue((s + ST - 1) % ST, kt + ST - 1);
+    rd1(stage(s));
 #pragma unroll
-    for (int s = 0; s < ST; ++s) {
-      const int kt = kt0 + s;
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(LPT));
-      asm volatile("s_barrier" ::: "memory");
-      issue((s + ST - 1) % ST, kt + ST - 1);
-      rd1(stage(s));
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb0[j], fa0[i], acc[i][j], 0, 0, 0);
+    if (next) rd0(stage((s + 1) % ST));
 #pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb0[j], fa0[i], acc[i][j], 0, 0, 0);
-      rd0(stage((s + 1) % ST));
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb1[j], fa1[i], acc[i][j], 0, 0, 0);
+  };
+  for (int kt0 = 0; kt0 < nk - ST; kt0 += ST) {
 #pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb1[j], fa1[i], acc[i][j], 0, 0, 0);
-    }
+    for (int s = 0; s < ST; ++s) step(s, ST - 3, true, kt0 + s, true);
   }
+  // the last ST steps: only the first issues (stage nk - 1)
+#pragma unroll
+  for (int s = 0; s < ST; ++s)
+    step(s, s == 0 ? ST - 3 : (s >= ST - 2 ? 0 : ST - 2 - s), s == 0, nk - ST + s, s < ST - 1);
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
 
   // acc[i][j] register 4q+e holds row wm+32i+(lane&31), column
@@ -1250,9 +1297,20 @@ static void launch_gemm(int M, int N, int K, const bf16* A, long lda, const bf16
              (size_t)tiles * splits * 2 * BM * BN * sizeof(float) <= ws_bytes)
         splits *= 2;
     }
+    // eight stages when every block has a CU of its own
+    const int blocks = splits > 1 ? tiles * splits : tiles;
+    const bool deep = ncu > 0 && blocks <= ncu && (nk / splits) % 8 == 0;
+    auto mid = [&](auto out_f32_t, auto st_t, int grid, int sp, void* c, float* p) {
+      hipLaunchKernelGGL((gemm_bf16_mid_kernel<decltype(out_f32_t)::value, decltype(st_t)::value>), dim3(grid),
+                         dim3(256), 0, st, M, N, K, A, lda, B, ldb, c, ldc, sp, sp ? nk / sp : 0, p);
+    };
+    using T = std::true_type;
+    using F = std::false_type;
+    using S4 = std::integral_constant<int, 4>;
+    using S8 = std::integral_constant<int, 8>;
     if (splits > 1) {
-      hipLaunchKernelGGL((gemm_bf16_mid_kernel<true>), dim3(tiles * splits), dim3(256), 0, st, M, N, K, A, lda,
-                         B, ldb, C, ldc, splits, nk / splits, ws);
+      if (deep) mid(T{}, S8{}, tiles * splits, splits, C, ws);
+      else mid(T{}, S4{}, tiles * splits, splits, C, ws);
       const long n4 = (long)M * (N / 4);
       if (out_f32)
         hipLaunchKernelGGL((gemm_small_reduce4_kernel<BM, BN, true>), dim3((n4 + 255) / 256), dim3(256), 0, st,
@@ -1261,11 +1319,11 @@ static void launch_gemm(int M, int N, int K, const bf16* A, long lda, const bf16
         hipLaunchKernelGGL((gemm_small_reduce4_kernel<BM, BN, false>), dim3((n4 + 255) / 256), dim3(256), 0,
                            st, M, N, splits, (const float*)ws, C, ldc);
     } else if (out_f32) {
-      hipLaunchKernelGGL((gemm_bf16_mid_kernel<true>), dim3(tiles), dim3(256), 0, st, M, N, K, A, lda, B, ldb,
-                         C, ldc, 0, 0, (float*)nullptr);
+      if (deep) mid(T{}, S8{}, tiles, 0, C, nullptr);
+      else mid(T{}, S4{}, tiles, 0, C, nullptr);
     } else {
-      hipLaunchKernelGGL((gemm_bf16_mid_kernel<false>), dim3(tiles), dim3(256), 0, st, M, N, K, A, lda, B, ldb,
-                         C, ldc, 0, 0, (float*)nullptr);
+      if (deep) mid(F{}, S8{}, tiles, 0, C, nullptr);
+      else mid(F{}, S4{}, tiles, 0, C, nullptr);
     }
     return;
   }
