@@ -161,7 +161,7 @@ __global__ __launch_bounds__(256) void conv_xproj_kernel(int Tn, int E, int P,
                                                          const int32_t* __restrict__ cu, int nseq,
                                                          int R, int RP, bf16* __restrict__ dsplit) {
   constexpr int NC = NCS * 32;
-  __shared__ float red[3][32 * NC];
+  __shared__ float red[4][32 * NC];
   const int lane = lane_id(), w = wave_id();
   const int tr = lane & 31, kh = lane >> 5;
   const int t0 = blockIdx.x * 32;
@@ -181,8 +181,11 @@ __global__ __launch_bounds__(256) void conv_xproj_kernel(int Tn, int E, int P,
     for (int r = 0; r < 16; ++r) acc[c][r] = 0.0f;
 
   const bf16x8 zero8 = {};
-  // Operands of one 16-channel k-step; the next step's are loaded while the
-  // current one is computed (the loads would otherwise stall every step).
+  // Operands of one 16-channel k-step, loaded PF steps ahead: a wave of a
+  // small input has only a few steps (4 at 16 channel splits of 4096), and
+  // with every step's loads in flight together it waits for one memory
+  // latency instead of one per step.
+  constexpr int PF = 4;
   struct Step {
     bf16x8 wv[4], bv, xv[KC], wx[NCS];
   };
@@ -211,10 +214,7 @@ __global__ __launch_bounds__(256) void conv_xproj_kernel(int Tn, int E, int P,
       s.wx[c] = *(const bf16x8*)(Wx + (long)row * E + c0);
     }
   };
-  Step cur, nxt;
-  load_step(cur, cbeg);
-  for (int k0 = cbeg; k0 < cbeg + Ew; k0 += 16) {
-    if (k0 + 16 < cbeg + Ew) load_step(nxt, k0 + 16);
+  auto compute_step = [&](const Step& cur, int k0) {
     const int c0 = k0 + kh * 8;
     float ca[8];
 #pragma unroll
@@ -238,33 +238,52 @@ __global__ __launch_bounds__(256) void conv_xproj_kernel(int Tn, int E, int P,
       const bf16x8 bfr = (c * 32 + tr < P) ? cur.wx[c] : zero8;
       acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bfr, acc[c], 0, 0, 0);
     }
-    cur = nxt;
+  };
+  const int nst = Ew / 16;
+  Step ring[PF];
+#pragma unroll
+  for (int i = 0; i < PF; ++i)
+    if (i < nst) load_step(ring[i], cbeg + 16 * i);
+  for (int g = 0; g < nst; g += PF) {
+#pragma unroll
+    for (int i = 0; i < PF; ++i) {
+      if (g + i < nst) {
+        compute_step(ring[i], cbeg + 16 * (g + i));
+        if (g + i + PF < nst) load_step(ring[i], cbeg + 16 * (g + i + PF));
+      }
+    }
   }
   // D layout: lane holds output column (lane & 31) of each 32-wide slice and
-  // token rows 8*(r/4) + 4*(lane/32) + r%4.
-  if (w > 0) {
+  // token rows 8*(r/4) + 4*(lane/32) + r%4.  Every wave's partial sums go to
+  // LDS; wave w then adds, for its token rows 8 w .. 8 w + 7 (its registers
+  // r = 4 w .. 4 w + 3), the four waves' values in the fixed order 0, 1, 2, 3.
+  // All the LDS reads come before the (bounds-checked) stores, so their
+  // latencies overlap.
 #pragma unroll
-    for (int c = 0; c < NCS; ++c)
+  for (int c = 0; c < NCS; ++c)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = 8 * (r >> 2) + 4 * kh + (r & 3);
-        red[w - 1][row * NC + c * 32 + tr] = acc[c][r];
-      }
-  }
+    for (int r = 0; r < 16; ++r) {
+      const int row = 8 * (r >> 2) + 4 * kh + (r & 3);
+      red[w][row * NC + c * 32 + tr] = acc[c][r];
+    }
   __syncthreads();
-  if (w == 0) {
+  float vs[NCS][4];
 #pragma unroll
-    for (int c = 0; c < NCS; ++c) {
-      const int col = c * 32 + tr;
+  for (int c = 0; c < NCS; ++c)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = 8 * (r >> 2) + 4 * kh + (r & 3);
-        const int idx = row * NC + col;
-        const float v = acc[c][r] + red[0][idx] + red[1][idx] + red[2][idx];
-        if (col < P && t0 + row < Tn) {
-          xdbl[(long)(t0 + row) * P + col] = v;
-          if (dsplit != nullptr) split_store<1>(dsplit, t0 + row, col, R, RP, &v);
-        }
+    for (int q = 0; q < 4; ++q) {
+      const int idx = (8 * w + 4 * kh + q) * NC + c * 32 + tr;
+      vs[c][q] = ((red[0][idx] + red[1][idx]) + red[2][idx]) + red[3][idx];
+    }
+#pragma unroll
+  for (int c = 0; c < NCS; ++c) {
+    const int col = c * 32 + tr;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int row = 8 * w + 4 * kh + q;
+      if (col < P && t0 + row < Tn) {
+        xdbl[(long)(t0 + row) * P + col] = vs[c][q];
+        if (dsplit != nullptr) split_store<1>(dsplit, t0 + row, col, R, RP, &vs[c][q]);
       }
     }
   }
