@@ -272,29 +272,56 @@ __global__ __launch_bounds__(256, KS > 4 ? 1 : 2) void scan_kernel(ScanArgs a) {
   const int r8 = tid >> 3, c8 = tid & 7;   // A/C row and channel group
   const int ea = e0 + 8 * c8;              // A/C first channel
 
+  // Per-channel parameters in 16-byte loads where the pointers allow (a
+  // block of a short input runs a single 32-token block, and element loads
+  // would be a large part of its time).  The layer's tensors are 16-byte
+  // aligned; the standalone scan's A_log and Dskip need not be.
   float A2[4];
+  if ((reinterpret_cast<uintptr_t>(a.A_log) & 15) == 0) {
+    const f32x4 al = *(const f32x4*)(a.A_log + (long)e * NS + 4 * w);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) A2[i] = -expf(a.A_log[(long)e * NS + 4 * w + i]) * kLog2e;
+    for (int i = 0; i < 4; ++i) A2[i] = -expf(al[i]) * kLog2e;
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) A2[i] = -expf(a.A_log[(long)e * NS + 4 * w + i]) * kLog2e;
+  }
   float dsk8[8], cb8[8];
   float cwr[BF ? 1 : 8][4];        // fp32 conv taps
   unsigned w10[8], w32[8];         // bf16 conv taps as pairs (tap for row t | row t+1), (t+2 | t+3)
+  if (a.Dskip == nullptr) {
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    dsk8[i] = a.Dskip ? a.Dskip[ea + i] : 0.0f;
-    cb8[i] = FUSED ? to_f32(((const T*)a.conv_b)[ea + i]) : 0.0f;
+    for (int i = 0; i < 8; ++i) dsk8[i] = 0.0f;
+  } else if ((reinterpret_cast<uintptr_t>(a.Dskip) & 15) == 0) {
+    const f32x4 d0 = *(const f32x4*)(a.Dskip + ea), d1 = *(const f32x4*)(a.Dskip + ea + 4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { dsk8[i] = d0[i]; dsk8[4 + i] = d1[i]; }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) dsk8[i] = a.Dskip[ea + i];
   }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) cb8[i] = 0.0f;
   if constexpr (FUSED) {
     if constexpr (BF) {
+      const bf16x8 cb = *(const bf16x8*)((const bf16*)a.conv_b + ea);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) cb8[i] = (float)cb[i];
       // taps k = 0..3 of channel i as two dwords (k0|k1), (k2|k3); the conv
       // weight for row t + j is tap 3 - j
-      const unsigned* cw = (const unsigned*)a.conv_w;
+      const u32x4* cw = (const u32x4*)((const unsigned*)a.conv_w + (long)ea * 2);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const unsigned k01 = cw[(long)(ea + i) * 2], k23 = cw[(long)(ea + i) * 2 + 1];
-        w10[i] = __builtin_amdgcn_alignbit(k23, k23, 16);   // (tap 3 | tap 2)
-        w32[i] = __builtin_amdgcn_alignbit(k01, k01, 16);   // (tap 1 | tap 0)
+      for (int q = 0; q < 4; ++q) {
+        const u32x4 v = cw[q];   // channels ea + 2q, ea + 2q + 1
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const int i = 2 * q + hh;
+          w10[i] = __builtin_amdgcn_alignbit(v[2 * hh + 1], v[2 * hh + 1], 16);   // (tap 3 | tap 2)
+          w32[i] = __builtin_amdgcn_alignbit(v[2 * hh], v[2 * hh], 16);           // (tap 1 | tap 0)
+        }
       }
     } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) cb8[i] = ((const float*)a.conv_b)[ea + i];
 #pragma unroll
       for (int i = 0; i < 8; ++i)
 #pragma unroll
@@ -312,10 +339,16 @@ __global__ __launch_bounds__(256, KS > 4 ? 1 : 2) void scan_kernel(ScanArgs a) {
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       const int k = ks * 32 + (lane >> 4) * 8;
+      if ((a.R & 7) == 0) {
+        // whole 16-byte row pieces; those past dt_rank read as zeros
+        wdt[ks] = *(const bf16x8*)(W + rowoff + min(k, a.R - 8));
+        if (k >= a.R) wdt[ks] = bf16x8{};
+      } else {
 #pragma unroll
-      for (int p = 0; p < 8; ++p) wdt[ks][p] = W[rowoff + min(k + p, a.R - 1)];
+        for (int p = 0; p < 8; ++p) wdt[ks][p] = W[rowoff + min(k + p, a.R - 1)];
 #pragma unroll
-      for (int p = 0; p < 8; ++p) if (k + p >= a.R) wdt[ks][p] = (bf16)0.0f;
+        for (int p = 0; p < 8; ++p) if (k + p >= a.R) wdt[ks][p] = (bf16)0.0f;
+      }
     }
     dtb_col = a.dt_b[e0 + dcol];
   }
