@@ -745,11 +745,26 @@ int r2l_layer_fwd(const r2l_dims* d, r2l_dtype act, uint32_t flags, const r2l_we
     // reads all of o in training mode), then the LayerNorm kernel
     if (Tf < T) {
       const long r0 = Tf;
-      R2L_RUN("out_proj_gemm", st, gemm_bf16_nt(T - Tf, D, E, y + r0 * E, E, (const bf16*)w->out_proj_w, E,
-                                                o + r0 * D, D, true, st, scratch, kSplitScratch, ncu));
-      R2L_RUN("ln_gate", st, (ln_gate<bf16, float>(T - Tf, D, o + r0 * D, (const bf16*)h_in + r0 * D, (bf16*)h_out + r0 * D,
-                                                    w->ln_w, w->ln_b, w->s, branch_out ? branch_out + r0 * D : nullptr,
-                                                    no_ln, R2L_LN_EPS, st)));
+      // few rows (out_proj split along K): the LayerNorm kernel adds the
+      // split's partial tiles itself, one launch fewer than summing them
+      // into o first
+      const int parts = gemm_bf16_nt_parts_split(T - Tf, D, E, y + r0 * E, E, (const bf16*)w->out_proj_w, E,
+                                                 scratch, kSplitScratch, ncu);
+      if (parts > 0 && ln_gate_parts_fits(D, parts)) {
+        R2L_RUN("out_proj_gemm", st, gemm_bf16_nt_parts(T - Tf, D, E, y + r0 * E, E, (const bf16*)w->out_proj_w, E,
+                                                        parts, st, scratch, ncu));
+        R2L_RUN("ln_gate", st, (ln_gate_parts<bf16>(T - Tf, D, parts, scratch, (const bf16*)h_in + r0 * D,
+                                                    (bf16*)h_out + r0 * D, w->ln_w, w->ln_b, w->s,
+                                                    branch_out ? branch_out + r0 * D : nullptr,
+                                                    (flags & R2L_FLAG_TRAIN) ? o + r0 * D : nullptr, no_ln,
+                                                    R2L_LN_EPS, st)));
+      } else {
+        R2L_RUN("out_proj_gemm", st, gemm_bf16_nt(T - Tf, D, E, y + r0 * E, E, (const bf16*)w->out_proj_w, E,
+                                                  o + r0 * D, D, true, st, scratch, kSplitScratch, ncu));
+        R2L_RUN("ln_gate", st, (ln_gate<bf16, float>(T - Tf, D, o + r0 * D, (const bf16*)h_in + r0 * D, (bf16*)h_out + r0 * D,
+                                                      w->ln_w, w->ln_b, w->s, branch_out ? branch_out + r0 * D : nullptr,
+                                                      no_ln, R2L_LN_EPS, st)));
+      }
     }
   } else {
     float* xz = at<float>(workspace, lp.off_xz);

@@ -1278,39 +1278,56 @@ __global__ __launch_bounds__(256) void gemm_small_reduce4_kernel(int M, int N, i
   else *(bf16x4*)((bf16*)Cv + (long)m * ldc + n) = bf16x4{(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]};
 }
 
+// The mid-size kernel takes whole 128-wide K chunks and 16-byte operand rows
+// whose 128-row byte ranges fit the 32-bit buffer descriptor.
+static bool mid_fits(int K, const bf16* A, long lda, const bf16* B, long ldb) {
+  return K % (kBigBK * kBigST) == 0 && lda % 8 == 0 && ldb % 8 == 0 && ((uintptr_t)A & 15) == 0 &&
+         ((uintptr_t)B & 15) == 0 && (long)kMidB * lda * 2 < (1L << 31) && (long)kMidB * ldb * 2 < (1L << 31);
+}
+
+// Its K split: while the tiles do not fill the GPU, doubled as long as every
+// split keeps whole 128-wide chunks of at least 8 steps and the fp32 partial
+// tiles fit the workspace.
+static int mid_split(int tiles, int nk, const float* ws, size_t ws_bytes, int ncu) {
+  int splits = 1;
+  if (ws != nullptr && ((uintptr_t)ws & 15) == 0 && ncu > 0 && tiles * 2 <= ncu) {
+    while (tiles * splits * 2 <= ncu && nk % (splits * 2 * kBigST) == 0 && nk / (splits * 2) >= 8 &&
+           (size_t)tiles * splits * 2 * kMidB * kMidB * sizeof(float) <= ws_bytes)
+      splits *= 2;
+  }
+  return splits;
+}
+
+// One launch of the mid-size kernel: whole tiles into C (splits == 1), or
+// the fp32 partial tiles of a K split into part.  Eight LDS stages when every
+// block has a CU of its own.
+template <bool OUT_F32>
+static void launch_mid(int M, int N, int K, const bf16* A, long lda, const bf16* B, long ldb, void* C, long ldc,
+                       int tiles, int splits, float* part, hipStream_t st, int ncu) {
+  const int nk = K / kBigBK;
+  const int blocks = splits > 1 ? tiles * splits : tiles;
+  const bool deep = ncu > 0 && blocks <= ncu && (nk / splits) % 8 == 0;
+  const int sp = splits > 1 ? splits : 0;
+  if (deep)
+    hipLaunchKernelGGL((gemm_bf16_mid_kernel<OUT_F32, 8>), dim3(blocks), dim3(256), 0, st, M, N, K, A, lda, B, ldb,
+                       C, ldc, sp, sp ? nk / sp : 0, part);
+  else
+    hipLaunchKernelGGL((gemm_bf16_mid_kernel<OUT_F32, 4>), dim3(blocks), dim3(256), 0, st, M, N, K, A, lda, B, ldb,
+                       C, ldc, sp, sp ? nk / sp : 0, part);
+}
+
 template <int BM, int BN>
 static void launch_gemm(int M, int N, int K, const bf16* A, long lda, const bf16* B, long ldb,
                         void* C, long ldc, bool out_f32, hipStream_t st, float* ws, size_t ws_bytes,
                         int ncu) {
   const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
-  // The mid-size kernel (direct-to-LDS, four stages) for whole 128-wide K
-  // chunks, 4-column output groups and 16-byte operand rows; the K split,
-  // when the tiles do not fill the GPU, keeps whole 128-wide chunks per split.
+  // The mid-size kernel, with 4-column output groups; the K split, when the
+  // tiles do not fill the GPU, keeps whole 128-wide chunks per split.
   static_assert(BM == kMidB && BN == kMidB, "the mid-size kernel has 128 x 128 tiles");
-  if (K % (kBigBK * kBigST) == 0 && N % 4 == 0 && ldc % 4 == 0 && lda % 8 == 0 && ldb % 8 == 0 &&
-      ((uintptr_t)A & 15) == 0 && ((uintptr_t)B & 15) == 0 && ((uintptr_t)C & (out_f32 ? 15 : 7)) == 0 &&
-      (long)kMidB * lda * 2 < (1L << 31) && (long)kMidB * ldb * 2 < (1L << 31)) {
-    const int nk = K / kBigBK;
-    int splits = 1;
-    if (ws != nullptr && ((uintptr_t)ws & 15) == 0 && ncu > 0 && tiles * 2 <= ncu) {
-      while (tiles * splits * 2 <= ncu && nk % (splits * 2 * kBigST) == 0 && nk / (splits * 2) >= 8 &&
-             (size_t)tiles * splits * 2 * BM * BN * sizeof(float) <= ws_bytes)
-        splits *= 2;
-    }
-    // eight stages when every block has a CU of its own
-    const int blocks = splits > 1 ? tiles * splits : tiles;
-    const bool deep = ncu > 0 && blocks <= ncu && (nk / splits) % 8 == 0;
-    auto mid = [&](auto out_f32_t, auto st_t, int grid, int sp, void* c, float* p) {
-      hipLaunchKernelGGL((gemm_bf16_mid_kernel<decltype(out_f32_t)::value, decltype(st_t)::value>), dim3(grid),
-                         dim3(256), 0, st, M, N, K, A, lda, B, ldb, c, ldc, sp, sp ? nk / sp : 0, p);
-    };
-    using T = std::true_type;
-    using F = std::false_type;
-    using S4 = std::integral_constant<int, 4>;
-    using S8 = std::integral_constant<int, 8>;
+  if (mid_fits(K, A, lda, B, ldb) && N % 4 == 0 && ldc % 4 == 0 && ((uintptr_t)C & (out_f32 ? 15 : 7)) == 0) {
+    const int splits = mid_split(tiles, K / kBigBK, ws, ws_bytes, ncu);
     if (splits > 1) {
-      if (deep) mid(T{}, S8{}, tiles * splits, splits, C, ws);
-      else mid(T{}, S4{}, tiles * splits, splits, C, ws);
+      launch_mid<true>(M, N, K, A, lda, B, ldb, C, ldc, tiles, splits, ws, st, ncu);
       const long n4 = (long)M * (N / 4);
       if (out_f32)
         hipLaunchKernelGGL((gemm_small_reduce4_kernel<BM, BN, true>), dim3((n4 + 255) / 256), dim3(256), 0, st,
@@ -1319,11 +1336,9 @@ static void launch_gemm(int M, int N, int K, const bf16* A, long lda, const bf16
         hipLaunchKernelGGL((gemm_small_reduce4_kernel<BM, BN, false>), dim3((n4 + 255) / 256), dim3(256), 0,
                            st, M, N, splits, (const float*)ws, C, ldc);
     } else if (out_f32) {
-      if (deep) mid(T{}, S8{}, tiles, 0, C, nullptr);
-      else mid(T{}, S4{}, tiles, 0, C, nullptr);
+      launch_mid<true>(M, N, K, A, lda, B, ldb, C, ldc, tiles, 1, nullptr, st, ncu);
     } else {
-      if (deep) mid(F{}, S8{}, tiles, 0, C, nullptr);
-      else mid(F{}, S4{}, tiles, 0, C, nullptr);
+      launch_mid<false>(M, N, K, A, lda, B, ldb, C, ldc, tiles, 1, nullptr, st, ncu);
     }
     return;
   }
@@ -1387,6 +1402,23 @@ static void launch_big(int M, int N, int K, const bf16* A, long lda, const bf16*
       hipLaunchKernelGGL((gemm_tail_reduce_kernel<false, G>), dim3(rem * (kBigBM / 4)), dim3(256), 0, st, M,
                          N, n_dp, splits, (const float*)ws, C, ldc);
   }
+}
+
+int gemm_bf16_nt_parts_split(int M, int N, int K, const bf16* A, long lda, const bf16* B, long ldb,
+                             const float* ws, size_t ws_bytes, int ncu) {
+  if (M <= 0 || N <= 0 || N % 4 != 0) return 0;
+  const long big_tiles = (long)((M + kBigBM - 1) / kBigBM) * ((N + kBigBN - 1) / kBigBN);
+  if (big_tiles >= 128 || !mid_fits(K, A, lda, B, ldb)) return 0;   // not the mid-size kernel's problem
+  const int tiles = ((M + kMidB - 1) / kMidB) * ((N + kMidB - 1) / kMidB);
+  const int splits = mid_split(tiles, K / kBigBK, ws, ws_bytes, ncu);
+  return splits > 1 ? splits : 0;
+}
+
+hipError_t gemm_bf16_nt_parts(int M, int N, int K, const bf16* A, long lda, const bf16* B, long ldb, int splits,
+                              hipStream_t st, float* ws, int ncu) {
+  const int tiles = ((M + kMidB - 1) / kMidB) * ((N + kMidB - 1) / kMidB);
+  launch_mid<true>(M, N, K, A, lda, B, ldb, nullptr, N, tiles, splits, ws, st, ncu);
+  return hipGetLastError();
 }
 
 OutLnPlan plan_out_ln(int T, int D, int K, int ncu) {

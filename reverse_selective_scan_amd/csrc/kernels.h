@@ -15,6 +15,16 @@ namespace r2l {
 hipError_t gemm_bf16_nt(int M, int N, int K, const bf16* A, long lda, const bf16* B, long ldb,
                         void* C, long ldc, bool out_f32, hipStream_t st, float* ws = nullptr,
                         size_t ws_bytes = 0, int ncu = 0);
+// The K-split part alone.  gemm_bf16_nt_parts_split: the split count with
+// which gemm_bf16_nt would run this problem on its mid-size kernel split
+// along K (few 128 x 128 tiles for the GPU), else 0.  gemm_bf16_nt_parts:
+// that kernel alone with that count, its fp32 partial tiles left in ws (tile
+// t of the row-major tile grid, split s at ws + (t * splits + s) * 128 * 128,
+// row-major inside the tile).
+int gemm_bf16_nt_parts_split(int M, int N, int K, const bf16* A, long lda, const bf16* B, long ldb,
+                             const float* ws, size_t ws_bytes, int ncu);
+hipError_t gemm_bf16_nt_parts(int M, int N, int K, const bf16* A, long lda, const bf16* B, long ldb, int splits,
+                              hipStream_t st, float* ws, int ncu);
 // out_proj fused with the stream LayerNorm and the gated residual (bf16):
 // h_out = h + tanh(s) LN(y W^T) for the first `rows` token rows, which the
 // plan makes whole rounds of 256-row blocks over a persistent grid (rows = 0:
@@ -185,5 +195,15 @@ template <typename T, typename O>
 hipError_t ln_gate(int T_, int D, const O* o, const T* h_in, T* h_out, const float* gamma,
                    const float* beta, const float* s, float* branch, bool no_ln, float eps,
                    hipStream_t st);
+// ln_gate on the split-K parts of o that gemm_bf16_nt_parts left: o is
+// their sum in the order of the split index (the values the GEMM's own sum
+// would store), saved to o_save (optional, f32 [T_, D]) for training.
+// Returns hipErrorInvalidValue, launching nothing, for widths or split
+// counts it does not take (D of 2048, 4096 or 8192; 2, 4 or 8 splits).
+bool ln_gate_parts_fits(int D, int splits);
+template <typename T>
+hipError_t ln_gate_parts(int T_, int D, int splits, const float* part, const T* h_in, T* h_out,
+                         const float* gamma, const float* beta, const float* s, float* branch, float* o_save,
+                         bool no_ln, float eps, hipStream_t st);
 
 }  // namespace r2l

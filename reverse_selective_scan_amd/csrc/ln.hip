@@ -185,6 +185,152 @@ __global__ __launch_bounds__(256) void ln_gate_generic_kernel(int Tn, int D, con
     }
 }
 
+// The same step on the K-split parts of o (a small input's out_proj): o is
+// the sum over s, in order, of the partial tiles part[(t splits + s) 128 128]
+// (tile t of the row-major grid of 128 x 128 output tiles, row-major inside),
+// the order the GEMM's own sum uses, so o has the same values.  One block per
+// token row; thread tid holds columns 8 (tid + 256 c) .. +7, and the row's two
+// reductions run across the block (wave sums, then the four waves' totals in
+// a fixed order).  Every load of the row is issued before the first wait.
+template <typename T, int NCH, int S>
+__global__ __launch_bounds__(256) void ln_gate_parts_kernel(int Tn, int D, const float* __restrict__ part,
+                                                            const T* h_in, T* h_out,  // may alias
+                                                            const float* __restrict__ gamma,
+                                                            const float* __restrict__ beta,
+                                                            const float* __restrict__ s,
+                                                            float* __restrict__ branch,
+                                                            float* __restrict__ o_save, int no_ln, float eps) {
+  __shared__ float red[2][4];
+  const int row = blockIdx.x;
+  if (row >= Tn) return;
+  const int tid = threadIdx.x, lane = lane_id(), w = wave_id();
+  const long tile_row = (long)(row / 128) * (D / 128);
+  const int rr = row % 128;
+  const long rb = (long)row * D;
+  f32x4 pa[NCH][S][2];
+  Raw8h<T> hraw[NCH];
+  float gm[NCH][8], bt[NCH][8];
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    const int col = 8 * (tid + 256 * c);
+    const float* p = part + ((tile_row + col / 128) * S) * (128 * 128) + rr * 128 + (col % 128);
+#pragma unroll
+    for (int sp = 0; sp < S; ++sp) {
+      pa[c][sp][0] = *(const f32x4*)(p + (long)sp * (128 * 128));
+      pa[c][sp][1] = *(const f32x4*)(p + (long)sp * (128 * 128) + 4);
+    }
+    const long off = rb + col;
+    if constexpr (sizeof(T) == 2) {
+      hraw[c].v = *(const bf16x8*)(h_in + off);
+    } else {
+      hraw[c].a = *(const f32x4*)(h_in + off);
+      hraw[c].b = *(const f32x4*)(h_in + off + 4);
+    }
+    if (!no_ln) {
+      ld8(gamma + col, gm[c]);
+      ld8(beta + col, bt[c]);
+    }
+  }
+  float v[NCH][8];
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    f32x4 a0 = {0.0f, 0.0f, 0.0f, 0.0f}, a1 = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int sp = 0; sp < S; ++sp) {
+      a0 = a0 + pa[c][sp][0];
+      a1 = a1 + pa[c][sp][1];
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { v[c][i] = a0[i]; v[c][4 + i] = a1[i]; }
+    if (o_save != nullptr) st8(o_save + rb + 8 * (tid + 256 * c), v[c]);
+  }
+  auto block_sum = [&](float x, int k) {
+    x = wave_sum(x);
+    if (lane == 0) red[k][w] = x;
+    __syncthreads();
+    return ((red[k][0] + red[k][1]) + red[k][2]) + red[k][3];
+  };
+  const float invD = 1.0f / (float)D;
+  if (!no_ln) {
+    float sum = 0.0f;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) sum += v[c][i];
+    const float mu = block_sum(sum, 0) * invD;
+    float sq = 0.0f;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        v[c][i] -= mu;
+        sq = fmaf(v[c][i], v[c][i], sq);
+      }
+    const float rstd = 1.0f / sqrtf(block_sum(sq, 1) * invD + eps);
+#pragma unroll
+    for (int c = 0; c < NCH; ++c)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[c][i] = fmaf(gm[c][i], v[c][i] * rstd, bt[c][i]);
+  }
+  const float g = tanhf(s[0]);
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    const long off = rb + 8 * (tid + 256 * c);
+    if (branch != nullptr) st8(branch + off, v[c]);
+    if (g == 0.0f) {
+      // a zero gate copies h bit for bit (no arithmetic on it at all)
+      if constexpr (sizeof(T) == 2) {
+        *(bf16x8*)(h_out + off) = hraw[c].v;
+      } else {
+        *(f32x4*)(h_out + off) = hraw[c].a;
+        *(f32x4*)(h_out + off + 4) = hraw[c].b;
+      }
+    } else {
+      float hv[8];
+      if constexpr (sizeof(T) == 2) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) hv[i] = (float)hraw[c].v[i];
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) { hv[i] = hraw[c].a[i]; hv[4 + i] = hraw[c].b[i]; }
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) hv[i] = fmaf(g, v[c][i], hv[i]);
+      st8(h_out + off, hv);
+    }
+  }
+}
+
+bool ln_gate_parts_fits(int D, int splits) {
+  return (D == 2048 || D == 4096 || D == 8192) && (splits == 2 || splits == 4 || splits == 8);
+}
+
+template <typename T>
+hipError_t ln_gate_parts(int Tn, int D, int splits, const float* part, const T* h_in, T* h_out,
+                         const float* gamma, const float* beta, const float* s, float* branch, float* o_save,
+                         bool no_ln, float eps, hipStream_t st) {
+  if (!ln_gate_parts_fits(D, splits)) return hipErrorInvalidValue;
+  if (Tn <= 0) return hipSuccess;
+  const int nl = no_ln ? 1 : 0;
+#define R2L_LNP(C, S)                                                                                      \
+  hipLaunchKernelGGL((ln_gate_parts_kernel<T, C, S>), dim3(Tn), dim3(256), 0, st, Tn, D, part, h_in, h_out, \
+                     gamma, beta, s, branch, o_save, nl, eps)
+#define R2L_LNP_S(C)              \
+  if (splits == 2) R2L_LNP(C, 2); \
+  else if (splits == 4) R2L_LNP(C, 4); \
+  else R2L_LNP(C, 8);
+  if (D == 2048) { R2L_LNP_S(1) }
+  else if (D == 4096) { R2L_LNP_S(2) }
+  else { R2L_LNP_S(4) }
+#undef R2L_LNP_S
+#undef R2L_LNP
+  return hipGetLastError();
+}
+template hipError_t ln_gate_parts<bf16>(int, int, int, const float*, const bf16*, bf16*, const float*, const float*,
+                                        const float*, float*, float*, bool, float, hipStream_t);
+template hipError_t ln_gate_parts<float>(int, int, int, const float*, const float*, float*, const float*,
+                                         const float*, const float*, float*, float*, bool, float, hipStream_t);
+
 template <typename T, typename O>
 hipError_t ln_gate(int Tn, int D, const O* o, const T* h_in, T* h_out, const float* gamma,
                    const float* beta, const float* s, float* branch, bool no_ln, float eps,

@@ -161,6 +161,32 @@ def test_fused_out_proj_layernorm_path_matches_oracle():
         assert "out_proj_ln" in names and "ln_gate" in names, names
 
 
+def test_split_out_proj_layernorm_parts_path_matches_oracle():
+    """300 tokens at the pages' widths (D = 2048, E = 4096): out_proj runs on
+    the mid-size GEMM split four ways along K, and the LayerNorm kernel adds
+    the split's partial tiles itself (no separate sum kernel).  The last
+    128-row tile is ragged, and sequences of 100, 7 and 193 tokens run across
+    tiles.  Affine LayerNorm with the branch r, without the LayerNorm, and
+    s = 0 (an exact copy)."""
+    lens = [100, 7, 193]
+    _case(f"split out_proj + LN parts path lens={lens}")
+    wl = synth.custom(lens, seed=35, h_kind="rms", d_model=2048, d_inner=4096, dt_rank=128)
+    W = synth.make_weights(wl, affine_ln=True)
+    h, cu = synth.make_hidden(wl), wl.cu_seqlens()
+    s = float(W["s"])
+    g, gr = _gpu_layer(wl, W, h, cu, branch=True)
+    ref, rref = O.reverse_mamba_layer(h, cu, W, s, return_branch=True)
+    fo, fr = bf16_floor.layer_rounded(h, cu, W, s)
+    check_bf16("parts out", g, ref, fo, TOL_BF16)
+    check_bf16("parts branch", gr, rref, fr, TOL_BF16_BRANCH)
+    ref, _ = O.reverse_mamba_layer(h, cu, W, s, use_ln=False, return_branch=True)
+    fo, _ = bf16_floor.layer_rounded(h, cu, W, s, use_ln=False)
+    g2, _ = _gpu_layer(wl, W, h, cu, flags=B.R2L_FLAG_NO_LN)
+    check_bf16("parts out no-ln", g2, ref, fo, TOL_BF16)
+    g0, _ = _gpu_layer(wl, W, h, cu, s=0.0)
+    assert np.array_equal(g0.astype(np.float32).view(np.uint32), h.view(np.uint32))
+
+
 @pytest.mark.parametrize("hint", ["too_small", "too_large"])
 def test_max_seqlen_hint_does_not_change_results(hint):
     """max_seqlen only plans the scan's time chunks: a value below the true
