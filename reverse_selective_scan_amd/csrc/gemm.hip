@@ -1278,6 +1278,13 @@ __global__ __launch_bounds__(256) void gemm_small_reduce4_kernel(int M, int N, i
   else *(bf16x4*)((bf16*)Cv + (long)m * ldc + n) = bf16x4{(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]};
 }
 
+// Enough 256 x 256 tiles for the large-problem kernel: a whole round over
+// the CUs, or at least half of one with a long K (a weight gradient summed
+// over tokens), which that kernel splits along K.  With fewer tiles and a
+// short K, the 128 x 128 kernel's four times as many tiles fill the GPU
+// instead (measured at 1024 x 8192 x 2048: 48 us against 50-57).
+static bool big_enough(long big_tiles, int K) { return big_tiles >= 256 || (big_tiles >= 128 && K > 4096); }
+
 // The mid-size kernel takes whole 128-wide K chunks and 16-byte operand rows
 // whose 128-row byte ranges fit the 32-bit buffer descriptor.
 static bool mid_fits(int K, const bf16* A, long lda, const bf16* B, long ldb) {
@@ -1408,7 +1415,7 @@ int gemm_bf16_nt_parts_split(int M, int N, int K, const bf16* A, long lda, const
                              const float* ws, size_t ws_bytes, int ncu) {
   if (M <= 0 || N <= 0 || N % 4 != 0) return 0;
   const long big_tiles = (long)((M + kBigBM - 1) / kBigBM) * ((N + kBigBN - 1) / kBigBN);
-  if (big_tiles >= 128 || !mid_fits(K, A, lda, B, ldb)) return 0;   // not the mid-size kernel's problem
+  if (big_enough(big_tiles, K) || !mid_fits(K, A, lda, B, ldb)) return 0;   // not the mid-size kernel's problem
   const int tiles = ((M + kMidB - 1) / kMidB) * ((N + kMidB - 1) / kMidB);
   const int splits = mid_split(tiles, K / kBigBK, ws, ws_bytes, ncu);
   return splits > 1 ? splits : 0;
@@ -1476,7 +1483,7 @@ hipError_t gemm_bf16_nt(int M, int N, int K, const bf16* A, long lda, const bf16
                    lda % 8 == 0 && ldb % 8 == 0 && ((uintptr_t)A & 15) == 0 &&
                    ((uintptr_t)B & 15) == 0 && ((uintptr_t)C & (align - 1)) == 0 &&
                    (long)kBigBM * lda * 2 < (1L << 31) && (long)kBigBN * ldb * 2 < (1L << 31) &&
-                   big_tiles >= 128;
+                   big_enough(big_tiles, K);
   if (big) {
     // Tiles beyond the last whole round (tiles mod #CUs) would take a round of
     // their own; with a workspace they are split along K over up to all CUs

@@ -49,7 +49,10 @@ def _case(name):
                                    (9000, 4096, 768), (4352, 8192, 2048),
                                    # few rows (the 128 x 128 kernel split along K): 7 rows; 256 rows with
                                    # K = 768
-                                   (7, 2048, 2048), (256, 4096, 768)])
+                                   (7, 2048, 2048), (256, 4096, 768),
+                                   # 128 and 192 tiles of 256 x 256 with a short K: the 128 x 128 kernel
+                                   # (512 and 768 tiles, ragged rows in the second)
+                                   (1024, 8192, 2048), (1500, 8192, 2048)])
 def test_gemm_bf16_matches_fp64_product(M, N, K):
     _case(f"gemm bf16 {M}x{N}x{K}")
     A = synth.make_aux(M * 7 + 1, (M, K))
