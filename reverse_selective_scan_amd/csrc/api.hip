@@ -694,12 +694,15 @@ int r2l_layer_fwd(const r2l_dims* d, r2l_dtype act, uint32_t flags, const r2l_we
   a.sumP = at<float>(workspace, sp.off_sumP);
   a.l2r = l2r;
 
-  // chunk table first: the conv kernel also reads the sanitised offsets (and
-  // the fused out_proj's counters start at zero)
+  // the chunk table (the conv kernel also reads the sanitised offsets, and
+  // the fused out_proj's counters start at zero) before the conv
   const OutLnPlan oln = lp.fuse_ln ? plan_out_ln(T, D, E, num_cus()) : OutLnPlan{};
   int* lncnt = at<int>(workspace, lp.off_lncnt);
-  R2L_RUN("plan_chunks", st, plan_chunks(cu_seqlens, nseq, T, sp.Lc, sp.max_chunks, l2r, cu_clean, chunks, nch, st,
-                                         lncnt, oln.row_blocks));
+  PlanArgs plan = plan_args(cu_seqlens, nseq, T, sp.Lc, sp.max_chunks, l2r, cu_clean, chunks, nch, lncnt,
+                            oln.row_blocks);
+  if (act != R2L_BF16)
+    R2L_RUN("plan_chunks", st, plan_chunks(cu_seqlens, nseq, T, sp.Lc, sp.max_chunks, l2r, cu_clean, chunks, nch, st,
+                                           lncnt, oln.row_blocks));
 
   if (act == R2L_BF16) {
     bf16* xz = at<bf16>(workspace, lp.off_xz);
@@ -707,8 +710,13 @@ int r2l_layer_fwd(const r2l_dims* d, r2l_dtype act, uint32_t flags, const r2l_we
     const int ncu = num_cus();
     float* scratch = at<float>(workspace, lp.off_scratch);
     bf16* dsplit = delta_split_width(R) > 0 ? at<bf16>(workspace, lp.off_dsplit) : nullptr;
+    // in_proj; when it runs (or ends) on the mid-size kernel, that launch
+    // also runs the chunk planning, as one extra block (a launch fewer)
     R2L_RUN("in_proj_gemm", st, gemm_bf16_nt(T, 2 * E, D, (const bf16*)h_in, D, (const bf16*)w->in_proj_w, D, xz, 2L * E, false, st,
-                                             scratch, kSplitScratch, ncu));
+                                             scratch, kSplitScratch, ncu, &plan));
+    if (!plan.hosted)
+      R2L_RUN("plan_chunks", st, plan_chunks(cu_seqlens, nseq, T, sp.Lc, sp.max_chunks, l2r, cu_clean, chunks, nch, st,
+                                             lncnt, oln.row_blocks));
     if (!lp.need_u) {
       // (the split kernel counts (tile, step) pairs in 32 bits)
       if ((T + 127) / 128 >= ncu && (long)((T + 127) / 128) * (E / 32) < (1L << 31)) {

@@ -1076,13 +1076,14 @@ R2L_DEV void wait_stages(int n) {
   }
 }
 
-template <bool OUT_F32, int ST>
+template <bool OUT_F32, int ST, bool PLAN>
 __global__ __launch_bounds__(256, ST == 4 ? 2 : 1) void gemm_bf16_mid_kernel(int M, int N, int K,
                                                                              const bf16* __restrict__ A, long lda,
                                                                              const bf16* __restrict__ B, long ldb,
                                                                              void* __restrict__ Cv, long ldc,
                                                                              int splits, int ksteps,
-                                                                             float* __restrict__ part) {
+                                                                             float* __restrict__ part,
+                                                                             PlanArgs plan) {
   static_assert(ST == 4 || ST == 8, "four or eight stages");
   constexpr int BK = kBigBK, SROW = kBigSROW, LPT = 4, XB = ST == 8 ? kMidSBYTES : 16;
   // one object per stage: the compiler orders LDS copies against reads per object
@@ -1094,6 +1095,14 @@ __global__ __launch_bounds__(256, ST == 4 ? 2 : 1) void gemm_bf16_mid_kernel(int
   __shared__ __attribute__((aligned(1024))) char s5[XB];
   __shared__ __attribute__((aligned(1024))) char s6[XB];
   __shared__ __attribute__((aligned(1024))) char s7[XB];
+  if constexpr (PLAN) {
+    // PLAN: one extra block at the end of the grid runs the scan's chunk
+    // planning (dispatched last, it takes the first CU a tile block frees)
+    if (blockIdx.x == gridDim.x - 1) {
+      plan_chunks_block(plan, (int*)s0);
+      return;
+    }
+  }
   auto stage = [&](int s) -> char* {
     switch (s) {
       case 0: return s0;
@@ -1310,23 +1319,30 @@ static int mid_split(int tiles, int nk, const float* ws, size_t ws_bytes, int nc
 // block has a CU of its own.
 template <bool OUT_F32>
 static void launch_mid(int M, int N, int K, const bf16* A, long lda, const bf16* B, long ldb, void* C, long ldc,
-                       int tiles, int splits, float* part, hipStream_t st, int ncu) {
+                       int tiles, int splits, float* part, hipStream_t st, int ncu, PlanArgs* plan = nullptr) {
   const int nk = K / kBigBK;
   const int blocks = splits > 1 ? tiles * splits : tiles;
   const bool deep = ncu > 0 && blocks <= ncu && (nk / splits) % 8 == 0;
   const int sp = splits > 1 ? splits : 0;
-  if (deep)
-    hipLaunchKernelGGL((gemm_bf16_mid_kernel<OUT_F32, 8>), dim3(blocks), dim3(256), 0, st, M, N, K, A, lda, B, ldb,
-                       C, ldc, sp, sp ? nk / sp : 0, part);
-  else
-    hipLaunchKernelGGL((gemm_bf16_mid_kernel<OUT_F32, 4>), dim3(blocks), dim3(256), 0, st, M, N, K, A, lda, B, ldb,
-                       C, ldc, sp, sp ? nk / sp : 0, part);
+  const PlanArgs pa = plan ? *plan : PlanArgs{};
+#define R2L_MID(S, P)                                                                                          \
+  hipLaunchKernelGGL((gemm_bf16_mid_kernel<OUT_F32, S, P>), dim3(blocks + (P ? 1 : 0)), dim3(256), 0, st, M, N, \
+                     K, A, lda, B, ldb, C, ldc, sp, sp ? nk / sp : 0, part, pa)
+  if (plan) {
+    if (deep) R2L_MID(8, true);
+    else R2L_MID(4, true);
+    plan->hosted = 1;
+  } else {
+    if (deep) R2L_MID(8, false);
+    else R2L_MID(4, false);
+  }
+#undef R2L_MID
 }
 
 template <int BM, int BN>
 static void launch_gemm(int M, int N, int K, const bf16* A, long lda, const bf16* B, long ldb,
                         void* C, long ldc, bool out_f32, hipStream_t st, float* ws, size_t ws_bytes,
-                        int ncu) {
+                        int ncu, PlanArgs* plan) {
   const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
   // The mid-size kernel, with 4-column output groups; the K split, when the
   // tiles do not fill the GPU, keeps whole 128-wide chunks per split.
@@ -1334,7 +1350,7 @@ static void launch_gemm(int M, int N, int K, const bf16* A, long lda, const bf16
   if (mid_fits(K, A, lda, B, ldb) && N % 4 == 0 && ldc % 4 == 0 && ((uintptr_t)C & (out_f32 ? 15 : 7)) == 0) {
     const int splits = mid_split(tiles, K / kBigBK, ws, ws_bytes, ncu);
     if (splits > 1) {
-      launch_mid<true>(M, N, K, A, lda, B, ldb, C, ldc, tiles, splits, ws, st, ncu);
+      launch_mid<true>(M, N, K, A, lda, B, ldb, C, ldc, tiles, splits, ws, st, ncu, plan);
       const long n4 = (long)M * (N / 4);
       if (out_f32)
         hipLaunchKernelGGL((gemm_small_reduce4_kernel<BM, BN, true>), dim3((n4 + 255) / 256), dim3(256), 0, st,
@@ -1343,9 +1359,9 @@ static void launch_gemm(int M, int N, int K, const bf16* A, long lda, const bf16
         hipLaunchKernelGGL((gemm_small_reduce4_kernel<BM, BN, false>), dim3((n4 + 255) / 256), dim3(256), 0,
                            st, M, N, splits, (const float*)ws, C, ldc);
     } else if (out_f32) {
-      launch_mid<true>(M, N, K, A, lda, B, ldb, C, ldc, tiles, 1, nullptr, st, ncu);
+      launch_mid<true>(M, N, K, A, lda, B, ldb, C, ldc, tiles, 1, nullptr, st, ncu, plan);
     } else {
-      launch_mid<false>(M, N, K, A, lda, B, ldb, C, ldc, tiles, 1, nullptr, st, ncu);
+      launch_mid<false>(M, N, K, A, lda, B, ldb, C, ldc, tiles, 1, nullptr, st, ncu, plan);
     }
     return;
   }
@@ -1472,7 +1488,7 @@ hipError_t gemm_out_ln(const OutLnPlan& p, int K, const bf16* y, long ldy, const
 
 hipError_t gemm_bf16_nt(int M, int N, int K, const bf16* A, long lda, const bf16* B, long ldb,
                         void* C, long ldc, bool out_f32, hipStream_t st, float* ws, size_t ws_bytes,
-                        int ncu) {
+                        int ncu, PlanArgs* plan) {
   if (M <= 0 || N <= 0) return hipSuccess;
   const long big_tiles = (long)((M + kBigBM - 1) / kBigBM) * ((N + kBigBN - 1) / kBigBN);
   const unsigned long align = out_f32 ? 16 : 8;
@@ -1518,7 +1534,7 @@ hipError_t gemm_bf16_nt(int M, int N, int K, const bf16* A, long lda, const bf16
       else launch_big<4>(m_tail, N, K, A, lda, B, ldb, C, ldc, out_f32, (int)big_tiles - rem, 0, 0, nk, ws, st, ncu);
       const long ce = out_f32 ? 4 : 2;
       launch_gemm<128, 128>(M - m_tail, N, K, A + (long)m_tail * lda, lda, B, ldb,
-                            (char*)C + (long)m_tail * ldc * ce, ldc, out_f32, st, ws, ws_bytes, ncu);
+                            (char*)C + (long)m_tail * ldc * ce, ldc, out_f32, st, ws, ws_bytes, ncu, plan);
       return hipGetLastError();
     }
     const int n_dp = (int)big_tiles - (splits ? rem : 0);
@@ -1527,7 +1543,7 @@ hipError_t gemm_bf16_nt(int M, int N, int K, const bf16* A, long lda, const bf16
     return hipGetLastError();
   }
   // 128 x 128 tiles (4 waves of 64 x 64, two blocks per CU).
-  launch_gemm<128, 128>(M, N, K, A, lda, B, ldb, C, ldc, out_f32, st, ws, ws_bytes, ncu);
+  launch_gemm<128, 128>(M, N, K, A, lda, B, ldb, C, ldc, out_f32, st, ws, ws_bytes, ncu, plan);
   return hipGetLastError();
 }
 

@@ -6,15 +6,19 @@
 #include <stdint.h>
 
 #include "common.h"
+#include "plan.h"
 
 namespace r2l {
 
 // C[M,N] = A[M,K] . B[N,K]^T.  bf16 inputs on MFMA; output bf16 or f32.
 // ws (optional, 16-byte aligned, ws_bytes long; may be NULL): scratch for the
 // K-split partial sums of the tiles past the last whole round over ncu CUs.
+// plan (optional): when the problem (or its last tile row) runs on the
+// mid-size kernel, that launch also runs the scan's chunk planning as one
+// extra block and sets plan->hosted; otherwise plan is left as it is.
 hipError_t gemm_bf16_nt(int M, int N, int K, const bf16* A, long lda, const bf16* B, long ldb,
                         void* C, long ldc, bool out_f32, hipStream_t st, float* ws = nullptr,
-                        size_t ws_bytes = 0, int ncu = 0);
+                        size_t ws_bytes = 0, int ncu = 0, PlanArgs* plan = nullptr);
 // The K-split part alone.  gemm_bf16_nt_parts_split: the split count with
 // which gemm_bf16_nt would run this problem on its mid-size kernel split
 // along K (few 128 x 128 tiles for the GPU), else 0.  gemm_bf16_nt_parts:
@@ -88,6 +92,10 @@ hipError_t split_delta(int T_, int P, int R, const float* xdbl, bf16* dsplit, hi
 hipError_t plan_chunks(const int32_t* cu, int nseq, int T_, int Lc, int max_chunks, bool l2r,
                        int32_t* cu_clean, ChunkDesc* chunks, int32_t* n_chunks, hipStream_t st,
                        int* zero = nullptr, int n_zero = 0);
+// The same planning as the arguments of one extra block of another launch
+// (gemm_bf16_nt's plan argument; PlanArgs in plan.h).
+PlanArgs plan_args(const int32_t* cu, int nseq, int T_, int Lc, int max_chunks, bool l2r, int32_t* cu_clean,
+                   ChunkDesc* chunks, int32_t* n_chunks, int* zero = nullptr, int n_zero = 0);
 
 struct ScanArgs {
   int T, E, R, ldp;            // ldp: row stride of xdbl (fused) in floats

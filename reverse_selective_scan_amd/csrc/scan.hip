@@ -30,101 +30,27 @@ namespace r2l {
 constexpr int NS = 16;    // d_state (§4.1)
 
 // ---------------------------------------------------------------------------
-// chunk planning (one block): sanitised cu_seqlens (clamped to [0, T] and
-// made non-decreasing) and the chunk table, each sequence's chunks in scan
-// order (the chunk the scan starts in first).
+// chunk planning (one block; plan.h)
 // ---------------------------------------------------------------------------
-// Exclusive block-wide scan of one value per thread (256 threads), max or
-// sum: a shuffle scan inside each wave, then the earlier waves' totals from
-// LDS (two barriers instead of a barrier per step).
-template <bool MAX>
-R2L_DEV int block_exclusive_scan(int v, int* buf) {
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  auto op = [](int a, int b) { return MAX ? max(a, b) : a + b; };   // values are >= 0: 0 is neutral for both
-  int x = v;   // inclusive scan within the wave
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int o = __shfl_up(x, off, 64);
-    if (lane >= off) x = op(x, o);
-  }
-  if (lane == 63) buf[w] = x;
-  __syncthreads();
-  int pre = 0;
-  for (int k = 0; k < w; ++k) pre = op(pre, buf[k]);
-  const int below = __shfl_up(x, 1, 64);
-  const int excl = lane > 0 ? op(pre, below) : pre;
-  __syncthreads();   // buf is reused by the next scan
-  return excl;
+__global__ __launch_bounds__(256) void plan_chunks_kernel(PlanArgs p) {
+  __shared__ int s_v[256];
+  plan_chunks_block(p, s_v);
 }
 
-__global__ __launch_bounds__(256) void plan_chunks_kernel(const int32_t* __restrict__ cu, int nseq,
-                                                          int Tn, int Lc, int max_chunks, int l2r,
-                                                          int32_t* __restrict__ cu_clean,
-                                                          ChunkDesc* __restrict__ chunks,
-                                                          int32_t* __restrict__ n_chunks,
-                                                          int* __restrict__ zero, int n_zero) {
-  __shared__ int s_v[256];
-  const int tid = threadIdx.x;
-  for (int i = tid; i < n_zero; i += 256) zero[i] = 0;
-  const int n1 = nseq + 1;
-  const int per = (n1 + 255) / 256;
-  const int qa = min(tid * per, n1), qb = min(qa + per, n1);
-  auto clampT = [&](int v) { return v < 0 ? 0 : (v > Tn ? Tn : v); };
-  // sanitised offsets: clamp into [0, T], then running maximum
-  int m = 0;
-  for (int q = qa; q < qb; ++q) m = max(m, clampT(cu[q]));
-  int run = block_exclusive_scan<true>(m, s_v);
-  for (int q = qa; q < qb; ++q) {
-    run = max(run, clampT(cu[q]));
-    cu_clean[q] = run;
-  }
-  __syncthreads();
-  // chunk counts and each sequence's first table index
-  const int ps = (nseq + 255) / 256;
-  const int sa = min(tid * ps, nseq), sb = min(sa + ps, nseq);
-  // (and the number of 16-token state slots of the chunks: only the last
-  // chunk of a sequence can be partial)
-  int cnt = 0, slots = 0;
-  for (int q = sa; q < sb; ++q) {
-    const int len = cu_clean[q + 1] - cu_clean[q];
-    const int nc = (len + Lc - 1) / Lc;
-    cnt += nc;
-    slots += nc > 0 ? (nc - 1) * ((Lc + 15) / 16) + (len - (nc - 1) * Lc + 15) / 16 : 0;
-  }
-  int base = block_exclusive_scan<false>(cnt, s_v);
-  int slot = block_exclusive_scan<false>(slots, s_v);
-  if (tid == 255) *n_chunks = min(base + cnt, max_chunks);
-  for (int q = sa; q < sb; ++q) {
-    const int slo = cu_clean[q], send = cu_clean[q + 1];
-    const int nc = (send - slo + Lc - 1) / Lc;
-    for (int j = 0; j < nc; ++j) {
-      if (base + j >= max_chunks) break;
-      ChunkDesc d;
-      if (l2r) {            // cut from the sequence start, leftmost first
-        d.lo = slo + j * Lc;
-        d.hi = min(send, d.lo + Lc);
-      } else {              // cut from the sequence end, rightmost first
-        d.hi = send - j * Lc;
-        d.lo = max(slo, d.hi - Lc);
-      }
-      d.seq_lo = slo;
-      d.seq_end = send;
-      d.first = base;
-      d.j = j;
-      d.n_in_seq = nc;
-      d.slot0 = slot;
-      slot += (d.hi - d.lo + 15) / 16;
-      chunks[base + j] = d;
-    }
-    base += nc;
-  }
+PlanArgs plan_args(const int32_t* cu, int nseq, int Tn, int Lc, int max_chunks, bool l2r, int32_t* cu_clean,
+                   ChunkDesc* chunks, int32_t* n_chunks, int* zero, int n_zero) {
+  PlanArgs p{};
+  p.cu = cu; p.nseq = nseq; p.Tn = Tn; p.Lc = Lc; p.max_chunks = max_chunks; p.l2r = l2r ? 1 : 0;
+  p.cu_clean = cu_clean; p.chunks = chunks; p.n_chunks = n_chunks;
+  p.zero = zero; p.n_zero = zero ? n_zero : 0;
+  return p;
 }
 
 hipError_t plan_chunks(const int32_t* cu, int nseq, int Tn, int Lc, int max_chunks, bool l2r,
                        int32_t* cu_clean, ChunkDesc* chunks, int32_t* n_chunks, hipStream_t st, int* zero,
                        int n_zero) {
-  hipLaunchKernelGGL(plan_chunks_kernel, dim3(1), dim3(256), 0, st, cu, nseq, Tn, Lc, max_chunks,
-                     l2r ? 1 : 0, cu_clean, chunks, n_chunks, zero, zero ? n_zero : 0);
+  hipLaunchKernelGGL(plan_chunks_kernel, dim3(1), dim3(256), 0, st,
+                     plan_args(cu, nseq, Tn, Lc, max_chunks, l2r, cu_clean, chunks, n_chunks, zero, n_zero));
   return hipGetLastError();
 }
 
