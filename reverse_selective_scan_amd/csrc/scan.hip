@@ -410,17 +410,32 @@ __global__ __launch_bounds__(256, KS > 4 ? 1 : 2) void scan_kernel(ScanArgs a) {
           }
         }
         if constexpr (MFMA_DT) {
-          // the delta split's hi and lo halves, as they are (zeros past dt_rank)
+          // the delta split's hi and lo halves; columns at or past dt_rank
+          // are set to zero here: the split's writers cover only the x_proj
+          // width, so when it is narrower than RP the last columns hold
+          // whatever the workspace held, and a NaN there would survive its
+          // product with the zeroed weights
           bf16* dst = dl_s + r8 * DLS + c8 * DPT;
+          const int R = a.R;
+          // a bf16 pair at columns c, c + 1 (column c in the low half)
+          auto keep = [R](unsigned v, int c) { return c + 1 < R ? v : (c < R ? (v & 0xffffu) : 0u); };
           if constexpr (DPT >= 8) {
 #pragma unroll
             for (int q = 0; q < DPT / 8; ++q) {
-              *(u32x4*)(dst + 8 * q) = pd[q];
-              *(u32x4*)(dst + RP + 8 * q) = pd[DPT / 8 + q];
+              const int c0 = c8 * DPT + 8 * q;
+              u32x4 vh = pd[q], vl = pd[DPT / 8 + q];
+#pragma unroll
+              for (int d = 0; d < 4; ++d) {
+                vh[d] = keep(vh[d], c0 + 2 * d);
+                vl[d] = keep(vl[d], c0 + 2 * d);
+              }
+              *(u32x4*)(dst + 8 * q) = vh;
+              *(u32x4*)(dst + RP + 8 * q) = vl;
             }
           } else {
-            *(u32x2*)dst = u32x2{pd[0][0], pd[0][1]};
-            *(u32x2*)(dst + RP) = u32x2{pd[0][2], pd[0][3]};
+            const int c0 = c8 * DPT;
+            *(u32x2*)dst = u32x2{keep(pd[0][0], c0), keep(pd[0][1], c0 + 2)};
+            *(u32x2*)(dst + RP) = u32x2{keep(pd[0][2], c0), keep(pd[0][3], c0 + 2)};
           }
         }
         *(f32x4*)&u_s[r8][8 * c8] = f32x4{uu[0], uu[1], uu[2], uu[3]};

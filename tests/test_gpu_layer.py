@@ -187,6 +187,50 @@ def test_split_out_proj_layernorm_parts_path_matches_oracle():
     assert np.array_equal(g0.astype(np.float32).view(np.uint32), h.view(np.uint32))
 
 
+_WS_CASES = {
+    # small-input conv path; dt_rank 192 makes the delta split (256 columns)
+    # wider than the x_proj output (224), so its last columns are never written
+    "small_dt192": ([100, 7, 193, 1, 60], 256, 512, 192, 0),
+    "small_dt192_l2r": ([100, 7, 193, 1, 60], 256, 512, 192, B.R2L_FLAG_L2R),
+    # split-K conv path (more than 256 tiles of 128 tokens), same split widths
+    "split_k_dt192": ([20000, 7, 13000, 1, 300], 256, 512, 192, 0),
+    # the pages' widths at 300 tokens: in_proj on the mid-size GEMM running the
+    # chunk planning, out_proj split along K into the LayerNorm kernel
+    "pages_widths_300": ([100, 7, 193], 2048, 4096, 128, 0),
+}
+
+
+@pytest.mark.parametrize("case", sorted(_WS_CASES))
+def test_layer_output_does_not_depend_on_workspace_contents(case):
+    """The workspace's contents on entry are ignored: a workspace filled with
+    0xFF bytes (NaN as bf16 and as fp32) and one filled with zeros give the
+    same h+ and branch, bit for bit, and every value is finite.  A read of a
+    workspace byte that the same call did not write shows up here as a NaN
+    or as a difference between the two runs."""
+    lens, dm, di, dtr, flags = _WS_CASES[case]
+    _case(f"workspace contents ignored: {case} lens={lens}")
+    wl = synth.custom(lens, seed=37, h_kind="rms", d_model=dm, d_inner=di, dt_rank=dtr)
+    W = synth.make_weights(wl, affine_ln=True)
+    h, cu = synth.make_hidden(wl), wl.cu_seqlens()
+    w = B.to_device_weights(W, torch.bfloat16, DEV)
+    hd = torch.from_numpy(np.ascontiguousarray(h, np.float32)).to(torch.bfloat16).to(DEV)
+    need = B.r2l_layer_workspace_bytes(B.dims_of(w), B.R2L_BF16, wl.n_tokens, len(lens), max(lens))
+    outs = []
+    for fill in (0xFF, 0x00):
+        ws = torch.full((need,), fill, dtype=torch.uint8, device=DEV)
+        br = torch.empty(hd.shape, dtype=torch.float32, device=DEV)
+        o = B.r2l_layer_fwd(hd, w, cu, flags=flags, branch_out=br, workspace=ws)
+        torch.cuda.synchronize()
+        outs.append((o.view(torch.int16).cpu().numpy(), br.cpu().numpy()))
+        del ws
+    (oa, ba), (ob, bb) = outs
+    oa_f = torch.from_numpy(oa).view(torch.bfloat16).float().numpy()
+    assert np.isfinite(oa_f).all(), "non-finite h+ with a NaN-filled workspace"
+    assert np.isfinite(ba).all(), "non-finite branch with a NaN-filled workspace"
+    assert np.array_equal(oa, ob), "h+ depends on the workspace's contents"
+    assert np.array_equal(ba.view(np.uint32), bb.view(np.uint32)), "branch depends on the workspace's contents"
+
+
 @pytest.mark.parametrize("hint", ["too_small", "too_large"])
 def test_max_seqlen_hint_does_not_change_results(hint):
     """max_seqlen only plans the scan's time chunks: a value below the true
