@@ -120,6 +120,48 @@ def _layer_bwd_case(wl, W, h, cu, g, dtype, flags, saved=False):
     return to_np(dh), {k: to_np(v) for k, v in grads.items()}
 
 
+@pytest.mark.parametrize("dt_rank", [16, 192])
+@pytest.mark.parametrize("saved", [False, True])
+def test_layer_bwd_does_not_depend_on_buffer_contents(dt_rank, saved):
+    """The backward's workspace, the training forward's saved workspace before
+    that forward writes it, and the gradient and dh buffers handed in: filled
+    with 0xFF bytes (NaN as bf16 and as fp32) or with zeros, the gradients are
+    the same bit for bit and finite.  (dt_rank 192: the delta split is wider
+    than the x_proj output.)"""
+    lens = [300, 7, 129, 1, 64]
+    _case(f"backward buffer contents ignored: dt_rank={dt_rank} saved={saved}")
+    wl = synth.custom(lens, seed=39, h_kind="rms", d_model=256, d_inner=512, dt_rank=dt_rank)
+    W = synth.make_weights(wl, affine_ln=True)
+    h, cu = synth.make_hidden(wl), wl.cu_seqlens()
+    g = synth.make_hidden(wl, hook=5)
+    w = B.to_device_weights(W, torch.bfloat16, DEV)
+    hd = torch.from_numpy(np.ascontiguousarray(h, np.float32)).to(torch.bfloat16).to(DEV)
+    gd = torch.from_numpy(np.ascontiguousarray(g, np.float32)).to(torch.bfloat16).to(DEV)
+    dims, T, ns, ms = B.dims_of(w), wl.n_tokens, len(lens), max(lens)
+    res = []
+    for fill in (0xFF, 0x00):
+        sv = None
+        if saved:
+            need = B.r2l_layer_train_workspace_bytes(dims, B.R2L_BF16, T, ns, ms)
+            sv = torch.full((need,), fill, dtype=torch.uint8, device=DEV)
+            B.r2l_layer_fwd(hd, w, cu, flags=B.R2L_FLAG_TRAIN, workspace=sv)
+        ws = torch.full((B.r2l_layer_bwd_workspace_bytes(dims, B.R2L_BF16, T, ns, ms),), fill, dtype=torch.uint8,
+                        device=DEV)
+        grads = {k: torch.empty(w[k].shape, dtype=torch.float32, device=DEV).view(torch.uint8).fill_(fill)
+                 .view(torch.float32) for k, _ in B.Grads._fields_}
+        dh = torch.empty_like(hd).view(torch.uint8).fill_(fill).view(torch.bfloat16)
+        dh, grads = B.r2l_layer_bwd(hd, w, cu, gd, dh=dh, workspace=ws, grads=grads, saved=sv)
+        torch.cuda.synchronize()
+        res.append((dh.view(torch.int16).cpu().numpy(), {k: v.cpu().numpy() for k, v in grads.items()}))
+        del ws, sv
+    (dha, ga), (dhb, gb) = res
+    assert np.isfinite(torch.from_numpy(dha).view(torch.bfloat16).float().numpy()).all(), "non-finite dh"
+    assert np.array_equal(dha, dhb), "dh depends on the buffers' contents"
+    for k in ga:
+        assert np.isfinite(ga[k]).all(), f"non-finite d{k}"
+        assert np.array_equal(ga[k].view(np.uint32), gb[k].view(np.uint32)), f"d{k} depends on the buffers' contents"
+
+
 def _layer_err(f, got, ref, names, tol, tag):
     worst = 0.0
     for k in names:
