@@ -1076,21 +1076,22 @@ R2L_DEV void wait_stages(int n) {
   }
 }
 
-template <bool OUT_F32, int ST, bool PLAN>
-__global__ __launch_bounds__(256, ST == 4 ? 2 : 1) void gemm_bf16_mid_kernel(int M, int N, int K,
-                                                                             const bf16* __restrict__ A, long lda,
-                                                                             const bf16* __restrict__ B, long ldb,
-                                                                             void* __restrict__ Cv, long ldc,
-                                                                             int splits, int ksteps,
-                                                                             float* __restrict__ part,
-                                                                             PlanArgs plan) {
+template <bool OUT_F32, int ST, bool PLAN, int BN = kMidB>
+__global__ __launch_bounds__(256, ST == 4 && BN == kMidB ? 2 : 1) void gemm_bf16_mid_kernel(
+    int M, int N, int K, const bf16* __restrict__ A, long lda, const bf16* __restrict__ B, long ldb,
+    void* __restrict__ Cv, long ldc, int splits, int ksteps, float* __restrict__ part, PlanArgs plan) {
   static_assert(ST == 4 || ST == 8, "four or eight stages");
-  constexpr int BK = kBigBK, SROW = kBigSROW, LPT = 4, XB = ST == 8 ? kMidSBYTES : 16;
+  static_assert(BN == kMidB || BN == 2 * kMidB, "128- or 256-wide tiles");
+  // BN = 256: each wave owns 64 x 128 (2 x 4 MFMA tiles), twice the MFMAs per
+  // barrier and fragment read; no K split (the partial tiles are 128 x 128)
+  constexpr int BM = kMidB, NJ = BN / 64, STAGE = (BM + BN) * kBigSROW;
+  constexpr int BK = kBigBK, SROW = kBigSROW, LPT = (BM + BN) / 64;
+  constexpr int XB = ST == 8 ? STAGE : 16;
   // one object per stage: the compiler orders LDS copies against reads per object
-  __shared__ __attribute__((aligned(1024))) char s0[kMidSBYTES];
-  __shared__ __attribute__((aligned(1024))) char s1[kMidSBYTES];
-  __shared__ __attribute__((aligned(1024))) char s2[kMidSBYTES];
-  __shared__ __attribute__((aligned(1024))) char s3[kMidSBYTES];
+  __shared__ __attribute__((aligned(1024))) char s0[STAGE];
+  __shared__ __attribute__((aligned(1024))) char s1[STAGE];
+  __shared__ __attribute__((aligned(1024))) char s2[STAGE];
+  __shared__ __attribute__((aligned(1024))) char s3[STAGE];
   __shared__ __attribute__((aligned(1024))) char s4[XB];
   __shared__ __attribute__((aligned(1024))) char s5[XB];
   __shared__ __attribute__((aligned(1024))) char s6[XB];
@@ -1117,18 +1118,18 @@ __global__ __launch_bounds__(256, ST == 4 ? 2 : 1) void gemm_bf16_mid_kernel(int
   };
 
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
-  const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64, fr = lane & 31, fh = lane >> 5;
-  const int nTn = (N + kMidB - 1) / kMidB;
+  const int wm = (wave >> 1) * 64, wn = (wave & 1) * (BN / 2), fr = lane & 31, fh = lane >> 5;
+  const int nTn = (N + BN - 1) / BN;
   const int u = blockIdx.x;
   const int tile = splits ? u / splits : u;
   const int kbeg = splits ? (u % splits) * ksteps : 0;
   const int nk = splits ? ksteps : K / BK;
-  const int m0 = (tile / nTn) * kMidB, n0 = (tile % nTn) * kMidB;
+  const int m0 = (tile / nTn) * BM, n0 = (tile % nTn) * BN;
   // rows past M or N read as 0 through the descriptors' ranges
   const __amdgpu_buffer_rsrc_t rA = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(A + (long)m0 * lda), 0, (int)((long)min(kMidB, M - m0) * lda * 2), 0x00020000);
+      (void*)(A + (long)m0 * lda), 0, (int)((long)min(BM, M - m0) * lda * 2), 0x00020000);
   const __amdgpu_buffer_rsrc_t rB = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(B + (long)n0 * ldb), 0, (int)((long)min(kMidB, N - n0) * ldb * 2), 0x00020000);
+      (void*)(B + (long)n0 * ldb), 0, (int)((long)min(BN, N - n0) * ldb * 2), 0x00020000);
   // load i fills stage slot 256 i + tid: stage row 64 i + tid / 4 (A rows for
   // i < 2, then B rows), physical chunk tid % 4
   unsigned voff[LPT];
@@ -1137,7 +1138,7 @@ __global__ __launch_bounds__(256, ST == 4 ? 2 : 1) void gemm_bf16_mid_kernel(int
     const int row = 64 * i + tid / 4;
     const int kc = big_swz(row, tid % 4);
     voff[i] = i < 2 ? (unsigned)(((long)row * lda + kc * 8) * 2)
-                    : (unsigned)(((long)(row - kMidB) * ldb + kc * 8) * 2);
+                    : (unsigned)(((long)(row - BM) * ldb + kc * 8) * 2);
   }
   auto issue = [&](int s, int kt) {
     char* base = stage(s);
@@ -1145,35 +1146,37 @@ __global__ __launch_bounds__(256, ST == 4 ? 2 : 1) void gemm_bf16_mid_kernel(int
 #pragma unroll
     for (int i = 0; i < LPT; ++i) lds_dma16(i < 2 ? rA : rB, base + (i * 256 + wave * 64) * 16, voff[i], kb);
   };
-  int offA0[2], offB0[2], offA1[2], offB1[2];
+  int offA0[2], offA1[2], offB0[NJ], offB1[NJ];
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
-    const int ra = wm + 32 * i + fr, rb = kMidB + wn + 32 * i + fr;
+    const int ra = wm + 32 * i + fr;
     offA0[i] = ra * SROW + big_swz(ra, fh) * 16;
-    offB0[i] = rb * SROW + big_swz(rb, fh) * 16;
     offA1[i] = ra * SROW + big_swz(ra, 2 + fh) * 16;
-    offB1[i] = rb * SROW + big_swz(rb, 2 + fh) * 16;
   }
-  bf16x8 fa0[2], fb0[2], fa1[2], fb1[2];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const int rb = BM + wn + 32 * j + fr;
+    offB0[j] = rb * SROW + big_swz(rb, fh) * 16;
+    offB1[j] = rb * SROW + big_swz(rb, 2 + fh) * 16;
+  }
+  bf16x8 fa0[2], fa1[2], fb0[NJ], fb1[NJ];
   auto rd0 = [&](const char* base) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      fa0[i] = *(const bf16x8*)(base + offA0[i]);
-      fb0[i] = *(const bf16x8*)(base + offB0[i]);
-    }
+    for (int i = 0; i < 2; ++i) fa0[i] = *(const bf16x8*)(base + offA0[i]);
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) fb0[j] = *(const bf16x8*)(base + offB0[j]);
   };
   auto rd1 = [&](const char* base) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      fa1[i] = *(const bf16x8*)(base + offA1[i]);
-      fb1[i] = *(const bf16x8*)(base + offB1[i]);
-    }
+    for (int i = 0; i < 2; ++i) fa1[i] = *(const bf16x8*)(base + offA1[i]);
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) fb1[j] = *(const bf16x8*)(base + offB1[j]);
   };
-  f32x16 acc[2][2];
+  f32x16 acc[2][NJ];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < NJ; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
@@ -1197,12 +1200,12 @@ __global__ __launch_bounds__(256, ST == 4 ? 2 : 1) void gemm_bf16_mid_kernel(int
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
-      for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb0[j], fa0[i], acc[i][j], 0, 0, 0);
+      for (int j = 0; j < NJ; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb0[j], fa0[i], acc[i][j], 0, 0, 0);
     if (next) rd0(stage((s + 1) % ST));
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
-      for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb1[j], fa1[i], acc[i][j], 0, 0, 0);
+      for (int j = 0; j < NJ; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb1[j], fa1[i], acc[i][j], 0, 0, 0);
   };
   for (int kt0 = 0; kt0 < nk - ST; kt0 += ST) {
 #pragma unroll
@@ -1219,12 +1222,12 @@ __global__ __launch_bounds__(256, ST == 4 ? 2 : 1) void gemm_bf16_mid_kernel(int
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < NJ; ++j)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int r = wm + 32 * i + fr, c = wn + 32 * j + 8 * q + 4 * fh;
         const f32x4 v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
-        if (splits) {
+        if (BN == kMidB && splits) {
           *(f32x4*)(part + (long)u * (kMidB * kMidB) + r * kMidB + c) = v;
         } else if (m0 + r < M && n0 + c < N) {   // N % 4 == 0: all four columns or none
           const long off = (long)(m0 + r) * ldc + n0 + c;
@@ -1316,25 +1319,32 @@ static int mid_split(int tiles, int nk, const float* ws, size_t ws_bytes, int nc
 
 // One launch of the mid-size kernel: whole tiles into C (splits == 1), or
 // the fp32 partial tiles of a K split into part.  Eight LDS stages when every
-// block has a CU of its own.
+// block has a CU of its own.  Without a split, 128 x 256 tiles when they
+// still give every CU a block (twice the MFMAs per barrier and per fragment
+// read: 1,024 x 8,192 x 2,048 in 43 us against 48 on 128 x 128 tiles,
+// graph replays).
 template <bool OUT_F32>
 static void launch_mid(int M, int N, int K, const bf16* A, long lda, const bf16* B, long ldb, void* C, long ldc,
                        int tiles, int splits, float* part, hipStream_t st, int ncu, PlanArgs* plan = nullptr) {
   const int nk = K / kBigBK;
-  const int blocks = splits > 1 ? tiles * splits : tiles;
-  const bool deep = ncu > 0 && blocks <= ncu && (nk / splits) % 8 == 0;
+  const int wide_tiles = ((M + kMidB - 1) / kMidB) * ((N + 2 * kMidB - 1) / (2 * kMidB));
+  const bool wide = splits <= 1 && ncu > 0 && wide_tiles >= ncu;
+  const int blocks = wide ? wide_tiles : splits > 1 ? tiles * splits : tiles;
+  const bool deep = !wide && ncu > 0 && blocks <= ncu && (nk / splits) % 8 == 0;
   const int sp = splits > 1 ? splits : 0;
   const PlanArgs pa = plan ? *plan : PlanArgs{};
-#define R2L_MID(S, P)                                                                                          \
-  hipLaunchKernelGGL((gemm_bf16_mid_kernel<OUT_F32, S, P>), dim3(blocks + (P ? 1 : 0)), dim3(256), 0, st, M, N, \
-                     K, A, lda, B, ldb, C, ldc, sp, sp ? nk / sp : 0, part, pa)
+#define R2L_MID(S, P, W)                                                                                      \
+  hipLaunchKernelGGL((gemm_bf16_mid_kernel<OUT_F32, S, P, W>), dim3(blocks + (P ? 1 : 0)), dim3(256), 0, st, M, \
+                     N, K, A, lda, B, ldb, C, ldc, sp, sp ? nk / sp : 0, part, pa)
   if (plan) {
-    if (deep) R2L_MID(8, true);
-    else R2L_MID(4, true);
+    if (wide) R2L_MID(4, true, 2 * kMidB);
+    else if (deep) R2L_MID(8, true, kMidB);
+    else R2L_MID(4, true, kMidB);
     plan->hosted = 1;
   } else {
-    if (deep) R2L_MID(8, false);
-    else R2L_MID(4, false);
+    if (wide) R2L_MID(4, false, 2 * kMidB);
+    else if (deep) R2L_MID(8, false, kMidB);
+    else R2L_MID(4, false, kMidB);
   }
 #undef R2L_MID
 }
