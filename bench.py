@@ -82,8 +82,8 @@ def main():
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU: this build runs the layer on a single MI355X "
-              "(sequences shard across GPUs with no communication; see DESIGN.md). "
+        print("bench.py measures one GPU: the library runs the layer on a single MI355X "
+              "(sequences would shard across GPUs with no communication). "
               f"--gpus {args.gpus} is not supported.", file=sys.stderr)
         sys.exit(2)
 
