@@ -1275,10 +1275,20 @@ __global__ __launch_bounds__(256) void gemm_small_reduce_kernel(int M, int N, in
 
 // The same sum four columns at a time (N % 4 == 0): one 16-byte load per
 // partial and one 16- or 8-byte store per thread, partials added in order of s.
-template <int BM, int BN, bool OUT_F32>
+// PLAN: one extra block at the end of the grid runs the scan's chunk planning
+// (this kernel takes no LDS, so that block starts at once, beside the sum).
+template <int BM, int BN, bool OUT_F32, bool PLAN = false>
 __global__ __launch_bounds__(256) void gemm_small_reduce4_kernel(int M, int N, int splits,
                                                                  const float* __restrict__ part,
-                                                                 void* __restrict__ Cv, long ldc) {
+                                                                 void* __restrict__ Cv, long ldc,
+                                                                 PlanArgs plan = PlanArgs{}) {
+  if constexpr (PLAN) {
+    __shared__ int s_v[256];
+    if (blockIdx.x == gridDim.x - 1) {
+      plan_chunks_block(plan, s_v);
+      return;
+    }
+  }
   const int nTn = (N + BN - 1) / BN, nq = N / 4;
   const long e = blockIdx.x * 256L + threadIdx.x;
   const int m = (int)(e / nq), n = (int)(e % nq) * 4;
@@ -1360,14 +1370,26 @@ static void launch_gemm(int M, int N, int K, const bf16* A, long lda, const bf16
   if (mid_fits(K, A, lda, B, ldb) && N % 4 == 0 && ldc % 4 == 0 && ((uintptr_t)C & (out_f32 ? 15 : 7)) == 0) {
     const int splits = mid_split(tiles, K / kBigBK, ws, ws_bytes, ncu);
     if (splits > 1) {
-      launch_mid<true>(M, N, K, A, lda, B, ldb, C, ldc, tiles, splits, ws, st, ncu, plan);
+      // the chunk planning (when asked for) rides on the sum: a block of the
+      // split GEMM would wait for a whole CU's LDS to come free
+      launch_mid<true>(M, N, K, A, lda, B, ldb, C, ldc, tiles, splits, ws, st, ncu);
       const long n4 = (long)M * (N / 4);
-      if (out_f32)
-        hipLaunchKernelGGL((gemm_small_reduce4_kernel<BM, BN, true>), dim3((n4 + 255) / 256), dim3(256), 0, st,
-                           M, N, splits, (const float*)ws, C, ldc);
-      else
-        hipLaunchKernelGGL((gemm_small_reduce4_kernel<BM, BN, false>), dim3((n4 + 255) / 256), dim3(256), 0,
-                           st, M, N, splits, (const float*)ws, C, ldc);
+      const unsigned g4 = (unsigned)((n4 + 255) / 256);
+      if (plan) {
+        if (out_f32)
+          hipLaunchKernelGGL((gemm_small_reduce4_kernel<BM, BN, true, true>), dim3(g4 + 1), dim3(256), 0, st,
+                             M, N, splits, (const float*)ws, C, ldc, *plan);
+        else
+          hipLaunchKernelGGL((gemm_small_reduce4_kernel<BM, BN, false, true>), dim3(g4 + 1), dim3(256), 0, st,
+                             M, N, splits, (const float*)ws, C, ldc, *plan);
+        plan->hosted = 1;
+      } else if (out_f32) {
+        hipLaunchKernelGGL((gemm_small_reduce4_kernel<BM, BN, true>), dim3(g4), dim3(256), 0, st,
+                           M, N, splits, (const float*)ws, C, ldc, PlanArgs{});
+      } else {
+        hipLaunchKernelGGL((gemm_small_reduce4_kernel<BM, BN, false>), dim3(g4), dim3(256), 0,
+                           st, M, N, splits, (const float*)ws, C, ldc, PlanArgs{});
+      }
     } else if (out_f32) {
       launch_mid<true>(M, N, K, A, lda, B, ldb, C, ldc, tiles, 1, nullptr, st, ncu, plan);
     } else {
