@@ -710,8 +710,9 @@ int r2l_layer_fwd(const r2l_dims* d, r2l_dtype act, uint32_t flags, const r2l_we
     const int ncu = num_cus();
     float* scratch = at<float>(workspace, lp.off_scratch);
     bf16* dsplit = delta_split_width(R) > 0 ? at<bf16>(workspace, lp.off_dsplit) : nullptr;
-    // in_proj; when it runs (or ends) on the mid-size kernel, that launch
-    // also runs the chunk planning, as one extra block (a launch fewer)
+    // in_proj; when it runs (or ends) on the mid-size kernel, one of its
+    // launches (the GEMM, or its split-K sum) also runs the chunk planning,
+    // as one extra block (a launch fewer)
     R2L_RUN("in_proj_gemm", st, gemm_bf16_nt(T, 2 * E, D, (const bf16*)h_in, D, (const bf16*)w->in_proj_w, D, xz, 2L * E, false, st,
                                              scratch, kSplitScratch, ncu, &plan));
     if (!plan.hosted)

@@ -14,8 +14,9 @@ namespace r2l {
 // ws (optional, 16-byte aligned, ws_bytes long; may be NULL): scratch for the
 // K-split partial sums of the tiles past the last whole round over ncu CUs.
 // plan (optional): when the problem (or its last tile row) runs on the
-// mid-size kernel, that launch also runs the scan's chunk planning as one
-// extra block and sets plan->hosted; otherwise plan is left as it is.
+// mid-size kernel, one of its launches (the GEMM, or the sum of a K split)
+// also runs the scan's chunk planning as one extra block and sets
+// plan->hosted; otherwise plan is left as it is.
 hipError_t gemm_bf16_nt(int M, int N, int K, const bf16* A, long lda, const bf16* B, long ldb,
                         void* C, long ldc, bool out_f32, hipStream_t st, float* ws = nullptr,
                         size_t ws_bytes = 0, int ncu = 0, PlanArgs* plan = nullptr);
