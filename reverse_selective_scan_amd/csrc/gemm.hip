@@ -1047,14 +1047,15 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_pers_kernel(int M, int N, in
   }
 }
 
-// Mid-size kernel (the 128 x 128 tiles of small problems and of the last
-// tile row of large ones): the big kernel's pipeline on 128 x 128 tiles.
-// ST LDS stages of 32-wide K steps (16 KB each) filled by buffer_load ... lds
-// ST - 1 steps ahead, the same swizzle and the same barrier / vmcnt
-// discipline; each wave owns a 64 x 64 quarter (2 x 2 MFMA tiles).  ST = 4
-// fits two blocks in a CU; ST = 8 (128 KB) is for launches of at most one
-// block per CU, where a block's own copies in flight set the pace.  The last
-// ST steps issue nothing new and wait for exactly the copies they read.
+// Mid-size kernel (the tiles of small problems and of the last tile row of
+// large ones): the big kernel's pipeline on 128 x BN tiles, BN = 128 or 256.
+// ST LDS stages of 32-wide K steps ((128 + BN) rows of 64 bytes: 16 KB, or
+// 24 KB for 256-wide tiles) filled by buffer_load ... lds ST - 1 steps
+// ahead, the same swizzle and the same barrier / vmcnt discipline; each wave
+// owns a 64 x BN/2 part (2 x BN/64 MFMA tiles).  ST = 4 fits two 128 x 128
+// blocks in a CU; ST = 8 (128 KB) is for launches of at most one block per
+// CU, where a block's own copies in flight set the pace.  The last ST steps
+// issue nothing new and wait for exactly the copies they read.
 // splits == 0: block b computes tile b (row-major) into C.  splits > 0:
 // block u computes K steps [s ksteps, (s+1) ksteps), s = u % splits, of tile
 // u / splits as an fp32 partial sum into part[u][128][128], added by
@@ -1082,8 +1083,8 @@ __global__ __launch_bounds__(256, ST == 4 && BN == kMidB ? 2 : 1) void gemm_bf16
     void* __restrict__ Cv, long ldc, int splits, int ksteps, float* __restrict__ part, PlanArgs plan) {
   static_assert(ST == 4 || ST == 8, "four or eight stages");
   static_assert(BN == kMidB || BN == 2 * kMidB, "128- or 256-wide tiles");
-  // BN = 256: each wave owns 64 x 128 (2 x 4 MFMA tiles), twice the MFMAs per
-  // barrier and fragment read; no K split (the partial tiles are 128 x 128)
+  // BN = 256: twice the MFMAs per barrier and per fragment read; no K split
+  // (the partial tiles are 128 x 128)
   constexpr int BM = kMidB, NJ = BN / 64, STAGE = (BM + BN) * kBigSROW;
   constexpr int BK = kBigBK, SROW = kBigSROW, LPT = (BM + BN) / 64;
   constexpr int XB = ST == 8 ? STAGE : 16;
@@ -1303,8 +1304,8 @@ __global__ __launch_bounds__(256) void gemm_small_reduce4_kernel(int M, int N, i
 // Enough 256 x 256 tiles for the large-problem kernel: a whole round over
 // the CUs, or at least half of one with a long K (a weight gradient summed
 // over tokens), which that kernel splits along K.  With fewer tiles and a
-// short K, the 128 x 128 kernel's four times as many tiles fill the GPU
-// instead (measured at 1024 x 8192 x 2048: 48 us against 50-57).
+// short K, the mid-size kernel's smaller tiles fill the GPU instead
+// (measured at 1024 x 8192 x 2048: 43-48 us against 50-57).
 static bool big_enough(long big_tiles, int K) { return big_tiles >= 256 || (big_tiles >= 128 && K > 4096); }
 
 // The mid-size kernel takes whole 128-wide K chunks and 16-byte operand rows
