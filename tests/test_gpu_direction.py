@@ -195,6 +195,24 @@ def test_bf16_layer_l2r_split_k_conv_path_matches_oracle():
     check_bf16("branch l2r", gr, rref, fr, TOL_BF16_BRANCH)
 
 
+def test_bf16_layer_l2r_at_pages_widths_matches_oracle():
+    """300 tokens at the pages' widths (D = 2048, E = 4096, dt_rank 128),
+    left to right: in_proj on the mid-size GEMM whose extra block plans the
+    time chunks, and out_proj split along K with the LayerNorm kernel adding
+    the partial tiles.  Sequences of 100, 7 and 193 tokens cross the 128-row
+    tiles and the last tile is ragged."""
+    lens = [100, 7, 193]
+    _case(f"pages widths l2r lens={lens}")
+    wl = synth.custom(lens, seed=36, h_kind="rms", d_model=2048, d_inner=4096, dt_rank=128)
+    W = synth.make_weights(wl, affine_ln=True)
+    h, cu = synth.make_hidden(wl), wl.cu_seqlens()
+    ref, rref = O.reverse_mamba_layer(h, cu, W, float(W["s"]), return_branch=True, direction="l2r")
+    fo, fr = bf16_floor.layer_rounded(h, cu, W, float(W["s"]), direction="l2r")
+    g, gr = _gpu_layer(W, h, cu, torch.bfloat16, L2R, branch=True)
+    check_bf16("out l2r", g, ref, fo, TOL_BF16)
+    check_bf16("branch l2r", gr, rref, fr, TOL_BF16_BRANCH)
+
+
 @pytest.mark.parametrize("act", ["f32", "bf16"])
 def test_layer_l2r_is_mirrored_r2l_bitwise(act):
     """Below the split-K conv's size every per-token step is independent of

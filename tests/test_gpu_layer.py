@@ -197,6 +197,7 @@ _WS_CASES = {
     # the pages' widths at 300 tokens: in_proj on the mid-size GEMM running the
     # chunk planning, out_proj split along K into the LayerNorm kernel
     "pages_widths_300": ([100, 7, 193], 2048, 4096, 128, 0),
+    "pages_widths_300_l2r": ([100, 7, 193], 2048, 4096, 128, B.R2L_FLAG_L2R),
 }
 
 
