@@ -424,10 +424,12 @@ __global__ __launch_bounds__(256, KS > 4 ? 1 : 2) void scan_kernel(ScanArgs a) {
             for (int q = 0; q < DPT / 8; ++q) {
               const int c0 = c8 * DPT + 8 * q;
               u32x4 vh = pd[q], vl = pd[DPT / 8 + q];
+              if (R < RP) {   // uniform: at a dt_rank that fills RP nothing is masked
 #pragma unroll
-              for (int d = 0; d < 4; ++d) {
-                vh[d] = keep(vh[d], c0 + 2 * d);
-                vl[d] = keep(vl[d], c0 + 2 * d);
+                for (int d = 0; d < 4; ++d) {
+                  vh[d] = keep(vh[d], c0 + 2 * d);
+                  vl[d] = keep(vl[d], c0 + 2 * d);
+                }
               }
               *(u32x4*)(dst + 8 * q) = vh;
               *(u32x4*)(dst + RP + 8 * q) = vl;
