@@ -121,7 +121,12 @@ template <typename T> R2L_DEV float softplus_dt(float v);
 template <> R2L_DEV float softplus_dt<float>(float v) { return softplus_f(v); }
 template <> R2L_DEV float softplus_dt<bf16>(float v) {
   const float w = exp2_fast(-fabsf(v) * kLog2e);
-  return fmaxf(v, 0.0f) + __builtin_amdgcn_logf(1.0f + w) * kLn2;
+  // max(v, 0) as the median of (v, 0, 3e38): fmaxf on an MFMA result would
+  // first be canonicalised (one more instruction), and with +inf as the bound
+  // the compiler turns the median back into that fmaxf.  Pre-activations
+  // above 3e38 (clamped here) give no meaningful dt either way; a NaN still
+  // reaches dt through the log term.
+  return __builtin_amdgcn_fmed3f(v, 0.0f, 3.0e38f) + __builtin_amdgcn_logf(1.0f + w) * kLn2;
 }
 
 // ---------------------------------------------------------------------------
@@ -475,30 +480,29 @@ __global__ __launch_bounds__(256, KS > 4 ? 1 : 2) void scan_kernel(ScanArgs a) {
     // ---------------- M: dt = softplus(delta . W_dt^T + b) ----------------
     if constexpr (FUSED) {
       if constexpr (MFMA_DT) {
-        // four independent accumulator chains (two row tiles x the lo and
-        // hi parts of delta), interleaved so that no MFMA waits for the
-        // previous one's result
-        f32x4 acc[TB / 16][2];
+        // one accumulator chain per row tile, started at the dt bias, taking
+        // the hi and the lo part of delta in turn (an MFMA that only adds to
+        // the previous one's accumulator issues back to back with it); the
+        // two row tiles' chains alternate
+        f32x4 acc[TB / 16];
 #pragma unroll
-        for (int rt = 0; rt < TB / 16; ++rt)
-#pragma unroll
-          for (int part = 0; part < 2; ++part) acc[rt][part] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        for (int rt = 0; rt < TB / 16; ++rt) acc[rt] = f32x4{dtb_col, dtb_col, dtb_col, dtb_col};
         const bf16* drow = dl_s + (lane & 15) * DLS + (lane >> 4) * 8;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-          for (int rt = 0; rt < TB / 16; ++rt)
+          for (int part = 0; part < 2; ++part)
 #pragma unroll
-            for (int part = 0; part < 2; ++part)
-              acc[rt][part] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                  *(const bf16x8*)(drow + rt * 16 * DLS + part * RP + ks * 32), wdt[ks], acc[rt][part], 0, 0, 0);
+            for (int rt = 0; rt < TB / 16; ++rt)
+              acc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                  *(const bf16x8*)(drow + rt * 16 * DLS + part * RP + ks * 32), wdt[ks], acc[rt], 0, 0, 0);
 #pragma unroll
         for (int rt = 0; rt < TB / 16; ++rt) {
           // D layout: lane holds rows 4 (lane >> 4) + i, column (lane & 15)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int rr = rt * 16 + 4 * (lane >> 4) + i;
-            const float dtv = softplus_dt<T>((acc[rt][1][i] + acc[rt][0][i]) + dtb_col);
+            const float dtv = softplus_dt<T>(acc[rt][i]);
             pre_s[rr][dcol] = make_float2(dtv, dtv * u_s[rr][dcol]);
           }
         }
