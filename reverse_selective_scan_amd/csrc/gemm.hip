@@ -1479,7 +1479,9 @@ hipError_t gemm_bf16_nt_parts(int M, int N, int K, const bf16* A, long lda, cons
 
 OutLnPlan plan_out_ln(int T, int D, int K, int ncu) {
   OutLnPlan p{};
-  if (D % kBigBN || K % kBigBK || ncu <= 0) return p;
+  // (the K loop walks whole groups of four 32-deep stages, as the big
+  // kernel's does: a K of 64 modulo 128 runs the unfused path)
+  if (D % kBigBN || K % (kBigBK * kBigST) || ncu <= 0) return p;
   const int nt = D / kBigBN;
   const int grid = 8 * nt * (ncu / (8 * nt));   // whole row blocks on every XCD, at most one block per CU
   if (grid <= 0) return p;

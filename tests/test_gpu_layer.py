@@ -161,6 +161,30 @@ def test_fused_out_proj_layernorm_path_matches_oracle():
         assert "out_proj_ln" in names and "ln_gate" in names, names
 
 
+def test_out_proj_with_d_inner_64_mod_128_matches_oracle():
+    """d_inner 576 (9 x 64; out_proj's K is 18 steps of 32, not whole groups
+    of four): the fused out_proj + LayerNorm kernel, whose K loop walks whole
+    groups of four steps, must not run; the layer takes the unfused path and
+    still matches the oracle, with a round's worth of rows at d_model 512."""
+    lens = [20000, 7, 13000, 1, 300]
+    _case(f"d_inner 576 out_proj lens={lens}")
+    wl = synth.custom(lens, seed=39, h_kind="rms", d_model=512, d_inner=576, dt_rank=32)
+    W = synth.make_weights(wl, affine_ln=True)
+    h, cu = synth.make_hidden(wl), wl.cu_seqlens()
+    s = float(W["s"])
+    B.timing_reset()
+    B.timing_enable(True)
+    g, gr = _gpu_layer(wl, W, h, cu, branch=True)
+    names = B.timing_read()
+    B.timing_enable(False)
+    print(f"kernels: {sorted(names)}", flush=True)
+    ref, rref = O.reverse_mamba_layer(h, cu, W, s, return_branch=True)
+    fo, fr = bf16_floor.layer_rounded(h, cu, W, s)
+    check_bf16("d_inner 576 out", g, ref, fo, TOL_BF16)
+    check_bf16("d_inner 576 branch", gr, rref, fr, TOL_BF16_BRANCH)
+    assert "out_proj_ln" not in names, names
+
+
 def test_split_out_proj_layernorm_parts_path_matches_oracle():
     """300 tokens at the pages' widths (D = 2048, E = 4096): out_proj runs on
     the mid-size GEMM split four ways along K, and the LayerNorm kernel adds
