@@ -338,7 +338,7 @@ int run_scan_bwd(r2l_dtype act, int E, int R, int T, int nseq, const void* u, in
 
 // Workspace of the layer backward: every recomputed activation, the
 // gradient buffers and the transposed GEMM operands (tokens padded to Tp, a
-// multiple of 128, in the transposes), the forward scan's and the scan
+// multiple of 128 or 1,024, in the transposes), the forward scan's and the scan
 // backward's own regions, and the GEMM split scratch.
 struct LayerBwdPlan {
   size_t xz, u, xdbl, xdbl2, xdbl3, delta, dt, yg, o, scanf, dout, gx, gr, do_a, doT, ygT, wT, dyg, du, ddt, dz, dB,
@@ -354,7 +354,13 @@ LayerBwdPlan plan_layer_bwd(const r2l_dims* d, r2l_dtype act, int64_t T, int32_t
   const size_t sa = act == R2L_BF16 ? 2 : 4, f = 4;
   const size_t D = d->d_model, E = d->d_inner, N = d->d_state, R = d->dt_rank, P = R + 2 * N;
   const size_t Tz = (size_t)T;
-  p.Tp = (int)(((T + 127) / 128) * 128);
+  // Tp is the K of the weight-gradient GEMMs (sums over tokens).  A multiple
+  // of 1,024 (when that pads by at most 1/32 of T) lets them split K over
+  // the CUs their few output tiles leave idle: the splits keep whole 128-deep
+  // chunks, so e.g. 33,024 tokens as 33,152 (1,036 steps of 32) allow none,
+  // as 33,792 (1,056 steps) two to eight.  The padded tokens are zeros.
+  p.Tp = (int)(((T + 1023) / 1024) * 1024);
+  if (p.Tp - T > T / 32) p.Tp = (int)(((T + 127) / 128) * 128);
   const size_t Tp = (size_t)p.Tp;
   size_t off = 0;
   auto take = [&](size_t bytes) { const size_t o = off; off = align_up(off + bytes); return o; };
