@@ -3,9 +3,13 @@
 // Models", §3.4 steps 1-4, for training the sidecar: §3.5, plug-in mode).
 // Each is a plain, memory-bound pass; every sum over tokens is taken in a
 // fixed order (per-block partial sums, then a second pass over the blocks).
+#include <type_traits>
+
 #include "kernels.h"
 
 namespace r2l {
+
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int KC_ = 4;   // d_conv
 
@@ -30,9 +34,44 @@ __global__ __launch_bounds__(256) void transpose_kernel(int rows, int cols, int 
   }
 }
 
+// The same for bf16 with 16-byte rows (cols, ld_in and rows_pad multiples of
+// 8, both pointers 16-byte aligned): each lane moves an 8 x 8 block, eight
+// 16-byte row loads, the 16-bit transpose in registers (one byte permute per
+// output dword) and eight 16-byte row stores; a wave covers 64 x 64, so
+// eight lanes share each 128-byte row segment on both sides.  Block = four
+// waves side by side along the columns.
+__global__ __launch_bounds__(256) void transpose16_kernel(int rows, int cols, int rows_pad, const bf16* __restrict__ in,
+                                                          long ld_in, bf16* __restrict__ out) {
+  const int lane = lane_id(), w = wave_id();
+  const int c = (blockIdx.x * 4 + w) * 64 + 8 * (lane >> 3);   // the lane's first input column
+  const int r = blockIdx.y * 64 + 8 * (lane & 7);              // its first input row
+  if (c >= cols || r >= rows_pad) return;
+  u32x4 v[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    v[j] = r + j < rows ? *(const u32x4*)(in + (long)(r + j) * ld_in + c) : u32x4{0u, 0u, 0u, 0u};
+  // output row c + i, dword d = (element i of input row 2d, of row 2d + 1)
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const unsigned sel = (i & 1) ? 0x07060302u : 0x05040100u;   // high / low bf16 of each input dword
+    u32x4 o;
+#pragma unroll
+    for (int d = 0; d < 4; ++d) o[d] = __builtin_amdgcn_perm(v[2 * d + 1][i >> 1], v[2 * d][i >> 1], sel);
+    *(u32x4*)(out + (long)(c + i) * rows_pad + r) = o;
+  }
+}
+
 template <typename Tin, typename Tout>
 hipError_t transpose(int rows, int cols, int rows_pad, const Tin* in, long ld_in, Tout* out, hipStream_t st) {
   if (cols <= 0 || rows_pad <= 0) return hipSuccess;
+  if constexpr (std::is_same<Tin, bf16>::value && std::is_same<Tout, bf16>::value) {
+    if (cols % 8 == 0 && ld_in % 8 == 0 && rows_pad % 8 == 0 && ((uintptr_t)in & 15) == 0 &&
+        ((uintptr_t)out & 15) == 0) {
+      dim3 grid((cols + 255) / 256, (rows_pad + 63) / 64);
+      hipLaunchKernelGGL(transpose16_kernel, grid, dim3(256), 0, st, rows, cols, rows_pad, in, ld_in, out);
+      return hipGetLastError();
+    }
+  }
   dim3 grid((cols + 63) / 64, (rows_pad + 63) / 64);
   hipLaunchKernelGGL((transpose_kernel<Tin, Tout>), grid, dim3(256), 0, st, rows, cols, rows_pad, in, ld_in, out);
   return hipGetLastError();

@@ -225,13 +225,13 @@ __global__ __launch_bounds__(256, 2) void scan_bwd_adj_kernel(ScanBwdArgs a) {
       for (int i = 0; i < 4; ++i) {
         const float at = exp2_fast(p.x * A2[i]);
         const float lam = fmaf(g, Cv[i], mu[i]);
-        const float qa = lam * hn[i] * at;       // lambda h_{t+1} a_t
+        mu[i] = at * lam;                        // a_t lambda_t, carried to t+1
+        const float qa = mu[i] * hn[i];          // lambda h_{t+1} a_t
         v[i] = g * hs[r][i];                     // dC
         v[4 + i] = lam * p.y;                    // dB
         s1 = fmaf(lam, Bv[i], s1);
         s2 = fmaf(qa, An[i], s2);
         dAacc[i] = fmaf(qa, p.x, dAacc[i]);
-        mu[i] = at * lam;
       }
       s1_s[w][r][lane] = s1;
       s2_s[w][r][lane] = s2;
