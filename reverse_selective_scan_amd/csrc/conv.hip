@@ -6,6 +6,8 @@
 // with x past the end of t's sequence taken as 0.  With L2R (the left-to-
 // right control of §4.4, Table 4) the taps look left instead: x[t-j], with
 // x before the start of t's sequence taken as 0.
+#include <type_traits>
+
 #include "kernels.h"
 
 namespace r2l {
@@ -116,10 +118,92 @@ __global__ __launch_bounds__(256) void conv_silu_kernel(int Tn, int E, const T* 
   }
 }
 
+// The same for bf16 with 16-byte channel groups (E and ld_x multiples of 8;
+// x, u, taps and bias 16-byte aligned): a lane owns 8 consecutive channels,
+// so a wave covers 8 tokens of 512 channels and every load and store
+// instruction moves 1 KB of one token row in 16-byte pieces.  The
+// arithmetic per (token, channel) is the kernel's above, in the same order,
+// so both give the same bits.
+template <bool L2R>
+__global__ __launch_bounds__(256) void conv_silu16_kernel(int Tn, int E, const bf16* __restrict__ x, long ld_x,
+                                                          const bf16* __restrict__ cw, const bf16* __restrict__ cb,
+                                                          bf16* __restrict__ u, const int32_t* __restrict__ cu,
+                                                          int nseq) {
+  const int lane = lane_id();
+  const int e = (blockIdx.y * 64 + lane) * 8;   // the lane's first channel
+  const int t0 = __builtin_amdgcn_readfirstlane(blockIdx.x * 32 + wave_id() * 8);
+  if (t0 >= Tn) return;
+  const bool on = e < E;                        // lanes past the channels load and store nothing
+  float wt[8][KC], b[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    b[c] = 0.0f;
+#pragma unroll
+    for (int k = 0; k < KC; ++k) wt[c][k] = 0.0f;
+  }
+  if (on) {
+    // taps of channels e + 2q and e + 2q + 1 in one 16-byte piece
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const bf16x8 tv = *(const bf16x8*)(cw + (long)e * KC + 8 * q);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) wt[2 * q + k / KC][k % KC] = (float)tv[k];
+    }
+    const bf16x8 bv = *(const bf16x8*)(cb + e);
+#pragma unroll
+    for (int c = 0; c < 8; ++c) b[c] = (float)bv[c];
+  }
+  // rows t0 .. t0+10 (R2L) or t0-3 .. t0+7 (L2R), all loads first
+  constexpr int NR = 8 + KC - 1;
+  const int rbase = L2R ? t0 - (KC - 1) : t0;
+  bf16x8 xv[NR];
+#pragma unroll
+  for (int i = 0; i < NR; ++i) {
+    const int row = rbase + i;
+    xv[i] = on && row >= 0 && row < Tn ? *(const bf16x8*)(x + (long)row * ld_x + e) : bf16x8{};
+  }
+  int sl = seq_start_of(cu, nseq, t0), se = seq_end_of(cu, nseq, t0, Tn);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int t = t0 + i;
+    if (t >= Tn) break;
+    if (t >= se) {
+      sl = seq_start_of(cu, nseq, t);
+      se = seq_end_of(cu, nseq, t, Tn);
+    }
+    bf16x8 o;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      float acc = b[c];
+#pragma unroll
+      for (int j = 0; j < KC; ++j) {
+        const int row = L2R ? t - j : t + j;
+        const float xr = (float)xv[L2R ? i + KC - 1 - j : i + j][c];
+        if (L2R ? row >= sl : row < se) acc = fmaf(wt[c][KC - 1 - j], xr, acc);
+      }
+      o[c] = from_f32<bf16>(silu_fast(acc));
+    }
+    if (on) *(bf16x8*)(u + (long)t * E + e) = o;
+  }
+}
+
 template <typename T>
 hipError_t conv_silu(int Tn, int E, const T* x, long ld_x, const T* conv_w, const T* conv_b, T* u,
                      const int32_t* cu, int nseq, bool l2r, hipStream_t st) {
   if (Tn <= 0) return hipSuccess;
+  if constexpr (std::is_same<T, bf16>::value) {
+    auto a16 = [](const void* p) { return ((uintptr_t)p & 15) == 0; };
+    if (E % 8 == 0 && ld_x % 8 == 0 && a16(x) && a16(u) && a16(conv_w) && a16(conv_b)) {
+      dim3 grid16((Tn + 31) / 32, (E + 511) / 512);
+      if (l2r)
+        hipLaunchKernelGGL((conv_silu16_kernel<true>), grid16, dim3(256), 0, st, Tn, E, x, ld_x, conv_w, conv_b, u,
+                           cu, nseq);
+      else
+        hipLaunchKernelGGL((conv_silu16_kernel<false>), grid16, dim3(256), 0, st, Tn, E, x, ld_x, conv_w, conv_b, u,
+                           cu, nseq);
+      return hipGetLastError();
+    }
+  }
   dim3 grid((Tn + 31) / 32, E / 64);
   if (l2r)
     hipLaunchKernelGGL((conv_silu_kernel<T, true>), grid, dim3(256), 0, st, Tn, E, x, ld_x, conv_w,
