@@ -109,10 +109,51 @@ __global__ __launch_bounds__(256) void elementwise_kernel(int rows, int cols, co
   }
 }
 
+// The same for f32 -> f32 four columns per thread (16-byte accesses), the
+// same arithmetic per element.
+template <int OP>
+__global__ __launch_bounds__(256) void elementwise4_kernel(int rows, int cols, const float* __restrict__ in,
+                                                           long ld_in, const float* __restrict__ aux, long ld_aux,
+                                                           const float* __restrict__ vec, float* __restrict__ out,
+                                                           long ld_out) {
+  const int c = (blockIdx.x * 256 + threadIdx.x) * 4;
+  if (c >= cols) return;
+  f32x4 vv = {};
+  if (OP == kSoftplusBias) vv = *(const f32x4*)(vec + c);
+  for (int r = blockIdx.y; r < rows; r += gridDim.y) {
+    const f32x4 x = *(const f32x4*)(in + (long)r * ld_in + c);
+    f32x4 a = {};
+    if (OP == kDtPre || OP == kAddTo) a = *(const f32x4*)(aux + (long)r * ld_aux + c);
+    f32x4 o;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const float v = x[k];
+      if (OP == kConvert) o[k] = v;
+      else if (OP == kSoftplusBias) o[k] = softplus_f(v + vv[k]);
+      else if (OP == kDtPre) o[k] = v * (1.0f - expf(-a[k]));
+      else o[k] = v + a[k];
+    }
+    *(f32x4*)(out + (long)r * ld_out + c) = o;
+  }
+}
+
 template <int OP, typename Tin, typename Tout>
 hipError_t elementwise(int rows, int cols, const Tin* in, long ld_in, const float* aux, long ld_aux,
                        const float* vec, Tout* out, long ld_out, hipStream_t st) {
   if (rows <= 0 || cols <= 0) return hipSuccess;
+  if constexpr (std::is_same<Tin, float>::value && std::is_same<Tout, float>::value) {
+    auto a16 = [](const void* p) { return ((uintptr_t)p & 15) == 0; };
+    const bool aux_ok = !(OP == kDtPre || OP == kAddTo) || (ld_aux % 4 == 0 && a16(aux));
+    if (cols % 4 == 0 && ld_in % 4 == 0 && ld_out % 4 == 0 && a16(in) && a16(out) && aux_ok &&
+        (OP != kSoftplusBias || a16(vec))) {
+      const int cb4 = (cols / 4 + 255) / 256;
+      const int rg4 = rows < 65535 ? rows : 65535;
+      const int ry4 = cb4 * rg4 > 16384 ? (16384 + cb4 - 1) / cb4 : rg4;
+      hipLaunchKernelGGL((elementwise4_kernel<OP>), dim3(cb4, ry4 > 0 ? ry4 : 1), dim3(256), 0, st, rows, cols, in,
+                         ld_in, aux, ld_aux, vec, out, ld_out);
+      return hipGetLastError();
+    }
+  }
   const int cb = (cols + 255) / 256;
   const int rg = rows < 65535 ? rows : 65535;
   const int ry = cb * rg > 16384 ? (16384 + cb - 1) / cb : rg;   // about 16K blocks
@@ -161,10 +202,91 @@ __global__ __launch_bounds__(256) void fused_t_kernel(int rows, int cols, int ro
   }
 }
 
+// The same pass for f32 -> bf16 with 16-byte rows (cols, ld_rm and rows_pad
+// multiples of 8, ld_in and ld_aux of 4, pointers 16-byte aligned): each lane
+// takes an 8 x 8 block as transpose16_kernel does (32-byte f32 row loads,
+// 16-byte bf16 row stores, the transposed copy by byte permutes in
+// registers).  Column sums: each lane adds its 8 rows in order, then the 8
+// lanes of a 64-row tile combine by a fixed butterfly.
+template <int OP>
+__global__ __launch_bounds__(256) void fused_t16_kernel(int rows, int cols, int rows_pad, const float* __restrict__ in,
+                                                        long ld_in, const float* __restrict__ aux, long ld_aux,
+                                                        bf16* __restrict__ out_rm, long ld_rm,
+                                                        bf16* __restrict__ out_t, float* __restrict__ colpart) {
+  const int lane = lane_id(), w = wave_id();
+  const int c = (blockIdx.x * 4 + w) * 64 + 8 * (lane >> 3);   // the lane's first column
+  const int r0 = blockIdx.y * 64, r = r0 + 8 * (lane & 7);     // the tile's and the lane's first row
+  if (c >= cols) return;                                       // (whole 8-lane groups: no lane of a butterfly leaves)
+  u32x4 pk[8];
+  float sum[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) sum[k] = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    float v[8];
+    if (r + j < rows) {
+      const f32x4 a0 = *(const f32x4*)(in + (long)(r + j) * ld_in + c);
+      const f32x4 a1 = *(const f32x4*)(in + (long)(r + j) * ld_in + c + 4);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) { v[k] = a0[k]; v[4 + k] = a1[k]; }
+      if (OP == kDtPre) {
+        const f32x4 b0 = *(const f32x4*)(aux + (long)(r + j) * ld_aux + c);
+        const f32x4 b1 = *(const f32x4*)(aux + (long)(r + j) * ld_aux + c + 4);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          v[k] = v[k] * (1.0f - expf(-b0[k]));
+          v[4 + k] = v[4 + k] * (1.0f - expf(-b1[k]));
+        }
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) v[k] = 0.0f;
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) sum[k] += v[k];
+    const bf16x8 b = {(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3], (bf16)v[4], (bf16)v[5], (bf16)v[6], (bf16)v[7]};
+    pk[j] = __builtin_bit_cast(u32x4, b);
+    if (out_rm && r + j < rows) *(u32x4*)(out_rm + (long)(r + j) * ld_rm + c) = pk[j];
+  }
+  if (colpart && r0 < rows) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      sum[k] += __shfl_xor(sum[k], 1, 64);
+      sum[k] += __shfl_xor(sum[k], 2, 64);
+      sum[k] += __shfl_xor(sum[k], 4, 64);
+    }
+    if ((lane & 7) == 0) {
+      float* dst = colpart + (long)blockIdx.y * cols + c;
+      *(f32x4*)dst = f32x4{sum[0], sum[1], sum[2], sum[3]};
+      *(f32x4*)(dst + 4) = f32x4{sum[4], sum[5], sum[6], sum[7]};
+    }
+  }
+  if (out_t && r < rows_pad) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const unsigned sel = (i & 1) ? 0x07060302u : 0x05040100u;
+      u32x4 o;
+#pragma unroll
+      for (int d = 0; d < 4; ++d) o[d] = __builtin_amdgcn_perm(pk[2 * d + 1][i >> 1], pk[2 * d][i >> 1], sel);
+      *(u32x4*)(out_t + (long)(c + i) * rows_pad + r) = o;
+    }
+  }
+}
+
 template <int OP, typename Tin, typename Tout>
 hipError_t fused_t(int rows, int cols, int rows_pad, const Tin* in, long ld_in, const float* aux, long ld_aux,
                    Tout* out_rm, long ld_rm, Tout* out_t, float* colpart, hipStream_t st) {
   if (rows <= 0 || cols <= 0) return hipSuccess;
+  if constexpr (std::is_same<Tin, float>::value && std::is_same<Tout, bf16>::value) {
+    auto a16 = [](const void* p) { return ((uintptr_t)p & 15) == 0; };
+    if (cols % 8 == 0 && rows_pad % 8 == 0 && ld_in % 4 == 0 && a16(in) && (OP != kDtPre || (ld_aux % 4 == 0 && a16(aux))) &&
+        (!out_rm || (ld_rm % 8 == 0 && a16(out_rm))) && (!out_t || a16(out_t)) && (!colpart || a16(colpart))) {
+      const int ry16 = ((out_t ? rows_pad : rows) + 63) / 64;
+      hipLaunchKernelGGL((fused_t16_kernel<OP>), dim3((cols + 255) / 256, ry16), dim3(256), 0, st, rows, cols, rows_pad,
+                         in, ld_in, aux, ld_aux, out_rm, ld_rm, out_t, colpart);
+      return hipGetLastError();
+    }
+  }
   const int ry = ((out_t ? rows_pad : rows) + 63) / 64;
   hipLaunchKernelGGL((fused_t_kernel<OP, Tin, Tout>), dim3((cols + 63) / 64, ry), dim3(256), 0, st, rows, cols,
                      rows_pad, in, ld_in, aux, ld_aux, out_rm, ld_rm, out_t, colpart);
