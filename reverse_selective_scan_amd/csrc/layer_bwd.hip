@@ -459,12 +459,135 @@ __global__ __launch_bounds__(256) void ln_gate_bwd_kernel(int Tn, int D, const T
 
 int ln_bwd_parts(int Tn) { return (Tn + kLnRowsPerBlock - 1) / kLnRowsPerBlock; }
 
+// The same for bf16 g and D a multiple of 512 (16-byte aligned rows): a block
+// is one wave and walks the same kLnRowsPerBlock rows; lane l owns columns
+// 512 c + 8 l .. +7 of every 512-column chunk c, read and written in 16-byte
+// (g) and 32-byte (o, dout) pieces.  Row statistics are wave sums (no block
+// barriers); the per-column sums stay in the lane's registers and leave as
+// the block's partial row, as above.
+template <int NC>
+__global__ __launch_bounds__(64) void ln_gate_bwd16_kernel(int Tn, int D, const bf16* __restrict__ g,
+                                                           const float* __restrict__ o,
+                                                           const float* __restrict__ gamma,
+                                                           const float* __restrict__ beta,
+                                                           const float* __restrict__ s, int no_ln, float eps,
+                                                           float* __restrict__ dout, float* __restrict__ part,
+                                                           float* __restrict__ gr) {
+  constexpr int V = 8 * NC;   // columns per lane
+  const int lane = lane_id();
+  const int row0 = blockIdx.x * kLnRowsPerBlock;
+  const float th = tanhf(s[0]);
+  const float invD = 1.0f / (float)D;
+  auto col = [&](int c) { return 512 * c + 8 * lane; };
+  float gm[V], bt[V], ax[V], ag[V];
+#pragma unroll
+  for (int c = 0; c < NC; ++c)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const f32x4 a = no_ln ? f32x4{} : *(const f32x4*)(gamma + col(c) + 4 * h);
+      const f32x4 b = no_ln ? f32x4{} : *(const f32x4*)(beta + col(c) + 4 * h);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        gm[8 * c + 4 * h + k] = a[k];
+        bt[8 * c + 4 * h + k] = b[k];
+        ax[8 * c + 4 * h + k] = ag[8 * c + 4 * h + k] = 0.0f;
+      }
+    }
+  const int nrows = min(kLnRowsPerBlock, Tn - row0);
+  for (int k = 0; k < nrows; ++k) {
+    const long row = row0 + k;
+    float x[V], gg[V];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const f32x4 a0 = *(const f32x4*)(o + row * D + col(c));
+      const f32x4 a1 = *(const f32x4*)(o + row * D + col(c) + 4);
+      const bf16x8 gv = *(const bf16x8*)(g + row * D + col(c));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) { x[8 * c + i] = a0[i]; x[8 * c + 4 + i] = a1[i]; }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) gg[8 * c + i] = (float)gv[i];
+    }
+    float dv[V];
+    if (no_ln) {
+      float p = 0.0f;
+#pragma unroll
+      for (int i = 0; i < V; ++i) {
+        dv[i] = th * gg[i];
+        p = fmaf(gg[i], x[i], p);
+      }
+      p = wave_sum(p);
+      if (lane == 0) gr[row] = (1.0f - th * th) * p;
+    } else {
+      float sum = 0.0f;
+#pragma unroll
+      for (int i = 0; i < V; ++i) sum += x[i];
+      const float mu = wave_sum(sum) * invD;
+      float sq = 0.0f;
+#pragma unroll
+      for (int i = 0; i < V; ++i) {
+        x[i] -= mu;
+        sq = fmaf(x[i], x[i], sq);
+      }
+      const float rstd = 1.0f / sqrtf(wave_sum(sq) * invD + eps);
+      float m1 = 0.0f, m2 = 0.0f, p = 0.0f;
+#pragma unroll
+      for (int i = 0; i < V; ++i) {
+        x[i] *= rstd;                                  // xhat
+        const float gg_gamma = gg[i] * gm[i];
+        m1 += gg_gamma;
+        m2 = fmaf(gg_gamma, x[i], m2);
+        p = fmaf(gg[i], fmaf(gm[i], x[i], bt[i]), p);
+        ax[i] = fmaf(th * gg[i], x[i], ax[i]);
+        ag[i] = fmaf(th, gg[i], ag[i]);
+      }
+      m1 = wave_sum(m1) * invD;
+      m2 = wave_sum(m2) * invD;
+      p = wave_sum(p);
+      if (lane == 0) gr[row] = (1.0f - th * th) * p;
+#pragma unroll
+      for (int i = 0; i < V; ++i) dv[i] = th * rstd * (gg[i] * gm[i] - m1 - x[i] * m2);
+    }
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      *(f32x4*)(dout + row * D + col(c)) = f32x4{dv[8 * c], dv[8 * c + 1], dv[8 * c + 2], dv[8 * c + 3]};
+      *(f32x4*)(dout + row * D + col(c) + 4) = f32x4{dv[8 * c + 4], dv[8 * c + 5], dv[8 * c + 6], dv[8 * c + 7]};
+    }
+  }
+  if (!no_ln && nrows > 0) {
+    float* pa = part + (long)blockIdx.x * 2 * D;
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int i0 = 8 * c + 4 * h;
+        *(f32x4*)(pa + col(c) + 4 * h) = f32x4{ax[i0], ax[i0 + 1], ax[i0 + 2], ax[i0 + 3]};
+        *(f32x4*)(pa + D + col(c) + 4 * h) = f32x4{ag[i0], ag[i0 + 1], ag[i0 + 2], ag[i0 + 3]};
+      }
+  }
+}
+
 template <typename T>
 hipError_t ln_gate_bwd(int Tn, int D, const T* g, const float* o, const float* gamma, const float* beta,
                        const float* s, bool no_ln, float eps, float* dout, float* part, float* gr, hipStream_t st) {
   if (Tn <= 0) return hipSuccess;
   dim3 grid(ln_bwd_parts(Tn)), block(256);
   const int cnt = (D / 4 + 63) / 64, nl = no_ln ? 1 : 0;   // columns per lane
+  if constexpr (std::is_same<T, bf16>::value) {
+    auto a16 = [](const void* p) { return ((uintptr_t)p & 15) == 0; };
+    const int nc = D / 512;
+    if (D % 512 == 0 && nc <= 4 && a16(g) && a16(o) && a16(dout) && a16(part) &&
+        (no_ln || (a16(gamma) && a16(beta)))) {
+#define R2L_LNB16(C)                                                                                             \
+  hipLaunchKernelGGL((ln_gate_bwd16_kernel<C>), grid, dim3(64), 0, st, Tn, D, g, o, gamma, beta, s, nl, eps, dout, \
+                     part, gr)
+      if (nc == 1) R2L_LNB16(1);
+      else if (nc == 2) R2L_LNB16(2);
+      else if (nc == 3) R2L_LNB16(3);
+      else R2L_LNB16(4);
+#undef R2L_LNB16
+      return hipGetLastError();
+    }
+  }
 #define R2L_LNB(V) \
   hipLaunchKernelGGL((ln_gate_bwd_kernel<T, V>), grid, block, 0, st, Tn, D, g, o, gamma, beta, s, nl, eps, dout, part, gr)
   if (cnt <= 1) R2L_LNB(1);

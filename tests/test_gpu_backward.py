@@ -283,6 +283,34 @@ def test_small_bf16_layer_bwd_matches_oracle(lens, saved):
     assert report("small bf16 ds (against |g| |r|)", e, TOL_GRAD_BF16) <= TOL_GRAD_BF16
 
 
+@pytest.mark.parametrize("use_ln", [True, False])
+@pytest.mark.parametrize("d_model", [512, 1536])
+def test_bf16_layer_bwd_wide_rows_matches_oracle(d_model, use_ln):
+    """d_model 512 and 1536: the LayerNorm backward's one-wave form, with one
+    and three 512-column chunks per lane, with and without the LayerNorm
+    (dgamma and dbeta are defined only with it)."""
+    lens = [5, 0, 130, 1, 300]
+    _case(f"bf16 layer bwd d_model={d_model} ln={use_ln} lens={lens}")
+    wl = synth.custom(lens, seed=43, h_kind="rms", d_model=d_model, d_inner=2 * d_model, dt_rank=32)
+    W = synth.make_weights(wl, affine_ln=True)
+    h, cu = synth.make_hidden(wl), wl.cu_seqlens()
+    g = synth.make_hidden(wl, hook=9)
+    ref = G.layer_grads(h, cu, W, float(W["s"]), g, factors=True, use_ln=use_ln)
+    dh, got = _layer_bwd_case(wl, W, h, cu, g, torch.bfloat16, 0 if use_ln else B.R2L_FLAG_NO_LN)
+    got["h"] = dh
+    tag = f"d_model {d_model} ln={use_ln}"
+    names = [n for n in GRAD_NAMES if use_ln or n not in ("ln_w", "ln_b")]
+    assert report(f"{tag} dh (max / RMS)", err_rms(got["h"], ref["h"]), TOL_GRAD_BF16) <= TOL_GRAD_BF16
+    assert _layer_err(rel_fro, got, ref, names + ["h"], TOL_GRAD_BF16, f"{tag} (Frobenius)") <= TOL_GRAD_BF16
+    for k, sc in ref["cs"].items():
+        if k in names:
+            assert report(f"{tag} d{k} (max / Cauchy-Schwarz scale)", cs_err(got[k], ref[k], sc),
+                          TOL_GRAD_BF16) <= TOL_GRAD_BF16
+    _, r = O.reverse_mamba_layer(h, cu, W, float(W["s"]), use_ln=use_ln, return_branch=True)
+    e = ds_err(got["s"].reshape(()), ref["s"], g, r, float(W["s"]))
+    assert report(f"{tag} ds (against |g| |r|)", e, TOL_GRAD_BF16) <= TOL_GRAD_BF16
+
+
 @pytest.mark.parametrize("saved", [False, True])
 def test_serve_b8_backward_suffix_matches_oracle(saved):
     """The serving shape (B=8 x 4128 tokens, D=2048, E=4096: the launch
