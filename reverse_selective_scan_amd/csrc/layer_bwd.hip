@@ -722,6 +722,159 @@ __global__ __launch_bounds__(256) void conv_bwd_kernel(int Tn, int E, const T* _
   }
 }
 
+// The same walk for bf16 with 8 channels per lane (E a multiple of 512;
+// x, dx, du, du2 and the taps 16-byte aligned, ld_x and ld_dx multiples of
+// 8): a wave covers 512 channels of its run of rows, every access a 16- or
+// 32-byte piece of a token row.  The control flow (rows, sequence bounds) is
+// the wave's as above; per channel the arithmetic is the same, in the same
+// order, so dx and the partial sums are the same bits.
+__global__ __launch_bounds__(256) void conv_bwd16_kernel(int Tn, int E, const bf16* __restrict__ x, long ld_x,
+                                                         const bf16* __restrict__ cw, const bf16* __restrict__ cb,
+                                                         const float* __restrict__ du, const float* __restrict__ du2,
+                                                         bf16* __restrict__ dx, long ld_dx, float* __restrict__ part,
+                                                         const int32_t* __restrict__ cu, int nseq) {
+  constexpr int C = 8;
+  const int nb = gridDim.y, b = blockIdx.y;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int e = (blockIdx.x * 64 + lane) * C;   // the lane's first channel
+  const long r0 = (long)Tn * b / nb, r1 = (long)Tn * (b + 1) / nb;
+  const int ra = (int)(r0 + (r1 - r0) * wv / 4), rz = (int)(r0 + (r1 - r0) * (wv + 1) / 4);
+  float w[C][KC_], bias[C];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const bf16x8 tv = *(const bf16x8*)(cw + (long)e * KC_ + 8 * q);   // taps of channels e + 2q, e + 2q + 1
+#pragma unroll
+    for (int k = 0; k < 8; ++k) w[2 * q + k / KC_][k % KC_] = (float)tv[k];
+  }
+  {
+    const bf16x8 bv = *(const bf16x8*)(cb + e);
+#pragma unroll
+    for (int c = 0; c < C; ++c) bias[c] = (float)bv[c];
+  }
+  typedef float fv8 __attribute__((ext_vector_type(8)));
+  auto xat = [&](int t) __attribute__((always_inline)) {
+    fv8 v = {};
+    if (t < Tn) {
+      const bf16x8 q = *(const bf16x8*)(x + (long)t * ld_x + e);
+#pragma unroll
+      for (int c = 0; c < C; ++c) v[c] = (float)q[c];
+    }
+    return v;
+  };
+  auto gat = [&](int t) __attribute__((always_inline)) {
+    const long i = (long)t * E + e;
+    const f32x4 a0 = *(const f32x4*)(du + i), a1 = *(const f32x4*)(du + i + 4);
+    fv8 v = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+    if (du2) {
+      const f32x4 b0 = *(const f32x4*)(du2 + i), b1 = *(const f32x4*)(du2 + i + 4);
+      const fv8 u = {b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
+#pragma unroll
+      for (int c = 0; c < C; ++c) v[c] = v[c] + u[c];
+    }
+    return v;
+  };
+  // dc of channel c at t from the window x_t .. x_{t+3}, n = rows of it inside the sequence (>= 1)
+  auto dc_of = [&](int c, float g, float x0, float x1, float x2, float x3, int n) __attribute__((always_inline)) {
+    float cc = fmaf(w[c][KC_ - 1], x0, bias[c]);
+    cc = fmaf(w[c][KC_ - 2], n > 1 ? x1 : 0.0f, cc);
+    cc = fmaf(w[c][KC_ - 3], n > 2 ? x2 : 0.0f, cc);
+    cc = fmaf(w[c][KC_ - 4], n > 3 ? x3 : 0.0f, cc);
+    const float sg = sigmoid_fast(cc);
+    return g * sg * fmaf(cc, 1.0f - sg, 1.0f);
+  };
+  float acc[C][KC_ + 1];
+#pragma unroll
+  for (int c = 0; c < C; ++c)
+#pragma unroll
+    for (int k = 0; k <= KC_; ++k) acc[c][k] = 0.0f;
+  if (ra < rz) {
+    int q = 0;
+    {
+      int lo = 0, hi = nseq;   // the last q with cu[q] <= ra
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (cu[mid] <= ra) lo = mid; else hi = mid;
+      }
+      q = lo;
+    }
+    int sl = cu[q], se = max(cu[q + 1], ra + 1);
+    fv8 d1 = {}, d2 = {}, d3 = {};
+    {
+      fv8 xs[6];
+#pragma unroll
+      for (int i = 0; i < 6; ++i) xs[i] = ra - 3 + i >= sl ? xat(ra - 3 + i) : fv8{};
+      if (ra - 1 >= sl) {
+        const fv8 g = gat(ra - 1);
+#pragma unroll
+        for (int c = 0; c < C; ++c) d1[c] = dc_of(c, g[c], xs[2][c], xs[3][c], xs[4][c], xs[5][c], se - (ra - 1));
+      }
+      if (ra - 2 >= sl) {
+        const fv8 g = gat(ra - 2);
+#pragma unroll
+        for (int c = 0; c < C; ++c) d2[c] = dc_of(c, g[c], xs[1][c], xs[2][c], xs[3][c], xs[4][c], se - (ra - 2));
+      }
+      if (ra - 3 >= sl) {
+        const fv8 g = gat(ra - 3);
+#pragma unroll
+        for (int c = 0; c < C; ++c) d3[c] = dc_of(c, g[c], xs[0][c], xs[1][c], xs[2][c], xs[3][c], se - (ra - 3));
+      }
+    }
+    fv8 x0 = xat(ra), x1 = xat(ra + 1), x2 = xat(ra + 2);
+    auto step = [&](int t, const fv8& g, const fv8& x3) __attribute__((always_inline)) {
+      const int n = se - t;
+      bf16x8 o;
+      fv8 d;
+#pragma unroll
+      for (int c = 0; c < C; ++c) {
+        d[c] = dc_of(c, g[c], x0[c], x1[c], x2[c], x3[c], n);
+        const float v = fmaf(w[c][KC_ - 1], d[c], fmaf(w[c][KC_ - 2], d1[c], fmaf(w[c][KC_ - 3], d2[c], w[c][KC_ - 4] * d3[c])));
+        o[c] = from_f32<bf16>(v);
+        acc[c][KC_ - 1] = fmaf(d[c], x0[c], acc[c][KC_ - 1]);
+        acc[c][KC_ - 2] = fmaf(d[c], n > 1 ? x1[c] : 0.0f, acc[c][KC_ - 2]);
+        acc[c][KC_ - 3] = fmaf(d[c], n > 2 ? x2[c] : 0.0f, acc[c][KC_ - 3]);
+        acc[c][KC_ - 4] = fmaf(d[c], n > 3 ? x3[c] : 0.0f, acc[c][KC_ - 4]);
+        acc[c][KC_] += d[c];
+      }
+      *(bf16x8*)(dx + (long)t * ld_dx + e) = o;
+      d3 = d2; d2 = d1; d1 = d;
+      x0 = x1; x1 = x2; x2 = x3;
+    };
+    int t = ra;
+    while (t < rz) {
+      if (t >= se) {   // next non-empty sequence; the dc history starts over
+        while (q + 1 < nseq && cu[q + 1] <= t) ++q;
+        sl = cu[q];
+        se = max(cu[q + 1], t + 1);
+        d1 = d2 = d3 = fv8{};
+      }
+      if (t + 2 <= rz && t + 2 <= se) {
+        // two rows of one sequence: every load first
+        const fv8 xa = xat(t + 3), xb = xat(t + 4), ga = gat(t), gb = gat(t + 1);
+        step(t, ga, xa);
+        step(t + 1, gb, xb);
+        t += 2;
+      } else {
+        step(t, gat(t), xat(t + 3));
+        t += 1;
+      }
+    }
+  }
+  __shared__ float red[4][KC_ + 1][64 * C];
+#pragma unroll
+  for (int c = 0; c < C; ++c)
+#pragma unroll
+    for (int k = 0; k <= KC_; ++k) red[wv][k][lane * C + c] = acc[c][k];
+  __syncthreads();
+  if (wv == 0) {
+#pragma unroll
+    for (int c = 0; c < C; ++c)
+#pragma unroll
+      for (int k = 0; k <= KC_; ++k)
+        part[((long)b * E + e + c) * (KC_ + 1) + k] =
+            ((red[0][k][lane * C + c] + red[1][k][lane * C + c]) + red[2][k][lane * C + c]) + red[3][k][lane * C + c];
+  }
+}
+
 __global__ __launch_bounds__(256) void conv_wsum_kernel(int E, int nb, const float* __restrict__ part,
                                                         float* __restrict__ dw, float* __restrict__ db) {
   const long i = blockIdx.x * 256L + threadIdx.x;
@@ -743,8 +896,18 @@ hipError_t conv_bwd(int Tn, int E, const T* x, long ld_x, const T* cw, const T* 
                     hipStream_t st) {
   if (Tn <= 0) return hipSuccess;
   const int nb = conv_bwd_parts(Tn);
-  hipLaunchKernelGGL((conv_bwd_kernel<T, T>), dim3(E / 64, nb), dim3(256), 0, st, Tn, E, x, ld_x, cw, cb, du, du2,
-                     dx, ld_dx, part, cu, nseq);
+  bool wide = false;
+  if constexpr (std::is_same<T, bf16>::value) {
+    auto a16 = [](const void* p) { return ((uintptr_t)p & 15) == 0; };
+    wide = E % 512 == 0 && ld_x % 8 == 0 && ld_dx % 8 == 0 && a16(x) && a16(dx) && a16(du) && (!du2 || a16(du2)) &&
+           a16(cw) && a16(cb);
+    if (wide)
+      hipLaunchKernelGGL(conv_bwd16_kernel, dim3(E / 512, nb), dim3(256), 0, st, Tn, E, x, ld_x, cw, cb, du, du2, dx,
+                         ld_dx, part, cu, nseq);
+  }
+  if (!wide)
+    hipLaunchKernelGGL((conv_bwd_kernel<T, T>), dim3(E / 64, nb), dim3(256), 0, st, Tn, E, x, ld_x, cw, cb, du, du2,
+                       dx, ld_dx, part, cu, nseq);
   hipLaunchKernelGGL(conv_wsum_kernel, dim3((E * (KC_ + 1) + 255) / 256), dim3(256), 0, st, E, nb,
                      (const float*)part, dw, db);
   return hipGetLastError();
