@@ -43,6 +43,8 @@ R2L_DEV int block_exclusive_scan(int v, int* buf) {
   return excl;
 }
 
+constexpr int kLongestFirstMaxSeq = 256;
+
 // buf: 256 ints of LDS (only the first four are used)
 R2L_DEV void plan_chunks_block(const PlanArgs& p, int* buf) {
   const int tid = threadIdx.x;
@@ -76,9 +78,26 @@ R2L_DEV void plan_chunks_block(const PlanArgs& p, int* buf) {
   int base = block_exclusive_scan<false>(cnt, buf);
   int slot = block_exclusive_scan<false>(slots, buf);
   if (tid == 255) *p.n_chunks = min(base + cnt, max_chunks);
+  // When Lc covers the token count every non-empty sequence is one chunk
+  // and no chunk refers to another, so the table lists them longest first
+  // (ties in sequence order): the scans launch their blocks in table order,
+  // and the longest sequences then start first, a greedy longest-first
+  // schedule over the CUs.  (Quadratic in the sequence count, so only for a
+  // few hundred sequences; chunked tables keep sequence order, since a
+  // chunk's carry reads the summaries of its sequence's earlier entries.)
+  const bool longest_first = Lc >= Tn && nseq <= kLongestFirstMaxSeq;
   for (int q = sa; q < sb; ++q) {
     const int slo = p.cu_clean[q], send = p.cu_clean[q + 1];
     const int nc = (send - slo + Lc - 1) / Lc;
+    if (longest_first && nc == 1) {
+      const int len = send - slo;
+      int rank = 0;
+      for (int q2 = 0; q2 < nseq; ++q2) {
+        const int l2 = p.cu_clean[q2 + 1] - p.cu_clean[q2];
+        rank += l2 > len || (l2 == len && q2 < q);
+      }
+      base = rank;
+    }
     for (int j = 0; j < nc; ++j) {
       if (base + j >= max_chunks) break;
       ChunkDesc d;
