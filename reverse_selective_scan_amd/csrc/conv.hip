@@ -375,7 +375,7 @@ __global__ __launch_bounds__(256) void conv_xproj_kernel(int Tn, int E, int P,
 
 // out[i] = sum over k < ks of slab[k][i] (slab stride n), in order of k.
 // A thread owns 4 consecutive elements and loads all of its slabs (up to
-// 16) before adding, so the loads are in flight together.
+// 32) before adding, so the loads are in flight together.
 // dsplit (optional): also the delta split of the sum (out is [n / P, P]).
 __global__ __launch_bounds__(256) void sum_slabs_kernel(long n, int ks, const float* __restrict__ slab,
                                                         float* __restrict__ out, int P, int R, int RP,
@@ -383,13 +383,13 @@ __global__ __launch_bounds__(256) void sum_slabs_kernel(long n, int ks, const fl
   const long i = (blockIdx.x * 256L + threadIdx.x) * 4;
   if (i >= n) return;
   if (i + 4 <= n && (n & 3) == 0) {
-    f32x4 v[16];
+    f32x4 v[32];
 #pragma unroll
-    for (int k = 0; k < 16; ++k)
+    for (int k = 0; k < 32; ++k)
       if (k < ks) v[k] = *(const f32x4*)(slab + k * n + i);
     f32x4 acc = v[0];
 #pragma unroll
-    for (int k = 1; k < 16; ++k)
+    for (int k = 1; k < 32; ++k)
       if (k < ks) acc += v[k];
     *(f32x4*)(out + i) = acc;
     if (dsplit != nullptr)
@@ -421,7 +421,7 @@ hipError_t conv_xproj_bf16(int Tn, int E, int P, const bf16* x, long ld_x, const
   // (each wave keeps at least one 16-channel step), partial sums in ws.
   int ks = 1;
   if (ws != nullptr && u_out == nullptr && ncu > 0) {
-    while (ks < 16 && ntiles * ks * 2 <= ncu && (E / (ks * 2)) % 64 == 0 &&
+    while (ks < 32 && ntiles * ks * 2 <= ncu && (E / (ks * 2)) % 64 == 0 &&
            (size_t)(ks * 2) * Tn * P * sizeof(float) <= ws_bytes)
       ks *= 2;
   }
@@ -443,7 +443,7 @@ hipError_t conv_xproj_bf16(int Tn, int E, int P, const bf16* x, long ld_x, const
     default: return hipErrorInvalidValue;
   }
 #undef R2L_CX
-  if (ks > 1) {   // (ks <= 16, as sum_slabs_kernel needs)
+  if (ks > 1) {   // (ks <= 32, as sum_slabs_kernel needs)
     const long n = (long)Tn * P;
     hipLaunchKernelGGL(sum_slabs_kernel, dim3((unsigned)((n / 4 + 255) / 256 + 1)), dim3(256), 0, st, n, ks,
                        (const float*)ws, xdbl, P, R, RP, dsplit);
