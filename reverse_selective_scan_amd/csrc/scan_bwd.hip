@@ -199,6 +199,10 @@ __global__ __launch_bounds__(256, 2) void scan_bwd_adj_kernel(ScanBwdArgs a) {
     if (q > 0) issue(blo_of(q - 1), bhi_of(q - 1));
     __syncthreads();
     // ---------------- B1: the sub-block's states, right to left ----------------
+    // (the two recurrences at raised wave priority: each is one wave's
+    // dependency chain, and the other wave on the SIMD, in phase A or C,
+    // fills the gaps it leaves; measured 1.5% faster)
+    __builtin_amdgcn_s_setprio(2);
     const float* bsrc = (const float*)&bc_s[0][w] + (lane & 3);   // B_t[4 w + (lane & 3)] at row 0
     f32x4 hs[SB];
     {
@@ -250,6 +254,7 @@ __global__ __launch_bounds__(256, 2) void scan_bwd_adj_kernel(ScanBwdArgs a) {
         *(float2*)&dbc_s[r][col] = make_float2(y0, y1);
       }
     }
+    __builtin_amdgcn_s_setprio(0);
     __syncthreads();
     // ---------------- C: du, ddt; the sub-block's dB | dC ----------------
     {
